@@ -1,0 +1,254 @@
+"""CPU oracle for block-sparse attention with summary rows.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The product path (the HIP library
+and its Python binding) never imports, calls or falls back to it, and this
+module imports nothing from the product path.  It is deliberately plain and
+slow: numpy, float64 arithmetic, one query block at a time.
+
+What it computes, per (batch, head), with inputs of shape [N, d] (bfloat16
+values widened exactly to float):
+
+Sources (page titles and sections):
+  * "h3-sparse-attn 0.1.0" (PyPI page), opening paragraph: each query block
+    attends to its top-k key blocks of 128 tokens, and every skipped key block
+    is folded back in as one summary row; top_k counts 128-token key blocks
+    (section "Use"); bf16, head_dim 128, forward only.
+  * "Spark-H3: Block Sparse Attention Speeds Up MiniMax-H3 in ComfyUI",
+    section "What Spark-Attn changes": the exact branch computes the
+    top-ranked key/value blocks in full, the compressed branch covers the rest
+    cheaply; Spark-Reweight replaces the mean-pooled summary with weighted
+    summaries plus a log-mass bias, anchored on the mean of the video queries
+    of each head, because mean pooling puts exp(E[x]) where the attention mass
+    is E[exp(x)]; the caption of that section's figure states that the pooled
+    logit plus the bias exponentiates to the expected exponential.
+
+Readings taken where the pages are silent (each is exercised by a test):
+  R1 ragged last block: pooled by its real row count; its exact keys are its
+     real rows only.
+  R2 block score: plain dot product of the pooled query and key vectors (the
+     softmax scale does not change a ranking).
+  R3 ties: equal scores go to the lower block index; output ascending.
+  R4 no forced blocks (no diagonal or sink block is added to the top-k).
+  R5 a top-k ratio budget becomes k = ceil(ratio * n_blocks) computed exactly.
+  R6 softmax scale 1/sqrt(d) for exact and summary logits alike; the bias is
+     added in scaled-logit units.
+  R7 one summary row per skipped block, with no log(row count) mass term.
+  R8 reweight: summary key = softmax-weighted key rows, summary value =
+     softmax-weighted value rows, with weights softmax over the block of the
+     anchor logits a.k_j/sqrt(d); bias = log(mean_j exp(a.k_j/sqrt(d)))
+     - a.kbar/sqrt(d) with kbar the plain block mean of the keys.
+  R9 anchor = mean of the query rows [0, anchor_rows) (the video rows, which
+     lead the sequence); anchor_rows = 0 means all rows.
+  R10 selection uses the mean-pooled vectors in both summary modes.
+  R11 no causal mask.
+
+Precision: pooled vectors are summed in float64 and stored as float32 (the
+precision in which a block ranking is decided); block scores are float64 dot
+products of those float32 vectors; everything else is float64.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+BLOCK = 128
+
+
+# ----------------------------------------------------------------- blocks ---
+def n_blocks(N: int, block: int = BLOCK) -> int:
+    """Number of key/query blocks: ceil(N / block) (PyPI page, opening
+    paragraph: the sequence is cut into 128-token blocks)."""
+    return -(-N // block)
+
+
+def block_rows(N: int, block: int = BLOCK):
+    """[(start, end)] row ranges of every block; the last one may be short (R1)."""
+    return [(s, min(s + block, N)) for s in range(0, N, block)]
+
+
+def effective_k(top_k: int, nb: int) -> int:
+    """Key blocks kept per query block: top_k, capped at the number of blocks."""
+    if top_k < 0:
+        raise ValueError("top_k must be >= 0")
+    return min(top_k, nb)
+
+
+def k_from_ratio(ratio, nb: int) -> int:
+    """Top-k ratio budget (Spark-H3 page, "Workflows": topk_mode=topk_ratio)
+    turned into a block count, k = ceil(ratio * nb), in exact rational
+    arithmetic on the decimal string of the ratio (R5)."""
+    r = Fraction(str(ratio))
+    if r < 0 or r > 1:
+        raise ValueError("ratio must lie in [0, 1]")
+    return math.ceil(r * nb)
+
+
+# ------------------------------------------------------------------- pool ---
+def pool_mean(x: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """Per-block mean of the rows of x [N, d]: one pooled vector per block.
+
+    Summed in float64, divided by the block's real row count (R1), stored as
+    float32.  Spark-H3 page, "What Spark-Attn changes" (mean-pooled summary)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = []
+    for s, e in block_rows(x.shape[0], block):
+        out.append(x[s:e].sum(axis=0) / (e - s))
+    return np.array(out, dtype=np.float64).astype(np.float32)
+
+
+# ----------------------------------------------------------------- select ---
+def block_scores(q_pool: np.ndarray, k_pool: np.ndarray) -> np.ndarray:
+    """s[r, c] = q_pool[r] . k_pool[c] in float64 (R2).
+
+    Every element is reduced by the same code path, so two identical key
+    blocks score bit-identically against any query block."""
+    qp = np.asarray(q_pool, dtype=np.float64)
+    kp = np.asarray(k_pool, dtype=np.float64)
+    return (qp[:, None, :] * kp[None, :, :]).sum(axis=-1)
+
+
+def select_topk(scores: np.ndarray, top_k: int) -> np.ndarray:
+    """For each query block r the k key blocks of largest score, ties to the
+    lower index (R3), returned in ascending index order; int32 [nb, k].
+
+    PyPI page, opening paragraph ("attends to its top-k key blocks")."""
+    nq, nk = scores.shape
+    k = effective_k(top_k, nk)
+    idx = np.zeros((nq, k), dtype=np.int32)
+    for r in range(nq):
+        order = sorted(range(nk), key=lambda c: (-scores[r, c], c))
+        idx[r] = sorted(order[:k])
+    return idx
+
+
+# -------------------------------------------------------------- summaries ---
+def summaries_mean(k: np.ndarray, v: np.ndarray, block: int = BLOCK):
+    """Mean mode: summary key/value of block c are the block means; bias 0.
+
+    Returns float64 (sum_k [nb, d], sum_v [nb, d], bias [nb])."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    rows = block_rows(k.shape[0], block)
+    sk = np.array([k[s:e].mean(axis=0) for s, e in rows])
+    sv = np.array([v[s:e].mean(axis=0) for s, e in rows])
+    return sk, sv, np.zeros(len(rows))
+
+
+def anchor(q: np.ndarray, anchor_rows: int) -> np.ndarray:
+    """Per-head anchor: the mean of the query rows [0, anchor_rows) (R9;
+    Spark-H3 page, "What Spark-Attn changes": the mean of the video queries is
+    one anchor per head).  anchor_rows = 0 means every row."""
+    q = np.asarray(q, dtype=np.float64)
+    n = q.shape[0] if anchor_rows == 0 else anchor_rows
+    if not 0 < n <= q.shape[0]:
+        raise ValueError("anchor_rows out of range")
+    return q[:n].sum(axis=0) / n
+
+
+def summaries_reweight(k: np.ndarray, v: np.ndarray, a: np.ndarray, scale: float,
+                       block: int = BLOCK, bias_ref: str = "mean"):
+    """Spark-Reweight summaries (R8).
+
+    For block c with rows j:  l_j = scale * a . k_j,  w = softmax_c(l),
+    sum_k = sum_j w_j k_j,  sum_v = sum_j w_j v_j,
+    bias = log(mean_j exp(l_j)) - scale * a . kbar_c  (bias_ref="mean"), or
+    bias = log(mean_j exp(l_j)) - scale * a . sum_k   (bias_ref="weighted").
+
+    The log-mean-exp is evaluated as max + log(sum exp(l - max)) - log(n_c).
+    Spark-H3 page, "What Spark-Attn changes" (weighted summaries plus a
+    log-mass bias; exp(E[x]) versus E[exp(x)])."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    sks, svs, bs = [], [], []
+    for s, e in block_rows(k.shape[0], block):
+        kb, vb = k[s:e], v[s:e]
+        l = scale * (kb @ a)
+        m = l.max()
+        ex = np.exp(l - m)
+        w = ex / ex.sum()
+        sk = w @ kb
+        sv = w @ vb
+        lme = m + math.log(ex.sum()) - math.log(e - s)
+        ref = kb.mean(axis=0) if bias_ref == "mean" else sk
+        sks.append(sk)
+        svs.append(sv)
+        bs.append(lme - scale * float(ref @ a))
+    return np.array(sks), np.array(svs), np.array(bs)
+
+
+# -------------------------------------------------------------- attention ---
+def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK):
+    """Block-sparse attention with summary rows for one (batch, head).
+
+    For query i in block r, the logits are
+      [scale * q_i . k_j  for every row j of every selected block c in idx[r]]
+      ++ [scale * q_i . sum_k[c] + bias[c]  for every block c not in idx[r]],
+    one softmax runs over that whole list, and the output is the matching
+    weighted sum of [v_j ...] ++ [sum_v[c] ...].  PyPI page, opening paragraph
+    (top-k blocks plus one summary row per skipped block); Spark-H3 page,
+    "What Spark-Attn changes" (exact and compressed branches of one pass).
+
+    idx may be any [nb, k] array of distinct valid block indices per row (the
+    output is unique given idx).  Returns float64 [N, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    sum_k = np.asarray(sum_k, dtype=np.float64)
+    sum_v = np.asarray(sum_v, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    N, d = q.shape
+    rows = block_rows(N, block)
+    nb = len(rows)
+    out = np.zeros((N, d))
+    for r, (s, e) in enumerate(rows):
+        sel = [int(c) for c in idx[r]]
+        if len(set(sel)) != len(sel) or any(c < 0 or c >= nb for c in sel):
+            raise ValueError("idx row %d is not a set of valid blocks" % r)
+        chosen = set(sel)
+        skipped = [c for c in range(nb) if c not in chosen]
+        keys = [k[rows[c][0]:rows[c][1]] for c in sorted(chosen)] + [sum_k[skipped]]
+        vals = [v[rows[c][0]:rows[c][1]] for c in sorted(chosen)] + [sum_v[skipped]]
+        add = [np.zeros(rows[c][1] - rows[c][0]) for c in sorted(chosen)] + [bias[skipped]]
+        K = np.concatenate(keys, axis=0)
+        V = np.concatenate(vals, axis=0)
+        B = np.concatenate(add)
+        logits = scale * (q[s:e] @ K.T) + B[None, :]
+        logits -= logits.max(axis=1, keepdims=True)
+        p = np.exp(logits)
+        p /= p.sum(axis=1, keepdims=True)
+        out[s:e] = p @ V
+    return out
+
+
+# -------------------------------------------------------------- pipeline ---
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
+             scale: float | None = None, block: int = BLOCK, bias_ref: str = "mean"):
+    """All four stages for one (batch, head).  Returns a dict with the pooled
+    vectors, scores, selection, summaries and the float64 output."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d = q.shape[1]
+    sc = default_scale(d) if not scale else float(scale)
+    q_pool = pool_mean(q, block)
+    k_pool = pool_mean(k, block)
+    s = block_scores(q_pool, k_pool)
+    idx = select_topk(s, top_k)
+    if summary == "mean":
+        sk, sv, b = summaries_mean(k, v, block)
+    elif summary == "reweight":
+        a = anchor(q, anchor_rows)
+        sk, sv, b = summaries_reweight(k, v, a, sc, block, bias_ref)
+    else:
+        raise ValueError("summary must be 'mean' or 'reweight'")
+    out = attention(q, k, v, idx, sk, sv, b, sc, block)
+    return dict(q_pool=q_pool, k_pool=k_pool, scores=s, idx=idx, sum_k=sk,
+                sum_v=sv, bias=b, out=out, scale=sc)

@@ -1,0 +1,503 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: a library
+routine that the method reduces to in a special case (torch's CPU scaled-dot-
+product attention in float64), a closed form derived by hand, a brute-force
+search, or an invariant.  The last group plants plausible mistakes in the
+oracle and shows that some pin fails for each.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import bsa_oracle as O
+from block_sparse_attention_25_amd.synth import WORKLOADS, bf16_to_f32, custom, generate
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+D = 128
+
+
+def _rand_head(N, seed, d=D):
+    rng = np.random.default_rng(seed)
+    return [rng.standard_normal((N, d)) for _ in range(3)]
+
+
+def _synth_head(N, seed=0, h=0):
+    w = custom(N, heads=h + 1, seed=seed)
+    q, k, v = generate(w, heads=[h], threads=1)
+    return [bf16_to_f32(t[0, 0]).astype(np.float64) for t in (q, k, v)]
+
+
+def _sdpa(q, k, v, mask=None):
+    """torch CPU float64 scaled-dot-product attention (scale 1/sqrt(d))."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))[None, None]
+                  for x in (q, k, v))
+    tm = None if mask is None else torch.from_numpy(mask)[None, None]
+    return F.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm)[0, 0].numpy()
+
+
+# ------------------------------------------------------------ page values ---
+def test_page_workloads_block_layout():
+    """The pages' sequence lengths cut into 128-token blocks: the blocks tile
+    [0, N) without gaps or overlap, every block but the last holds 128 rows,
+    and the number of blocks leaves top_k=64 a strict subset."""
+    g = json.load(open(os.path.join(HERE, "golden", "pages_workloads.json")))
+    B = g["block_tokens"]
+    for name, N in g["sequence_lengths"].items():
+        rows = O.block_rows(N, B)
+        assert rows[0][0] == 0 and rows[-1][1] == N
+        assert all(a[1] == b[0] for a, b in zip(rows, rows[1:]))
+        assert all(e - s == B for s, e in rows[:-1])
+        assert 1 <= rows[-1][1] - rows[-1][0] <= B
+        assert O.n_blocks(N, B) == len(rows)
+        assert (len(rows) - 1) * B < N <= len(rows) * B
+        assert O.effective_k(g["top_k"], len(rows)) == g["top_k"]
+    # the synthetic workloads reproduce the pages' lengths exactly
+    ours = {"768p 5s": "768p_5s", "768p 10s": "768p_10s", "768p 15s": "768p_15s_reweight",
+            "2K 5s": "2k_5s"}
+    for page_name, key in ours.items():
+        assert WORKLOADS[key].seq_len == g["sequence_lengths"][page_name]
+        assert WORKLOADS[key].heads == g["heads"]
+
+
+def test_k_from_ratio_exact():
+    g = json.load(open(os.path.join(HERE, "golden", "pages_workloads.json")))
+    for r in g["topk_ratios"]:
+        for nb in (1, 7, 100, 295, 813, 1045):
+            k = O.k_from_ratio(r, nb)
+            # smallest integer with k >= ratio * nb, checked by rational comparison
+            assert Fraction(k) >= Fraction(r) * nb > Fraction(k - 1)
+    # decimal ratios whose float product misrounds upward
+    assert O.k_from_ratio(0.07, 100) == 7
+    assert O.k_from_ratio(0.55, 100) == 55
+    assert O.k_from_ratio("0.1", 813) == 82
+    assert O.k_from_ratio(0, 50) == 0 and O.k_from_ratio(1, 50) == 50
+
+
+# ------------------------------------------------------------------- pool ---
+@pytest.mark.parametrize("N", [128, 200, 300, 4076])
+def test_pool_closed_forms(N):
+    d = 8
+    # row j holds the value j in every column: block mean = (s + e - 1) / 2
+    x = np.repeat(np.arange(N, dtype=np.float64)[:, None], d, axis=1)
+    p = O.pool_mean(x)
+    for c, (s, e) in enumerate(O.block_rows(N)):
+        assert np.all(p[c] == np.float32((s + e - 1) / 2))
+    # constant rows inside every block: the mean is that row, also in a ragged
+    # tail (zero padding to 128 rows would shrink it)
+    rng = np.random.default_rng(1)
+    rows = O.block_rows(N)
+    const = rng.standard_normal((len(rows), d))
+    x = np.concatenate([np.repeat(const[c:c + 1], e - s, axis=0) for c, (s, e) in enumerate(rows)])
+    assert np.array_equal(O.pool_mean(x), const.astype(np.float32))
+    assert O.pool_mean(x).dtype == np.float32
+
+
+def test_pool_permutation_invariant():
+    q, _, _ = _synth_head(300)
+    perm = np.arange(300)
+    perm[128:256] = 128 + np.random.default_rng(3).permutation(128)
+    assert np.array_equal(O.pool_mean(q), O.pool_mean(q[perm]))
+
+
+# ----------------------------------------------------------------- select ---
+def _brute_force_select(s_row, k):
+    """The unique k-subset S such that every member beats every non-member:
+    higher score, or equal score and lower index.  Found by checking every
+    subset (tiny nb only)."""
+    import itertools
+    nb = len(s_row)
+    found = []
+    for S in itertools.combinations(range(nb), k):
+        Sset = set(S)
+        ok = all(s_row[a] > s_row[b] or (s_row[a] == s_row[b] and a < b)
+                 for a in Sset for b in range(nb) if b not in Sset)
+        if ok:
+            found.append(list(S))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("N", [128, 200, 384, 500, 512])
+def test_select_brute_force(N):
+    q, k, _ = _synth_head(N, seed=N)
+    qp, kp = O.pool_mean(q), O.pool_mean(k)
+    s = O.block_scores(qp, kp)
+    nb = O.n_blocks(N)
+    for top_k in range(0, nb + 2):
+        idx = O.select_topk(s, top_k)
+        kk = min(top_k, nb)
+        assert idx.shape == (nb, kk)
+        for r in range(nb):
+            assert list(idx[r]) == _brute_force_select(s[r], kk)
+
+
+def test_block_scores_exact_products():
+    # small integers: every product and sum is exact, so the score is known
+    qp = np.array([[1, 2, 3], [0, -1, 4]], dtype=np.float32)
+    kp = np.array([[2, 0, 1], [1, 1, 1], [-3, 2, 5]], dtype=np.float32)
+    s = O.block_scores(qp, kp)
+    assert np.array_equal(s, np.array([[5, 6, 16], [4, 3, 18]], dtype=np.float64))
+
+
+def test_select_exact_ties_go_to_lower_index():
+    N = 512
+    q, k, _ = _synth_head(N, seed=7)
+    # copy key block 1 into block 3: their scores tie bit-exactly everywhere
+    k = k.copy()
+    k[384:512] = k[128:256]
+    s = O.block_scores(O.pool_mean(q), O.pool_mean(k))
+    assert np.array_equal(s[:, 1], s[:, 3])
+    for r in range(4):
+        order = sorted(range(4), key=lambda c: -s[r, c])
+        # pick k so that exactly one of the tied pair fits
+        pos1 = order.index(1)
+        pos3 = order.index(3)
+        kk = min(pos1, pos3) + 1
+        sel = list(O.select_topk(s, kk)[r])
+        assert 1 in sel and 3 not in sel
+    # negative zero ties with positive zero
+    s0 = np.array([[0.0, -0.0, 1.0, -0.0]])
+    assert list(O.select_topk(s0, 2)[0]) == [0, 2]
+
+
+# -------------------------------------------------------------- attention ---
+@pytest.mark.parametrize("N", [128, 300, 512, 1000])
+def test_topk_all_blocks_is_dense_attention(N):
+    """top_k = n_blocks: no compressed branch; must equal dense softmax attention."""
+    q, k, v = _synth_head(N, seed=11)
+    res = O.run_head(q, k, v, top_k=O.n_blocks(N))
+    ref = _sdpa(q, k, v)
+    assert np.abs(res["out"] - ref).max() < 1e-10
+
+
+def test_dense_on_generator_tiny_head():
+    w = WORKLOADS["tiny"]
+    qb, kb, vb = generate(w, heads=[1], threads=1)
+    q, k, v = (bf16_to_f32(t[0, 0]).astype(np.float64) for t in (qb, kb, vb))
+    res = O.run_head(q, k, v, top_k=10 ** 6)
+    assert np.abs(res["out"] - _sdpa(q, k, v)).max() < 1e-10
+
+
+@pytest.mark.parametrize("N,summary", [(128, "mean"), (300, "mean"), (900, "mean"),
+                                       (300, "reweight"), (900, "reweight")])
+def test_topk_zero_is_summary_attention(N, summary):
+    """top_k = 0: only summary rows; equals attention over the summary keys and
+    values with the bias as an additive mask."""
+    q, k, v = _synth_head(N, seed=5)
+    res = O.run_head(q, k, v, top_k=0, summary=summary)
+    ref = _sdpa(q, res["sum_k"], res["sum_v"],
+                mask=np.repeat(res["bias"][None, :], N, axis=0))
+    assert np.abs(res["out"] - ref).max() < 1e-10
+    if N <= 128:
+        # one block and no exact keys: every query returns the one summary value
+        assert np.abs(res["out"] - res["sum_v"][0][None, :]).max() < 1e-12
+
+
+def _mask_formulation(q, k, v, idx, sk, sv, b):
+    """Independent formulation of the mixed case: one dense attention per
+    query block over all N keys followed by all nb summary rows, with an
+    additive mask: 0 for rows of selected blocks, -inf for rows of skipped
+    blocks, bias for summaries of skipped blocks, -inf for summaries of
+    selected blocks."""
+    N = q.shape[0]
+    rows = O.block_rows(N)
+    nb = len(rows)
+    Kc = np.concatenate([k, sk])
+    Vc = np.concatenate([v, sv])
+    out = np.zeros_like(q)
+    for r, (s, e) in enumerate(rows):
+        m = np.full(N + nb, -np.inf)
+        for c in range(nb):
+            if c in set(idx[r].tolist()):
+                m[rows[c][0]:rows[c][1]] = 0.0
+            else:
+                m[N + c] = b[c]
+        out[s:e] = _sdpa(q[s:e], Kc, Vc, mask=np.repeat(m[None, :], e - s, axis=0))
+    return out
+
+
+@pytest.mark.parametrize("N,top_k,summary", [(640, 2, "mean"), (1000, 3, "mean"),
+                                             (1000, 5, "reweight"), (4096, 8, "mean")])
+def test_mixed_matches_mask_formulation(N, top_k, summary):
+    q, k, v = _synth_head(N, seed=21)
+    res = O.run_head(q, k, v, top_k=top_k, summary=summary)
+    ref = _mask_formulation(q, k, v, res["idx"], res["sum_k"], res["sum_v"], res["bias"])
+    assert np.abs(res["out"] - ref).max() < 1e-10
+
+
+def test_attention_any_idx_matches_mask_formulation():
+    N = 700
+    q, k, v = _synth_head(N, seed=9)
+    sk, sv, b = O.summaries_mean(k, v)
+    b = np.random.default_rng(2).uniform(0, 1, size=len(b))   # a non-trivial bias
+    rng = np.random.default_rng(4)
+    nb = O.n_blocks(N)
+    idx = np.array([np.sort(rng.choice(nb, 3, replace=False)) for _ in range(nb)])
+    out = O.attention(q, k, v, idx, sk, sv, b, 1 / math.sqrt(D))
+    assert np.abs(out - _mask_formulation(q, k, v, idx, sk, sv, b)).max() < 1e-10
+
+
+def test_attention_python_loops_tiny():
+    """Brute force with pure-Python loops on a tiny head (d = 4, N = 260)."""
+    rng = np.random.default_rng(8)
+    N, d = 260, 4
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    sk, sv, b = O.summaries_mean(k, v)
+    b = b + np.array([0.3, -0.2, 0.7])
+    idx = np.array([[0], [2], [1]])
+    scale = 0.5
+    out = O.attention(q, k, v, idx, sk, sv, b, scale)
+    for i in range(0, N, 37):
+        r = i // 128
+        terms = []
+        for c in range(3):
+            if c == idx[r][0]:
+                for j in range(128 * c, min(128 * c + 128, N)):
+                    lg = scale * sum(q[i][t] * k[j][t] for t in range(d))
+                    terms.append((lg, v[j]))
+            else:
+                lg = scale * sum(q[i][t] * sk[c][t] for t in range(d)) + b[c]
+                terms.append((lg, sv[c]))
+        mx = max(t[0] for t in terms)
+        den = sum(math.exp(t[0] - mx) for t in terms)
+        ref = sum(math.exp(t[0] - mx) * t[1] for t in terms) / den
+        assert np.abs(out[i] - ref).max() < 1e-12
+
+
+def test_row_permutation_within_block_invariance():
+    N = 640
+    q, k, v = _synth_head(N, seed=13)
+    res = O.run_head(q, k, v, top_k=2)
+    perm = np.arange(N)
+    perm[256:384] = 256 + np.random.default_rng(5).permutation(128)
+    res2 = O.run_head(q, k[perm], v[perm], top_k=2)
+    assert np.array_equal(res["idx"], res2["idx"])
+    assert np.abs(res["out"] - res2["out"]).max() < 1e-12
+
+
+def test_two_level_closed_form():
+    """Hand-derived output when every block is constant: keys of block c are
+    kappa_c * e0, values nu_c * e1, queries phi * e0.  Then every logit from
+    block c is phi * kappa_c / sqrt(d), exact rows count n_c times, a summary
+    row once, and o_i = sum_c w_c nu_c e1 / sum_c w_c with
+    w_c = m_c exp(phi kappa_c / sqrt(d)), m_c = n_c if c selected else 1."""
+    N = 3 * 128 + 40
+    rows = O.block_rows(N)
+    kappa = [0.5, 2.0, -1.0, 3.0]
+    nu = [1.0, -2.0, 4.0, 0.25]
+    phi = 1.5
+    q = np.zeros((N, D)); q[:, 0] = phi
+    k = np.zeros((N, D)); v = np.zeros((N, D))
+    for c, (s, e) in enumerate(rows):
+        k[s:e, 0] = kappa[c]
+        v[s:e, 1] = nu[c]
+    res = O.run_head(q, k, v, top_k=2)
+    # scores phi*kappa_c: the two largest kappa are blocks 3 and 1
+    assert all(list(r) == [1, 3] for r in res["idx"])
+    n = [e - s for s, e in rows]
+    wts = [(n[c] if c in (1, 3) else 1) * math.exp(phi * kappa[c] / math.sqrt(D)) for c in range(4)]
+    expect = sum(w * x for w, x in zip(wts, nu)) / sum(wts)
+    assert np.abs(res["out"][:, 1] - expect).max() < 1e-12
+    assert np.abs(res["out"][:, [0] + list(range(2, D))]).max() == 0
+
+
+# --------------------------------------------------------------- reweight ---
+def test_anchor_closed_form():
+    N = 300
+    q = np.zeros((N, D))
+    q[:, 3] = np.arange(N)
+    a = O.anchor(q, 200)
+    assert a[3] == (199 / 2) and np.count_nonzero(a) == 1
+    assert O.anchor(q, 0)[3] == (N - 1) / 2
+
+
+def test_reweight_two_value_block_closed_form():
+    """A block with n1 rows at key x and n2 rows at key y: the anchor logits
+    take two values l1, l2, so w_x = e^l1 / (n1 e^l1 + n2 e^l2) per row and
+    sum_k = (n1 e^l1 x + n2 e^l2 y) / Z,  bias = log(Z / n) - (n1 l1 + n2 l2) / n
+    with Z = n1 e^l1 + n2 e^l2."""
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal(D)
+    x, y = rng.standard_normal(D), rng.standard_normal(D)
+    vx, vy = rng.standard_normal(D), rng.standard_normal(D)
+    n1, n2 = 50, 78
+    k = np.concatenate([np.repeat(x[None], n1, 0), np.repeat(y[None], n2, 0)])
+    v = np.concatenate([np.repeat(vx[None], n1, 0), np.repeat(vy[None], n2, 0)])
+    sc = 1 / math.sqrt(D)
+    sk, sv, b = O.summaries_reweight(k, v, a, sc)
+    l1, l2 = sc * float(a @ x), sc * float(a @ y)
+    Z = n1 * math.exp(l1) + n2 * math.exp(l2)
+    assert np.abs(sk[0] - (n1 * math.exp(l1) * x + n2 * math.exp(l2) * y) / Z).max() < 1e-12
+    assert np.abs(sv[0] - (n1 * math.exp(l1) * vx + n2 * math.exp(l2) * vy) / Z).max() < 1e-12
+    assert abs(b[0] - (math.log(Z / 128) - (n1 * l1 + n2 * l2) / 128)) < 1e-12
+
+
+def test_reweight_bias_nonnegative_and_mass_matches():
+    """Jensen: log mean exp(l) >= mean l, so every bias is >= 0; and at the
+    anchor itself the pooled logit plus the bias exponentiates to the mean of
+    the exponentials over the block (the caption of the Spark-Reweight
+    figure)."""
+    N = 1000
+    q, k, v = _synth_head(N, seed=17)
+    res = O.run_head(q, k, v, top_k=2, summary="reweight", anchor_rows=900)
+    assert np.all(res["bias"] >= -1e-15)
+    a = O.anchor(q, 900)
+    sc = res["scale"]
+    for c, (s, e) in enumerate(O.block_rows(N)):
+        kbar = k[s:e].mean(axis=0)
+        eff = sc * float(a @ kbar) + res["bias"][c]
+        assert abs(math.exp(eff) - np.exp(sc * (k[s:e] @ a)).mean()) < 1e-12 * math.exp(eff)
+
+
+def test_reweight_zero_anchor_equals_mean_mode():
+    """Queries whose anchor rows average to exactly zero: every anchor logit
+    is 0, the weights are uniform and the bias vanishes, so the reweight mode
+    equals the mean mode."""
+    N = 900
+    q, k, v = _synth_head(N, seed=19)
+    q = q.copy()
+    q[400:800] = -q[0:400]          # rows [0, 800) now sum to zero exactly
+    m = O.run_head(q, k, v, top_k=3, summary="mean")
+    r = O.run_head(q, k, v, top_k=3, summary="reweight", anchor_rows=800)
+    assert np.array_equal(O.anchor(q, 800), np.zeros(D))
+    assert np.abs(r["bias"]).max() == 0
+    assert np.abs(r["sum_k"] - m["sum_k"]).max() < 1e-15
+    assert np.abs(r["out"] - m["out"]).max() < 1e-13
+
+
+def test_reweight_constant_logit_block():
+    """Keys that differ only orthogonally to the anchor give equal logits:
+    uniform weights, zero bias, and the summary is the plain block mean."""
+    rng = np.random.default_rng(23)
+    a = np.zeros(D); a[0] = 2.0
+    k = rng.standard_normal((128, D)); k[:, 0] = 0.7
+    v = rng.standard_normal((128, D))
+    sk, sv, b = O.summaries_reweight(k, v, a, 1 / math.sqrt(D))
+    assert abs(b[0]) < 1e-15
+    assert np.abs(sk[0] - k.mean(0)).max() < 1e-14
+    assert np.abs(sv[0] - v.mean(0)).max() < 1e-14
+
+
+# -------------------------------------------------- planted mistakes fail ---
+def _all_pins_pass():
+    """Re-run a compact set of the pins above; True when every one holds."""
+    try:
+        test_pool_closed_forms(300)
+        test_select_brute_force(500)
+        test_select_exact_ties_go_to_lower_index()
+        test_block_scores_exact_products()
+        test_topk_all_blocks_is_dense_attention(300)
+        test_topk_zero_is_summary_attention(300, "mean")
+        test_topk_zero_is_summary_attention(300, "reweight")
+        test_mixed_matches_mask_formulation(640, 2, "mean")
+        test_two_level_closed_form()
+        test_reweight_two_value_block_closed_form()
+        test_reweight_bias_nonnegative_and_mass_matches()
+        test_anchor_closed_form()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_pins_pass_on_the_oracle():
+    assert _all_pins_pass()
+
+
+_orig_pool = O.pool_mean
+_orig_attn = O.attention
+_orig_rw = O.summaries_reweight
+_orig_scores = O.block_scores
+_orig_anchor = O.anchor
+
+
+def _pool_padded(x, block=128):
+    # mistake: ragged tail divided by 128 (zero padding)
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([x[s:e].sum(0) / block for s, e in O.block_rows(len(x), block)]).astype(np.float32)
+
+
+def _attn_no_bias(q, k, v, idx, sk, sv, b, scale, block=128):
+    return _orig_attn(q, k, v, idx, sk, sv, np.zeros_like(np.asarray(b, dtype=float)), scale, block)
+
+
+def _attn_bias_sign(q, k, v, idx, sk, sv, b, scale, block=128):
+    return _orig_attn(q, k, v, idx, sk, sv, -np.asarray(b, dtype=float), scale, block)
+
+
+def _attn_wrong_scale(q, k, v, idx, sk, sv, b, scale, block=128):
+    return _orig_attn(q, k, v, idx, sk, sv, b, scale * scale, block)
+
+
+def _attn_summaries_for_all(q, k, v, idx, sk, sv, b, scale, block=128):
+    # mistake: summary rows kept for the selected blocks too
+    N, d = np.asarray(q).shape
+    nb = O.n_blocks(N, block)
+    out = np.zeros((N, d))
+    rows = O.block_rows(N, block)
+    for r, (s, e) in enumerate(rows):
+        keys = [np.asarray(k)[rows[c][0]:rows[c][1]] for c in idx[r]] + [np.asarray(sk)]
+        vals = [np.asarray(v)[rows[c][0]:rows[c][1]] for c in idx[r]] + [np.asarray(sv)]
+        bb = np.concatenate([np.zeros(rows[c][1] - rows[c][0]) for c in idx[r]] + [np.asarray(b, float)])
+        lg = scale * (np.asarray(q)[s:e] @ np.concatenate(keys).T) + bb
+        p = np.exp(lg - lg.max(1, keepdims=True))
+        out[s:e] = (p / p.sum(1, keepdims=True)) @ np.concatenate(vals)
+    return out
+
+
+def _scores_transposed(qp, kp):
+    return _orig_scores(kp, qp)
+
+
+def _rw_no_weights(k, v, a, scale, block=128, bias_ref="mean"):
+    sk, sv, b = _orig_rw(k, v, a, scale, block, bias_ref)
+    mk, mv, _ = O.summaries_mean(k, v, block)
+    return mk, mv, b
+
+
+def _rw_log_sum(k, v, a, scale, block=128, bias_ref="mean"):
+    # mistake: log of the sum instead of the mean of the exponentials
+    sk, sv, b = _orig_rw(k, v, a, scale, block, bias_ref)
+    n = np.array([e - s for s, e in O.block_rows(np.asarray(k).shape[0], block)])
+    return sk, sv, b + np.log(n)
+
+
+def _anchor_off_by_one(q, anchor_rows):
+    q = np.asarray(q, dtype=np.float64)
+    n = q.shape[0] if anchor_rows == 0 else anchor_rows
+    return q[:n + 1].sum(0) / n
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("pool_mean", _pool_padded),
+    ("attention", _attn_no_bias),
+    ("attention", _attn_bias_sign),
+    ("attention", _attn_wrong_scale),
+    ("attention", _attn_summaries_for_all),
+    ("block_scores", _scores_transposed),
+    ("summaries_reweight", _rw_no_weights),
+    ("summaries_reweight", _rw_log_sum),
+    ("anchor", _anchor_off_by_one),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    assert not _all_pins_pass()
+
+
+def test_planted_tie_rule_mistake_is_caught(monkeypatch):
+    def select_high_index(scores, top_k):
+        nq, nk = scores.shape
+        k = O.effective_k(top_k, nk)
+        idx = np.zeros((nq, k), dtype=np.int32)
+        for r in range(nq):
+            order = sorted(range(nk), key=lambda c: (-scores[r, c], -c))
+            idx[r] = sorted(order[:k])
+        return idx
+    monkeypatch.setattr(O, "select_topk", select_high_index)
+    assert not _all_pins_pass()
