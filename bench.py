@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention hot path on one MI355X.
+
+One step = bsa_pool + bsa_select + bsa_forward over one batch of synthetic
+input already resident in HBM (the 768p 5s shape by default: 56 heads x
+37,740 tokens, head_dim 128, top_k 64 of 295 blocks, mean summaries).
+
+Prints one JSON line.  `value` is the effective TFLOP/s of a whole step
+counting only the selected blocks' attention FLOPs, 4 * 128 * sum_r n_r *
+sum_{c in S(r)} n_c; `ms_per_step` is milliseconds per call.  The roofline
+object describes the attention kernel (the dominant one), timed with HIP
+events recorded on the stream it runs on.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PAGES_MS = {"768p_5s": 30.7, "768p_10s": 61.8, "2k_5s": 121.8}  # RTX PRO 6000, context only
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="768p_5s")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate budget of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def counted_flops(torch, idx, N, nb, H, B):
+    """4 * d * sum over (b, h, r) of n_r * sum_{c in S(r)} n_c, exactly."""
+    n = torch.full((nb,), 128, dtype=torch.int64, device=idx.device)
+    n[-1] = N - 128 * (nb - 1)
+    k = idx.shape[-1]
+    per_row = n[idx.long()].sum(-1) if k > 0 else torch.zeros((B, H, nb), dtype=torch.int64,
+                                                               device=idx.device)
+    exact = int((per_row * n).sum().item())
+    summary = int((n * (nb - k)).sum().item()) * B * H
+    return 4 * 128 * exact, 4 * 128 * summary
+
+
+def cpu_baseline(w, qb, kb, vb, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload: whole
+    heads (pool, scores, top-k, summaries, attention of every query block) in
+    order until the time budget runs out, the last head possibly cut short.
+    Rate in the bench's unit: TFLOP/s of counted (selected-block) FLOPs."""
+    from oracle import bsa_oracle as O
+    from block_sparse_attention_25_amd.synth import bf16_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    N = w.seq_len
+    nb = O.n_blocks(N)
+    rows = O.block_rows(N)
+    top_k = w.top_k if w.top_k is not None else O.k_from_ratio(w.top_k_ratio, nb)
+    sc = O.default_scale(128)
+    flops, heads_done, blocks_done = 0, 0, 0
+    t0 = time.perf_counter()
+    for h in range(qb.shape[1]):
+        Q, K, V = (bf16_to_f32(x[0, h]).astype(np.float64) for x in (qb, kb, vb))
+        qp, kp = O.pool_mean(Q), O.pool_mean(K)
+        idx = O.select_topk(O.block_scores(qp, kp), top_k)
+        if w.summary == "reweight":
+            sk, sv, b = O.summaries_reweight(K, V, O.anchor(Q, w.anchor_rows), sc)
+        else:
+            sk, sv, b = O.summaries_mean(K, V)
+        for r in range(nb):
+            O.attention(Q, K, V, idx, sk, sv, b, sc, query_blocks=[r])
+            flops += 4 * 128 * (rows[r][1] - rows[r][0]) * sum(rows[c][1] - rows[c][0] for c in idx[r])
+            blocks_done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+        heads_done += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "%d query blocks (%d whole heads of %d, each with its pool, scores, top-k and "
+                      "summaries) of the %s workload; %.1f s wall" % (blocks_done, heads_done,
+                                                                     qb.shape[1], w.name, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs without communication). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_25_amd as bsa
+    from block_sparse_attention_25_amd.synth import WORKLOADS, generate
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bsa.lib()
+    w = WORKLOADS[args.workload]
+    B, H, N = w.batch, w.heads, w.seq_len
+    nb = -(-N // 128)
+    top_k = w.top_k if w.top_k is not None else bsa.k_from_ratio(w.top_k_ratio, nb)
+    t0 = time.time()
+    qb, kb, vb = generate(w, threads=16)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda:0")
+
+    def dev_bf16(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
+    p = bsa.make_problem(B, H, N, top_k, None, w.summary,
+                         w.anchor_rows if w.summary == "reweight" else 0)
+    nb, kk = bsa.bsa_problem_blocks(p)
+    f32 = torch.float32
+    q_pool = torch.empty((B, H, nb, 128), dtype=f32, device=dev)
+    k_pool = torch.empty_like(q_pool)
+    sum_k = torch.empty((B, H, nb, 128), dtype=torch.bfloat16, device=dev)
+    sum_v = torch.empty_like(sum_k)
+    sum_bias = torch.empty((B, H, nb), dtype=f32, device=dev)
+    idx = torch.empty((B, H, nb, kk), dtype=torch.int32, device=dev)
+    ws = torch.empty(bsa.bsa_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record()
+        bsa.bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws)
+        if e: e[1].record()
+        bsa.bsa_select(p, q_pool, k_pool, idx)
+        if e: e[2].record()
+        bsa.bsa_forward(p, q, k, sum_k, sum_bias, idx, ws, out)
+        if e: e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    pool_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    sel_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    attn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
+    flops, summary_flops = counted_flops(torch, idx, N, nb, H, B)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    value = flops / (step_ms * 1e-3) / 1e12
+    pool_bytes = 3 * B * H * N * 128 * 2 + B * H * nb * (2 * 512 + 2 * 256 + 4)
+    sel_bytes = 2 * B * H * nb * 128 * 4 + B * H * nb * kk * 4
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        for _ in range(3):
+            bcopy.copy_(a)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": "ms/call + effective TFLOP/s (% bf16 MFMA peak), 56 heads×37,740 tok, top_k=64",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(PAGES_MS[args.workload] / step_ms, 3) if args.workload in PAGES_MS else None),
+        "vs_baseline_basis": "speedup over the pages' sparse attention ms/call on an RTX PRO 6000 "
+                             "Blackwell (another machine; context only)",
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": 128,
+                   "n_blocks": nb, "top_k": kk, "summary": w.summary},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"pool": round(pool_ms, 4), "select": round(sel_ms, 4),
+                       "attention": round(attn_ms, 4)},
+        "wall_ms_per_step": round(wall_ms, 4),
+        "counted_tflop_per_step": round(flops / 1e12, 4),
+        "summary_tflop_per_step": round(summary_flops / 1e12, 4),
+        "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+        "select_gbs": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,205 @@
-"""Block-sparse self-attention with summary rows for gfx950 (MI355X)."""
+"""Block-sparse self-attention with summary rows for gfx950 (MI355X).
+
+A thin ctypes binding over the C ABI of ``libbsa.so`` (declared in
+``include/bsa.h``).  Every step of the computation runs in the library's HIP
+kernels; this module only checks tensor metadata, allocates outputs with
+PyTorch and passes pointers and torch's current HIP stream.  There is no CPU
+fallback: when the library is missing, every call raises.
+
+Method (PyPI page "h3-sparse-attn 0.1.0", opening paragraph and "Use"):
+each query block of 128 tokens attends to its top-k key blocks, and every
+skipped key block is folded back in as one summary row.  The Spark-Reweight
+summary mode follows "Spark-H3: Block Sparse Attention Speeds Up MiniMax-H3 in
+ComfyUI", section "What Spark-Attn changes".
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from fractions import Fraction
+
+__all__ = [
+    "BSA_OK", "BSA_ERR_INVALID", "BSA_ERR_UNSUPPORTED", "BSA_ERR_WORKSPACE", "BSA_ERR_HIP",
+    "SUMMARY_MEAN", "SUMMARY_REWEIGHT", "BsaError", "Problem", "lib", "library_path",
+    "bsa_status_str", "bsa_problem_blocks", "bsa_workspace_bytes", "bsa_pool", "bsa_select",
+    "bsa_forward", "k_from_ratio", "make_problem", "attention",
+]
+
+BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = 0, 1, 2, 3, 4
+SUMMARY_MEAN, SUMMARY_REWEIGHT = 0, 1
+BLOCK = 128
+HEAD_DIM = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libbsa.so")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``bsa_problem`` in include/bsa.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("summary", ctypes.c_int32), ("anchor_rows", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, bsa_status_str(status), status))
+
+
+_lib = None
+_P = ctypes.POINTER(Problem)
+_vp = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbsa.so (once).  Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError("libbsa.so is not built (%s); run __graft_entry__.build() or "
+                              "python -m block_sparse_attention_25_amd.build" % library_path)
+        L = ctypes.CDLL(library_path)
+        L.bsa_status_str.argtypes = [ctypes.c_int]
+        L.bsa_status_str.restype = ctypes.c_char_p
+        L.bsa_problem_blocks.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        L.bsa_problem_blocks.restype = ctypes.c_int
+        L.bsa_workspace_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
+        L.bsa_workspace_bytes.restype = ctypes.c_int
+        L.bsa_pool.argtypes = [_P] + [_vp] * 9 + [ctypes.c_size_t, _vp]
+        L.bsa_pool.restype = ctypes.c_int
+        L.bsa_select.argtypes = [_P, _vp, _vp, _vp, _vp]
+        L.bsa_select.restype = ctypes.c_int
+        L.bsa_forward.argtypes = [_P] + [_vp] * 6 + [ctypes.c_size_t, _vp, _vp]
+        L.bsa_forward.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _raise(status: int, where: str):
+    if status == BSA_OK:
+        return
+    if status == BSA_ERR_UNSUPPORTED:
+        raise NotImplementedError("%s: %s" % (where, bsa_status_str(status)))
+    if status in (BSA_ERR_INVALID, BSA_ERR_WORKSPACE):
+        raise ValueError("%s: %s" % (where, bsa_status_str(status)))
+    raise BsaError(status, where)
+
+
+# ------------------------------------------------------------ raw C calls ---
+def bsa_status_str(status: int) -> str:
+    return lib().bsa_status_str(int(status)).decode()
+
+
+def bsa_problem_blocks(p: Problem):
+    nb, k = ctypes.c_int32(), ctypes.c_int32()
+    _raise(lib().bsa_problem_blocks(ctypes.byref(p), ctypes.byref(nb), ctypes.byref(k)),
+           "bsa_problem_blocks")
+    return nb.value, k.value
+
+
+def bsa_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t()
+    _raise(lib().bsa_workspace_bytes(ctypes.byref(p), ctypes.byref(n)), "bsa_workspace_bytes")
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def bsa_pool(p: Problem, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, stream=None):
+    _raise(lib().bsa_pool(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(q_pool), _ptr(k_pool),
+                          _ptr(sum_k), _ptr(sum_v), _ptr(sum_bias), _ptr(workspace),
+                          0 if workspace is None else workspace.numel() * workspace.element_size(),
+                          _stream(stream)), "bsa_pool")
+
+
+def bsa_select(p: Problem, q_pool, k_pool, block_idx, stream=None):
+    _raise(lib().bsa_select(ctypes.byref(p), _ptr(q_pool), _ptr(k_pool), _ptr(block_idx),
+                            _stream(stream)), "bsa_select")
+
+
+def bsa_forward(p: Problem, q, k, sum_k, sum_bias, block_idx, workspace, out, stream=None):
+    _raise(lib().bsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(sum_k), _ptr(sum_bias),
+                             _ptr(block_idx), _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _ptr(out), _stream(stream)), "bsa_forward")
+
+
+# ---------------------------------------------------------------- helpers ---
+def k_from_ratio(ratio, n_blocks: int) -> int:
+    """Top-k ratio budget -> block count, ceil(ratio * n_blocks) computed on the
+    exact decimal value of the ratio (so 0.07 * 100 gives 7, not 8)."""
+    r = Fraction(str(ratio))
+    if not 0 <= r <= 1:
+        raise ValueError("top_k_ratio must lie in [0, 1]")
+    return math.ceil(r * n_blocks)
+
+
+def make_problem(batch, heads, seq_len, top_k=None, top_k_ratio=None, summary="mean",
+                 anchor_rows=0, scale=None) -> Problem:
+    nb = -(-int(seq_len) // BLOCK)
+    if (top_k is None) == (top_k_ratio is None):
+        raise ValueError("give exactly one of top_k and top_k_ratio")
+    if top_k is None:
+        top_k = k_from_ratio(top_k_ratio, nb)
+    if summary not in ("mean", "reweight"):
+        raise ValueError("summary must be 'mean' or 'reweight'")
+    return Problem(int(batch), int(heads), int(seq_len), HEAD_DIM, BLOCK, int(top_k),
+                   SUMMARY_MEAN if summary == "mean" else SUMMARY_REWEIGHT, int(anchor_rows),
+                   0.0 if scale is None else float(scale))
+
+
+def _check_qkv(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError("%s must be a contiguous bfloat16 CUDA tensor [B, H, N, 128]" % name)
+        if t.shape[-1] != HEAD_DIM:
+            raise NotImplementedError("head_dim must be 128")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must live on one device")
+
+
+def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows=0, scale=None,
+              return_aux=False, stream=None):
+    """Block-sparse attention of bf16 q, k, v [B, H, N, 128] on the GPU.
+
+    top_k counts 128-token key blocks (or give top_k_ratio, e.g. "0.1");
+    summary is "mean" or "reweight" (Spark-Reweight, anchor = mean of query
+    rows [0, anchor_rows), 0 meaning all rows).  Returns out [B, H, N, 128]
+    bf16, plus a dict of intermediate tensors when return_aux is set."""
+    import torch
+    _check_qkv(q, k, v)
+    B, H, N, _ = q.shape
+    p = make_problem(B, H, N, top_k, top_k_ratio, summary, anchor_rows, scale)
+    nb, kk = bsa_problem_blocks(p)
+    dev = q.device
+    f32, bf = torch.float32, torch.bfloat16
+    q_pool = torch.empty((B, H, nb, HEAD_DIM), dtype=f32, device=dev)
+    k_pool = torch.empty_like(q_pool)
+    sum_k = torch.empty((B, H, nb, HEAD_DIM), dtype=bf, device=dev)
+    sum_v = torch.empty_like(sum_k)
+    sum_bias = torch.empty((B, H, nb), dtype=f32, device=dev)
+    idx = torch.empty((B, H, nb, kk), dtype=torch.int32, device=dev)
+    ws = torch.empty(bsa_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws, stream)
+    bsa_select(p, q_pool, k_pool, idx if kk > 0 else None, stream)
+    bsa_forward(p, q, k, sum_k, sum_bias, idx if kk > 0 else None, ws, out, stream)
+    if return_aux:
+        return out, dict(q_pool=q_pool, k_pool=k_pool, sum_k=sum_k, sum_v=sum_v,
+                         sum_bias=sum_bias, block_idx=idx, workspace=ws, problem=p)
+    return out

@@ -1,0 +1,157 @@
+/*
+ * bsa.h - C ABI of the gfx950 (MI355X) block-sparse self-attention library.
+ *
+ * What is computed (per batch b and head h, sequence of N tokens, head_dim 128):
+ *   1. the sequence is cut into blocks of 128 tokens (the last may be short);
+ *      Q, K and V are mean-pooled per block;
+ *   2. every query block scores every key block with the dot product of the
+ *      pooled vectors and keeps its top_k key blocks;
+ *   3. each query attends exactly to every token of its kept key blocks;
+ *   4. every key block it did not keep enters the same softmax as one summary
+ *      row (mean-pooled, or Spark-Reweight weighted with a log-mass bias).
+ * Sources: "h3-sparse-attn 0.1.0" (PyPI page), opening paragraph and section
+ * "Use" (top-k 128-token key blocks, one summary row per skipped block; bf16,
+ * head_dim 128, forward only); "Spark-H3: Block Sparse Attention Speeds Up
+ * MiniMax-H3 in ComfyUI", section "What Spark-Attn changes" (exact branch over
+ * the top-ranked blocks, compressed branch for the rest, Spark-Reweight).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises, and keeps no state between calls.
+ *   - Tensors are contiguous.  Q, K, V and out are [B, H, N, 128] bfloat16
+ *     (raw 16-bit storage), row-major with the feature dimension fastest.
+ *   - nb = ceil(N / 128); k = min(top_k, nb).
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is launched and no output is touched.
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the null stream).  A failed launch returns BSA_ERR_HIP.
+ *   - Results are bit-deterministic: no floating-point atomics.
+ *   - Calls on one stream are ordered; the caller orders calls on different
+ *     streams that share buffers.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_BLOCK 128
+#define BSA_HEAD_DIM 128
+/* largest supported number of blocks per sequence (N <= 262144 tokens) */
+#define BSA_MAX_BLOCKS 2048
+
+enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID = 1,      /* bad pointer, size, range or mode */
+  BSA_ERR_UNSUPPORTED = 2,  /* head_dim or block size other than 128, or N too large */
+  BSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than bsa_workspace_bytes */
+  BSA_ERR_HIP = 4           /* a HIP launch failed */
+};
+
+enum { BSA_SUMMARY_MEAN = 0, BSA_SUMMARY_REWEIGHT = 1 };
+
+typedef struct bsa_problem {
+  int32_t batch;       /* B >= 1 */
+  int32_t heads;       /* H >= 1 */
+  int32_t seq_len;     /* N >= 1; any N, the last block may be short */
+  int32_t head_dim;    /* must be 128 */
+  int32_t block_size;  /* must be 128 */
+  int32_t top_k;       /* >= 0, counts key blocks; capped at nb */
+  int32_t summary;     /* BSA_SUMMARY_MEAN or BSA_SUMMARY_REWEIGHT */
+  int32_t anchor_rows; /* reweight: anchor = mean of query rows [0, anchor_rows);
+                          0 means N; must lie in [0, N] */
+  float scale;         /* softmax scale; 0 means 1/sqrt(head_dim); else > 0, finite */
+} bsa_problem;
+
+/* Text of a status code (static storage, never NULL). */
+const char* bsa_status_str(int status);
+
+/* Number of blocks per sequence and the effective k for a problem. */
+int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff);
+
+/*
+ * Bytes of device workspace that bsa_pool fills and bsa_forward reads, written
+ * to *bytes.  The workspace holds, for every (b, h): V of each key block
+ * transposed (feature-major, key order interleaved for the matrix cores, zero
+ * past the end of a short block), the summary values transposed in groups of
+ * 128 blocks, and in reweight mode the anchor and its per-block partial sums.
+ * Its contents are private to this library; it must be 256-byte aligned.
+ */
+int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes);
+
+/*
+ * Stage 1 (and the Spark-Reweight summaries): block pooling.
+ * Sources: PyPI page "h3-sparse-attn 0.1.0", opening paragraph (128-token
+ * blocks, one summary row per skipped block); Spark-H3 page, section "What
+ * Spark-Attn changes" (mean-pooled key/value summary; Spark-Reweight weighted
+ * summaries, log-mass bias, per-head mean-video-query anchor).
+ *
+ *   q, k, v    in   bf16 [B, H, N, 128]
+ *   q_pool     out  fp32 [B, H, nb, 128]  block means of Q (summed in float64)
+ *   k_pool     out  fp32 [B, H, nb, 128]  block means of K (summed in float64)
+ *   sum_k      out  bf16 [B, H, nb, 128]  summary key of each block
+ *   sum_v      out  bf16 [B, H, nb, 128]  summary value of each block
+ *   sum_bias   out  fp32 [B, H, nb]       additive summary logit bias
+ *   workspace  out  bsa_workspace_bytes() bytes, read later by bsa_forward
+ *
+ * Mean mode: sum_k / sum_v are the block means of K / V and sum_bias is 0.
+ * Reweight mode: with a = mean of the query rows [0, anchor_rows) and, for
+ * block c, l_j = scale * a . k_j over its rows j and w = softmax_c(l):
+ * sum_k = sum_j w_j k_j, sum_v = sum_j w_j v_j and
+ * sum_bias = log(mean_j exp(l_j)) - scale * a . kbar_c (kbar_c = block mean).
+ */
+int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v,
+             float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias,
+             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Stage 2: block scores and top-k selection.
+ * Sources: PyPI page "h3-sparse-attn 0.1.0", opening paragraph ("top-k key
+ * blocks"); Spark-H3 page, "What Spark-Attn changes" (top-ranked blocks).
+ *
+ *   q_pool, k_pool  in   fp32 [B, H, nb, 128] (from bsa_pool)
+ *   block_idx       out  int32 [B, H, nb, k]
+ *
+ * The score of query block r against key block c is q_pool[r] . k_pool[c],
+ * evaluated in float64 (exact products, float64 sums).  Row r of block_idx
+ * holds the k blocks of largest score, equal scores going to the lower block
+ * index, in strictly ascending order.  block_idx may be NULL when k == 0.
+ * Requires nb <= BSA_MAX_BLOCKS (else BSA_ERR_UNSUPPORTED).
+ */
+int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
+               int32_t* block_idx, void* hip_stream);
+
+/*
+ * Stages 3 and 4: exact attention over the selected blocks plus one summary
+ * row for every other block, in one online softmax.
+ * Sources: PyPI page "h3-sparse-attn 0.1.0", opening paragraph (skipped
+ * blocks folded back in as one summary row each); Spark-H3 page, "What
+ * Spark-Attn changes" (exact and compressed branches of one attention pass).
+ *
+ *   q, k       in   bf16 [B, H, N, 128]
+ *   sum_k      in   bf16 [B, H, nb, 128]   (may be NULL iff k == nb)
+ *   sum_bias   in   fp32 [B, H, nb]        (may be NULL iff k == nb)
+ *   block_idx  in   int32 [B, H, nb, k]    distinct, in [0, nb); the kernel
+ *                                          trusts this (bsa_select's output)
+ *   workspace  in   as filled by bsa_pool for the same q, k, v and problem
+ *   out        out  bf16 [B, H, N, 128]
+ *
+ * For query i of block r: logits scale * q_i . k_j for every row j of every
+ * block in block_idx[r], and scale * q_i . sum_k[c] + sum_bias[c] for every
+ * other block c; out_i = softmax(logits) . [v_j ... ; sum_v[c] ...], with
+ * float32 accumulation and one final bf16 rounding.  V and the summary values
+ * are read from the workspace.
+ */
+int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
+                const float* sum_bias, const int32_t* block_idx, const void* workspace,
+                size_t workspace_bytes, void* out, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

@@ -107,7 +107,10 @@ def block_scores(q_pool: np.ndarray, k_pool: np.ndarray) -> np.ndarray:
     blocks score bit-identically against any query block."""
     qp = np.asarray(q_pool, dtype=np.float64)
     kp = np.asarray(k_pool, dtype=np.float64)
-    return (qp[:, None, :] * kp[None, :, :]).sum(axis=-1)
+    s = np.empty((qp.shape[0], kp.shape[0]))
+    for r in range(qp.shape[0]):
+        s[r] = (qp[r][None, :] * kp).sum(axis=-1)
+    return s
 
 
 def select_topk(scores: np.ndarray, top_k: int) -> np.ndarray:
@@ -181,7 +184,8 @@ def summaries_reweight(k: np.ndarray, v: np.ndarray, a: np.ndarray, scale: float
 
 
 # -------------------------------------------------------------- attention ---
-def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK):
+def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK,
+              query_blocks=None):
     """Block-sparse attention with summary rows for one (batch, head).
 
     For query i in block r, the logits are
@@ -193,7 +197,8 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
     "What Spark-Attn changes" (exact and compressed branches of one pass).
 
     idx may be any [nb, k] array of distinct valid block indices per row (the
-    output is unique given idx).  Returns float64 [N, d]."""
+    output is unique given idx).  query_blocks restricts the work to those
+    query blocks (other output rows stay zero).  Returns float64 [N, d]."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -205,6 +210,8 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
     nb = len(rows)
     out = np.zeros((N, d))
     for r, (s, e) in enumerate(rows):
+        if query_blocks is not None and r not in query_blocks:
+            continue
         sel = [int(c) for c in idx[r]]
         if len(set(sel)) != len(sel) or any(c < 0 or c >= nb for c in sel):
             raise ValueError("idx row %d is not a set of valid blocks" % r)

@@ -1,0 +1,113 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/bsa.h declares, and rejects bad problems before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_25_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = bsa.lib()
+    names = _declared_functions()
+    assert {"bsa_pool", "bsa_select", "bsa_forward", "bsa_workspace_bytes",
+            "bsa_status_str"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for st in range(5):
+        assert bsa.bsa_status_str(st)
+    assert bsa.bsa_status_str(99) == "unknown status"
+
+
+def _prob(**kw):
+    base = dict(batch=1, heads=2, seq_len=4096, top_k=8)
+    base.update(kw)
+    return bsa.make_problem(**base)
+
+
+def test_blocks_and_workspace():
+    p = _prob(seq_len=37740, heads=56, top_k=64)
+    assert bsa.bsa_problem_blocks(p) == (295, 64)
+    p = _prob(seq_len=133644, heads=56, top_k=64)
+    assert bsa.bsa_problem_blocks(p) == (1045, 64)
+    p = _prob(seq_len=100, top_k=5)
+    assert bsa.bsa_problem_blocks(p) == (1, 1)
+    # workspace: V^T of every block + summary V^T groups (+ reweight anchor data)
+    p = _prob(seq_len=37740, heads=56, top_k=64)
+    ws = bsa.bsa_workspace_bytes(p)
+    assert ws >= 56 * 295 * 128 * 128 * 2 + 56 * 3 * 128 * 128 * 2
+    pr = _prob(seq_len=37740, heads=56, top_k=64, summary="reweight")
+    assert bsa.bsa_workspace_bytes(pr) >= ws + 56 * 295 * 128 * 8
+
+
+def test_ratio_budget():
+    p = _prob(seq_len=103996, heads=56, top_k=None, top_k_ratio="0.1", summary="reweight")
+    assert bsa.bsa_problem_blocks(p) == (813, 82)
+    assert bsa.k_from_ratio(0.07, 100) == 7
+
+
+@pytest.mark.parametrize("field,value,err", [
+    ("head_dim", 64, NotImplementedError), ("block_size", 64, NotImplementedError),
+    ("seq_len", 0, ValueError), ("heads", 0, ValueError), ("batch", -1, ValueError),
+    ("top_k", -1, ValueError), ("summary", 7, ValueError), ("anchor_rows", 5000, ValueError),
+    ("anchor_rows", -2, ValueError), ("scale", -1.0, ValueError), ("scale", float("inf"), ValueError),
+    ("scale", float("nan"), ValueError), ("seq_len", 2049 * 128, NotImplementedError),
+])
+def test_invalid_problems_rejected_before_launch(field, value, err):
+    p = _prob()
+    setattr(p, field, value)
+    with pytest.raises(err):
+        bsa.bsa_workspace_bytes(p)
+    # the entry points validate before touching any pointer or stream
+    L = bsa.lib()
+    st = L.bsa_pool(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0, None)
+    assert st in (bsa.BSA_ERR_INVALID, bsa.BSA_ERR_UNSUPPORTED)
+    st = L.bsa_forward(ctypes.byref(p), None, None, None, None, None, None, 0, None, None)
+    assert st in (bsa.BSA_ERR_INVALID, bsa.BSA_ERR_UNSUPPORTED)
+
+
+def test_null_pointers_and_small_workspace_rejected():
+    L = bsa.lib()
+    p = _prob()
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    assert L.bsa_pool(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake, fake, fake,
+                      1 << 30, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_pool(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                      16, None) == bsa.BSA_ERR_WORKSPACE
+    assert L.bsa_pool(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None,
+                      1 << 30, None) == bsa.BSA_ERR_WORKSPACE
+    assert L.bsa_select(ctypes.byref(p), fake, fake, None, None) == bsa.BSA_ERR_INVALID
+    # misaligned tensors
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L.bsa_pool(ctypes.byref(p), odd, fake, fake, fake, fake, fake, fake, fake, fake,
+                      1 << 30, None) == bsa.BSA_ERR_INVALID
+    # sum_k may be NULL only when every block is selected
+    assert L.bsa_forward(ctypes.byref(p), fake, fake, None, None, fake, fake, 1 << 30, fake,
+                         None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 16, fake,
+                         None) == bsa.BSA_ERR_WORKSPACE
+    # top_k = 0: select has nothing to do and needs no pointers
+    p0 = _prob(top_k=0)
+    assert L.bsa_select(ctypes.byref(p0), None, None, None, None) == bsa.BSA_OK
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(1, 1, 256, 128, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        bsa.attention(x, x, x, top_k=1)
+    with pytest.raises(ValueError):
+        bsa.make_problem(1, 1, 256, top_k=1, top_k_ratio=0.5)
