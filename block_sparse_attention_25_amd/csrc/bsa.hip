@@ -381,16 +381,36 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
 }
 
 // ------------------------------------------------------------- attention ---
-// One workgroup (4 wavefronts) per (b, h, query block r), 128 query rows;
-// wavefront w owns queries [32w, 32w + 32) of the block.  Per key tile (a
-// selected block, or 128 summary rows) the workgroup stages K (rows) and V^T
-// (feature rows) in LDS, XOR-swizzled by 16-byte chunk, then each wavefront
-// computes S^T = K Q^T (4 x 8 MFMA 32x32x16), updates its online softmax in
-// base 2, and accumulates O^T += V^T P^T (4 x 8 MFMA) with P taken directly
-// from the S^T accumulator.  Lane l holds query 32w + l%32; lanes l and l^32
-// hold the two halves of that query's keys.
+// One workgroup (4 wavefronts, 2 workgroups per CU) per (b, h, query block r):
+// 128 query rows, wavefront w owning queries [32w, 32w + 32).  The keys are
+// walked in half tiles of 64: the two halves of every selected block, then
+// the summary rows in groups of 64.
+//
+// Software pipeline, per half tile t (one barrier each):
+//   - direct global->LDS loads of K(t+2) and V^T(t+1) are issued first;
+//   - the MFMAs of S(t+1) = K(t+1) Q^T run interleaved with the softmax of
+//     S(t) (computed one step earlier), so the matrix cores and the vector
+//     ALUs of one wavefront work at the same time;
+//   - then O^T += V^T(t) P(t)^T, with P(t) taken straight from the S^T
+//     accumulator layout.
+// K is therefore staged two half tiles ahead and V^T one ahead, in two LDS
+// buffers each (64 KB per workgroup).  Lane l holds query 32w + l%32; lanes l
+// and l^32 hold the two halves of its 64 keys.
+//
+// The running max only moves when a tile's max exceeds it by more than
+// LAZY_MAX (base-2 units), so O is rescaled rarely; probabilities stay below
+// 2^LAZY_MAX, far from float or bfloat16 overflow.
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * HD + ((chunk ^ (row & 15)) << 3); }
+constexpr int HT = 64;            // keys per half tile
+constexpr float LAZY_MAX = 8.0f;
+
+// K half tile: 64 rows x 256 B, 16-byte chunks XOR-swizzled by row
+__device__ __forceinline__ int swz_k(int row, int chunk) { return row * HD + ((chunk ^ (row & 15)) << 3); }
+// V^T half tile: 128 rows x 128 B; rows 2i, 2i+1 share a swizzle and sit in
+// opposite halves of the 256-byte bank window
+__device__ __forceinline__ int swz_v(int row, int chunk) {
+  return row * HT + ((chunk ^ ((row >> 1) & 7)) << 3);
+}
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) { return *(const bf16x8*)p; }
 
@@ -402,29 +422,49 @@ __device__ __forceinline__ int xcd_remap(int hw, int total) {
   return (x < rem) ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer: byte offsets at or beyond `bytes` read as zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+struct TileSrc {
+  uint32_t koff;   // byte offset of the half tile's first key row (K or sum_k)
+  uint32_t voff;   // byte offset of the half tile in V^T (per-block or summary)
+  int nvalid;      // rows of the half tile that exist (may be <= 0)
+  int c0;          // summary tiles: first summary block
+  bool summary;
+};
+
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ sum_k,
     const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
     const int32_t* __restrict__ block_idx, uint16_t* __restrict__ out, int N, int nb, int ksel,
     int nsb, float scale_log2, int total_wg) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BLK * HD];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[HD * BLK];
-  __shared__ float addv[BLK];
+  // LDS buffers as distinct variables, so the compiler can tell the DMA
+  // targets from the buffers being read
+  __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t vs0[HD * HT], vs1[HD * HT];
+  __shared__ float addv0[HT], addv1[HT];
   __shared__ uint32_t selmask[BSA_MAX_BLOCKS / 32];
 
   const int logical = xcd_remap(blockIdx.x, total_wg);
   const int r = logical % nb;
   const size_t bh = (size_t)(logical / nb);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
   const int g = lane >> 5, ln = lane & 31;
 
-  const uint16_t* kb = k + bh * (size_t)N * HD;
-  const uint16_t* vtb = vt + bh * (size_t)nb * BLK * HD;
-  const uint16_t* skb = sum_k ? sum_k + bh * (size_t)nb * HD : nullptr;
-  const uint16_t* svtb = svt + bh * (size_t)nsb * BLK * HD;
   const float* biasb = sum_bias ? sum_bias + bh * (size_t)nb : nullptr;
   const int32_t* irow = block_idx + (bh * nb + r) * (size_t)ksel;
+  // per-head buffer descriptors: K, V^T, summary K, summary V^T
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * (size_t)N * HD, (uint32_t)N * HD * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + bh * (size_t)nb * BLK * HD, (uint32_t)nb * BLK * HD * 2);
+  const __amdgpu_buffer_rsrc_t rsk =
+      make_rsrc(sum_k ? sum_k + bh * (size_t)nb * HD : k, sum_k ? (uint32_t)nb * HD * 2 : 0u);
+  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(svt + bh * (size_t)nsb * BLK * HD, (uint32_t)nsb * BLK * HD * 2);
 
   // Q fragments (B operand of S^T = K Q^T): query qi, features 16kk + 8g + [0, 8)
   const int qi = r * BLK + 32 * wave + ln;
@@ -448,124 +488,229 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   }
   __syncthreads();
 
+  const int n_exact = 2 * ksel;
+  const int ntiles = n_exact + ((ksel < nb) ? 2 * nsb : 0);
+
+  auto describe = [&](int t) {
+    t = min(t, ntiles - 1);  // past the end: the last half tile again (never used)
+    TileSrc d;
+    const int h = t & 1;
+    if (t < n_exact) {
+      const int c = irow[t >> 1];
+      const int row0 = c * BLK + h * HT;
+      d.koff = (uint32_t)row0 * (HD * 2);
+      d.voff = (uint32_t)c * (BLK * HD * 2) + h * (HT * 2);
+      d.nvalid = min(HT, N - row0);
+      d.c0 = 0;
+      d.summary = false;
+    } else {
+      const int st = (t - n_exact) >> 1;
+      const int row0 = st * BLK + h * HT;
+      d.koff = (uint32_t)row0 * (HD * 2);
+      d.voff = (uint32_t)st * (BLK * HD * 2) + h * (HT * 2);
+      d.nvalid = min(HT, nb - row0);
+      d.c0 = row0;
+      d.summary = true;
+    }
+    return d;
+  };
+
+  // Direct global -> LDS loads.  Instruction j of wavefront w fills the 64
+  // consecutive 16-byte LDS chunks P = (4w + j) * 64 + lane; each lane fetches
+  // the global chunk that the XOR swizzle places at P.  Rows past the end of
+  // the buffer (ragged tails) arrive as zeros.
+  uint32_t kvo[4], vvo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int P = (4 * wave + j) * 64 + lane;
+    const int krow = P >> 4, kch = (P & 15) ^ (krow & 15);
+    kvo[j] = (uint32_t)(krow * (HD * 2) + kch * 16);
+    const int vrow = P >> 3, vch = (P & 7) ^ ((vrow >> 1) & 7);
+    vvo[j] = (uint32_t)(vrow * (BLK * 2) + vch * 16);
+  }
+  auto load_k = [&](const TileSrc& d, uint16_t* ksd) {
+    const __amdgpu_buffer_rsrc_t rK = d.summary ? rsk : rk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)(ksd + (4 * wave + j) * 512), 16,
+                                               (int)(d.koff + kvo[j]), 0, 0, 0);
+  };
+  auto load_v = [&](const TileSrc& d, uint16_t* vsd) {
+    const __amdgpu_buffer_rsrc_t rV = d.summary ? rsv : rv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(vsd + (4 * wave + j) * 512), 16,
+                                               (int)(d.voff + vvo[j]), 0, 0, 0);
+  };
+  // additive logit term of each key of a half tile (base-2 units)
+  auto store_mask = [&](const TileSrc& d, float* addvd) {
+    if (tid < HT) {
+      float a;
+      if (!d.summary) {
+        a = tid < d.nvalid ? 0.f : -INFINITY;
+      } else {
+        const int c = d.c0 + tid;
+        const bool skipped = c < nb && !((selmask[c >> 5] >> (c & 31)) & 1u);
+        a = skipped ? biasb[c] * LOG2E : -INFINITY;
+      }
+      addvd[tid] = a;
+    }
+  };
+
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16 sA[2], sB[2];
 
-  const int ntiles = ksel + ((ksel < nb) ? nsb : 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const bool summary = t >= ksel;
-    const uint16_t* ksrc;
-    const uint16_t* vsrc;
-    int nvalid, st = 0;
-    if (!summary) {
-      const int c = irow[t];
-      ksrc = kb + (size_t)c * BLK * HD;
-      vsrc = vtb + (size_t)c * BLK * HD;
-      nvalid = min(BLK, N - c * BLK);
-    } else {
-      st = t - ksel;
-      nvalid = min(BLK, nb - st * BLK);
-      int nsel = 0;
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        const int word = st * 4 + wd;
-        if (word < nwords) nsel += __popc(selmask[word]);
-      }
-      if (nsel == nvalid) continue;  // every block of this group is exact
-      ksrc = skb + (size_t)st * BLK * HD;
-      vsrc = svtb + (size_t)st * BLK * HD;
-    }
-    const bool need_add = summary || nvalid < BLK;
+  // ---------------------------------------------------------------------
+  // S^T(t) = K Q^T : s[mb] holds keys 32mb + 8(i/4) + 4g + i%4 of the half
+  // tile.  MFMA number i of a half tile uses mb = i & 1, kk = i >> 1, so the
+  // two accumulators alternate.
+  auto k_operand = [&](const uint16_t* ksc, int i) {
+    return ld_bf16x8(ksc + swz_k(32 * (i & 1) + ln, 2 * (i >> 1) + g));
+  };
+  auto v_operand = [&](const uint16_t* vsc, int i) {  // i = 4 kk + db
+    return ld_bf16x8(vsc + swz_v(32 * (i & 3) + ln, 2 * (i >> 2) + g));
+  };
 
-    __syncthreads();  // previous tile fully consumed
-    {
-      uint4 kv[8], vv[8];
+  // prologue S(0), plain order
+  auto qk_plain = [&](const uint16_t* ksc, f32x16* s) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int id = it * 256 + tid;
-        const int row = id >> 4, ch = id & 15;
-        kv[it] = zero_unless(*(const uint4*)(ksrc + min(row, nvalid - 1) * HD + ch * 8), row < nvalid);
-        vv[it] = *(const uint4*)(vsrc + row * BLK + ch * 8);
-      }
+    for (int i = 0; i < 16; ++i)
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(ksc, i), qf[i >> 1], s[i & 1], 0, 0, 0);
+  };
+
+  // Region A of a half tile: the 16 MFMAs of S(t+1) = K(t+1) Q^T, each
+  // followed by one slice of the softmax of S(t), in a fixed order (hard
+  // scheduling fences between slots).  Slot work:
+  //   0-3   scale (+ additive term) and running max over 8 of the 32 values
+  //   4     exchange the max with the partner lane (l ^ 32)
+  //   5     new reference max, rescale factor
+  //   6-13  exponentials of 4 values, bf16 packing, row sum
+  // Returns the O rescale factor (1 unless the reference max moved).
+  auto region_a = [&](const uint16_t* kn, f32x16* sn, f32x16* sc, bool need_add,
+                      const float* addvc, bf16x8* pb) -> float {
+    bf16x8 kop0 = k_operand(kn, 0), kop1 = k_operand(kn, 1), kop2;
+    float mpart[4];
+    float mx = -INFINITY, m_use = 0.f, alpha = 1.f, psum = 0.f;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int id = it * 256 + tid;
-        const int row = id >> 4, ch = id & 15;
-        *(uint4*)(ks + swz(row, ch)) = kv[it];
-        *(uint4*)(vs + swz(row, ch)) = vv[it];
-      }
-      if (need_add && tid < BLK) {
-        float a;
-        if (!summary) {
-          a = tid < nvalid ? 0.f : -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) kop2 = k_operand(kn, i + 2);
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop0, qf[i >> 1], i < 2 ? f32x16{} : sn[i & 1],
+                                                          0, 0, 0);
+      if (i < 4) {
+        // values v = 8i .. 8i+7 : mb = i >> 1, elements 8(i&1) .. +7
+        const int mb = i >> 1, e0 = 8 * (i & 1);
+        float m = -INFINITY;
+        if (need_add) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int ii = e0 + e;
+            const float x = fmaf(sc[mb][ii], scale_log2, addvc[32 * mb + 8 * (ii >> 2) + 4 * g + (ii & 3)]);
+            sc[mb][ii] = x;
+            m = fmaxf(m, x);
+          }
         } else {
-          const int c = st * BLK + tid;
-          const bool skipped = c < nb && !((selmask[c >> 5] >> (c & 31)) & 1u);
-          a = skipped ? biasb[c] * LOG2E : -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m = fmaxf(m, sc[mb][e0 + e]);
         }
-        addv[tid] = a;
+        mpart[i] = m;
+      } else if (i == 4) {
+        mx = fmaxf(fmaxf(mpart[0], mpart[1]), fmaxf(mpart[2], mpart[3]));
+        if (!need_add) mx *= scale_log2;
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+      } else if (i == 5) {
+        const float m_new = (mx > m_run + LAZY_MAX) ? mx : m_run;
+        m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_new;
+        psum = l_run * alpha;
+      } else if (i >= 6 && i < 14) {
+        // half slice j: keys of P slice kk = j >> 1, elements 4(j&1) .. +3
+        const int j = i - 6, kk = j >> 1, e0 = 4 * (j & 1);
+        const int mb = kk >> 1, base = 8 * (kk & 1) + e0;
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = sc[mb][base + e];
+          p[e] = need_add ? __builtin_amdgcn_exp2f(x - m_use)
+                          : __builtin_amdgcn_exp2f(fmaf(x, scale_log2, -m_use));
+        }
+        const bf16x2 p01 = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){p[0], p[1]}, bf16x2);
+        const bf16x2 p23 = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){p[2], p[3]}, bf16x2);
+        pb[kk][e0 + 0] = p01[0];
+        pb[kk][e0 + 1] = p01[1];
+        pb[kk][e0 + 2] = p23[0];
+        pb[kk][e0 + 3] = p23[1];
+        psum = __builtin_amdgcn_fdot2_f32_bf16(p01, one, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(p23, one, psum, false);
       }
+      kop0 = kop1;
+      kop1 = kop2;
+      __builtin_amdgcn_sched_barrier(0);
     }
+    l_run = psum;
+    return alpha;
+  };
+
+  // Region B: O^T += V^T(t) P(t)^T, 16 MFMAs (db fastest: 4 independent chains)
+  auto region_b = [&](const uint16_t* vc, const bf16x8* pb) {
+    bf16x8 vop0 = v_operand(vc, 0), vop1 = v_operand(vc, 1), vop2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) vop2 = v_operand(vc, i + 2);
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop0, pb[i >> 2], o[i & 3], 0, 0, 0);
+      vop0 = vop1;
+      vop1 = vop2;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // prologue: K(0), K(1), V(0) and the masks of tile 0; S(0)
+  TileSrc d0 = describe(0), d1 = describe(1), d2 = describe(2);
+  load_k(d0, ks0);
+  load_k(d1, ks1);
+  load_v(d0, vs0);
+  store_mask(d0, addv0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk_plain(ks0, sA);
+  __syncthreads();  // every wavefront is done with ks0 before K(2) lands there
+
+  // half tile t: d0 = tile t, d1 = t+1, d2 = t+2.  Reads K(t+1) from kn and
+  // V(t) from vc; loads K(t+2) into kd and V(t+1) into vd.
+  auto step = [&](f32x16* sc, f32x16* sn, const uint16_t* kn, const uint16_t* vc,
+                  uint16_t* kd, uint16_t* vd, const float* addvc, float* addvn, int t) {
+    load_k(d2, kd);
+    load_v(d1, vd);
+    const bool need_add = d0.summary || d0.nvalid < HT;
+    bf16x8 pb[4];
+    float alpha;
+    if (need_add)
+      alpha = region_a(kn, sn, sc, true, addvc, pb);
+    else
+      alpha = region_a(kn, sn, sc, false, addvc, pb);
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
+    region_b(vc, pb);
+    store_mask(d1, addvn);
+    d0 = d1;
+    d1 = d2;
+    d2 = describe(t + 3);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
 
-    // S^T = K Q^T : s[mb] holds keys 32mb + 8(i/4) + 4g + i%4, query ln
-    f32x16 s[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      s[mb] = f32x16{};
-      const int row = 32 * mb + ln;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(ks + swz(row, 2 * kk + g)),
-                                                         qf[kk], s[mb], 0, 0, 0);
-    }
-
-    // online softmax (base 2)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[mb][i] * scale_log2;
-        if (need_add) x += addv[32 * mb + 8 * (i >> 2) + 4 * g + (i & 3)];
-        s[mb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[mb][i] - m_use);
-        s[mb][i] = p;
-        psum += p;
-      }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const f32x16& sv = s[kk >> 1];
-      const int base = 8 * (kk & 1);
-      f32x8 pf = {sv[base + 0], sv[base + 1], sv[base + 2], sv[base + 3],
-                  sv[base + 4], sv[base + 5], sv[base + 6], sv[base + 7]};
-      const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld_bf16x8(vs + swz(32 * db + ln, 2 * kk + g)),
-                                                         pb, o[db], 0, 0, 0);
-    }
+  for (int t = 0; t < ntiles; t += 2) {
+    step(sA, sB, ks1, vs0, ks0, vs1, addv0, addv1, t);
+    if (t + 1 < ntiles) step(sB, sA, ks0, vs1, ks1, vs0, addv1, addv0, t + 1);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -576,12 +721,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = 32 * db + 8 * r4 + 4 * g;
+        const int d0o = 32 * db + 8 * r4 + 4 * g;
         const uint32_t w0 = (uint32_t)f2bf(o[db][4 * r4 + 0] * inv) |
                             ((uint32_t)f2bf(o[db][4 * r4 + 1] * inv) << 16);
         const uint32_t w1 = (uint32_t)f2bf(o[db][4 * r4 + 2] * inv) |
                             ((uint32_t)f2bf(o[db][4 * r4 + 3] * inv) << 16);
-        *(uint2*)(orow + d0) = make_uint2(w0, w1);
+        *(uint2*)(orow + d0o) = make_uint2(w0, w1);
       }
     }
   }
