@@ -41,6 +41,21 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a copy-kernel calibration),
+    or None when it was taken on another workload or another kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_%s_traffic.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = dict(line.split(None, 1) for line in open(path) if line.startswith(("source_sha256", "traffic_bytes")))
+    src = os.path.join(ROOT, "block_sparse_attention_25_amd", "csrc", "bsa.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("source_sha256", "").strip():
+        return None
+    return float(fields["traffic_bytes"])
+
+
 def counted_flops(torch, idx, N, nb, H, B):
     """4 * d * sum over (b, h, r) of n_r * sum_{c in S(r)} n_c, exactly."""
     n = torch.full((nb,), 128, dtype=torch.int64, device=idx.device)
@@ -162,7 +177,9 @@ def main():
     flops, summary_flops = counted_flops(torch, idx, N, nb, H, B)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
-    pool_bytes = 3 * B * H * N * 128 * 2 + B * H * nb * (2 * 512 + 2 * 256 + 4)
+    # pool: read Q, K, V once; write q_pool, k_pool (fp32), sum_k, sum_v (bf16),
+    # the bias, V^T of every block (32 KiB) and one summary-V^T column (256 B)
+    pool_bytes = 3 * B * H * N * 128 * 2 + B * H * nb * (2 * 512 + 2 * 256 + 4 + 32768 + 256)
     sel_bytes = 2 * B * H * nb * 128 * 4 + B * H * nb * kk * 4
 
     if args.calib_copy:
@@ -200,7 +217,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name),
+                     "traffic_unit": "bytes per launch (HBM, from rocprofv3 FETCH_SIZE + WRITE_SIZE)"},
         "input_gen_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:
