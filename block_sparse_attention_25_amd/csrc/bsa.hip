@@ -424,6 +424,14 @@ __device__ __forceinline__ int xcd_remap(int hw, int total) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// value of lane l ^ 32 (a VALU lane swap, no LDS round trip)
+__device__ __forceinline__ float other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // one of the two results holds this lane's half, the other the partner's
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return (a == x) ? b : a;
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   // raw buffer: byte offsets at or beyond `bytes` read as zero
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -449,6 +457,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t vs0[HD * HT], vs1[HD * HT];
   __shared__ float addv0[HT], addv1[HT];
   __shared__ uint32_t selmask[BSA_MAX_BLOCKS / 32];
+  __shared__ int32_t sidx[BSA_MAX_BLOCKS];  // this query block's selected blocks
 
   const int logical = xcd_remap(blockIdx.x, total_wg);
   const int r = logical % nb;
@@ -484,6 +493,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __syncthreads();
   for (int i = tid; i < ksel; i += 256) {
     const int c = irow[i];
+    sidx[i] = c;
     atomicOr(&selmask[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
@@ -491,12 +501,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int n_exact = 2 * ksel;
   const int ntiles = n_exact + ((ksel < nb) ? 2 * nsb : 0);
 
-  auto describe = [&](int t) {
+  // block index of half tile t (exact tiles), read from LDS; issued one step
+  // before describe() needs it
+  auto tile_block = [&](int t) {
+    t = min(t, ntiles - 1);
+    return t < n_exact ? sidx[t >> 1] : 0;
+  };
+  auto describe = [&](int t, int c) {
     t = min(t, ntiles - 1);  // past the end: the last half tile again (never used)
     TileSrc d;
     const int h = t & 1;
     if (t < n_exact) {
-      const int c = irow[t >> 1];
       const int row0 = c * BLK + h * HT;
       d.koff = (uint32_t)row0 * (HD * 2);
       d.voff = (uint32_t)c * (BLK * HD * 2) + h * (HT * 2);
@@ -519,33 +534,49 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // consecutive 16-byte LDS chunks P = (4w + j) * 64 + lane; each lane fetches
   // the global chunk that the XOR swizzle places at P.  Rows past the end of
   // the buffer (ragged tails) arrive as zeros.
-  uint32_t kvo[4], vvo[4];
+  // The swizzled offsets have XOR structure: for K instruction j the offset is
+  // kbase + 1024 j + (kx ^ 64 j); for V^T it is vvo[j & 1] + 4096 (j >> 1).  Keeping
+  // four registers instead of eight matters: the kernel sits at the VGPR limit.
+  const int P0 = 4 * wave * 64 + lane;
+  const uint32_t kbase = (uint32_t)((P0 >> 4) * (HD * 2));
+  const uint32_t kx = (uint32_t)((((P0 & 15) ^ ((P0 >> 4) & 15))) * 16);
+  uint32_t vvo[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int P = (4 * wave + j) * 64 + lane;
-    const int krow = P >> 4, kch = (P & 15) ^ (krow & 15);
-    kvo[j] = (uint32_t)(krow * (HD * 2) + kch * 16);
+  for (int j = 0; j < 2; ++j) {
+    const int P = P0 + j * 64;
     const int vrow = P >> 3, vch = (P & 7) ^ ((vrow >> 1) & 7);
     vvo[j] = (uint32_t)(vrow * (BLK * 2) + vch * 16);
   }
+  auto kvo = [&](int j) { return kbase + 1024u * j + (kx ^ (64u * j)); };
+  auto vvo_of = [&](int j) { return vvo[j & 1] + 4096u * (j >> 1); };
+  auto load_k1 = [&](const TileSrc& d, uint16_t* ksd, int j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.summary ? rsk : rk, (lds_ptr_t)(ksd + (4 * wave + j) * 512),
+                                             16, (int)(d.koff + kvo(j)), 0, 0, 0);
+  };
+  auto load_v1 = [&](const TileSrc& d, uint16_t* vsd, int j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.summary ? rsv : rv, (lds_ptr_t)(vsd + (4 * wave + j) * 512),
+                                             16, (int)(d.voff + vvo_of(j)), 0, 0, 0);
+  };
   auto load_k = [&](const TileSrc& d, uint16_t* ksd) {
     const __amdgpu_buffer_rsrc_t rK = d.summary ? rsk : rk;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)(ksd + (4 * wave + j) * 512), 16,
-                                               (int)(d.koff + kvo[j]), 0, 0, 0);
+                                               (int)(d.koff + kvo(j)), 0, 0, 0);
   };
   auto load_v = [&](const TileSrc& d, uint16_t* vsd) {
     const __amdgpu_buffer_rsrc_t rV = d.summary ? rsv : rv;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(vsd + (4 * wave + j) * 512), 16,
-                                               (int)(d.voff + vvo[j]), 0, 0, 0);
+                                               (int)(d.voff + vvo_of(j)), 0, 0, 0);
   };
   // additive logit term of each key of a half tile (base-2 units)
-  auto store_mask = [&](const TileSrc& d, float* addvd) {
+  // Only summary tiles and the short halves of the last block need it; full
+  // exact half tiles skip it (their softmax reads no additive term).
+  auto mask_value = [&](const TileSrc& d) {
+    float a = 0.f;
     if (tid < HT) {
-      float a;
       if (!d.summary) {
         a = tid < d.nvalid ? 0.f : -INFINITY;
       } else {
@@ -553,8 +584,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         const bool skipped = c < nb && !((selmask[c >> 5] >> (c & 31)) & 1u);
         a = skipped ? biasb[c] * LOG2E : -INFINITY;
       }
-      addvd[tid] = a;
     }
+    return a;
+  };
+  auto store_mask = [&](const TileSrc& d, float a, float* addvd) {
+    if (tid < HT && (d.summary || d.nvalid < HT)) addvd[tid] = a;
   };
 
   f32x16 o[4];
@@ -592,9 +626,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   //   6-13  exponentials of 4 values, bf16 packing, row sum
   // Returns the O rescale factor (1 unless the reference max moved).
   auto region_a = [&](const uint16_t* kn, f32x16* sn, f32x16* sc, bool need_add,
-                      const float* addvc, bf16x8* pb) -> float {
+                      const float* addvc, bf16x8* pb, const TileSrc& dk, uint16_t* kd,
+                      const TileSrc& dv, uint16_t* vd) -> float {
     bf16x8 kop0 = k_operand(kn, 0), kop1 = k_operand(kn, 1), kop2;
-    float mpart[4];
     float mx = -INFINITY, m_use = 0.f, alpha = 1.f, psum = 0.f;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -619,11 +653,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
           for (int e = 0; e < 8; ++e) m = fmaxf(m, sc[mb][e0 + e]);
         }
-        mpart[i] = m;
+        mx = (i == 0) ? m : fmaxf(mx, m);
       } else if (i == 4) {
-        mx = fmaxf(fmaxf(mpart[0], mpart[1]), fmaxf(mpart[2], mpart[3]));
         if (!need_add) mx *= scale_log2;
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = fmaxf(mx, other_half(mx));
       } else if (i == 5) {
         const float m_new = (mx > m_run + LAZY_MAX) ? mx : m_run;
         m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -650,6 +683,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         psum = __builtin_amdgcn_fdot2_f32_bf16(p01, one, psum, false);
         psum = __builtin_amdgcn_fdot2_f32_bf16(p23, one, psum, false);
       }
+      // spread the 8 direct-to-LDS loads of the next half tiles over the
+      // region (one every second slot) instead of issuing them back to back
+      if ((i & 1) == 0) {
+        const int j = i >> 1;
+        if (j < 4)
+          load_k1(dk, kd, j);
+        else
+          load_v1(dv, vd, j - 4);
+      }
       kop0 = kop1;
       kop1 = kop2;
       __builtin_amdgcn_sched_barrier(0);
@@ -672,11 +714,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   };
 
   // prologue: K(0), K(1), V(0) and the masks of tile 0; S(0)
-  TileSrc d0 = describe(0), d1 = describe(1), d2 = describe(2);
+  TileSrc d0 = describe(0, tile_block(0)), d1 = describe(1, tile_block(1)), d2 = describe(2, tile_block(2));
   load_k(d0, ks0);
   load_k(d1, ks1);
   load_v(d0, vs0);
-  store_mask(d0, addv0);
+  store_mask(d0, mask_value(d0), addv0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   qk_plain(ks0, sA);
@@ -686,24 +728,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // V(t) from vc; loads K(t+2) into kd and V(t+1) into vd.
   auto step = [&](f32x16* sc, f32x16* sn, const uint16_t* kn, const uint16_t* vc,
                   uint16_t* kd, uint16_t* vd, const float* addvc, float* addvn, int t) {
-    load_k(d2, kd);
-    load_v(d1, vd);
     const bool need_add = d0.summary || d0.nvalid < HT;
+    // early: the block index of half tile t+3 and the mask of half tile t+1
+    const int c3 = tile_block(t + 3);
+    const float mask1 = mask_value(d1);
     bf16x8 pb[4];
     float alpha;
     if (need_add)
-      alpha = region_a(kn, sn, sc, true, addvc, pb);
+      alpha = region_a(kn, sn, sc, true, addvc, pb, d2, kd, d1, vd);
     else
-      alpha = region_a(kn, sn, sc, false, addvc, pb);
+      alpha = region_a(kn, sn, sc, false, addvc, pb, d2, kd, d1, vd);
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
     region_b(vc, pb);
-    store_mask(d1, addvn);
+    store_mask(d1, mask1, addvn);
     d0 = d1;
     d1 = d2;
-    d2 = describe(t + 3);
+    d2 = describe(t + 3, c3);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
@@ -713,7 +756,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     if (t + 1 < ntiles) step(sB, sA, ks0, vs1, ks1, vs0, addv1, addv0, t + 1);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run);
   const float inv = 1.f / l_tot;
   if (qi < N) {
     uint16_t* orow = out + (bh * (size_t)N + qi) * HD;
