@@ -283,13 +283,22 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
 }
 
 // ---------------------------------------------------------------- select ---
-// One workgroup of 4 wavefronts per 4 query blocks of one (b, h).  Scores of
-// the 4 rows against all nb key blocks go to LDS in float64; then each
-// wavefront selects the top k of one row on order-preserving 64-bit keys with
-// an MSB-first bitwise search for the k-th largest key, and writes the chosen
-// indices in ascending order (ballot prefix counts).
-constexpr int SEL_RB = 4;
-constexpr int SEL_MAXPL = BSA_MAX_BLOCKS / 64;
+// One workgroup of 4 wavefronts per RB query blocks of one (b, h).
+//  1. Scores: thread t owns the key blocks c = t + 256 i (i < NKT) and
+//     accumulates, for each of the RB query blocks, the float64 dot product
+//     of the pooled vectors feature by feature in order 0..127 (float32
+//     products are exact in float64).  Key features come from L2 straight
+//     into registers, DCH at a time; the query features are the same for the
+//     whole wavefront.  The RB x nb scores go to LDS.
+//  2. Top-k: each wavefront takes one query block at a time.  Scores become
+//     order-preserving 64-bit keys held in registers (NCH keys per lane,
+//     key of block c in lane c % 64); an MSB-first bitwise search finds the
+//     threshold T, stopping early as soon as exactly k keys are >= the
+//     candidate (then those k are the answer).  Otherwise T is the k-th
+//     largest key; keys equal to T are taken lowest index first.  The chosen
+//     indices are written in ascending order with ballot prefix counts.
+// Every score is reduced in the same order, so identical key blocks tie
+// bit-exactly and the lower index wins.
 
 __device__ __forceinline__ uint64_t order_key(double s) {
   if (s == 0.0) s = 0.0;  // -0 ties with +0
@@ -297,86 +306,123 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+template <int NKT, int RB>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q_pool,
                                                      const float* __restrict__ k_pool,
                                                      int32_t* __restrict__ block_idx, int nb,
                                                      int ksel) {
-  extern __shared__ double sc[];  // [SEL_RB][nb]
-  __shared__ double qs[SEL_RB][HD];
-  __shared__ float kT[HD][65];
+  constexpr int NCH = NKT * 4;    // 64-key chunks per row in the top-k phase
+  constexpr int DCH = 32 / RB;    // features per step
+  extern __shared__ double sc[];  // [RB][nb]
   const int tid = threadIdx.x;
-  const int r0 = blockIdx.x * SEL_RB;
+  const int r0 = blockIdx.x * RB;
   const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
   const float* qpb = q_pool + bh * nb * HD;
   const float* kpb = k_pool + bh * nb * HD;
-  for (int i = tid; i < SEL_RB * HD; i += 256) {
-    const int r = i / HD, d = i % HD;
-    qs[r][d] = (r0 + r < nb) ? (double)qpb[(size_t)(r0 + r) * HD + d] : 0.0;
+
+  double acc[NKT][RB];
+#pragma unroll
+  for (int i = 0; i < NKT; ++i)
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) acc[i][rr] = 0.0;
+  int crow[NKT];
+#pragma unroll
+  for (int i = 0; i < NKT; ++i) crow[i] = min(tid + 256 * i, nb - 1);  // valid row to read
+  for (int d0 = 0; d0 < HD; d0 += DCH) {
+    double qv[RB][DCH];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int r = min(r0 + rr, nb - 1);
+#pragma unroll
+      for (int e = 0; e < DCH; ++e) qv[rr][e] = (double)qpb[(size_t)r * HD + d0 + e];
+    }
+#pragma unroll
+    for (int i = 0; i < NKT; ++i) {
+      float kv[DCH];
+      if constexpr (DCH % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < DCH; e += 4) {
+          const float4 t = *(const float4*)(kpb + (size_t)crow[i] * HD + d0 + e);
+          kv[e] = t.x;
+          kv[e + 1] = t.y;
+          kv[e + 2] = t.z;
+          kv[e + 3] = t.w;
+        }
+      } else {
+        static_assert(DCH == 2, "feature step");
+        const float2 t = *(const float2*)(kpb + (size_t)crow[i] * HD + d0);
+        kv[0] = t.x;
+        kv[1] = t.y;
+      }
+#pragma unroll
+      for (int e = 0; e < DCH; ++e) {
+        const double k64 = (double)kv[e];
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) acc[i][rr] = fma(qv[rr][e], k64, acc[i][rr]);
+      }
+    }
   }
-  for (int c0 = 0; c0 < nb; c0 += 64) {
-    __syncthreads();
-    for (int i = tid; i < 64 * 32; i += 256) {
-      const int c = i >> 5, d4 = i & 31;
-      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + c < nb) val = *(const float4*)(kpb + (size_t)(c0 + c) * HD + 4 * d4);
-      kT[4 * d4 + 0][c] = val.x;
-      kT[4 * d4 + 1][c] = val.y;
-      kT[4 * d4 + 2][c] = val.z;
-      kT[4 * d4 + 3][c] = val.w;
+#pragma unroll
+  for (int i = 0; i < NKT; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nb) {
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) sc[rr * nb + c] = acc[i][rr];
     }
-    __syncthreads();
-    const int c = tid & 63, r = tid >> 6;
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-#pragma unroll 8
-    for (int d = 0; d < HD; d += 4) {
-      a0 = fma(qs[r][d + 0], (double)kT[d + 0][c], a0);
-      a1 = fma(qs[r][d + 1], (double)kT[d + 1][c], a1);
-      a2 = fma(qs[r][d + 2], (double)kT[d + 2][c], a2);
-      a3 = fma(qs[r][d + 3], (double)kT[d + 3][c], a3);
-    }
-    if (c0 + c < nb) sc[r * nb + c0 + c] = (a0 + a1) + (a2 + a3);
   }
   __syncthreads();
 
   const int w = tid >> 6, lane = tid & 63;
-  const int r = r0 + w;
-  if (r >= nb || ksel == 0) return;
-  const double* srow = sc + w * nb;
-  uint64_t key[SEL_MAXPL];
-#pragma unroll
-  for (int i = 0; i < SEL_MAXPL; ++i) {
-    const int c = i * 64 + lane;
-    key[i] = (c < nb) ? order_key(srow[c]) : 0ull;  // real keys are > 0
-  }
-  // T = largest value with #{key >= T} >= ksel, i.e. the ksel-th largest key
-  uint64_t T = 0;
-  for (int bit = 63; bit >= 0; --bit) {
-    const uint64_t cand = T | (1ull << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < SEL_MAXPL; ++i)
-      if (i * 64 < nb) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= ksel) T = cand;
-  }
-  int gt = 0;
-#pragma unroll
-  for (int i = 0; i < SEL_MAXPL; ++i)
-    if (i * 64 < nb) gt += __popcll(__ballot(key[i] > T));
-  const int need_eq = ksel - gt;  // keys equal to T taken lowest index first
   const uint64_t lt = (1ull << lane) - 1ull;
-  int eq_before = 0, sel_before = 0;
-  int32_t* orow = block_idx + (bh * nb + r) * (size_t)ksel;
+  for (int rr = w; rr < RB; rr += 4) {
+    const int r = r0 + rr;
+    if (r >= nb || ksel == 0) break;
+    const double* srow = sc + rr * nb;
+    uint64_t key[NCH];
 #pragma unroll
-  for (int i = 0; i < SEL_MAXPL; ++i) {
-    if (i * 64 >= nb) break;
-    const bool is_eq = key[i] == T, is_gt = key[i] > T;
-    const uint64_t em = __ballot(is_eq);
-    const int erank = eq_before + __popcll(em & lt);
-    const bool sel = is_gt || (is_eq && erank < need_eq);
-    const uint64_t sm = __ballot(sel);
-    if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
-    eq_before += __popcll(em);
-    sel_before += __popcll(sm);
+    for (int i = 0; i < NCH; ++i) {
+      const int cc = i * 64 + lane;
+      key[i] = (cc < nb) ? order_key(srow[cc]) : 0ull;  // real keys are > 0
+    }
+    uint64_t T = 0;
+    bool exact = false;  // exactly ksel keys are >= T
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = T | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= ksel) {
+        T = cand;
+        if (cnt == ksel) {
+          exact = true;
+          break;
+        }
+      }
+    }
+    int need_eq = 0;
+    if (!exact) {
+      int gt = 0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) gt += __popcll(__ballot(key[i] > T));
+      need_eq = ksel - gt;  // keys equal to T taken lowest index first
+    }
+    int eq_before = 0, sel_before = 0;
+    int32_t* orow = block_idx + (bh * nb + r) * (size_t)ksel;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      bool sel;
+      if (exact) {
+        sel = key[i] >= T;
+      } else {
+        const bool is_eq = key[i] == T;
+        const uint64_t em = __ballot(is_eq);
+        sel = key[i] > T || (is_eq && eq_before + __popcll(em & lt) < need_eq);
+        eq_before += __popcll(em);
+      }
+      const uint64_t sm = __ballot(sel);
+      if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
+      sel_before += __popcll(sm);
+    }
   }
 }
 
@@ -734,6 +780,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const float mask1 = mask_value(d1);
     bf16x8 pb[4];
     float alpha;
+    // the softmax-heavy region issues at raised priority so its VALU work
+    // is not starved by the other wavefront's MFMA-only region on this SIMD
+    __builtin_amdgcn_s_setprio(3);
     if (need_add)
       alpha = region_a(kn, sn, sc, true, addvc, pb, d2, kd, d1, vd);
     else
@@ -742,6 +791,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
+    __builtin_amdgcn_s_setprio(0);
     region_b(vc, pb);
     store_mask(d1, mask1, addvn);
     d0 = d1;
@@ -834,6 +884,22 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
 
+template <int NKT, int RB>
+int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, int32_t* block_idx,
+                  hipStream_t stream) {
+  const dim3 grid((unsigned)((g.nb + RB - 1) / RB), (unsigned)g.H, (unsigned)g.B);
+  const size_t lds = (size_t)RB * g.nb * sizeof(double);
+  if (lds > 48 * 1024) {
+    // allow the score rows of large sequences beyond the default dynamic LDS cap
+    if (hipFuncSetAttribute((const void*)select_kernel<NKT, RB>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return BSA_ERR_HIP;
+  }
+  hipLaunchKernelGGL((select_kernel<NKT, RB>), grid, dim3(256), lds, stream, q_pool, k_pool, block_idx,
+                     (int)g.nb, (int)g.k);
+  return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -915,17 +981,13 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   if (g.k == 0) return BSA_OK;
   if (!q_pool || !k_pool || !block_idx) return BSA_ERR_INVALID;
   if (!aligned16(q_pool) || !aligned16(k_pool)) return BSA_ERR_INVALID;
-  const dim3 grid((unsigned)((g.nb + SEL_RB - 1) / SEL_RB), (unsigned)g.H, (unsigned)g.B);
-  const size_t lds = (size_t)SEL_RB * g.nb * sizeof(double);
-  if (lds > 48 * 1024) {
-    // allow the score rows of large sequences beyond the default dynamic LDS cap
-    if (hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-      return BSA_ERR_HIP;
-  }
-  hipLaunchKernelGGL(select_kernel, grid, dim3(256), lds, (hipStream_t)hip_stream, q_pool, k_pool,
-                     block_idx, (int)g.nb, (int)g.k);
-  return launch_status();
+  hipStream_t s = (hipStream_t)hip_stream;
+  // key blocks per thread sized to nb; query blocks per workgroup sized so
+  // the float64 score rows fit in 64 KiB of LDS
+  if (g.nb <= 256) return launch_select<1, 16>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 512) return launch_select<2, 16>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 1024) return launch_select<4, 8>(g, q_pool, k_pool, block_idx, s);
+  return launch_select<8, 4>(g, q_pool, k_pool, block_idx, s);
 }
 
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
