@@ -545,7 +545,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __syncthreads();
 
   const int n_exact = 2 * ksel;
-  const int ntiles = n_exact + ((ksel < nb) ? 2 * nsb : 0);
+  // summary half tiles: only those holding rows below nb (a group of 128
+  // summary rows past the end contributes nothing)
+  const int ntiles = n_exact + ((ksel < nb) ? (nb + HT - 1) / HT : 0);
 
   // block index of half tile t (exact tiles), read from LDS; issued one step
   // before describe() needs it
@@ -748,13 +750,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 
   // Region B: O^T += V^T(t) P(t)^T, 16 MFMAs (db fastest: 4 independent chains)
   auto region_b = [&](const uint16_t* vc, const bf16x8* pb) {
-    bf16x8 vop0 = v_operand(vc, 0), vop1 = v_operand(vc, 1), vop2;
+    // operands read three slots ahead (region B has no VALU work to hide
+    // the LDS latency behind)
+    bf16x8 vop0 = v_operand(vc, 0), vop1 = v_operand(vc, 1), vop2 = v_operand(vc, 2), vop3;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) vop2 = v_operand(vc, i + 2);
+      if (i + 3 < 16) vop3 = v_operand(vc, i + 3);
       o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop0, pb[i >> 2], o[i & 3], 0, 0, 0);
       vop0 = vop1;
       vop1 = vop2;
+      vop2 = vop3;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
