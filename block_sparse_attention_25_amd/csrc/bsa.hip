@@ -749,7 +749,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   };
 
   // Region B: O^T += V^T(t) P(t)^T, 16 MFMAs (db fastest: 4 independent chains)
-  auto region_b = [&](const uint16_t* vc, const bf16x8* pb) {
+  auto region_b = [&](const uint16_t* vc, const bf16x8* pb, auto&& bookkeeping) {
     // operands read three slots ahead (region B has no VALU work to hide
     // the LDS latency behind)
     bf16x8 vop0 = v_operand(vc, 0), vop1 = v_operand(vc, 1), vop2 = v_operand(vc, 2), vop3;
@@ -757,6 +757,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     for (int i = 0; i < 16; ++i) {
       if (i + 3 < 16) vop3 = v_operand(vc, i + 3);
       o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop0, pb[i >> 2], o[i & 3], 0, 0, 0);
+      // the next step's descriptors and key mask, in the issue slots this
+      // MFMA-only region leaves free
+      if (i == 4) bookkeeping();
       vop0 = vop1;
       vop1 = vop2;
       vop2 = vop3;
@@ -797,11 +800,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
     __builtin_amdgcn_s_setprio(0);
-    region_b(vc, pb);
-    store_mask(d1, mask1, addvn);
-    d0 = d1;
-    d1 = d2;
-    d2 = describe(t + 3, c3);
+    region_b(vc, pb, [&]() {
+      store_mask(d1, mask1, addvn);
+      d0 = d1;
+      d1 = d2;
+      d2 = describe(t + 3, c3);
+    });
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
