@@ -29,7 +29,8 @@ Readings taken where the pages are silent (each is exercised by a test):
   R2 block score: plain dot product of the pooled query and key vectors (the
      softmax scale does not change a ranking).
   R3 ties: equal scores go to the lower block index; output ascending.
-  R4 no forced blocks (no diagonal or sink block is added to the top-k).
+  R4 no forced blocks (no diagonal or sink block is added to the top-k)
+     unless a conditioning range is given (R12).
   R5 a top-k ratio budget becomes k = ceil(ratio * n_blocks) computed exactly.
   R6 softmax scale 1/sqrt(d) for exact and summary logits alike; the bias is
      added in scaled-logit units.
@@ -42,6 +43,19 @@ Readings taken where the pages are silent (each is exercised by a test):
      lead the sequence); anchor_rows = 0 means all rows.
   R10 selection uses the mean-pooled vectors in both summary modes.
   R11 no causal mask.
+  R12 conditioning sinks (the "exact_kv_and_rows" routing): the conditioning
+     rows (prompt, reference, audio) form one contiguous row range.  Every
+     block holding at least one of its rows is a sink block: it is forced
+     into every query block's exact set, on top of the top_k picked among the
+     other blocks (so a row holds min(top_k, nb - n_sink) + n_sink blocks),
+     and a query block that is itself a sink block attends to every key block
+     exactly (no summary rows).  Sources: "H3 Sparse Attention" (WAS Node
+     Suite node page), section "The inputs that matter" (sink_conditioning
+     reads the prompt, reference and audio rows exactly and runs those rows
+     dense); "H3 Sparse Attention" (the node page on video budgets), opening
+     section (conditioning, non-video queries and the tiles on the boundary
+     between contexts stay fully dense; only video-to-video attention is
+     cut).  The block straddling the boundary counts as a sink block.
 
 Precision: pooled vectors are summed in float64 and stored as float32 (the
 precision in which a block ranking is decided); block scores are float64 dot
@@ -113,18 +127,35 @@ def block_scores(q_pool: np.ndarray, k_pool: np.ndarray) -> np.ndarray:
     return s
 
 
-def select_topk(scores: np.ndarray, top_k: int) -> np.ndarray:
+def select_topk(scores: np.ndarray, top_k: int, forced=()) -> np.ndarray:
     """For each query block r the k key blocks of largest score, ties to the
     lower index (R3), returned in ascending index order; int32 [nb, k].
 
+    With forced blocks (R12) every row holds all of them plus the top_k of the
+    remaining blocks, k = min(top_k, nb - n_forced) + n_forced.
+
     PyPI page, opening paragraph ("attends to its top-k key blocks")."""
     nq, nk = scores.shape
-    k = effective_k(top_k, nk)
-    idx = np.zeros((nq, k), dtype=np.int32)
+    F = sorted(set(int(c) for c in forced))
+    if any(c < 0 or c >= nk for c in F):
+        raise ValueError("forced block out of range")
+    rest = [c for c in range(nk) if c not in set(F)]
+    k = effective_k(top_k, len(rest))
+    idx = np.zeros((nq, len(F) + k), dtype=np.int32)
     for r in range(nq):
-        order = sorted(range(nk), key=lambda c: (-scores[r, c], c))
-        idx[r] = sorted(order[:k])
+        order = sorted(rest, key=lambda c: (-scores[r, c], c))
+        idx[r] = sorted(F + order[:k])
     return idx
+
+
+def sink_blocks(N: int, sink_start: int, sink_rows: int, block: int = BLOCK):
+    """Blocks holding at least one row of the conditioning range
+    [sink_start, sink_start + sink_rows) (R12); empty when sink_rows is 0."""
+    if sink_start < 0 or sink_rows < 0 or sink_start + sink_rows > N:
+        raise ValueError("conditioning range out of bounds")
+    if sink_rows == 0:
+        return []
+    return list(range(sink_start // block, (sink_start + sink_rows - 1) // block + 1))
 
 
 # -------------------------------------------------------------- summaries ---
@@ -185,7 +216,7 @@ def summaries_reweight(k: np.ndarray, v: np.ndarray, a: np.ndarray, scale: float
 
 # -------------------------------------------------------------- attention ---
 def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK,
-              query_blocks=None):
+              query_blocks=None, dense_blocks=()):
     """Block-sparse attention with summary rows for one (batch, head).
 
     For query i in block r, the logits are
@@ -197,8 +228,10 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
     "What Spark-Attn changes" (exact and compressed branches of one pass).
 
     idx may be any [nb, k] array of distinct valid block indices per row (the
-    output is unique given idx).  query_blocks restricts the work to those
-    query blocks (other output rows stay zero).  Returns float64 [N, d]."""
+    output is unique given idx).  Query blocks listed in dense_blocks attend to
+    every key block exactly, whatever idx holds for them (R12).  query_blocks
+    restricts the work to those query blocks (other output rows stay zero).
+    Returns float64 [N, d]."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -212,7 +245,7 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
     for r, (s, e) in enumerate(rows):
         if query_blocks is not None and r not in query_blocks:
             continue
-        sel = [int(c) for c in idx[r]]
+        sel = list(range(nb)) if r in set(dense_blocks) else [int(c) for c in idx[r]]
         if len(set(sel)) != len(sel) or any(c < 0 or c >= nb for c in sel):
             raise ValueError("idx row %d is not a set of valid blocks" % r)
         chosen = set(sel)
@@ -237,9 +270,12 @@ def default_scale(d: int) -> float:
 
 
 def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
-             scale: float | None = None, block: int = BLOCK, bias_ref: str = "mean"):
+             scale: float | None = None, block: int = BLOCK, bias_ref: str = "mean",
+             sink_start: int = 0, sink_rows: int = 0):
     """All four stages for one (batch, head).  Returns a dict with the pooled
-    vectors, scores, selection, summaries and the float64 output."""
+    vectors, scores, selection, summaries, sink blocks and the float64 output.
+    sink_rows > 0 routes the conditioning rows [sink_start, sink_start +
+    sink_rows) as sinks (R12)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -248,7 +284,8 @@ def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
     q_pool = pool_mean(q, block)
     k_pool = pool_mean(k, block)
     s = block_scores(q_pool, k_pool)
-    idx = select_topk(s, top_k)
+    sinks = sink_blocks(q.shape[0], sink_start, sink_rows, block)
+    idx = select_topk(s, top_k, sinks)
     if summary == "mean":
         sk, sv, b = summaries_mean(k, v, block)
     elif summary == "reweight":
@@ -256,6 +293,6 @@ def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
         sk, sv, b = summaries_reweight(k, v, a, sc, block, bias_ref)
     else:
         raise ValueError("summary must be 'mean' or 'reweight'")
-    out = attention(q, k, v, idx, sk, sv, b, sc, block)
+    out = attention(q, k, v, idx, sk, sv, b, sc, block, dense_blocks=sinks)
     return dict(q_pool=q_pool, k_pool=k_pool, scores=s, idx=idx, sum_k=sk,
-                sum_v=sv, bias=b, out=out, scale=sc)
+                sum_v=sv, bias=b, out=out, scale=sc, sinks=sinks)

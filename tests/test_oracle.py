@@ -385,6 +385,87 @@ def test_reweight_constant_logit_block():
     assert np.abs(sv[0] - v.mean(0)).max() < 1e-14
 
 
+# ------------------------------------------------- conditioning sinks (R12) ---
+def test_sink_blocks_ranges():
+    """Blocks holding the conditioning rows, by hand: the range's first and
+    last row, each divided by the block size."""
+    assert O.sink_blocks(4096, 4032, 64) == [31]
+    assert O.sink_blocks(4096, 3968, 128) == [31]          # starts on a block boundary
+    assert O.sink_blocks(4096, 3967, 129) == [30, 31]      # one row into the previous block
+    assert O.sink_blocks(4096, 3968, 127) == [31]          # ends one row short of N
+    assert O.sink_blocks(4096, 0, 1) == [0]
+    assert O.sink_blocks(4096, 0, 128) == [0]              # ends exactly on a boundary
+    assert O.sink_blocks(4096, 128, 256) == [1, 2]
+    assert O.sink_blocks(4096, 100, 0) == []
+    # the 768p 5s shape: 36,288 video rows then 1,452 conditioning rows
+    assert O.sink_blocks(37740, 36288, 1452) == list(range(283, 295))
+    # the 2K 5s shape: the last 1,024 of 133,644 rows
+    assert O.sink_blocks(133644, 132620, 1024) == list(range(1036, 1045))
+    for bad in [(-1, 4), (4000, 97), (0, 4097)]:
+        with pytest.raises(ValueError):
+            O.sink_blocks(4096, *bad)
+
+
+@pytest.mark.parametrize("N,forced", [(500, [1]), (640, [0, 4]), (640, [4]), (512, [0, 1, 2, 3])])
+def test_select_forced_brute_force(N, forced):
+    """Every row holds the forced blocks plus the brute-force top-k of the
+    other blocks."""
+    q, k, _ = _synth_head(N, seed=N + 1)
+    s = O.block_scores(O.pool_mean(q), O.pool_mean(k))
+    nb = O.n_blocks(N)
+    rest = [c for c in range(nb) if c not in forced]
+    for top_k in range(0, nb + 2):
+        idx = O.select_topk(s, top_k, forced)
+        kk = min(top_k, len(rest))
+        assert idx.shape == (nb, len(forced) + kk)
+        for r in range(nb):
+            sub = _brute_force_select(s[r, rest], kk)
+            assert list(idx[r]) == sorted(forced + [rest[i] for i in sub])
+    assert np.array_equal(O.select_topk(s, 2, []), O.select_topk(s, 2))
+
+
+@pytest.mark.parametrize("N,start,rows,top_k", [(700, 600, 100, 1), (1000, 250, 300, 2), (640, 500, 10, 0)])
+def test_sink_query_blocks_are_dense(N, start, rows, top_k):
+    """A query block holding conditioning rows attends densely: its output
+    rows equal plain softmax attention over the whole sequence."""
+    q, k, v = _synth_head(N, seed=start)
+    res = O.run_head(q, k, v, top_k=top_k, sink_start=start, sink_rows=rows)
+    ref = _sdpa(q, k, v)
+    assert res["sinks"] == O.sink_blocks(N, start, rows)
+    for c in res["sinks"]:
+        r0, r1 = O.block_rows(N)[c]
+        assert np.abs(res["out"][r0:r1] - ref[r0:r1]).max() < 1e-10
+    # the other query blocks are not dense (their summary rows are in play)
+    others = [c for c in range(O.n_blocks(N)) if c not in res["sinks"]]
+    r0, r1 = O.block_rows(N)[others[0]]
+    assert np.abs(res["out"][r0:r1] - ref[r0:r1]).max() > 1e-6
+
+
+def test_sink_covering_everything_is_dense_attention():
+    q, k, v = _synth_head(600, seed=3)
+    res = O.run_head(q, k, v, top_k=0, sink_start=0, sink_rows=600)
+    assert np.abs(res["out"] - _sdpa(q, k, v)).max() < 1e-10
+
+
+@pytest.mark.parametrize("summary", ["mean", "reweight"])
+def test_sink_with_topk_zero_is_sinks_plus_summaries(summary):
+    """top_k = 0 with sinks: a non-sink query attends exactly to the rows of
+    the sink blocks and to one summary row (with its bias) per other block."""
+    N, start, rows = 900, 700, 200
+    q, k, v = _synth_head(N, seed=21)
+    res = O.run_head(q, k, v, top_k=0, summary=summary, sink_start=start, sink_rows=rows)
+    sinks = res["sinks"]
+    assert sinks == [5, 6, 7]
+    blocks = O.block_rows(N)
+    others = [c for c in range(len(blocks)) if c not in sinks]
+    K = np.concatenate([k[blocks[c][0]:blocks[c][1]] for c in sinks] + [res["sum_k"][others]])
+    V = np.concatenate([v[blocks[c][0]:blocks[c][1]] for c in sinks] + [res["sum_v"][others]])
+    add = np.concatenate([np.zeros(blocks[c][1] - blocks[c][0]) for c in sinks] + [res["bias"][others]])
+    r1 = blocks[others[-1]][1]
+    ref = _sdpa(q[:r1], K, V, mask=np.repeat(add[None, :], r1, axis=0))
+    assert np.abs(res["out"][:r1] - ref).max() < 1e-10
+
+
 # -------------------------------------------------- planted mistakes fail ---
 def _all_pins_pass():
     """Re-run a compact set of the pins above; True when every one holds."""
@@ -401,6 +482,10 @@ def _all_pins_pass():
         test_reweight_two_value_block_closed_form()
         test_reweight_bias_nonnegative_and_mass_matches()
         test_anchor_closed_form()
+        test_sink_blocks_ranges()
+        test_select_forced_brute_force(640, [0, 4])
+        test_sink_query_blocks_are_dense(700, 600, 100, 1)
+        test_sink_with_topk_zero_is_sinks_plus_summaries("mean")
     except AssertionError:
         return False
     return True
@@ -415,6 +500,8 @@ _orig_attn = O.attention
 _orig_rw = O.summaries_reweight
 _orig_scores = O.block_scores
 _orig_anchor = O.anchor
+_orig_select = O.select_topk
+_orig_sink_blocks = O.sink_blocks
 
 
 def _pool_padded(x, block=128):
@@ -423,19 +510,40 @@ def _pool_padded(x, block=128):
     return np.array([x[s:e].sum(0) / block for s, e in O.block_rows(len(x), block)]).astype(np.float32)
 
 
-def _attn_no_bias(q, k, v, idx, sk, sv, b, scale, block=128):
-    return _orig_attn(q, k, v, idx, sk, sv, np.zeros_like(np.asarray(b, dtype=float)), scale, block)
+def _attn_no_bias(q, k, v, idx, sk, sv, b, scale, block=128, **kw):
+    return _orig_attn(q, k, v, idx, sk, sv, np.zeros_like(np.asarray(b, dtype=float)), scale, block, **kw)
 
 
-def _attn_bias_sign(q, k, v, idx, sk, sv, b, scale, block=128):
-    return _orig_attn(q, k, v, idx, sk, sv, -np.asarray(b, dtype=float), scale, block)
+def _attn_bias_sign(q, k, v, idx, sk, sv, b, scale, block=128, **kw):
+    return _orig_attn(q, k, v, idx, sk, sv, -np.asarray(b, dtype=float), scale, block, **kw)
 
 
-def _attn_wrong_scale(q, k, v, idx, sk, sv, b, scale, block=128):
-    return _orig_attn(q, k, v, idx, sk, sv, b, scale * scale, block)
+def _attn_wrong_scale(q, k, v, idx, sk, sv, b, scale, block=128, **kw):
+    return _orig_attn(q, k, v, idx, sk, sv, b, scale * scale, block, **kw)
 
 
-def _attn_summaries_for_all(q, k, v, idx, sk, sv, b, scale, block=128):
+def _attn_dense_ignored(q, k, v, idx, sk, sv, b, scale, block=128, query_blocks=None, dense_blocks=()):
+    # mistake: conditioning query blocks routed like every other block
+    return _orig_attn(q, k, v, idx, sk, sv, b, scale, block, query_blocks=query_blocks)
+
+
+def _select_forced_in_pool(scores, top_k, forced=()):
+    # mistake: forced blocks unioned with the top-k of all blocks (a forced
+    # block that also ranks high takes a top-k place)
+    base = _orig_select(scores, top_k)
+    rows = [sorted(set(r) | set(forced)) for r in base.tolist()]
+    width = max(len(r) for r in rows)
+    return np.array([r + r[-1:] * (width - len(r)) for r in rows], dtype=np.int32)
+
+
+def _sink_blocks_end_inclusive(N, sink_start, sink_rows, block=128):
+    # mistake: the end of the range taken as inclusive
+    if sink_rows == 0:
+        return []
+    return list(range(sink_start // block, min((sink_start + sink_rows) // block, -(-N // block) - 1) + 1))
+
+
+def _attn_summaries_for_all(q, k, v, idx, sk, sv, b, scale, block=128, **kw):
     # mistake: summary rows kept for the selected blocks too
     N, d = np.asarray(q).shape
     nb = O.n_blocks(N, block)
@@ -484,6 +592,9 @@ def _anchor_off_by_one(q, anchor_rows):
     ("summaries_reweight", _rw_no_weights),
     ("summaries_reweight", _rw_log_sum),
     ("anchor", _anchor_off_by_one),
+    ("attention", _attn_dense_ignored),
+    ("select_topk", _select_forced_in_pool),
+    ("sink_blocks", _sink_blocks_end_inclusive),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
@@ -491,7 +602,7 @@ def test_planted_mistake_is_caught(monkeypatch, name, fn):
 
 
 def test_planted_tie_rule_mistake_is_caught(monkeypatch):
-    def select_high_index(scores, top_k):
+    def select_high_index(scores, top_k, forced=()):
         nq, nk = scores.shape
         k = O.effective_k(top_k, nk)
         idx = np.zeros((nq, k), dtype=np.int32)
