@@ -56,15 +56,20 @@ def measured_traffic(workload):
     return float(fields["traffic_bytes"])
 
 
-def counted_flops(torch, idx, N, nb, H, B):
-    """4 * d * sum over (b, h, r) of n_r * sum_{c in S(r)} n_c, exactly."""
+def counted_flops(torch, idx, N, nb, H, B, dense=()):
+    """4 * d * sum over (b, h, r) of n_r * sum_{c in S(r)} n_c, exactly; query
+    blocks in `dense` (conditioning sinks) attend to all N keys."""
     n = torch.full((nb,), 128, dtype=torch.int64, device=idx.device)
     n[-1] = N - 128 * (nb - 1)
     k = idx.shape[-1]
     per_row = n[idx.long()].sum(-1) if k > 0 else torch.zeros((B, H, nb), dtype=torch.int64,
                                                                device=idx.device)
+    n_skip = torch.full((nb,), nb - k, dtype=torch.int64, device=idx.device)
+    if len(dense):
+        per_row[..., list(dense)] = N
+        n_skip[list(dense)] = 0
     exact = int((per_row * n).sum().item())
-    summary = int((n * (nb - k)).sum().item()) * B * H
+    summary = int((n * n_skip).sum().item()) * B * H
     return 4 * 128 * exact, 4 * 128 * summary
 
 
@@ -85,19 +90,21 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
     rows = O.block_rows(N)
     top_k = w.top_k if w.top_k is not None else O.k_from_ratio(w.top_k_ratio, nb)
     sc = O.default_scale(128)
+    sinks = O.sink_blocks(N, w.sink_start, w.sink_rows)
     flops, heads_done, blocks_done = 0, 0, 0
     t0 = time.perf_counter()
     for h in range(qb.shape[1]):
         Q, K, V = (bf16_to_f32(x[0, h]).astype(np.float64) for x in (qb, kb, vb))
         qp, kp = O.pool_mean(Q), O.pool_mean(K)
-        idx = O.select_topk(O.block_scores(qp, kp), top_k)
+        idx = O.select_topk(O.block_scores(qp, kp), top_k, sinks)
         if w.summary == "reweight":
             sk, sv, b = O.summaries_reweight(K, V, O.anchor(Q, w.anchor_rows), sc)
         else:
             sk, sv, b = O.summaries_mean(K, V)
         for r in range(nb):
-            O.attention(Q, K, V, idx, sk, sv, b, sc, query_blocks=[r])
-            flops += 4 * 128 * (rows[r][1] - rows[r][0]) * sum(rows[c][1] - rows[c][0] for c in idx[r])
+            O.attention(Q, K, V, idx, sk, sv, b, sc, query_blocks=[r], dense_blocks=sinks)
+            keys = N if r in sinks else sum(rows[c][1] - rows[c][0] for c in idx[r])
+            flops += 4 * 128 * (rows[r][1] - rows[r][0]) * keys
             blocks_done += 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -139,7 +146,10 @@ def main():
 
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     p = bsa.make_problem(B, H, N, top_k, None, w.summary,
-                         w.anchor_rows if w.summary == "reweight" else 0)
+                         w.anchor_rows if w.summary == "reweight" else 0,
+                         sink_rows=w.sink_rows, sink_start=w.sink_start)
+    dense = list(range(w.sink_start // 128, (w.sink_start + w.sink_rows - 1) // 128 + 1)) \
+        if w.sink_rows > 0 else []
     nb, kk = bsa.bsa_problem_blocks(p)
     f32 = torch.float32
     q_pool = torch.empty((B, H, nb, 128), dtype=f32, device=dev)
@@ -174,7 +184,7 @@ def main():
     sel_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     attn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
     step_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
-    flops, summary_flops = counted_flops(torch, idx, N, nb, H, B)
+    flops, summary_flops = counted_flops(torch, idx, N, nb, H, B, dense)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
     # pool: read Q, K, V once; write q_pool, k_pool (fp32), sum_k, sum_v (bf16),
@@ -205,7 +215,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": 128,
-                   "n_blocks": nb, "top_k": kk, "summary": w.summary},
+                   "n_blocks": nb, "top_k": kk, "summary": w.summary,
+                   "sink_rows": w.sink_rows},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"pool": round(pool_ms, 4), "select": round(sel_ms, 4),
                        "attention": round(attn_ms, 4)},

@@ -41,6 +41,7 @@ class Problem(ctypes.Structure):
         ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("summary", ctypes.c_int32), ("anchor_rows", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("sink_start", ctypes.c_int32), ("sink_rows", ctypes.c_int32),
     ]
 
 
@@ -147,7 +148,10 @@ def k_from_ratio(ratio, n_blocks: int) -> int:
 
 
 def make_problem(batch, heads, seq_len, top_k=None, top_k_ratio=None, summary="mean",
-                 anchor_rows=0, scale=None) -> Problem:
+                 anchor_rows=0, scale=None, sink_rows=0, sink_start=None) -> Problem:
+    """Fill a bsa_problem.  sink_rows > 0 routes the conditioning rows
+    [sink_start, sink_start + sink_rows) as sinks; sink_start defaults to
+    N - sink_rows (conditioning rows after the video rows)."""
     nb = -(-int(seq_len) // BLOCK)
     if (top_k is None) == (top_k_ratio is None):
         raise ValueError("give exactly one of top_k and top_k_ratio")
@@ -155,9 +159,12 @@ def make_problem(batch, heads, seq_len, top_k=None, top_k_ratio=None, summary="m
         top_k = k_from_ratio(top_k_ratio, nb)
     if summary not in ("mean", "reweight"):
         raise ValueError("summary must be 'mean' or 'reweight'")
+    sink_rows = int(sink_rows)
+    if sink_start is None:
+        sink_start = int(seq_len) - sink_rows if sink_rows > 0 else 0
     return Problem(int(batch), int(heads), int(seq_len), HEAD_DIM, BLOCK, int(top_k),
                    SUMMARY_MEAN if summary == "mean" else SUMMARY_REWEIGHT, int(anchor_rows),
-                   0.0 if scale is None else float(scale))
+                   0.0 if scale is None else float(scale), int(sink_start), sink_rows)
 
 
 def _check_qkv(q, k, v):
@@ -174,17 +181,21 @@ def _check_qkv(q, k, v):
 
 
 def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows=0, scale=None,
-              return_aux=False, stream=None):
+              sink_rows=0, sink_start=None, return_aux=False, stream=None):
     """Block-sparse attention of bf16 q, k, v [B, H, N, 128] on the GPU.
 
     top_k counts 128-token key blocks (or give top_k_ratio, e.g. "0.1");
     summary is "mean" or "reweight" (Spark-Reweight, anchor = mean of query
-    rows [0, anchor_rows), 0 meaning all rows).  Returns out [B, H, N, 128]
-    bf16, plus a dict of intermediate tensors when return_aux is set."""
+    rows [0, anchor_rows), 0 meaning all rows).  sink_rows > 0 routes the
+    conditioning rows [sink_start, sink_start + sink_rows) (by default the
+    last sink_rows rows) as sinks: their blocks are kept exactly by every
+    query block, and their query blocks attend densely.  Returns out
+    [B, H, N, 128] bf16, plus a dict of intermediate tensors when return_aux
+    is set."""
     import torch
     _check_qkv(q, k, v)
     B, H, N, _ = q.shape
-    p = make_problem(B, H, N, top_k, top_k_ratio, summary, anchor_rows, scale)
+    p = make_problem(B, H, N, top_k, top_k_ratio, summary, anchor_rows, scale, sink_rows, sink_start)
     nb, kk = bsa_problem_blocks(p)
     dev = q.device
     f32, bf = torch.float32, torch.bfloat16

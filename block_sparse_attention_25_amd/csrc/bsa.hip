@@ -310,7 +310,7 @@ template <int NKT, int RB>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q_pool,
                                                      const float* __restrict__ k_pool,
                                                      int32_t* __restrict__ block_idx, int nb,
-                                                     int ksel) {
+                                                     int ksel, int f0, int f1) {
   constexpr int NCH = NKT * 4;    // 64-key chunks per row in the top-k phase
   constexpr int DCH = 32 / RB;    // features per step
   extern __shared__ double sc[];  // [RB][nb]
@@ -382,7 +382,9 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int cc = i * 64 + lane;
-      key[i] = (cc < nb) ? order_key(srow[cc]) : 0ull;  // real keys are > 0
+      // real keys are > 0; sink blocks [f0, f1] take the largest key, so
+      // they are always kept and the rest of the row is the top-k of the others
+      key[i] = (cc < nb) ? ((cc >= f0 && cc <= f1) ? ~0ull : order_key(srow[cc])) : 0ull;
     }
     uint64_t T = 0;
     bool exact = false;  // exactly ksel keys are >= T
@@ -495,8 +497,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ sum_k,
     const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
-    const int32_t* __restrict__ block_idx, uint16_t* __restrict__ out, int N, int nb, int ksel,
-    int nsb, float scale_log2, int total_wg) {
+    const int32_t* __restrict__ block_idx, uint16_t* __restrict__ out, int N, int nb, int krow,
+    int nsb, float scale_log2, int total_wg, int f0, int f1) {
   // LDS buffers as distinct variables, so the compiler can tell the DMA
   // targets from the buffers being read
   __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
@@ -506,14 +508,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ int32_t sidx[BSA_MAX_BLOCKS];  // this query block's selected blocks
 
   const int logical = xcd_remap(blockIdx.x, total_wg);
-  const int r = logical % nb;
+  // each head's query blocks in sequence order starting at the first sink
+  // block, so the longer dense sink rows are dispatched first (identity when
+  // there are no sinks, f0 = 0)
+  const int r = (logical % nb + f0) % nb;
   const size_t bh = (size_t)(logical / nb);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
   const int g = lane >> 5, ln = lane & 31;
 
   const float* biasb = sum_bias ? sum_bias + bh * (size_t)nb : nullptr;
-  const int32_t* irow = block_idx + (bh * nb + r) * (size_t)ksel;
+  const int32_t* irow = block_idx + (bh * nb + r) * (size_t)krow;
+  // a conditioning sink query block attends to every key block exactly
+  const bool dense_row = r >= f0 && r <= f1;
+  const int ksel = dense_row ? nb : krow;
   // per-head buffer descriptors: K, V^T, summary K, summary V^T
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * (size_t)N * HD, (uint32_t)N * HD * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + bh * (size_t)nb * BLK * HD, (uint32_t)nb * BLK * HD * 2);
@@ -538,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   for (int i = tid; i < nwords; i += 256) selmask[i] = 0u;
   __syncthreads();
   for (int i = tid; i < ksel; i += 256) {
-    const int c = irow[i];
+    const int c = dense_row ? i : irow[i];
     sidx[i] = c;
     atomicOr(&selmask[c >> 5], 1u << (c & 31));
   }
@@ -837,6 +845,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 // ------------------------------------------------------------------ host ---
 struct Geometry {
   int64_t B, H, N, nb, nsb, k;
+  int64_t f0, f1;  // conditioning sink blocks [f0, f1]; f1 < f0 when there are none
   bool reweight;
   int anchor_rows;
   double scale;
@@ -856,13 +865,23 @@ int make_geometry(const bsa_problem* p, Geometry* g) {
   if (p->summary != BSA_SUMMARY_MEAN && p->summary != BSA_SUMMARY_REWEIGHT) return BSA_ERR_INVALID;
   if (p->anchor_rows < 0 || p->anchor_rows > p->seq_len) return BSA_ERR_INVALID;
   if (!(p->scale >= 0.f) || !isfinite(p->scale)) return BSA_ERR_INVALID;
+  if (p->sink_start < 0 || p->sink_rows < 0 || (int64_t)p->sink_start + p->sink_rows > p->seq_len)
+    return BSA_ERR_INVALID;
   g->B = p->batch;
   g->H = p->heads;
   g->N = p->seq_len;
   g->nb = (g->N + BLK - 1) / BLK;
   if (g->nb > BSA_MAX_BLOCKS) return BSA_ERR_UNSUPPORTED;
   g->nsb = (g->nb + BLK - 1) / BLK;
-  g->k = p->top_k < g->nb ? p->top_k : g->nb;
+  if (p->sink_rows > 0) {
+    g->f0 = p->sink_start / BLK;
+    g->f1 = ((int64_t)p->sink_start + p->sink_rows - 1) / BLK;
+  } else {
+    g->f0 = 0;
+    g->f1 = -1;
+  }
+  const int64_t n_sink = g->f1 - g->f0 + 1, rest = g->nb - n_sink;
+  g->k = n_sink + (p->top_k < rest ? p->top_k : rest);
   g->reweight = p->summary == BSA_SUMMARY_REWEIGHT;
   g->anchor_rows = p->anchor_rows == 0 ? p->seq_len : p->anchor_rows;
   g->scale = p->scale == 0.f ? 1.0 / sqrt((double)HD) : (double)p->scale;
@@ -905,7 +924,7 @@ int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, i
       return BSA_ERR_HIP;
   }
   hipLaunchKernelGGL((select_kernel<NKT, RB>), grid, dim3(256), lds, stream, q_pool, k_pool, block_idx,
-                     (int)g.nb, (int)g.k);
+                     (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1);
   return launch_status();
 }
 
@@ -1018,7 +1037,8 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, (hipStream_t)hip_stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)(ws + w.vt),
                      (const uint16_t*)sum_k, (const uint16_t*)(ws + w.svt), sum_bias, block_idx,
-                     (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total);
+                     (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total,
+                     (int)g.f0, (int)g.f1);
   return launch_status();
 }
 

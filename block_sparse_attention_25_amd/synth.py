@@ -49,6 +49,15 @@ class Workload:
     top_k_ratio: str | None = None   # exact decimal string, e.g. "0.1"
     summary: str = "mean"  # "mean" or "reweight"
     seed: int = 0
+    sinks: bool = False    # route the conditioning rows as sinks
+
+    @property
+    def sink_start(self) -> int:
+        return self.n_video if self.sinks else 0
+
+    @property
+    def sink_rows(self) -> int:
+        return self.n_cond if self.sinks else 0
 
     @property
     def seq_len(self) -> int:
@@ -67,6 +76,8 @@ WORKLOADS = {
     "2k_5s": Workload("2k_5s", 1, 56, (10, 90, 160), 132620, 1024, 64),
     "768p_15s_reweight": Workload("768p_15s_reweight", 1, 56, (25, 48, 84), 100800,
                                   3196, None, "0.1", "reweight"),
+    # the 768p 5s shape with its 1,452 conditioning rows routed as sinks
+    "768p_5s_sinks": Workload("768p_5s_sinks", 1, 56, (9, 48, 84), 36288, 1452, 64, sinks=True),
 }
 
 

@@ -20,7 +20,8 @@
  *     never allocates, frees or synchronises, and keeps no state between calls.
  *   - Tensors are contiguous.  Q, K, V and out are [B, H, N, 128] bfloat16
  *     (raw 16-bit storage), row-major with the feature dimension fastest.
- *   - nb = ceil(N / 128); k = min(top_k, nb).
+ *   - nb = ceil(N / 128); k = min(top_k, nb) without conditioning sinks, else
+ *     k = n_sink + min(top_k, nb - n_sink) (see bsa_problem.sink_rows).
  *   - Arguments are validated on the host before anything is launched; on any
  *     error nothing is launched and no output is touched.
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
@@ -65,6 +66,20 @@ typedef struct bsa_problem {
   int32_t anchor_rows; /* reweight: anchor = mean of query rows [0, anchor_rows);
                           0 means N; must lie in [0, N] */
   float scale;         /* softmax scale; 0 means 1/sqrt(head_dim); else > 0, finite */
+  /* Conditioning sinks: the rows [sink_start, sink_start + sink_rows) are
+   * conditioning rows (prompt, reference, audio).  The n_sink blocks holding
+   * any of them are sink blocks: every query block keeps all of them exactly,
+   * on top of the top_k it picks among the other blocks, and a query block
+   * that is a sink block attends to every key block exactly.  sink_rows = 0
+   * (with sink_start 0) means no sinks: pure top-k.  The range must lie in
+   * [0, N].  Sources: "H3 Sparse Attention" (WAS Node Suite node page),
+   * section "The inputs that matter" (sink_conditioning reads the prompt,
+   * reference and audio rows exactly and runs those rows dense); "H3 Sparse
+   * Attention" (node page on video budgets), opening section (conditioning
+   * and non-video queries, and the tiles on the boundary between contexts,
+   * stay dense). */
+  int32_t sink_start;
+  int32_t sink_rows;
 } bsa_problem;
 
 /* Text of a status code (static storage, never NULL). */
@@ -119,7 +134,9 @@ int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v,
  * The score of query block r against key block c is q_pool[r] . k_pool[c],
  * evaluated in float64 (exact products, float64 sums).  Row r of block_idx
  * holds the k blocks of largest score, equal scores going to the lower block
- * index, in strictly ascending order.  block_idx may be NULL when k == 0.
+ * index, in strictly ascending order; with conditioning sinks it holds the
+ * sink blocks plus the k - n_sink best of the other blocks.  block_idx may be
+ * NULL when k == 0.
  * Requires nb <= BSA_MAX_BLOCKS (else BSA_ERR_UNSUPPORTED).
  */
 int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
@@ -144,7 +161,8 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
  * block in block_idx[r], and scale * q_i . sum_k[c] + sum_bias[c] for every
  * other block c; out_i = softmax(logits) . [v_j ... ; sum_v[c] ...], with
  * float32 accumulation and one final bf16 rounding.  V and the summary values
- * are read from the workspace.
+ * are read from the workspace.  A query block that is a conditioning sink
+ * block attends to every key block exactly and ignores its block_idx row.
  */
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
                 const float* sum_bias, const int32_t* block_idx, const void* workspace,

@@ -50,6 +50,23 @@ def check_idx_row(gpu_row, scores_row, k):
     return ok, True
 
 
+def check_idx_row_forced(gpu_row, scores_row, k, forced):
+    """check_idx_row with conditioning sinks: the row holds every forced block,
+    and its other entries are the top-(k - len(forced)) of the remaining
+    blocks, under the same tie-zone rule."""
+    g = [int(x) for x in gpu_row]
+    F = set(int(c) for c in forced)
+    nb = len(scores_row)
+    if len(g) != k or any(b <= a for a, b in zip(g, g[1:])) or any(c < 0 or c >= nb for c in g):
+        return False, False
+    if not F <= set(g):
+        return False, False
+    rest = [c for c in range(nb) if c not in F]
+    pos = {c: i for i, c in enumerate(rest)}
+    sub = sorted(pos[c] for c in g if c not in F)
+    return check_idx_row(sub, np.asarray(scores_row)[rest], k - len(F))
+
+
 def check_output(gpu_out, ref_out):
     d = np.abs(np.asarray(gpu_out, dtype=np.float64) - ref_out)
     return float(d.max()), float(d.mean())

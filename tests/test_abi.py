@@ -53,6 +53,38 @@ def test_blocks_and_workspace():
     assert bsa.bsa_workspace_bytes(pr) >= ws + 56 * 295 * 128 * 8
 
 
+def test_struct_layout_matches_header():
+    """The ctypes mirror has the header's fields, in order, with the
+    header's size (11 four-byte fields)."""
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    body = text[text.index("typedef struct bsa_problem {"):text.index("} bsa_problem;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(?:int32_t|float)\s+(\w+);", body)
+    assert fields == [f for f, _ in bsa.Problem._fields_]
+    assert ctypes.sizeof(bsa.Problem) == 4 * len(fields) == 44
+
+
+def test_sink_blocks_and_k():
+    # 768p 5s: conditioning rows 36,288 .. 37,739 sit in blocks 283 .. 294
+    p = _prob(seq_len=37740, heads=56, top_k=64, sink_rows=1452)
+    assert (p.sink_start, p.sink_rows) == (36288, 1452)
+    assert bsa.bsa_problem_blocks(p) == (295, 64 + 12)
+    # k capped by the blocks left after the sinks
+    p = _prob(seq_len=4096, top_k=40, sink_start=0, sink_rows=129)
+    assert bsa.bsa_problem_blocks(p) == (32, 32)
+    p = _prob(seq_len=4096, top_k=0, sink_start=4032, sink_rows=64)
+    assert bsa.bsa_problem_blocks(p) == (32, 1)
+    p = _prob(seq_len=4096, top_k=3, sink_start=128, sink_rows=256)
+    assert bsa.bsa_problem_blocks(p) == (32, 5)
+
+
+@pytest.mark.parametrize("start,rows", [(-1, 10), (4000, 97), (0, -1), (4096, 1)])
+def test_bad_sink_range_rejected(start, rows):
+    p = _prob(seq_len=4096, sink_start=start, sink_rows=rows)
+    with pytest.raises(ValueError):
+        bsa.bsa_problem_blocks(p)
+
+
 def test_ratio_budget():
     p = _prob(seq_len=103996, heads=56, top_k=None, top_k_ratio="0.1", summary="reweight")
     assert bsa.bsa_problem_blocks(p) == (813, 82)

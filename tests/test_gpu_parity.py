@@ -16,8 +16,8 @@ import pytest
 import block_sparse_attention_25_amd as bsa
 from block_sparse_attention_25_amd.synth import WORKLOADS, custom, generate
 from oracle import bsa_oracle as O
-from tests.parity import (MAX_ABS, MEAN_ABS, check_idx_row, check_output, tensor_bits,
-                          to_device, widen)
+from tests.parity import (MAX_ABS, MEAN_ABS, check_idx_row, check_idx_row_forced, check_output,
+                          tensor_bits, to_device, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,12 +45,13 @@ def _run_gpu(torch, qb, kb, vb, **kw):
 
 
 def _check_head(host, qb, kb, vb, b, h, top_k, summary="mean", anchor_rows=0,
-                query_blocks=None, label=""):
+                query_blocks=None, label="", sink_start=0, sink_rows=0):
     """Compare one (b, h) of a GPU run with the oracle; returns tie-zone rows."""
     Q, K, V = (widen(x[b, h]) for x in (qb, kb, vb))
     N = Q.shape[0]
     nb = O.n_blocks(N)
-    k = O.effective_k(top_k, nb)
+    sinks = O.sink_blocks(N, sink_start, sink_rows)
+    k = len(sinks) + O.effective_k(top_k, nb - len(sinks))
     sc = O.default_scale(Q.shape[1])
     # stage 1: pooled vectors bit-exact
     qp, kp = O.pool_mean(Q), O.pool_mean(K)
@@ -76,12 +77,15 @@ def _check_head(host, qb, kb, vb, b, h, top_k, summary="mean", anchor_rows=0,
     ties = 0
     if k > 0:
         for r in range(nb):
-            ok, tie = check_idx_row(gidx[r], s[r], k)
+            if sinks:
+                ok, tie = check_idx_row_forced(gidx[r], s[r], k, sinks)
+            else:
+                ok, tie = check_idx_row(gidx[r], s[r], k)
             assert ok, "%s idx row %d: gpu %s" % (label, r, list(gidx[r]))
             ties += tie
     # stages 3+4: output with the GPU's (validated) selection
     ref = O.attention(Q, K, V, gidx if k > 0 else np.zeros((nb, 0), np.int32), sk, sv, bias, sc,
-                      query_blocks=query_blocks)
+                      query_blocks=query_blocks, dense_blocks=sinks)
     gout = widen(tensor_bits(host["out"][b, h].cpu()))
     if query_blocks is None:
         rows = np.arange(N)
@@ -134,6 +138,27 @@ def test_reweight_sizes(torch_cuda, N, top_k, anchor_rows):
     host = _run_gpu(torch_cuda, qb, kb, vb, top_k=top_k, summary="reweight", anchor_rows=anchor_rows)
     for h in range(2):
         _check_head(host, qb, kb, vb, 0, h, top_k, "reweight", anchor_rows, label="rw%d" % N)
+
+
+@pytest.mark.parametrize("N,top_k,start,rows,summary", [
+    (4096, 8, 4032, 64, "mean"),      # the tiny shape: conditioning rows in the last block
+    (1000, 3, 900, 100, "mean"),      # sinks in the short last block
+    (1000, 2, 300, 200, "mean"),      # sinks in the middle, straddling a block boundary
+    (1000, 0, 0, 1, "mean"),          # top_k 0: sink block plus summaries
+    (300, 5, 0, 300, "mean"),         # every block a sink: dense attention
+    (1000, 3, 900, 100, "reweight"),
+    (2000, 20, 1900, 100, "mean"),    # top_k above the blocks left after the sinks
+])
+def test_conditioning_sinks(torch_cuda, N, top_k, start, rows, summary):
+    _log("case sinks N=%d top_k=%d sink=[%d,+%d) %s" % (N, top_k, start, rows, summary))
+    w = custom(N, heads=2, seed=N + 3 * top_k + start)
+    qb, kb, vb = generate(w)
+    anchor = start if summary == "reweight" else 0
+    host = _run_gpu(torch_cuda, qb, kb, vb, top_k=top_k, summary=summary, anchor_rows=anchor,
+                    sink_start=start, sink_rows=rows)
+    for h in range(2):
+        _check_head(host, qb, kb, vb, 0, h, top_k, summary, anchor, label="sink%d" % N,
+                    sink_start=start, sink_rows=rows)
 
 
 def test_batch_and_heads(torch_cuda):
@@ -226,7 +251,8 @@ def test_guard_bands_untouched(torch_cuda):
 
 
 # ---------------------------------------------------------- full sizes ---
-FULL = [("768p_5s", [0, 37]), ("768p_10s", [5]), ("2k_5s", [55]), ("768p_15s_reweight", [0, 21])]
+FULL = [("768p_5s", [0, 37]), ("768p_10s", [5]), ("2k_5s", [55]), ("768p_15s_reweight", [0, 21]),
+        ("768p_5s_sinks", [9])]
 
 
 @pytest.mark.parametrize("name,heads", FULL)
@@ -239,15 +265,20 @@ def test_full_size_workloads_sampled(torch_cuda, name, heads):
     qb, kb, vb = generate(w, threads=16)
     nb = O.n_blocks(w.seq_len)
     top_k = w.top_k if w.top_k is not None else O.k_from_ratio(w.top_k_ratio, nb)
-    kw = dict(top_k=top_k, summary=w.summary)
+    kw = dict(top_k=top_k, summary=w.summary, sink_start=w.sink_start, sink_rows=w.sink_rows)
     if w.summary == "reweight":
         kw["anchor_rows"] = w.anchor_rows
     host = _run_gpu(torch_cuda, qb, kb, vb, **kw)
     # every row of every head: k distinct ascending valid indices
+    sinks = O.sink_blocks(w.seq_len, w.sink_start, w.sink_rows)
+    kk = len(sinks) + min(top_k, nb - len(sinks))
     idx = host["block_idx"].numpy()
-    assert idx.shape == (1, w.heads, nb, top_k)
+    assert idx.shape == (1, w.heads, nb, kk)
     assert np.all(np.diff(idx, axis=-1) > 0) and idx.min() >= 0 and idx.max() < nb
     qbs = [0, 1, nb // 2, nb - 2, nb - 1]
+    if sinks:
+        qbs = sorted(set(qbs + [sinks[0] - 1, sinks[0]]))  # last video block, first sink block
     for h in heads:
         _check_head(host, qb, kb, vb, 0, h, top_k, w.summary, w.anchor_rows if w.summary ==
-                    "reweight" else 0, query_blocks=qbs, label=name)
+                    "reweight" else 0, query_blocks=qbs, label=name, sink_start=w.sink_start,
+                    sink_rows=w.sink_rows)
