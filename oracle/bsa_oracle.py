@@ -30,7 +30,7 @@ Readings taken where the pages are silent (each is exercised by a test):
      softmax scale does not change a ranking).
   R3 ties: equal scores go to the lower block index; output ascending.
   R4 no forced blocks (no diagonal or sink block is added to the top-k)
-     unless a conditioning range is given (R12).
+     unless a conditioning range is given (R13).
   R5 a top-k ratio budget becomes k = ceil(ratio * n_blocks) computed exactly.
   R6 softmax scale 1/sqrt(d) for exact and summary logits alike; the bias is
      added in scaled-logit units.
@@ -43,7 +43,7 @@ Readings taken where the pages are silent (each is exercised by a test):
      lead the sequence); anchor_rows = 0 means all rows.
   R10 selection uses the mean-pooled vectors in both summary modes.
   R11 no causal mask.
-  R12 conditioning sinks (the "exact_kv_and_rows" routing): the conditioning
+  R13 conditioning sinks (the "exact_kv_and_rows" routing): the conditioning
      rows (prompt, reference, audio) form one contiguous row range.  Every
      block holding at least one of its rows is a sink block: it is forced
      into every query block's exact set, on top of the top_k picked among the
@@ -131,7 +131,7 @@ def select_topk(scores: np.ndarray, top_k: int, forced=()) -> np.ndarray:
     """For each query block r the k key blocks of largest score, ties to the
     lower index (R3), returned in ascending index order; int32 [nb, k].
 
-    With forced blocks (R12) every row holds all of them plus the top_k of the
+    With forced blocks (R13) every row holds all of them plus the top_k of the
     remaining blocks, k = min(top_k, nb - n_forced) + n_forced.
 
     PyPI page, opening paragraph ("attends to its top-k key blocks")."""
@@ -150,7 +150,7 @@ def select_topk(scores: np.ndarray, top_k: int, forced=()) -> np.ndarray:
 
 def sink_blocks(N: int, sink_start: int, sink_rows: int, block: int = BLOCK):
     """Blocks holding at least one row of the conditioning range
-    [sink_start, sink_start + sink_rows) (R12); empty when sink_rows is 0."""
+    [sink_start, sink_start + sink_rows) (R13); empty when sink_rows is 0."""
     if sink_start < 0 or sink_rows < 0 or sink_start + sink_rows > N:
         raise ValueError("conditioning range out of bounds")
     if sink_rows == 0:
@@ -229,7 +229,7 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
 
     idx may be any [nb, k] array of distinct valid block indices per row (the
     output is unique given idx).  Query blocks listed in dense_blocks attend to
-    every key block exactly, whatever idx holds for them (R12).  query_blocks
+    every key block exactly, whatever idx holds for them (R13).  query_blocks
     restricts the work to those query blocks (other output rows stay zero).
     Returns float64 [N, d]."""
     q = np.asarray(q, dtype=np.float64)
@@ -275,7 +275,7 @@ def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
     """All four stages for one (batch, head).  Returns a dict with the pooled
     vectors, scores, selection, summaries, sink blocks and the float64 output.
     sink_rows > 0 routes the conditioning rows [sink_start, sink_start +
-    sink_rows) as sinks (R12)."""
+    sink_rows) as sinks (R13)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)

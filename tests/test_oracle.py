@@ -385,7 +385,7 @@ def test_reweight_constant_logit_block():
     assert np.abs(sv[0] - v.mean(0)).max() < 1e-14
 
 
-# ------------------------------------------------- conditioning sinks (R12) ---
+# ------------------------------------------------- conditioning sinks (R13) ---
 def test_sink_blocks_ranges():
     """Blocks holding the conditioning rows, by hand: the range's first and
     last row, each divided by the block size."""
