@@ -56,6 +56,15 @@ Readings taken where the pages are silent (each is exercised by a test):
      section (conditioning, non-video queries and the tiles on the boundary
      between contexts stay fully dense; only video-to-video attention is
      cut).  The block straddling the boundary counts as a sink block.
+  R14 threshold (variable-k) selection with parameter tau: a key block is
+     kept when its score exceeds the mean of its row's block scores by more
+     than tau population standard deviations, s > mean + tau * std (both over
+     all nb blocks of the row, in float64); at most top_k blocks are kept
+     (the highest, ties to the lower index), sink blocks always.  Rows are
+     padded with -1 after their kept blocks.  Source: "H3 Sparse Attention"
+     (WAS Node Suite node page), section "The inputs that matter" (tau 1.0
+     keeps roughly 16% of key blocks exact, 1.5 about 7%, 2.0 about 3%): the
+     normal tail beyond tau standard deviations is 15.9%, 6.7% and 2.3%.
 
 Precision: pooled vectors are summed in float64 and stored as float32 (the
 precision in which a block ranking is decided); block scores are float64 dot
@@ -148,6 +157,29 @@ def select_topk(scores: np.ndarray, top_k: int, forced=()) -> np.ndarray:
     return idx
 
 
+def select_threshold(scores: np.ndarray, tau: float, top_k: int, forced=()) -> np.ndarray:
+    """Variable-k selection (R14): for each row r, the blocks c whose score is
+    above mean_r + tau * std_r (population statistics of the row, float64),
+    at most top_k of them (largest first, ties to the lower index), plus the
+    forced blocks; ascending, padded with -1 to n_forced + min(top_k, nb -
+    n_forced) entries."""
+    nq, nk = scores.shape
+    F = sorted(set(int(c) for c in forced))
+    rest = [c for c in range(nk) if c not in set(F)]
+    k = effective_k(top_k, len(rest))
+    idx = np.full((nq, len(F) + k), -1, dtype=np.int32)
+    for r in range(nq):
+        row = np.asarray(scores[r], dtype=np.float64)
+        mean = row.sum() / nk
+        std = math.sqrt(((row - mean) ** 2).sum() / nk)
+        thr = mean + tau * std
+        above = [c for c in rest if row[c] > thr]
+        order = sorted(above, key=lambda c: (-row[c], c))
+        kept = sorted(F + order[:k])
+        idx[r, :len(kept)] = kept
+    return idx
+
+
 def sink_blocks(N: int, sink_start: int, sink_rows: int, block: int = BLOCK):
     """Blocks holding at least one row of the conditioning range
     [sink_start, sink_start + sink_rows) (R13); empty when sink_rows is 0."""
@@ -228,7 +260,7 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
     "What Spark-Attn changes" (exact and compressed branches of one pass).
 
     idx may be any [nb, k] array of distinct valid block indices per row (the
-    output is unique given idx).  Query blocks listed in dense_blocks attend to
+    output is unique given idx); entries of -1 are padding and ignored.  Query blocks listed in dense_blocks attend to
     every key block exactly, whatever idx holds for them (R13).  query_blocks
     restricts the work to those query blocks (other output rows stay zero).
     Returns float64 [N, d]."""
@@ -245,7 +277,7 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
     for r, (s, e) in enumerate(rows):
         if query_blocks is not None and r not in query_blocks:
             continue
-        sel = list(range(nb)) if r in set(dense_blocks) else [int(c) for c in idx[r]]
+        sel = list(range(nb)) if r in set(dense_blocks) else [int(c) for c in idx[r] if c >= 0]
         if len(set(sel)) != len(sel) or any(c < 0 or c >= nb for c in sel):
             raise ValueError("idx row %d is not a set of valid blocks" % r)
         chosen = set(sel)
@@ -271,11 +303,12 @@ def default_scale(d: int) -> float:
 
 def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
              scale: float | None = None, block: int = BLOCK, bias_ref: str = "mean",
-             sink_start: int = 0, sink_rows: int = 0):
+             sink_start: int = 0, sink_rows: int = 0, tau: float | None = None):
     """All four stages for one (batch, head).  Returns a dict with the pooled
     vectors, scores, selection, summaries, sink blocks and the float64 output.
     sink_rows > 0 routes the conditioning rows [sink_start, sink_start +
-    sink_rows) as sinks (R13)."""
+    sink_rows) as sinks (R13); tau selects blocks by threshold (R14) with top_k
+    as the cap."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -285,7 +318,7 @@ def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
     k_pool = pool_mean(k, block)
     s = block_scores(q_pool, k_pool)
     sinks = sink_blocks(q.shape[0], sink_start, sink_rows, block)
-    idx = select_topk(s, top_k, sinks)
+    idx = select_topk(s, top_k, sinks) if tau is None else select_threshold(s, tau, top_k, sinks)
     if summary == "mean":
         sk, sv, b = summaries_mean(k, v, block)
     elif summary == "reweight":

@@ -466,6 +466,87 @@ def test_sink_with_topk_zero_is_sinks_plus_summaries(summary):
     assert np.abs(res["out"][:r1] - ref).max() < 1e-10
 
 
+# ------------------------------------------- threshold selection (R14) ---
+def test_threshold_keeps_the_pages_fractions():
+    """On Gaussian block scores, keeping s > mean + tau * std keeps the
+    fractions the page states for tau 1.0, 1.5 and 2.0 (to its stated
+    precision), which are the normal tails erfc(tau / sqrt 2) / 2."""
+    g = json.load(open(os.path.join(HERE, "golden", "tau_keep_fractions.json")))
+    rng = np.random.default_rng(41)
+    nb = 100_000
+    s = rng.standard_normal((1, nb))
+    for tau_s, frac_page in g["keep_fraction"].items():
+        tau = float(tau_s)
+        idx = O.select_threshold(s, tau, nb)
+        frac = float((idx[0] >= 0).sum()) / nb
+        assert abs(frac - frac_page) <= g["stated_precision"] + 1e-3, (tau, frac)
+        assert abs(frac - 0.5 * math.erfc(tau / math.sqrt(2))) < 4e-3, (tau, frac)
+
+
+def test_threshold_closed_forms():
+    ar = np.arange(10, dtype=np.float64)[None, :]     # mean 4.5, population std sqrt(8.25)
+    assert list(O.select_threshold(ar, 1.0, 10)[0]) == [8, 9] + [-1] * 8
+    assert list(O.select_threshold(ar, 0.0, 10)[0]) == [5, 6, 7, 8, 9] + [-1] * 5
+    assert list(O.select_threshold(ar, -1.0, 10)[0]) == list(range(2, 10)) + [-1] * 2
+    assert list(O.select_threshold(ar, -1.0, 3)[0]) == [7, 8, 9]          # capped at top_k
+    # population, not sample, deviation: mean 0.25, std sqrt(3)/4; thr = 0.943 at tau 1.6
+    assert list(O.select_threshold(np.array([[0., 0., 0., 1.]]), 1.6, 4)[0]) == [3, -1, -1, -1]
+    # strictly above the threshold: a score equal to it is not kept
+    assert list(O.select_threshold(np.array([[0., 2.]]), 1.0, 2)[0]) == [-1, -1]
+    # equal scores: nothing is above the mean
+    assert list(O.select_threshold(np.full((1, 5), 3.0), 0.0, 5)[0]) == [-1] * 5
+    # forced blocks always kept; the statistics run over every block of the row
+    sc = np.array([[10., 0., 1., 2., 3.]])              # mean 3.2
+    assert list(O.select_threshold(sc, 0.0, 4, forced=[0])[0]) == [0, -1, -1, -1, -1]
+    assert list(O.select_threshold(sc, -0.5, 4, forced=[0])[0]) == [0, 3, 4, -1, -1]
+
+
+@pytest.mark.parametrize("N,tau,top_k", [(640, 0.5, 5), (1000, 1.0, 3), (1000, -0.5, 8)])
+def test_threshold_brute_force(N, tau, top_k):
+    """Kept blocks are the brute-force top-min(top_k, m) of the m blocks above
+    the row threshold."""
+    q, k, _ = _synth_head(N, seed=int(100 * tau) + N)
+    s = O.block_scores(O.pool_mean(q), O.pool_mean(k))
+    nb = O.n_blocks(N)
+    idx = O.select_threshold(s, tau, top_k)
+    assert idx.shape == (nb, min(top_k, nb))
+    for r in range(nb):
+        row = s[r]
+        thr = row.mean() + tau * row.std()
+        above = [c for c in range(nb) if row[c] > thr]
+        m = min(top_k, len(above))
+        sub = _brute_force_select(row[above], m)
+        kept = [int(c) for c in idx[r] if c >= 0]
+        assert kept == sorted(above[i] for i in sub)
+        assert all(c == -1 for c in idx[r][len(kept):])
+
+
+def test_threshold_attention_ignores_padding():
+    """run_head with tau equals the mask formulation over the kept blocks."""
+    N = 1000
+    q, k, v = _synth_head(N, seed=9)
+    res = O.run_head(q, k, v, top_k=6, tau=0.8)
+    idx = res["idx"]
+    assert (idx == -1).any() and (idx >= 0).any()
+    rows = O.block_rows(N)
+    mask = np.full((N, N), -np.inf)
+    for r, (s0, e0) in enumerate(rows):
+        for c in idx[r]:
+            if c >= 0:
+                mask[s0:e0, rows[c][0]:rows[c][1]] = 0.0
+    # exact part via the mask, summaries appended as extra keys with their bias
+    Kx = np.concatenate([k, res["sum_k"]])
+    Vx = np.concatenate([v, res["sum_v"]])
+    summ = np.full((N, len(rows)), -np.inf)
+    for r, (s0, e0) in enumerate(rows):
+        kept = set(int(c) for c in idx[r] if c >= 0)
+        for c in range(len(rows)):
+            if c not in kept:
+                summ[s0:e0, c] = res["bias"][c]
+    ref = _sdpa(q, Kx, Vx, mask=np.concatenate([mask, summ], axis=1))
+    assert np.abs(res["out"] - ref).max() < 1e-10
+
+
 # -------------------------------------------------- planted mistakes fail ---
 def _all_pins_pass():
     """Re-run a compact set of the pins above; True when every one holds."""
@@ -486,6 +567,9 @@ def _all_pins_pass():
         test_select_forced_brute_force(640, [0, 4])
         test_sink_query_blocks_are_dense(700, 600, 100, 1)
         test_sink_with_topk_zero_is_sinks_plus_summaries("mean")
+        test_threshold_closed_forms()
+        test_threshold_brute_force(640, 0.5, 5)
+        test_threshold_attention_ignores_padding()
     except AssertionError:
         return False
     return True
@@ -502,6 +586,45 @@ _orig_scores = O.block_scores
 _orig_anchor = O.anchor
 _orig_select = O.select_topk
 _orig_sink_blocks = O.sink_blocks
+_orig_threshold = O.select_threshold
+
+
+def _threshold_sample_std(scores, tau, top_k, forced=()):
+    # mistake: sample (n - 1) standard deviation
+    nb = scores.shape[1]
+    return _orig_threshold(scores, tau * math.sqrt(nb / (nb - 1)), top_k, forced)
+
+
+def _threshold_inclusive(scores, tau, top_k, forced=()):
+    # mistake: scores equal to the threshold kept
+    F = set(forced)
+    nq, nk = scores.shape
+    rest = [c for c in range(nk) if c not in F]
+    out = _orig_threshold(scores, tau, top_k, forced)
+    for r in range(nq):
+        row = scores[r]
+        thr = row.mean() + tau * row.std()
+        above = sorted([c for c in rest if row[c] >= thr], key=lambda c: (-row[c], c))
+        kept = sorted(list(F) + above[:min(top_k, len(rest))])
+        out[r] = -1
+        out[r, :len(kept)] = kept
+    return out
+
+
+def _threshold_stats_without_forced(scores, tau, top_k, forced=()):
+    # mistake: mean and deviation over the non-forced blocks only
+    F = set(forced)
+    nq, nk = scores.shape
+    rest = [c for c in range(nk) if c not in F]
+    out = _orig_threshold(scores, tau, top_k, forced)
+    for r in range(nq):
+        row = scores[r]
+        thr = row[rest].mean() + tau * row[rest].std()
+        above = sorted([c for c in rest if row[c] > thr], key=lambda c: (-row[c], c))
+        kept = sorted(list(F) + above[:min(top_k, len(rest))])
+        out[r] = -1
+        out[r, :len(kept)] = kept
+    return out
 
 
 def _pool_padded(x, block=128):
@@ -595,6 +718,9 @@ def _anchor_off_by_one(q, anchor_rows):
     ("attention", _attn_dense_ignored),
     ("select_topk", _select_forced_in_pool),
     ("sink_blocks", _sink_blocks_end_inclusive),
+    ("select_threshold", _threshold_sample_std),
+    ("select_threshold", _threshold_inclusive),
+    ("select_threshold", _threshold_stats_without_forced),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
