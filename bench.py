@@ -64,12 +64,18 @@ def counted_flops(torch, idx, N, nb, H, B, dense=()):
     k = idx.shape[-1]
     per_row = n[idx.long()].sum(-1) if k > 0 else torch.zeros((B, H, nb), dtype=torch.int64,
                                                                device=idx.device)
-    n_skip = torch.full((nb,), nb - k, dtype=torch.int64, device=idx.device)
+    if k > 0:
+        # threshold selection pads rows with -1
+        valid = idx >= 0
+        per_row = (n[idx.clamp(min=0).long()] * valid).sum(-1)
+        n_skip = nb - valid.sum(-1)
+    else:
+        n_skip = torch.full((B, H, nb), nb, dtype=torch.int64, device=idx.device)
     if len(dense):
         per_row[..., list(dense)] = N
-        n_skip[list(dense)] = 0
+        n_skip[..., list(dense)] = 0
     exact = int((per_row * n).sum().item())
-    summary = int((n * n_skip).sum().item()) * B * H
+    summary = int((n * n_skip).sum().item())
     return 4 * 128 * exact, 4 * 128 * summary
 
 
@@ -96,14 +102,16 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
     for h in range(qb.shape[1]):
         Q, K, V = (bf16_to_f32(x[0, h]).astype(np.float64) for x in (qb, kb, vb))
         qp, kp = O.pool_mean(Q), O.pool_mean(K)
-        idx = O.select_topk(O.block_scores(qp, kp), top_k, sinks)
+        sc_ = O.block_scores(qp, kp)
+        idx = O.select_topk(sc_, top_k, sinks) if w.tau is None else \
+            O.select_threshold(sc_, w.tau, top_k, sinks)
         if w.summary == "reweight":
             sk, sv, b = O.summaries_reweight(K, V, O.anchor(Q, w.anchor_rows), sc)
         else:
             sk, sv, b = O.summaries_mean(K, V)
         for r in range(nb):
             O.attention(Q, K, V, idx, sk, sv, b, sc, query_blocks=[r], dense_blocks=sinks)
-            keys = N if r in sinks else sum(rows[c][1] - rows[c][0] for c in idx[r])
+            keys = N if r in sinks else sum(rows[c][1] - rows[c][0] for c in idx[r] if c >= 0)
             flops += 4 * 128 * (rows[r][1] - rows[r][0]) * keys
             blocks_done += 1
             if time.perf_counter() - t0 > budget_s:
@@ -147,7 +155,7 @@ def main():
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     p = bsa.make_problem(B, H, N, top_k, None, w.summary,
                          w.anchor_rows if w.summary == "reweight" else 0,
-                         sink_rows=w.sink_rows, sink_start=w.sink_start)
+                         sink_rows=w.sink_rows, sink_start=w.sink_start, tau=w.tau)
     dense = list(range(w.sink_start // 128, (w.sink_start + w.sink_rows - 1) // 128 + 1)) \
         if w.sink_rows > 0 else []
     nb, kk = bsa.bsa_problem_blocks(p)
@@ -216,7 +224,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": 128,
                    "n_blocks": nb, "top_k": kk, "summary": w.summary,
-                   "sink_rows": w.sink_rows},
+                   "sink_rows": w.sink_rows, "tau": w.tau},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"pool": round(pool_ms, 4), "select": round(sel_ms, 4),
                        "attention": round(attn_ms, 4)},

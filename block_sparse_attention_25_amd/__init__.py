@@ -28,6 +28,7 @@ __all__ = [
 
 BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = 0, 1, 2, 3, 4
 SUMMARY_MEAN, SUMMARY_REWEIGHT = 0, 1
+SELECT_TOPK, SELECT_THRESHOLD = 0, 1
 BLOCK = 128
 HEAD_DIM = 128
 
@@ -42,6 +43,7 @@ class Problem(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("summary", ctypes.c_int32), ("anchor_rows", ctypes.c_int32), ("scale", ctypes.c_float),
         ("sink_start", ctypes.c_int32), ("sink_rows", ctypes.c_int32),
+        ("select_mode", ctypes.c_int32), ("select_tau", ctypes.c_float),
     ]
 
 
@@ -148,10 +150,12 @@ def k_from_ratio(ratio, n_blocks: int) -> int:
 
 
 def make_problem(batch, heads, seq_len, top_k=None, top_k_ratio=None, summary="mean",
-                 anchor_rows=0, scale=None, sink_rows=0, sink_start=None) -> Problem:
+                 anchor_rows=0, scale=None, sink_rows=0, sink_start=None, tau=None) -> Problem:
     """Fill a bsa_problem.  sink_rows > 0 routes the conditioning rows
     [sink_start, sink_start + sink_rows) as sinks; sink_start defaults to
-    N - sink_rows (conditioning rows after the video rows)."""
+    N - sink_rows (conditioning rows after the video rows).  tau selects
+    blocks by threshold (score above mean + tau * std of the row), with
+    top_k as the cap."""
     nb = -(-int(seq_len) // BLOCK)
     if (top_k is None) == (top_k_ratio is None):
         raise ValueError("give exactly one of top_k and top_k_ratio")
@@ -164,7 +168,9 @@ def make_problem(batch, heads, seq_len, top_k=None, top_k_ratio=None, summary="m
         sink_start = int(seq_len) - sink_rows if sink_rows > 0 else 0
     return Problem(int(batch), int(heads), int(seq_len), HEAD_DIM, BLOCK, int(top_k),
                    SUMMARY_MEAN if summary == "mean" else SUMMARY_REWEIGHT, int(anchor_rows),
-                   0.0 if scale is None else float(scale), int(sink_start), sink_rows)
+                   0.0 if scale is None else float(scale), int(sink_start), sink_rows,
+                   SELECT_TOPK if tau is None else SELECT_THRESHOLD,
+                   0.0 if tau is None else float(tau))
 
 
 def _check_qkv(q, k, v):
@@ -181,7 +187,7 @@ def _check_qkv(q, k, v):
 
 
 def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows=0, scale=None,
-              sink_rows=0, sink_start=None, return_aux=False, stream=None):
+              sink_rows=0, sink_start=None, tau=None, return_aux=False, stream=None):
     """Block-sparse attention of bf16 q, k, v [B, H, N, 128] on the GPU.
 
     top_k counts 128-token key blocks (or give top_k_ratio, e.g. "0.1");
@@ -189,13 +195,16 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     rows [0, anchor_rows), 0 meaning all rows).  sink_rows > 0 routes the
     conditioning rows [sink_start, sink_start + sink_rows) (by default the
     last sink_rows rows) as sinks: their blocks are kept exactly by every
-    query block, and their query blocks attend densely.  Returns out
+    query block, and their query blocks attend densely.  tau switches to
+    threshold selection (blocks scoring above mean + tau * std of their row,
+    at most top_k; rows of block_idx padded with -1).  Returns out
     [B, H, N, 128] bf16, plus a dict of intermediate tensors when return_aux
     is set."""
     import torch
     _check_qkv(q, k, v)
     B, H, N, _ = q.shape
-    p = make_problem(B, H, N, top_k, top_k_ratio, summary, anchor_rows, scale, sink_rows, sink_start)
+    p = make_problem(B, H, N, top_k, top_k_ratio, summary, anchor_rows, scale, sink_rows, sink_start,
+                     tau)
     nb, kk = bsa_problem_blocks(p)
     dev = q.device
     f32, bf = torch.float32, torch.bfloat16

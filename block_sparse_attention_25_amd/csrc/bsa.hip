@@ -300,6 +300,13 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
 // Every score is reduced in the same order, so identical key blocks tie
 // bit-exactly and the lower index wins.
 
+// sum over the 64 lanes of a wavefront; every lane gets the same bits
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 __device__ __forceinline__ uint64_t order_key(double s) {
   if (s == 0.0) s = 0.0;  // -0 ties with +0
   const uint64_t u = (uint64_t)__double_as_longlong(s);
@@ -310,7 +317,8 @@ template <int NKT, int RB>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q_pool,
                                                      const float* __restrict__ k_pool,
                                                      int32_t* __restrict__ block_idx, int nb,
-                                                     int ksel, int f0, int f1) {
+                                                     int ksel, int f0, int f1, int thr_mode,
+                                                     double tau) {
   constexpr int NCH = NKT * 4;    // 64-key chunks per row in the top-k phase
   constexpr int DCH = 32 / RB;    // features per step
   extern __shared__ double sc[];  // [RB][nb]
@@ -378,53 +386,88 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     const int r = r0 + rr;
     if (r >= nb || ksel == 0) break;
     const double* srow = sc + rr * nb;
+    // threshold mode: only scores above mean + tau * std of the row compete
+    double thr = 0.0;
+    if (thr_mode) {
+      double sum = 0.0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int cc = i * 64 + lane;
+        if (cc < nb) sum += srow[cc];
+      }
+      const double mean = wave_sum(sum) / nb;
+      double sq = 0.0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int cc = i * 64 + lane;
+        if (cc < nb) {
+          const double dv = srow[cc] - mean;
+          sq = fma(dv, dv, sq);
+        }
+      }
+      thr = mean + tau * sqrt(wave_sum(sq) / nb);
+    }
     uint64_t key[NCH];
+    int navail = 0;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int cc = i * 64 + lane;
-      // real keys are > 0; sink blocks [f0, f1] take the largest key, so
-      // they are always kept and the rest of the row is the top-k of the others
-      key[i] = (cc < nb) ? ((cc >= f0 && cc <= f1) ? ~0ull : order_key(srow[cc])) : 0ull;
+      // real keys are > 0 and 0 marks a block that cannot be kept; sink
+      // blocks [f0, f1] take the largest key, so they are always kept and the
+      // rest of the row is the top-k of the others
+      uint64_t kv = 0ull;
+      if (cc < nb) {
+        if (cc >= f0 && cc <= f1)
+          kv = ~0ull;
+        else if (!thr_mode || srow[cc] > thr)
+          kv = order_key(srow[cc]);
+      }
+      key[i] = kv;
+      navail += __popcll(__ballot(kv != 0ull));
     }
-    uint64_t T = 0;
-    bool exact = false;  // exactly ksel keys are >= T
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t cand = T | (1ull << bit);
-      int cnt = 0;
+    const int kr = min(ksel, navail);  // blocks this row keeps
+    int32_t* orow = block_idx + (bh * nb + r) * (size_t)ksel;
+    if (kr > 0) {
+      uint64_t T = 0;
+      bool exact = false;  // exactly kr keys are >= T
+      for (int bit = 63; bit >= 0; --bit) {
+        const uint64_t cand = T | (1ull << bit);
+        int cnt = 0;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-      if (cnt >= ksel) {
-        T = cand;
-        if (cnt == ksel) {
-          exact = true;
-          break;
+        for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+        if (cnt >= kr) {
+          T = cand;
+          if (cnt == kr) {
+            exact = true;
+            break;
+          }
         }
       }
-    }
-    int need_eq = 0;
-    if (!exact) {
-      int gt = 0;
+      int need_eq = 0;
+      if (!exact) {
+        int gt = 0;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) gt += __popcll(__ballot(key[i] > T));
-      need_eq = ksel - gt;  // keys equal to T taken lowest index first
-    }
-    int eq_before = 0, sel_before = 0;
-    int32_t* orow = block_idx + (bh * nb + r) * (size_t)ksel;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      bool sel;
-      if (exact) {
-        sel = key[i] >= T;
-      } else {
-        const bool is_eq = key[i] == T;
-        const uint64_t em = __ballot(is_eq);
-        sel = key[i] > T || (is_eq && eq_before + __popcll(em & lt) < need_eq);
-        eq_before += __popcll(em);
+        for (int i = 0; i < NCH; ++i) gt += __popcll(__ballot(key[i] > T));
+        need_eq = kr - gt;  // keys equal to T taken lowest index first
       }
-      const uint64_t sm = __ballot(sel);
-      if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
-      sel_before += __popcll(sm);
+      int eq_before = 0, sel_before = 0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        bool sel;
+        if (exact) {
+          sel = key[i] >= T;
+        } else {
+          const bool is_eq = key[i] == T;
+          const uint64_t em = __ballot(is_eq);
+          sel = key[i] > T || (is_eq && eq_before + __popcll(em & lt) < need_eq);
+          eq_before += __popcll(em);
+        }
+        const uint64_t sm = __ballot(sel);
+        if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
+        sel_before += __popcll(sm);
+      }
     }
+    for (int j = kr + lane; j < ksel; j += 64) orow[j] = -1;  // unused slots
   }
 }
 
@@ -521,7 +564,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int32_t* irow = block_idx + (bh * nb + r) * (size_t)krow;
   // a conditioning sink query block attends to every key block exactly
   const bool dense_row = r >= f0 && r <= f1;
-  const int ksel = dense_row ? nb : krow;
+  const int kslots = dense_row ? nb : krow;
   // per-head buffer descriptors: K, V^T, summary K, summary V^T
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * (size_t)N * HD, (uint32_t)N * HD * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + bh * (size_t)nb * BLK * HD, (uint32_t)nb * BLK * HD * 2);
@@ -545,11 +588,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const int nwords = (nb + 31) >> 5;
   for (int i = tid; i < nwords; i += 256) selmask[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < ksel; i += 256) {
-    const int c = dense_row ? i : irow[i];
-    sidx[i] = c;
-    atomicOr(&selmask[c >> 5], 1u << (c & 31));
+  // the row's kept blocks: a prefix of its slots, -1 padding after them
+  // (threshold selection keeps a different number per row)
+  int kcount = 0;
+  for (int base = 0; base < kslots; base += 256) {
+    const int i = base + tid;
+    const int c = i < kslots ? (dense_row ? i : irow[i]) : -1;
+    if (c >= 0) {
+      sidx[i] = c;
+      atomicOr(&selmask[c >> 5], 1u << (c & 31));
+    }
+    kcount += __syncthreads_count(c >= 0);
   }
+  const int ksel = __builtin_amdgcn_readfirstlane(kcount);
   __syncthreads();
 
   const int n_exact = 2 * ksel;
@@ -846,6 +897,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 struct Geometry {
   int64_t B, H, N, nb, nsb, k;
   int64_t f0, f1;  // conditioning sink blocks [f0, f1]; f1 < f0 when there are none
+  bool threshold;
+  double tau;
   bool reweight;
   int anchor_rows;
   double scale;
@@ -867,6 +920,10 @@ int make_geometry(const bsa_problem* p, Geometry* g) {
   if (!(p->scale >= 0.f) || !isfinite(p->scale)) return BSA_ERR_INVALID;
   if (p->sink_start < 0 || p->sink_rows < 0 || (int64_t)p->sink_start + p->sink_rows > p->seq_len)
     return BSA_ERR_INVALID;
+  if (p->select_mode != BSA_SELECT_TOPK && p->select_mode != BSA_SELECT_THRESHOLD) return BSA_ERR_INVALID;
+  if (!isfinite(p->select_tau)) return BSA_ERR_INVALID;
+  g->threshold = p->select_mode == BSA_SELECT_THRESHOLD;
+  g->tau = (double)p->select_tau;
   g->B = p->batch;
   g->H = p->heads;
   g->N = p->seq_len;
@@ -924,7 +981,7 @@ int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, i
       return BSA_ERR_HIP;
   }
   hipLaunchKernelGGL((select_kernel<NKT, RB>), grid, dim3(256), lds, stream, q_pool, k_pool, block_idx,
-                     (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1);
+                     (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1, g.threshold ? 1 : 0, g.tau);
   return launch_status();
 }
 

@@ -50,6 +50,7 @@ class Workload:
     summary: str = "mean"  # "mean" or "reweight"
     seed: int = 0
     sinks: bool = False    # route the conditioning rows as sinks
+    tau: float | None = None  # threshold selection (top_k is then the cap)
 
     @property
     def sink_start(self) -> int:
@@ -78,6 +79,8 @@ WORKLOADS = {
                                   3196, None, "0.1", "reweight"),
     # the 768p 5s shape with its 1,452 conditioning rows routed as sinks
     "768p_5s_sinks": Workload("768p_5s_sinks", 1, 56, (9, 48, 84), 36288, 1452, 64, sinks=True),
+    # the 768p 5s shape with threshold selection at tau 1.0, uncapped
+    "768p_5s_tau1": Workload("768p_5s_tau1", 1, 56, (9, 48, 84), 36288, 1452, 295, tau=1.0),
 }
 
 

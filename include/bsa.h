@@ -80,7 +80,19 @@ typedef struct bsa_problem {
    * stay dense). */
   int32_t sink_start;
   int32_t sink_rows;
+  /* Block selection rule.  BSA_SELECT_TOPK: the top_k blocks of largest
+   * score.  BSA_SELECT_THRESHOLD (variable k): the blocks whose score exceeds
+   * mean + select_tau * std of their row's nb block scores (population
+   * statistics, float64), at most top_k of them (largest first), so rows keep
+   * different numbers of blocks and are padded with -1.  Source: "H3 Sparse
+   * Attention" (WAS Node Suite node page), section "The inputs that matter"
+   * (tau 1.0 keeps roughly 16% of key blocks, 1.5 about 7%, 2.0 about 3%:
+   * the normal tail beyond tau standard deviations). */
+  int32_t select_mode;
+  float select_tau;    /* threshold mode only; finite */
 } bsa_problem;
+
+enum { BSA_SELECT_TOPK = 0, BSA_SELECT_THRESHOLD = 1 };
 
 /* Text of a status code (static storage, never NULL). */
 const char* bsa_status_str(int status);
@@ -135,8 +147,10 @@ int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v,
  * evaluated in float64 (exact products, float64 sums).  Row r of block_idx
  * holds the k blocks of largest score, equal scores going to the lower block
  * index, in strictly ascending order; with conditioning sinks it holds the
- * sink blocks plus the k - n_sink best of the other blocks.  block_idx may be
- * NULL when k == 0.
+ * sink blocks plus the k - n_sink best of the other blocks.  In threshold
+ * mode a row holds its kept blocks (sink blocks, then at most k - n_sink
+ * blocks above the row threshold) ascending, followed by -1 in the unused
+ * slots.  block_idx may be NULL when k == 0.
  * Requires nb <= BSA_MAX_BLOCKS (else BSA_ERR_UNSUPPORTED).
  */
 int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
@@ -152,8 +166,9 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
  *   q, k       in   bf16 [B, H, N, 128]
  *   sum_k      in   bf16 [B, H, nb, 128]   (may be NULL iff k == nb)
  *   sum_bias   in   fp32 [B, H, nb]        (may be NULL iff k == nb)
- *   block_idx  in   int32 [B, H, nb, k]    distinct, in [0, nb); the kernel
- *                                          trusts this (bsa_select's output)
+ *   block_idx  in   int32 [B, H, nb, k]    distinct, in [0, nb), ascending,
+ *                                          then -1 padding; the kernel trusts
+ *                                          this (bsa_select's output)
  *   workspace  in   as filled by bsa_pool for the same q, k, v and problem
  *   out        out  bf16 [B, H, N, 128]
  *

@@ -67,6 +67,45 @@ def check_idx_row_forced(gpu_row, scores_row, k, forced):
     return check_idx_row(sub, np.asarray(scores_row)[rest], k - len(F))
 
 
+# Threshold selection: a block whose score lies this close (relative to the
+# row's |threshold| + deviation) to the threshold may fall on either side,
+# since the GPU sums the row statistics in another order
+THR_REL = 1e-9
+
+
+def check_idx_row_threshold(gpu_row, scores_row, want_row, forced, tau):
+    """A threshold-selection row: kept blocks ascending then -1 padding, every
+    forced block kept, and equal to the oracle's row except for blocks at the
+    row threshold (within THR_REL) or inside the cap's tie zone."""
+    g = [int(x) for x in gpu_row]
+    w = [int(x) for x in want_row]
+    nb = len(scores_row)
+    nv = sum(1 for c in g if c >= 0)
+    valid = g[:nv]
+    if any(c != -1 for c in g[nv:]) or any(b <= a for a, b in zip(valid, valid[1:])):
+        return False, False
+    if any(c < 0 or c >= nb for c in valid) or not set(forced) <= set(valid):
+        return False, False
+    if g == w:
+        return True, False
+    row = np.asarray(scores_row, dtype=np.float64)
+    mean = row.mean()
+    std = row.std()
+    thr = mean + tau * std
+    scale = abs(thr) + std + 1e-300
+    F = set(forced)
+    kept_g = set(valid) - F
+    kept_w = set(c for c in w if c >= 0) - F
+    cap_bound = len(kept_w) > 0 and min(row[c] for c in kept_w)
+    cap = len(w) - len(F)
+    for c in kept_g ^ kept_w:
+        at_thr = abs(row[c] - thr) <= THR_REL * scale
+        at_cap = len(kept_w) == cap and abs(row[c] - cap_bound) <= TIE_REL * max(abs(cap_bound), 1e-300)
+        if not (at_thr or at_cap):
+            return False, False
+    return True, True
+
+
 def check_output(gpu_out, ref_out):
     d = np.abs(np.asarray(gpu_out, dtype=np.float64) - ref_out)
     return float(d.max()), float(d.mean())

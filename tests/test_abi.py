@@ -55,13 +55,13 @@ def test_blocks_and_workspace():
 
 def test_struct_layout_matches_header():
     """The ctypes mirror has the header's fields, in order, with the
-    header's size (11 four-byte fields)."""
+    header's size (13 four-byte fields)."""
     text = open(os.path.join(ROOT, "include", "bsa.h")).read()
     body = text[text.index("typedef struct bsa_problem {"):text.index("} bsa_problem;")]
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     fields = re.findall(r"\b(?:int32_t|float)\s+(\w+);", body)
     assert fields == [f for f, _ in bsa.Problem._fields_]
-    assert ctypes.sizeof(bsa.Problem) == 4 * len(fields) == 44
+    assert ctypes.sizeof(bsa.Problem) == 4 * len(fields) == 52
 
 
 def test_sink_blocks_and_k():
@@ -92,6 +92,7 @@ def test_ratio_budget():
 
 
 @pytest.mark.parametrize("field,value,err", [
+    ("select_mode", 2, ValueError), ("select_tau", float("nan"), ValueError),
     ("head_dim", 64, NotImplementedError), ("block_size", 64, NotImplementedError),
     ("seq_len", 0, ValueError), ("heads", 0, ValueError), ("batch", -1, ValueError),
     ("top_k", -1, ValueError), ("summary", 7, ValueError), ("anchor_rows", 5000, ValueError),

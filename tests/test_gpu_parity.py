@@ -16,8 +16,8 @@ import pytest
 import block_sparse_attention_25_amd as bsa
 from block_sparse_attention_25_amd.synth import WORKLOADS, custom, generate
 from oracle import bsa_oracle as O
-from tests.parity import (MAX_ABS, MEAN_ABS, check_idx_row, check_idx_row_forced, check_output,
-                          tensor_bits, to_device, widen)
+from tests.parity import (MAX_ABS, MEAN_ABS, check_idx_row, check_idx_row_forced,
+                          check_idx_row_threshold, check_output, tensor_bits, to_device, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def _run_gpu(torch, qb, kb, vb, **kw):
 
 
 def _check_head(host, qb, kb, vb, b, h, top_k, summary="mean", anchor_rows=0,
-                query_blocks=None, label="", sink_start=0, sink_rows=0):
+                query_blocks=None, label="", sink_start=0, sink_rows=0, tau=None):
     """Compare one (b, h) of a GPU run with the oracle; returns tie-zone rows."""
     Q, K, V = (widen(x[b, h]) for x in (qb, kb, vb))
     N = Q.shape[0]
@@ -76,8 +76,11 @@ def _check_head(host, qb, kb, vb, b, h, top_k, summary="mean", anchor_rows=0,
     assert gidx.shape == (nb, k)
     ties = 0
     if k > 0:
+        want = O.select_threshold(s, tau, top_k, sinks) if tau is not None else None
         for r in range(nb):
-            if sinks:
+            if tau is not None:
+                ok, tie = check_idx_row_threshold(gidx[r], s[r], want[r], sinks, tau)
+            elif sinks:
                 ok, tie = check_idx_row_forced(gidx[r], s[r], k, sinks)
             else:
                 ok, tie = check_idx_row(gidx[r], s[r], k)
@@ -159,6 +162,26 @@ def test_conditioning_sinks(torch_cuda, N, top_k, start, rows, summary):
     for h in range(2):
         _check_head(host, qb, kb, vb, 0, h, top_k, summary, anchor, label="sink%d" % N,
                     sink_start=start, sink_rows=rows)
+
+
+@pytest.mark.parametrize("N,top_k,tau,sink,summary", [
+    (1000, 8, 0.5, 0, "mean"),
+    (4096, 32, 1.0, 0, "mean"),      # the tiny shape, uncapped
+    (2000, 5, -0.5, 0, "mean"),      # the cap binds on most rows
+    (1000, 8, 3.0, 0, "mean"),       # most rows keep nothing: summary rows only
+    (1000, 8, 0.5, 100, "mean"),     # with conditioning sinks in the last block
+    (1000, 6, 0.8, 0, "reweight"),
+])
+def test_threshold_selection(torch_cuda, N, top_k, tau, sink, summary):
+    _log("case threshold N=%d cap=%d tau=%g sink=%d %s" % (N, top_k, tau, sink, summary))
+    w = custom(N, heads=2, seed=N + int(10 * tau) + sink)
+    qb, kb, vb = generate(w)
+    anchor = 800 if summary == "reweight" else 0
+    host = _run_gpu(torch_cuda, qb, kb, vb, top_k=top_k, summary=summary, anchor_rows=anchor,
+                    sink_rows=sink, tau=tau)
+    for h in range(2):
+        _check_head(host, qb, kb, vb, 0, h, top_k, summary, anchor, label="thr%d" % N,
+                    sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau)
 
 
 def test_batch_and_heads(torch_cuda):
@@ -252,7 +275,7 @@ def test_guard_bands_untouched(torch_cuda):
 
 # ---------------------------------------------------------- full sizes ---
 FULL = [("768p_5s", [0, 37]), ("768p_10s", [5]), ("2k_5s", [55]), ("768p_15s_reweight", [0, 21]),
-        ("768p_5s_sinks", [9])]
+        ("768p_5s_sinks", [9]), ("768p_5s_tau1", [17])]
 
 
 @pytest.mark.parametrize("name,heads", FULL)
@@ -265,7 +288,8 @@ def test_full_size_workloads_sampled(torch_cuda, name, heads):
     qb, kb, vb = generate(w, threads=16)
     nb = O.n_blocks(w.seq_len)
     top_k = w.top_k if w.top_k is not None else O.k_from_ratio(w.top_k_ratio, nb)
-    kw = dict(top_k=top_k, summary=w.summary, sink_start=w.sink_start, sink_rows=w.sink_rows)
+    kw = dict(top_k=top_k, summary=w.summary, sink_start=w.sink_start, sink_rows=w.sink_rows,
+              tau=w.tau)
     if w.summary == "reweight":
         kw["anchor_rows"] = w.anchor_rows
     host = _run_gpu(torch_cuda, qb, kb, vb, **kw)
@@ -274,11 +298,16 @@ def test_full_size_workloads_sampled(torch_cuda, name, heads):
     kk = len(sinks) + min(top_k, nb - len(sinks))
     idx = host["block_idx"].numpy()
     assert idx.shape == (1, w.heads, nb, kk)
-    assert np.all(np.diff(idx, axis=-1) > 0) and idx.min() >= 0 and idx.max() < nb
+    if w.tau is None:
+        assert np.all(np.diff(idx, axis=-1) > 0) and idx.min() >= 0 and idx.max() < nb
+    else:
+        nvalid = (idx >= 0).sum(-1)
+        _log("  kept blocks per row: min %d mean %.1f max %d of %d"
+             % (nvalid.min(), nvalid.mean(), nvalid.max(), nb))
     qbs = [0, 1, nb // 2, nb - 2, nb - 1]
     if sinks:
         qbs = sorted(set(qbs + [sinks[0] - 1, sinks[0]]))  # last video block, first sink block
     for h in heads:
         _check_head(host, qb, kb, vb, 0, h, top_k, w.summary, w.anchor_rows if w.summary ==
                     "reweight" else 0, query_blocks=qbs, label=name, sink_start=w.sink_start,
-                    sink_rows=w.sink_rows)
+                    sink_rows=w.sink_rows, tau=w.tau)
