@@ -300,6 +300,14 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
 // Every score is reduced in the same order, so identical key blocks tie
 // bit-exactly and the lower index wins.
 
+__device__ __forceinline__ int xcd_remap(int hw, int total) {
+  // workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+  // range of (head, query block) so neighbouring query blocks share its L2
+  const int per = total / 8, rem = total % 8;
+  const int x = hw & 7, j = hw >> 3;
+  return (x < rem) ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+}
+
 // sum over the 64 lanes of a wavefront; every lane gets the same bits
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
@@ -313,7 +321,7 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-template <int NKT, int RB>
+template <int NKT, int RB, bool ROWSPLIT>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q_pool,
                                                      const float* __restrict__ k_pool,
                                                      int32_t* __restrict__ block_idx, int nb,
@@ -323,59 +331,112 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
   constexpr int DCH = 32 / RB;    // features per step
   extern __shared__ double sc[];  // [RB][nb]
   const int tid = threadIdx.x;
-  const int r0 = blockIdx.x * RB;
-  const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  // 1-D grid: each XCD (its own L2) works through a contiguous range of
+  // (head, row group), so the pooled keys of a head are read from one L2
+  const int n_rg = (nb + RB - 1) / RB;
+  const int logical = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int r0 = (logical % n_rg) * RB;
+  const size_t bh = (size_t)(logical / n_rg);
   const float* qpb = q_pool + bh * nb * HD;
   const float* kpb = k_pool + bh * nb * HD;
 
-  double acc[NKT][RB];
+  if constexpr (!ROWSPLIT) {
+    double acc[NKT][RB];
 #pragma unroll
-  for (int i = 0; i < NKT; ++i)
+    for (int i = 0; i < NKT; ++i)
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) acc[i][rr] = 0.0;
-  int crow[NKT];
+      for (int rr = 0; rr < RB; ++rr) acc[i][rr] = 0.0;
+    int crow[NKT];
 #pragma unroll
-  for (int i = 0; i < NKT; ++i) crow[i] = min(tid + 256 * i, nb - 1);  // valid row to read
-  for (int d0 = 0; d0 < HD; d0 += DCH) {
-    double qv[RB][DCH];
+    for (int i = 0; i < NKT; ++i) crow[i] = min(tid + 256 * i, nb - 1);  // valid row to read
+    for (int d0 = 0; d0 < HD; d0 += DCH) {
+      double qv[RB][DCH];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int r = min(r0 + rr, nb - 1);
+#pragma unroll
+        for (int e = 0; e < DCH; ++e) qv[rr][e] = (double)qpb[(size_t)r * HD + d0 + e];
+      }
+#pragma unroll
+      for (int i = 0; i < NKT; ++i) {
+        float kv[DCH];
+        if constexpr (DCH % 4 == 0) {
+#pragma unroll
+          for (int e = 0; e < DCH; e += 4) {
+            const float4 t = *(const float4*)(kpb + (size_t)crow[i] * HD + d0 + e);
+            kv[e] = t.x;
+            kv[e + 1] = t.y;
+            kv[e + 2] = t.z;
+            kv[e + 3] = t.w;
+          }
+        } else {
+          static_assert(DCH == 2, "feature step");
+          const float2 t = *(const float2*)(kpb + (size_t)crow[i] * HD + d0);
+          kv[0] = t.x;
+          kv[1] = t.y;
+        }
+#pragma unroll
+        for (int e = 0; e < DCH; ++e) {
+          const double k64 = (double)kv[e];
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr) acc[i][rr] = fma(qv[rr][e], k64, acc[i][rr]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NKT; ++i) {
+      const int c = tid + 256 * i;
+      if (c < nb) {
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) sc[rr * nb + c] = acc[i][rr];
+      }
+    }
+  } else {
+    // Large nb: LPK lanes share one key row, each lane holding 128 / LPK of
+    // its features (16-byte chunks, 4 * LPK features apart), so every load of
+    // the wavefront reads whole 128-byte lines; the RB query rows' matching
+    // features stay in registers for the whole sweep (64 float64 values per
+    // lane), and the LPK partial dot products meet in a butterfly.
+    constexpr int LPK = 2 * RB, FPL = HD / LPK, CPL = FPL / 4;
+    static_assert(RB * FPL == 64, "row-split scores hold 64 query values per lane");
+    const int lane = tid & 63, sub = lane % LPK, grp = lane / LPK, wv = tid >> 6;
+    double qv[RB][FPL];
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
       const int r = min(r0 + rr, nb - 1);
 #pragma unroll
-      for (int e = 0; e < DCH; ++e) qv[rr][e] = (double)qpb[(size_t)r * HD + d0 + e];
-    }
-#pragma unroll
-    for (int i = 0; i < NKT; ++i) {
-      float kv[DCH];
-      if constexpr (DCH % 4 == 0) {
-#pragma unroll
-        for (int e = 0; e < DCH; e += 4) {
-          const float4 t = *(const float4*)(kpb + (size_t)crow[i] * HD + d0 + e);
-          kv[e] = t.x;
-          kv[e + 1] = t.y;
-          kv[e + 2] = t.z;
-          kv[e + 3] = t.w;
-        }
-      } else {
-        static_assert(DCH == 2, "feature step");
-        const float2 t = *(const float2*)(kpb + (size_t)crow[i] * HD + d0);
-        kv[0] = t.x;
-        kv[1] = t.y;
-      }
-#pragma unroll
-      for (int e = 0; e < DCH; ++e) {
-        const double k64 = (double)kv[e];
-#pragma unroll
-        for (int rr = 0; rr < RB; ++rr) acc[i][rr] = fma(qv[rr][e], k64, acc[i][rr]);
+      for (int j = 0; j < CPL; ++j) {
+        const float4 t = *(const float4*)(qpb + (size_t)r * HD + 4 * LPK * j + 4 * sub);
+        qv[rr][4 * j] = t.x;
+        qv[rr][4 * j + 1] = t.y;
+        qv[rr][4 * j + 2] = t.z;
+        qv[rr][4 * j + 3] = t.w;
       }
     }
-  }
+    constexpr int KPW = 64 / LPK;  // key rows per wavefront per sweep step
+    for (int c0 = KPW * wv; c0 < nb; c0 += 4 * KPW) {
+      const int c = c0 + grp;
+      const float* krow = kpb + (size_t)min(c, nb - 1) * HD;
+      double part[RB];
 #pragma unroll
-  for (int i = 0; i < NKT; ++i) {
-    const int c = tid + 256 * i;
-    if (c < nb) {
+      for (int rr = 0; rr < RB; ++rr) part[rr] = 0.0;
 #pragma unroll
-      for (int rr = 0; rr < RB; ++rr) sc[rr * nb + c] = acc[i][rr];
+      for (int j = 0; j < CPL; ++j) {
+        const float4 t = *(const float4*)(krow + 4 * LPK * j + 4 * sub);
+        const double kd[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr) part[rr] = fma(qv[rr][4 * j + e], kd[e], part[rr]);
+      }
+#pragma unroll
+      for (int off = 1; off < LPK; off <<= 1)
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) part[rr] += __shfl_xor(part[rr], off, 64);
+      if (sub == 0 && c < nb) {
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) sc[rr * nb + c] = part[rr];
+      }
     }
   }
   __syncthreads();
@@ -505,13 +566,6 @@ __device__ __forceinline__ int swz_v(int row, int chunk) {
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) { return *(const bf16x8*)p; }
 
-__device__ __forceinline__ int xcd_remap(int hw, int total) {
-  // workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
-  // range of (head, query block) so neighbouring query blocks share its L2
-  const int per = total / 8, rem = total % 8;
-  const int x = hw & 7, j = hw >> 3;
-  return (x < rem) ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
-}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -969,18 +1023,18 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
 
-template <int NKT, int RB>
+template <int NKT, int RB, bool ROWSPLIT>
 int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, int32_t* block_idx,
                   hipStream_t stream) {
-  const dim3 grid((unsigned)((g.nb + RB - 1) / RB), (unsigned)g.H, (unsigned)g.B);
+  const dim3 grid((unsigned)(((g.nb + RB - 1) / RB) * g.H * g.B));
   const size_t lds = (size_t)RB * g.nb * sizeof(double);
   if (lds > 48 * 1024) {
     // allow the score rows of large sequences beyond the default dynamic LDS cap
-    if (hipFuncSetAttribute((const void*)select_kernel<NKT, RB>,
+    if (hipFuncSetAttribute((const void*)select_kernel<NKT, RB, ROWSPLIT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return BSA_ERR_HIP;
   }
-  hipLaunchKernelGGL((select_kernel<NKT, RB>), grid, dim3(256), lds, stream, q_pool, k_pool, block_idx,
+  hipLaunchKernelGGL((select_kernel<NKT, RB, ROWSPLIT>), grid, dim3(256), lds, stream, q_pool, k_pool, block_idx,
                      (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1, g.threshold ? 1 : 0, g.tau);
   return launch_status();
 }
@@ -1068,11 +1122,12 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   if (!aligned16(q_pool) || !aligned16(k_pool)) return BSA_ERR_INVALID;
   hipStream_t s = (hipStream_t)hip_stream;
   // key blocks per thread sized to nb; query blocks per workgroup sized so
-  // the float64 score rows fit in 64 KiB of LDS
-  if (g.nb <= 256) return launch_select<1, 16>(g, q_pool, k_pool, block_idx, s);
-  if (g.nb <= 512) return launch_select<2, 16>(g, q_pool, k_pool, block_idx, s);
-  if (g.nb <= 1024) return launch_select<4, 8>(g, q_pool, k_pool, block_idx, s);
-  return launch_select<8, 4>(g, q_pool, k_pool, block_idx, s);
+  // the float64 score rows fit in 64 KiB of LDS; past 1024 blocks the
+  // row-split score phase keeps four query rows in registers
+  if (g.nb <= 256) return launch_select<1, 16, false>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 512) return launch_select<2, 16, false>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 1024) return launch_select<4, 8, false>(g, q_pool, k_pool, block_idx, s);
+  return launch_select<8, 4, true>(g, q_pool, k_pool, block_idx, s);
 }
 
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,

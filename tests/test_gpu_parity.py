@@ -184,6 +184,34 @@ def test_threshold_selection(torch_cuda, N, top_k, tau, sink, summary):
                     sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau)
 
 
+@pytest.mark.parametrize("variant", ["plain", "ties", "sinks", "threshold"])
+def test_many_blocks_selection(torch_cuda, variant):
+    """Past 1024 blocks the selection runs its row-split score phase: every
+    index of the head against the oracle, and sampled query blocks."""
+    N = 140000                                  # 1094 blocks, short last block
+    _log("case many blocks %s" % variant)
+    w = custom(N, heads=1, seed=17)
+    qb, kb, vb = generate(w, threads=16)
+    kw = dict(top_k=16)
+    check = dict()
+    if variant == "ties":
+        kb = kb.copy()
+        for dst in (1000, 1001):
+            kb[0, 0, dst * 128:(dst + 1) * 128] = kb[0, 0, 256:384]
+    elif variant == "sinks":
+        kw.update(sink_rows=1000)
+        check.update(sink_start=N - 1000, sink_rows=1000)
+    elif variant == "threshold":
+        kw.update(tau=1.5, top_k=40)
+        check.update(tau=1.5)
+    host = _run_gpu(torch_cuda, qb, kb, vb, **kw)
+    _check_head(host, qb, kb, vb, 0, 0, kw["top_k"], query_blocks=[0, 250, 1092, 1093],
+                label="nb1094-" + variant, **check)
+    if variant == "ties":
+        s = O.block_scores(O.pool_mean(widen(qb[0, 0])), O.pool_mean(widen(kb[0, 0])))
+        assert np.array_equal(host["block_idx"][0, 0].numpy(), O.select_topk(s, 16))
+
+
 def test_batch_and_heads(torch_cuda):
     _log("case batch 2 x heads 3")
     w = custom(1500, heads=3, batch=2, seed=3)
