@@ -123,16 +123,26 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const uint16_t* __restrict_
   }
 }
 
-// anchor[b,h,:] = (sum over blocks of the partial sums, in block order) / rows
-__global__ __launch_bounds__(128) void anchor_kernel(const double* __restrict__ anchor_part,
-                                                     double* __restrict__ anchor, int nb,
-                                                     int anchor_rows) {
+// anchor[b,h,:] = (sum of the per-block partial sums) / rows.  Eight strided
+// partial sums per feature (blocks c = g mod 8, in block order), combined in
+// a fixed order, so the result is deterministic.
+__global__ __launch_bounds__(1024) void anchor_kernel(const double* __restrict__ anchor_part,
+                                                      double* __restrict__ anchor, int nb,
+                                                      int anchor_rows) {
+  __shared__ double part[8][HD];
   const size_t bh = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x & (HD - 1), g = threadIdx.x >> 7;
   const int nblk = (anchor_rows + BLK - 1) / BLK;
   double s = 0.0;
-  for (int c = 0; c < nblk; ++c) s += anchor_part[(bh * nb + c) * HD + d];
-  anchor[bh * HD + d] = s / (double)anchor_rows;
+#pragma unroll 4
+  for (int c = g; c < nblk; c += 8) s += anchor_part[(bh * nb + c) * HD + d];
+  part[g][d] = s;
+  __syncthreads();
+  if (g == 0) {
+    const double t = ((part[0][d] + part[1][d]) + (part[2][d] + part[3][d])) +
+                     ((part[4][d] + part[5][d]) + (part[6][d] + part[7][d]));
+    anchor[bh * HD + d] = t / (double)anchor_rows;
+  }
 }
 
 template <bool REWEIGHT>
@@ -144,6 +154,7 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
   __shared__ double red[16][HD];
   __shared__ uint16_t vl[BLK][HD + 2];  // V block, rows padded against bank conflicts
   __shared__ double rowred[16][3];
+  __shared__ double lrow[BLK];  // reweight: anchor logit, then weight, of each row
   const int c = blockIdx.x, tid = threadIdx.x;
   const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
   const int s = c * BLK, n = min(BLK, N - s);
@@ -209,17 +220,23 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
       l[i] = scale * part;
       if (rp + 16 * i < n) lmax = fmax(lmax, l[i]);
     }
-    if (cc == 0) rowred[rp][0] = lmax;
+    if (cc == 0) {
+      rowred[rp][0] = lmax;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lrow[rp + 16 * i] = l[i];
+    }
     __syncthreads();
     double m = rowred[0][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) m = fmax(m, rowred[i][0]);
+    // one float64 exponential per row (the 16 lanes of a row share it)
+    if (tid < BLK) lrow[tid] = tid < n ? exp(lrow[tid] - m) : 0.0;
     __syncthreads();
     double w[8], zpart = 0.0, lsum = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const bool ok = rp + 16 * i < n;
-      w[i] = ok ? exp(l[i] - m) : 0.0;
+      w[i] = lrow[rp + 16 * i];
       zpart += w[i];
       lsum += ok ? l[i] : 0.0;
     }
@@ -1093,7 +1110,7 @@ int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v, 
     hipLaunchKernelGGL(pool_q_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)q, q_pool, apart,
                        (int)g.N, (int)g.nb, g.anchor_rows);
     if ((st = launch_status()) != BSA_OK) return st;
-    hipLaunchKernelGGL(anchor_kernel, dim3((unsigned)g.H, (unsigned)g.B), dim3(HD), 0, s,
+    hipLaunchKernelGGL(anchor_kernel, dim3((unsigned)g.H, (unsigned)g.B), dim3(8 * HD), 0, s,
                        (const double*)apart, anc, (int)g.nb, g.anchor_rows);
     if ((st = launch_status()) != BSA_OK) return st;
     hipLaunchKernelGGL(pool_kv_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)k,
