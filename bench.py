@@ -56,6 +56,25 @@ def measured_traffic(workload):
     return float(fields["traffic_bytes"])
 
 
+def reported_clock_peak():
+    """The bf16 dense MFMA peak recomputed from the device's reported maximum
+    engine clock and compute-unit count (4 SIMDs x 1024 bf16 flop per clock
+    each); None when the runtime does not report them."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        clk, cus = ctypes.c_int(), ctypes.c_int()
+        # hipDeviceAttributeClockRate (kHz) and hipDeviceAttributeMultiprocessorCount
+        ok1 = hip.hipDeviceGetAttribute(ctypes.byref(clk), 5, 0) == 0
+        ok2 = hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, 0) == 0
+        if not (ok1 and ok2) or clk.value <= 0 or cus.value <= 0:
+            return None
+        return {"clock_mhz": clk.value / 1e3, "compute_units": cus.value,
+                "peak_tflops": round(cus.value * 4 * 1024 * clk.value * 1e3 / 1e12, 1)}
+    except OSError:
+        return None
+
+
 def counted_flops(torch, idx, N, nb, H, B, dense=()):
     """4 * d * sum over (b, h, r) of n_r * sum_{c in S(r)} n_c, exactly; query
     blocks in `dense` (conditioning sinks) attend to all N keys."""
@@ -238,6 +257,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name),
                      "traffic_unit": "bytes per launch (HBM, from rocprofv3 FETCH_SIZE + WRITE_SIZE)"},
+        "peak_from_reported_clock": reported_clock_peak(),
         "input_gen_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:

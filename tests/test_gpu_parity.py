@@ -212,6 +212,33 @@ def test_many_blocks_selection(torch_cuda, variant):
         assert np.array_equal(host["block_idx"][0, 0].numpy(), O.select_topk(s, 16))
 
 
+def test_forward_with_given_indices(torch_cuda):
+    """bsa_forward on an index set chosen here (random ascending rows, not the
+    GPU's own selection) against the oracle's attention on the same rows."""
+    torch = torch_cuda
+    _log("case forward with given indices")
+    N, H, top_k = 3000, 2, 7
+    w = custom(N, heads=H, seed=31)
+    qb, kb, vb = generate(w)
+    q, k, v = (to_device(x) for x in (qb, kb, vb))
+    out, aux = bsa.attention(q, k, v, top_k=top_k, return_aux=True)
+    nb = O.n_blocks(N)
+    rng = np.random.default_rng(5)
+    idx = np.stack([np.stack([np.sort(rng.choice(nb, top_k, replace=False)) for _ in range(nb)])
+                    for _ in range(H)])[None].astype(np.int32)
+    gidx = torch.from_numpy(idx).cuda()
+    out2 = torch.empty_like(q)
+    bsa.bsa_forward(aux["problem"], q, k, aux["sum_k"], aux["sum_bias"], gidx, aux["workspace"], out2)
+    torch.cuda.synchronize()
+    for h in range(H):
+        Q, K, V = (widen(x[0, h]) for x in (qb, kb, vb))
+        sk, sv, bias = O.summaries_mean(K, V)
+        ref = O.attention(Q, K, V, idx[0, h], sk, sv, bias, O.default_scale(128))
+        mx, mean = check_output(widen(tensor_bits(out2[0, h])), ref)
+        _log("  given idx h%d: out max %.3g mean %.3g" % (h, mx, mean))
+        assert mx <= MAX_ABS and mean <= MEAN_ABS
+
+
 def test_batch_and_heads(torch_cuda):
     _log("case batch 2 x heads 3")
     w = custom(1500, heads=3, batch=2, seed=3)
