@@ -65,6 +65,15 @@ Readings taken where the pages are silent (each is exercised by a test):
      (WAS Node Suite node page), section "The inputs that matter" (tau 1.0
      keeps roughly 16% of key blocks exact, 1.5 about 7%, 2.0 about 3%): the
      normal tail beyond tau standard deviations is 15.9%, 6.7% and 2.3%.
+  R15 extra tokens: besides its kept blocks, each query block r reads exactly
+     the E tokens j of the blocks it skipped with the largest q_pool[r] . k_j
+     (the same pooled-query score as block selection, float64), ties to the
+     lower token index; every skipped block keeps its summary row (R7 weighs
+     a summary row as one key, so nothing is counted twice).  Sink query
+     blocks skip nothing and read no extra tokens.  Source: "H3 Sparse
+     Attention" (WAS Node Suite node page), section "The inputs that matter"
+     (extra_tokens, the top-scoring tokens each query block reads beyond its
+     chosen blocks).
 
 Precision: pooled vectors are summed in float64 and stored as float32 (the
 precision in which a block ranking is decided); block scores are float64 dot
@@ -180,6 +189,27 @@ def select_threshold(scores: np.ndarray, tau: float, top_k: int, forced=()) -> n
     return idx
 
 
+def select_extra_tokens(q_pool, k, idx, extra: int, block: int = BLOCK, dense_blocks=()):
+    """Extra tokens (R15): for each query block r, the `extra` tokens of the
+    blocks not in idx[r] with the largest q_pool[r] . k_j (float64), ties to
+    the lower token index; ascending, padded with -1.  int32 [nb, extra]."""
+    qp = np.asarray(q_pool, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    rows = block_rows(k.shape[0], block)
+    nb = len(rows)
+    out = np.full((nb, extra), -1, dtype=np.int32)
+    for r in range(nb):
+        if r in set(dense_blocks) or extra == 0:
+            continue
+        chosen = set(int(c) for c in idx[r] if c >= 0)
+        cand = [j for c in range(nb) if c not in chosen for j in range(rows[c][0], rows[c][1])]
+        s = np.array([float(np.dot(qp[r], k[j])) for j in cand])
+        order = sorted(range(len(cand)), key=lambda i: (-s[i], cand[i]))[:extra]
+        kept = sorted(cand[i] for i in order)
+        out[r, :len(kept)] = kept
+    return out
+
+
 def sink_blocks(N: int, sink_start: int, sink_rows: int, block: int = BLOCK):
     """Blocks holding at least one row of the conditioning range
     [sink_start, sink_start + sink_rows) (R13); empty when sink_rows is 0."""
@@ -248,7 +278,7 @@ def summaries_reweight(k: np.ndarray, v: np.ndarray, a: np.ndarray, scale: float
 
 # -------------------------------------------------------------- attention ---
 def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK,
-              query_blocks=None, dense_blocks=()):
+              query_blocks=None, dense_blocks=(), extra=None):
     """Block-sparse attention with summary rows for one (batch, head).
 
     For query i in block r, the logits are
@@ -261,7 +291,9 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
 
     idx may be any [nb, k] array of distinct valid block indices per row (the
     output is unique given idx); entries of -1 are padding and ignored.  Query blocks listed in dense_blocks attend to
-    every key block exactly, whatever idx holds for them (R13).  query_blocks
+    every key block exactly, whatever idx holds for them (R13).  extra [nb, E]
+    lists tokens each query block also reads exactly (R15; -1 is padding).
+    query_blocks
     restricts the work to those query blocks (other output rows stay zero).
     Returns float64 [N, d]."""
     q = np.asarray(q, dtype=np.float64)
@@ -282,9 +314,11 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
             raise ValueError("idx row %d is not a set of valid blocks" % r)
         chosen = set(sel)
         skipped = [c for c in range(nb) if c not in chosen]
-        keys = [k[rows[c][0]:rows[c][1]] for c in sorted(chosen)] + [sum_k[skipped]]
-        vals = [v[rows[c][0]:rows[c][1]] for c in sorted(chosen)] + [sum_v[skipped]]
-        add = [np.zeros(rows[c][1] - rows[c][0]) for c in sorted(chosen)] + [bias[skipped]]
+        ext = [] if extra is None else [int(j) for j in extra[r] if j >= 0]
+        keys = [k[rows[c][0]:rows[c][1]] for c in sorted(chosen)] + [k[ext]] + [sum_k[skipped]]
+        vals = [v[rows[c][0]:rows[c][1]] for c in sorted(chosen)] + [v[ext]] + [sum_v[skipped]]
+        add = ([np.zeros(rows[c][1] - rows[c][0]) for c in sorted(chosen)] + [np.zeros(len(ext))] +
+               [bias[skipped]])
         K = np.concatenate(keys, axis=0)
         V = np.concatenate(vals, axis=0)
         B = np.concatenate(add)
@@ -303,12 +337,13 @@ def default_scale(d: int) -> float:
 
 def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
              scale: float | None = None, block: int = BLOCK, bias_ref: str = "mean",
-             sink_start: int = 0, sink_rows: int = 0, tau: float | None = None):
+             sink_start: int = 0, sink_rows: int = 0, tau: float | None = None,
+             extra_tokens: int = 0):
     """All four stages for one (batch, head).  Returns a dict with the pooled
     vectors, scores, selection, summaries, sink blocks and the float64 output.
     sink_rows > 0 routes the conditioning rows [sink_start, sink_start +
     sink_rows) as sinks (R13); tau selects blocks by threshold (R14) with top_k
-    as the cap."""
+    as the cap; extra_tokens adds that many exact tokens per query block (R15)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -326,6 +361,7 @@ def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
         sk, sv, b = summaries_reweight(k, v, a, sc, block, bias_ref)
     else:
         raise ValueError("summary must be 'mean' or 'reweight'")
-    out = attention(q, k, v, idx, sk, sv, b, sc, block, dense_blocks=sinks)
+    extra = select_extra_tokens(q_pool, k, idx, extra_tokens, block, sinks) if extra_tokens else None
+    out = attention(q, k, v, idx, sk, sv, b, sc, block, dense_blocks=sinks, extra=extra)
     return dict(q_pool=q_pool, k_pool=k_pool, scores=s, idx=idx, sum_k=sk,
-                sum_v=sv, bias=b, out=out, scale=sc, sinks=sinks)
+                sum_v=sv, bias=b, out=out, scale=sc, sinks=sinks, extra=extra)

@@ -547,6 +547,96 @@ def test_threshold_attention_ignores_padding():
     assert np.abs(res["out"] - ref).max() < 1e-10
 
 
+# ------------------------------------------------------ extra tokens (R15) ---
+def _py_score(a, b):
+    s = 0.0
+    for x, y in zip(a, b):
+        s += float(x) * float(y)
+    return s
+
+
+@pytest.mark.parametrize("N,top_k,E", [(900, 2, 40), (640, 1, 7), (1024, 3, 200)])
+def test_extra_tokens_brute_force(N, top_k, E):
+    """Every kept token beats every other candidate (higher score, or equal
+    score and lower index); candidates are exactly the skipped blocks' rows."""
+    q, k, _ = _synth_head(N, seed=N + E)
+    qp, kp = O.pool_mean(q), O.pool_mean(k)
+    idx = O.select_topk(O.block_scores(qp, kp), top_k)
+    ext = O.select_extra_tokens(qp, k, idx, E)
+    rows = O.block_rows(N)
+    assert ext.shape == (len(rows), E)
+    for r in range(len(rows)):
+        cand = [j for c in range(len(rows)) if c not in set(idx[r]) for j in range(*rows[c])]
+        kept = [int(j) for j in ext[r] if j >= 0]
+        assert len(kept) == min(E, len(cand)) and all(j == -1 for j in ext[r][len(kept):])
+        assert set(kept) <= set(cand) and kept == sorted(kept)
+        sc = {j: _py_score(qp[r], k[j]) for j in cand}
+        rest = [j for j in cand if j not in set(kept)]
+        for a in kept:
+            for b in rest[::7]:
+                assert sc[a] > sc[b] or (sc[a] == sc[b] and a < b)
+
+
+def test_extra_tokens_ties_and_zero():
+    N = 512
+    q, k, _ = _synth_head(N, seed=4)
+    k = k.copy()
+    k[300] = k[260]          # two equal rows in skipped block 2
+    qp, kp = O.pool_mean(q), O.pool_mean(k)
+    idx = np.array([[0], [0], [0], [0]], dtype=np.int32)
+    sc260 = float(np.dot(qp[0], k[260]))
+    cand = [j for j in range(128, 512)]
+    better = sum(1 for j in cand if float(np.dot(qp[0], k[j])) > sc260)
+    ext = O.select_extra_tokens(qp, k, idx, better + 1)
+    assert 260 in ext[0] and 300 not in ext[0]
+    ext0 = O.select_extra_tokens(qp, k, idx, 0)
+    assert ext0.shape == (4, 0)
+
+
+@pytest.mark.parametrize("summary", ["mean", "reweight"])
+def test_extra_tokens_all_candidates(summary):
+    """With E at least the skipped rows, every token is read exactly and each
+    skipped block still adds its summary row: SDPA over [K; summaries]."""
+    N = 700
+    q, k, v = _synth_head(N, seed=8)
+    res = O.run_head(q, k, v, top_k=2, summary=summary, extra_tokens=N)
+    rows = O.block_rows(N)
+    for r, (s0, e0) in enumerate(rows):
+        skipped = [c for c in range(len(rows)) if c not in set(res["idx"][r])]
+        K = np.concatenate([k, res["sum_k"][skipped]])
+        V = np.concatenate([v, res["sum_v"][skipped]])
+        add = np.concatenate([np.zeros(N), res["bias"][skipped]])
+        ref = _sdpa(q[s0:e0], K, V, mask=np.repeat(add[None, :], e0 - s0, axis=0))
+        assert np.abs(res["out"][s0:e0] - ref).max() < 1e-10
+
+
+def test_extra_tokens_mask_formulation_and_sinks():
+    N = 1000
+    q, k, v = _synth_head(N, seed=12)
+    res = O.run_head(q, k, v, top_k=2, extra_tokens=50, sink_start=900, sink_rows=100)
+    ext = res["extra"]
+    assert (ext[7] == -1).all()                       # the sink query block skips nothing
+    rows = O.block_rows(N)
+    nb = len(rows)
+    base = O.run_head(q, k, v, top_k=2, sink_start=900, sink_rows=100)
+    assert np.array_equal(base["idx"], res["idx"])
+    mask = np.full((N, N + nb), -np.inf)
+    for r, (s0, e0) in enumerate(rows):
+        kept = set(range(nb)) if r in res["sinks"] else set(int(c) for c in res["idx"][r])
+        for c in kept:
+            mask[s0:e0, rows[c][0]:rows[c][1]] = 0.0
+        for j in ext[r]:
+            if j >= 0:
+                mask[s0:e0, j] = 0.0
+        for c in range(nb):
+            if c not in kept:
+                mask[s0:e0, N + c] = res["bias"][c]
+    ref = _sdpa(q, np.concatenate([k, res["sum_k"]]), np.concatenate([v, res["sum_v"]]), mask=mask)
+    assert np.abs(res["out"] - ref).max() < 1e-10
+    z = O.run_head(q, k, v, top_k=2, extra_tokens=0)
+    assert np.array_equal(z["out"], O.run_head(q, k, v, top_k=2)["out"])
+
+
 # -------------------------------------------------- planted mistakes fail ---
 def _all_pins_pass():
     """Re-run a compact set of the pins above; True when every one holds."""
@@ -570,6 +660,9 @@ def _all_pins_pass():
         test_threshold_closed_forms()
         test_threshold_brute_force(640, 0.5, 5)
         test_threshold_attention_ignores_padding()
+        test_extra_tokens_brute_force(900, 2, 40)
+        test_extra_tokens_ties_and_zero()
+        test_extra_tokens_mask_formulation_and_sinks()
     except AssertionError:
         return False
     return True
@@ -645,9 +738,55 @@ def _attn_wrong_scale(q, k, v, idx, sk, sv, b, scale, block=128, **kw):
     return _orig_attn(q, k, v, idx, sk, sv, b, scale * scale, block, **kw)
 
 
-def _attn_dense_ignored(q, k, v, idx, sk, sv, b, scale, block=128, query_blocks=None, dense_blocks=()):
+def _attn_dense_ignored(q, k, v, idx, sk, sv, b, scale, block=128, query_blocks=None, dense_blocks=(),
+                        extra=None):
     # mistake: conditioning query blocks routed like every other block
-    return _orig_attn(q, k, v, idx, sk, sv, b, scale, block, query_blocks=query_blocks)
+    return _orig_attn(q, k, v, idx, sk, sv, b, scale, block, query_blocks=query_blocks, extra=extra)
+
+
+def _attn_extra_drops_summaries(q, k, v, idx, sk, sv, b, scale, block=128, query_blocks=None,
+                                dense_blocks=(), extra=None):
+    # mistake: a skipped block that gave extra tokens loses its summary row
+    if extra is None:
+        return _orig_attn(q, k, v, idx, sk, sv, b, scale, block, query_blocks, dense_blocks)
+    b = np.asarray(b, dtype=float).copy()
+    rows = O.block_rows(np.asarray(q).shape[0], block)
+    out = np.zeros(np.asarray(q).shape)
+    for r in range(len(rows)):
+        if query_blocks is not None and r not in query_blocks:
+            continue
+        bb = b.copy()
+        for j in extra[r]:
+            if j >= 0:
+                bb[j // block] = -np.inf
+        part = _orig_attn(q, k, v, idx, sk, sv, bb, scale, block, [r], dense_blocks, extra)
+        out[rows[r][0]:rows[r][1]] = part[rows[r][0]:rows[r][1]]
+    return out
+
+
+_orig_extra = O.select_extra_tokens
+
+
+def _extra_from_all_blocks(q_pool, k, idx, extra, block=128, dense_blocks=()):
+    # mistake: candidates drawn from every block, kept ones included
+    nb = np.asarray(idx).shape[0]
+    none = np.full((nb, 0), -1, dtype=np.int32)
+    return _orig_extra(q_pool, k, none, extra, block, dense_blocks)
+
+
+def _extra_ties_high(q_pool, k, idx, extra, block=128, dense_blocks=()):
+    # mistake: equal scores go to the higher token index
+    kk = np.asarray(k, dtype=np.float64)[::-1]
+    N = kk.shape[0]
+    nb = np.asarray(idx).shape[0]
+    rev_idx = np.array([[nb - 1 - c if c >= 0 else -1 for c in row] for row in np.asarray(idx)],
+                       dtype=np.int32)
+    if N % block:
+        return _orig_extra(q_pool, k, idx, extra, block, dense_blocks)
+    out = _orig_extra(np.asarray(q_pool)[::-1], kk, rev_idx, extra, block,
+                      [nb - 1 - c for c in dense_blocks])[::-1]
+    return np.array([sorted([N - 1 - j for j in row if j >= 0]) + [-1] * int((row < 0).sum())
+                     for row in out], dtype=np.int32)
 
 
 def _select_forced_in_pool(scores, top_k, forced=()):
@@ -721,6 +860,9 @@ def _anchor_off_by_one(q, anchor_rows):
     ("select_threshold", _threshold_sample_std),
     ("select_threshold", _threshold_inclusive),
     ("select_threshold", _threshold_stats_without_forced),
+    ("attention", _attn_extra_drops_summaries),
+    ("select_extra_tokens", _extra_from_all_blocks),
+    ("select_extra_tokens", _extra_ties_high),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
