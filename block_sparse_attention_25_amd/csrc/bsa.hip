@@ -300,13 +300,13 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
 }
 
 // ---------------------------------------------------------------- select ---
-// One workgroup of 4 wavefronts per RB query blocks of one (b, h).
-//  1. Scores: thread t owns the key blocks c = t + 256 i (i < NKT) and
-//     accumulates, for each of the RB query blocks, the float64 dot product
-//     of the pooled vectors feature by feature in order 0..127 (float32
-//     products are exact in float64).  Key features come from L2 straight
-//     into registers, DCH at a time; the query features are the same for the
-//     whole wavefront.  The RB x nb scores go to LDS.
+// One workgroup of 4 wavefronts per RB query blocks of one (b, h), on a 1-D
+// grid remapped so each XCD works through whole heads.
+//  1. Scores, float64 dot products of the pooled vectors (float32 products
+//     are exact in float64), RB x nb of them into LDS, in one of two layouts:
+//     thread-per-key (thread t owns the key blocks c = t + 256 i, i < NKT,
+//     features in order 0..127, key features DCH at a time) or row-split
+//     (LPK lanes share a key row; see below).
 //  2. Top-k: each wavefront takes one query block at a time.  Scores become
 //     order-preserving 64-bit keys held in registers (NCH keys per lane,
 //     key of block c in lane c % 64); an MSB-first bitwise search finds the
@@ -314,8 +314,8 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
 //     candidate (then those k are the answer).  Otherwise T is the k-th
 //     largest key; keys equal to T are taken lowest index first.  The chosen
 //     indices are written in ascending order with ballot prefix counts.
-// Every score is reduced in the same order, so identical key blocks tie
-// bit-exactly and the lower index wins.
+// Every score is reduced in the same order whatever its key block, so
+// identical key blocks tie bit-exactly and the lower index wins.
 
 __device__ __forceinline__ int xcd_remap(int hw, int total) {
   // workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -1138,11 +1138,12 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   if (!q_pool || !k_pool || !block_idx) return BSA_ERR_INVALID;
   if (!aligned16(q_pool) || !aligned16(k_pool)) return BSA_ERR_INVALID;
   hipStream_t s = (hipStream_t)hip_stream;
-  // key blocks per thread sized to nb; query blocks per workgroup sized so
-  // the float64 score rows fit in 64 KiB of LDS; past 1024 blocks the
-  // row-split score phase keeps four query rows in registers
-  if (g.nb <= 256) return launch_select<1, 16, false>(g, q_pool, k_pool, block_idx, s);
-  if (g.nb <= 512) return launch_select<2, 16, false>(g, q_pool, k_pool, block_idx, s);
+  // key blocks per lane (top-k phase) sized to nb.  The row-split score
+  // phase (four query rows in registers, whole-line key loads) is fastest
+  // except between 512 and 1024 blocks, where the thread-per-key phase with
+  // eight query rows per workgroup ties with it
+  if (g.nb <= 256) return launch_select<1, 4, true>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 512) return launch_select<2, 4, true>(g, q_pool, k_pool, block_idx, s);
   if (g.nb <= 1024) return launch_select<4, 8, false>(g, q_pool, k_pool, block_idx, s);
   return launch_select<8, 4, true>(g, q_pool, k_pool, block_idx, s);
 }
