@@ -110,6 +110,7 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = 1
+    host = {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "blas_threads": cores}
     N = w.seq_len
     nb = O.n_blocks(N)
     rows = O.block_rows(N)
@@ -139,7 +140,7 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
             break
         heads_done += 1
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle", "host": host,
             "sample": "%d query blocks (%d whole heads of %d, each with its pool, scores, top-k and "
                       "summaries) of the %s workload; %.1f s wall" % (blocks_done, heads_done,
                                                                      qb.shape[1], w.name, dt)}
@@ -211,6 +212,7 @@ def main():
     sel_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
     attn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
     step_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
+    step_med = float(np.median([e[0].elapsed_time(e[3]) for e in ev]))
     flops, summary_flops = counted_flops(torch, idx, N, nb, H, B, dense)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
@@ -248,6 +250,7 @@ def main():
         "kernels_ms": {"pool": round(pool_ms, 4), "select": round(sel_ms, 4),
                        "attention": round(attn_ms, 4)},
         "wall_ms_per_step": round(wall_ms, 4),
+        "median_ms_per_step": round(step_med, 4),
         "counted_tflop_per_step": round(flops / 1e12, 4),
         "summary_tflop_per_step": round(summary_flops / 1e12, 4),
         "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
