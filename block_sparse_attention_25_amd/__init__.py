@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(library_path):
-            raise ImportError("libbsa.so is not built (%s); run __graft_entry__.build() or "
+            raise ImportError("libbsa.so is not built (%s); build it with "
                               "python -m block_sparse_attention_25_amd.build" % library_path)
         L = ctypes.CDLL(library_path)
         L.bsa_status_str.argtypes = [ctypes.c_int]
