@@ -149,7 +149,7 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads would shard across GPUs without communication). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

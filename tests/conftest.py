@@ -14,5 +14,5 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests fail loudly (not skip) when selected with -m gpu on a machine
-    # without a GPU; without -m gpu they are simply deselected by the driver.
+    # without a GPU; -m "not gpu" deselects them.
     pass
