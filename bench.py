@@ -3,7 +3,8 @@
 
 One step = bsa_pool + bsa_select + bsa_forward over one batch of synthetic
 input already resident in HBM (the 768p 5s shape by default: 56 heads x
-37,740 tokens, head_dim 128, top_k 64 of 295 blocks, mean summaries).
+37,740 tokens, head_dim 128, top_k 64 of 295 blocks, mean summaries); with
+extra tokens, bsa_select_tokens + bsa_forward_tokens in place of bsa_forward.
 
 Prints one JSON line.  `value` is the effective TFLOP/s of a whole step
 counting only the selected blocks' attention FLOPs, 4 * 128 * sum_r n_r *
@@ -75,9 +76,10 @@ def reported_clock_peak():
         return None
 
 
-def counted_flops(torch, idx, N, nb, H, B, dense=()):
-    """4 * d * sum over (b, h, r) of n_r * sum_{c in S(r)} n_c, exactly; query
-    blocks in `dense` (conditioning sinks) attend to all N keys."""
+def counted_flops(torch, idx, N, nb, H, B, dense=(), tok=None):
+    """4 * d * sum over (b, h, r) of n_r * (sum_{c in S(r)} n_c + extra tokens
+    of r), exactly; query blocks in `dense` (conditioning sinks) attend to all
+    N keys."""
     n = torch.full((nb,), 128, dtype=torch.int64, device=idx.device)
     n[-1] = N - 128 * (nb - 1)
     k = idx.shape[-1]
@@ -90,6 +92,8 @@ def counted_flops(torch, idx, N, nb, H, B, dense=()):
         n_skip = nb - valid.sum(-1)
     else:
         n_skip = torch.full((B, H, nb), nb, dtype=torch.int64, device=idx.device)
+    if tok is not None:
+        per_row = per_row + (tok >= 0).sum(-1)
     if len(dense):
         per_row[..., list(dense)] = N
         n_skip[..., list(dense)] = 0
@@ -118,6 +122,7 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
     sc = O.default_scale(128)
     sinks = O.sink_blocks(N, w.sink_start, w.sink_rows)
     flops, heads_done, blocks_done = 0, 0, 0
+    no_tok = np.full((nb, 0), -1, dtype=np.int32)
     t0 = time.perf_counter()
     for h in range(qb.shape[1]):
         Q, K, V = (bf16_to_f32(x[0, h]).astype(np.float64) for x in (qb, kb, vb))
@@ -130,8 +135,12 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
         else:
             sk, sv, b = O.summaries_mean(K, V)
         for r in range(nb):
-            O.attention(Q, K, V, idx, sk, sv, b, sc, query_blocks=[r], dense_blocks=sinks)
-            keys = N if r in sinks else sum(rows[c][1] - rows[c][0] for c in idx[r] if c >= 0)
+            tok = O.select_extra_tokens(qp, K, idx, w.extra, dense_blocks=sinks, query_blocks=[r]) \
+                if w.extra else no_tok
+            O.attention(Q, K, V, idx, sk, sv, b, sc, query_blocks=[r], dense_blocks=sinks,
+                        extra=tok if w.extra else None)
+            keys = N if r in sinks else sum(rows[c][1] - rows[c][0] for c in idx[r] if c >= 0) + \
+                int((tok[r] >= 0).sum() if w.extra else 0)
             flops += 4 * 128 * (rows[r][1] - rows[r][0]) * keys
             blocks_done += 1
             if time.perf_counter() - t0 > budget_s:
@@ -141,9 +150,10 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
         heads_done += 1
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle", "host": host,
-            "sample": "%d query blocks (%d whole heads of %d, each with its pool, scores, top-k and "
-                      "summaries) of the %s workload; %.1f s wall" % (blocks_done, heads_done,
-                                                                     qb.shape[1], w.name, dt)}
+            "sample": "%d query blocks (%d whole heads of %d, each with its pool, scores, top-k%s and "
+                      "summaries) of the %s workload; %.1f s wall"
+                      % (blocks_done, heads_done, qb.shape[1], ", extra tokens" if w.extra else "",
+                         w.name, dt)}
 
 
 def main():
@@ -175,7 +185,8 @@ def main():
     q, k, v = dev_bf16(qb), dev_bf16(kb), dev_bf16(vb)
     p = bsa.make_problem(B, H, N, top_k, None, w.summary,
                          w.anchor_rows if w.summary == "reweight" else 0,
-                         sink_rows=w.sink_rows, sink_start=w.sink_start, tau=w.tau)
+                         sink_rows=w.sink_rows, sink_start=w.sink_start, tau=w.tau,
+                         extra_tokens=w.extra)
     dense = list(range(w.sink_start // 128, (w.sink_start + w.sink_rows - 1) // 128 + 1)) \
         if w.sink_rows > 0 else []
     nb, kk = bsa.bsa_problem_blocks(p)
@@ -188,8 +199,9 @@ def main():
     idx = torch.empty((B, H, nb, kk), dtype=torch.int32, device=dev)
     ws = torch.empty(bsa.bsa_workspace_bytes(p), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
+    tok = torch.empty((B, H, nb, w.extra), dtype=torch.int32, device=dev) if w.extra else None
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 
     def step(e=None):
         if e: e[0].record()
@@ -197,8 +209,14 @@ def main():
         if e: e[1].record()
         bsa.bsa_select(p, q_pool, k_pool, idx)
         if e: e[2].record()
-        bsa.bsa_forward(p, q, k, sum_k, sum_bias, idx, ws, out)
+        if tok is not None:
+            bsa.bsa_select_tokens(p, q_pool, k, idx, tok)
         if e: e[3].record()
+        if tok is not None:
+            bsa.bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx, tok, ws, out)
+        else:
+            bsa.bsa_forward(p, q, k, sum_k, sum_bias, idx, ws, out)
+        if e: e[4].record()
 
     for _ in range(args.warmup):
         step()
@@ -210,10 +228,11 @@ def main():
     wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
     pool_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     sel_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    attn_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
-    step_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
-    step_med = float(np.median([e[0].elapsed_time(e[3]) for e in ev]))
-    flops, summary_flops = counted_flops(torch, idx, N, nb, H, B, dense)
+    tok_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
+    attn_ms = sum(e[3].elapsed_time(e[4]) for e in ev) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[4]) for e in ev) / args.steps
+    step_med = float(np.median([e[0].elapsed_time(e[4]) for e in ev]))
+    flops, summary_flops = counted_flops(torch, idx, N, nb, H, B, dense, tok)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
     # pool: read Q, K, V once; write q_pool, k_pool (fp32), sum_k, sum_v (bf16),
@@ -245,17 +264,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": 128,
                    "n_blocks": nb, "top_k": kk, "summary": w.summary,
-                   "sink_rows": w.sink_rows, "tau": w.tau},
+                   "sink_rows": w.sink_rows, "tau": w.tau, "extra_tokens": w.extra},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"pool": round(pool_ms, 4), "select": round(sel_ms, 4),
-                       "attention": round(attn_ms, 4)},
+                       "attention": round(attn_ms, 4),
+                       **({"select_tokens": round(tok_ms, 4)} if tok is not None else {})},
         "wall_ms_per_step": round(wall_ms, 4),
         "median_ms_per_step": round(step_med, 4),
         "counted_tflop_per_step": round(flops / 1e12, 4),
         "summary_tflop_per_step": round(summary_flops / 1e12, 4),
         "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
         "select_gbs": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel",
+        "roofline": {"bound": "mfma",
+                     "kernel": "attn_fwd_kernel" if tok is None else "extra_attn_kernel + attn_fwd_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name),

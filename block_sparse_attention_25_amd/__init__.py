@@ -23,7 +23,8 @@ __all__ = [
     "BSA_OK", "BSA_ERR_INVALID", "BSA_ERR_UNSUPPORTED", "BSA_ERR_WORKSPACE", "BSA_ERR_HIP",
     "SUMMARY_MEAN", "SUMMARY_REWEIGHT", "BsaError", "Problem", "lib", "library_path",
     "bsa_status_str", "bsa_problem_blocks", "bsa_workspace_bytes", "bsa_pool", "bsa_select",
-    "bsa_forward", "k_from_ratio", "make_problem", "attention",
+    "bsa_forward", "bsa_select_tokens", "bsa_forward_tokens", "k_from_ratio", "make_problem",
+    "attention", "MAX_EXTRA",
 ]
 
 BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = 0, 1, 2, 3, 4
@@ -31,6 +32,7 @@ SUMMARY_MEAN, SUMMARY_REWEIGHT = 0, 1
 SELECT_TOPK, SELECT_THRESHOLD = 0, 1
 BLOCK = 128
 HEAD_DIM = 128
+MAX_EXTRA = 256
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libbsa.so")
@@ -44,6 +46,7 @@ class Problem(ctypes.Structure):
         ("summary", ctypes.c_int32), ("anchor_rows", ctypes.c_int32), ("scale", ctypes.c_float),
         ("sink_start", ctypes.c_int32), ("sink_rows", ctypes.c_int32),
         ("select_mode", ctypes.c_int32), ("select_tau", ctypes.c_float),
+        ("extra_tokens", ctypes.c_int32),
     ]
 
 
@@ -78,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.bsa_select.restype = ctypes.c_int
         L.bsa_forward.argtypes = [_P] + [_vp] * 6 + [ctypes.c_size_t, _vp, _vp]
         L.bsa_forward.restype = ctypes.c_int
+        L.bsa_select_tokens.argtypes = [_P] + [_vp] * 5
+        L.bsa_select_tokens.restype = ctypes.c_int
+        L.bsa_forward_tokens.argtypes = [_P] + [_vp] * 8 + [ctypes.c_size_t, _vp, _vp]
+        L.bsa_forward_tokens.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -139,6 +146,20 @@ def bsa_forward(p: Problem, q, k, sum_k, sum_bias, block_idx, workspace, out, st
                              _ptr(out), _stream(stream)), "bsa_forward")
 
 
+def bsa_select_tokens(p: Problem, q_pool, k, block_idx, token_idx, stream=None):
+    _raise(lib().bsa_select_tokens(ctypes.byref(p), _ptr(q_pool), _ptr(k), _ptr(block_idx),
+                                   _ptr(token_idx), _stream(stream)), "bsa_select_tokens")
+
+
+def bsa_forward_tokens(p: Problem, q, k, v, sum_k, sum_bias, block_idx, token_idx, workspace, out,
+                       stream=None):
+    _raise(lib().bsa_forward_tokens(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sum_k),
+                                    _ptr(sum_bias), _ptr(block_idx), _ptr(token_idx),
+                                    _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _ptr(out), _stream(stream)), "bsa_forward_tokens")
+
+
 # ---------------------------------------------------------------- helpers ---
 def k_from_ratio(ratio, n_blocks: int) -> int:
     """Top-k ratio budget -> block count, ceil(ratio * n_blocks) computed on the
@@ -150,12 +171,14 @@ def k_from_ratio(ratio, n_blocks: int) -> int:
 
 
 def make_problem(batch, heads, seq_len, top_k=None, top_k_ratio=None, summary="mean",
-                 anchor_rows=0, scale=None, sink_rows=0, sink_start=None, tau=None) -> Problem:
+                 anchor_rows=0, scale=None, sink_rows=0, sink_start=None, tau=None,
+                 extra_tokens=0) -> Problem:
     """Fill a bsa_problem.  sink_rows > 0 routes the conditioning rows
     [sink_start, sink_start + sink_rows) as sinks; sink_start defaults to
     N - sink_rows (conditioning rows after the video rows).  tau selects
     blocks by threshold (score above mean + tau * std of the row), with
-    top_k as the cap."""
+    top_k as the cap.  extra_tokens (0..256) adds, per query block, that
+    many exactly-read tokens from the blocks it skipped."""
     nb = -(-int(seq_len) // BLOCK)
     if (top_k is None) == (top_k_ratio is None):
         raise ValueError("give exactly one of top_k and top_k_ratio")
@@ -170,7 +193,7 @@ def make_problem(batch, heads, seq_len, top_k=None, top_k_ratio=None, summary="m
                    SUMMARY_MEAN if summary == "mean" else SUMMARY_REWEIGHT, int(anchor_rows),
                    0.0 if scale is None else float(scale), int(sink_start), sink_rows,
                    SELECT_TOPK if tau is None else SELECT_THRESHOLD,
-                   0.0 if tau is None else float(tau))
+                   0.0 if tau is None else float(tau), int(extra_tokens))
 
 
 def _check_qkv(q, k, v):
@@ -187,7 +210,8 @@ def _check_qkv(q, k, v):
 
 
 def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows=0, scale=None,
-              sink_rows=0, sink_start=None, tau=None, return_aux=False, stream=None):
+              sink_rows=0, sink_start=None, tau=None, extra_tokens=0, return_aux=False,
+              stream=None):
     """Block-sparse attention of bf16 q, k, v [B, H, N, 128] on the GPU.
 
     top_k counts 128-token key blocks (or give top_k_ratio, e.g. "0.1");
@@ -197,14 +221,16 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     last sink_rows rows) as sinks: their blocks are kept exactly by every
     query block, and their query blocks attend densely.  tau switches to
     threshold selection (blocks scoring above mean + tau * std of their row,
-    at most top_k; rows of block_idx padded with -1).  Returns out
-    [B, H, N, 128] bf16, plus a dict of intermediate tensors when return_aux
-    is set."""
+    at most top_k; rows of block_idx padded with -1).  extra_tokens > 0 lets
+    each query block also read exactly that many tokens of the blocks it
+    skipped, those scoring highest against its pooled query (token_idx in the
+    aux dict).  Returns out [B, H, N, 128] bf16, plus a dict of intermediate
+    tensors when return_aux is set."""
     import torch
     _check_qkv(q, k, v)
     B, H, N, _ = q.shape
     p = make_problem(B, H, N, top_k, top_k_ratio, summary, anchor_rows, scale, sink_rows, sink_start,
-                     tau)
+                     tau, extra_tokens)
     nb, kk = bsa_problem_blocks(p)
     dev = q.device
     f32, bf = torch.float32, torch.bfloat16
@@ -218,8 +244,15 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     out = torch.empty_like(q)
     bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws, stream)
     bsa_select(p, q_pool, k_pool, idx if kk > 0 else None, stream)
-    bsa_forward(p, q, k, sum_k, sum_bias, idx if kk > 0 else None, ws, out, stream)
+    tok = None
+    if p.extra_tokens > 0:
+        tok = torch.empty((B, H, nb, p.extra_tokens), dtype=torch.int32, device=dev)
+        bsa_select_tokens(p, q_pool, k, idx if kk > 0 else None, tok, stream)
+        bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx if kk > 0 else None, tok, ws, out,
+                           stream)
+    else:
+        bsa_forward(p, q, k, sum_k, sum_bias, idx if kk > 0 else None, ws, out, stream)
     if return_aux:
         return out, dict(q_pool=q_pool, k_pool=k_pool, sum_k=sum_k, sum_v=sum_v,
-                         sum_bias=sum_bias, block_idx=idx, workspace=ws, problem=p)
+                         sum_bias=sum_bias, block_idx=idx, token_idx=tok, workspace=ws, problem=p)
     return out

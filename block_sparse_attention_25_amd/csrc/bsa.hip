@@ -611,8 +611,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ sum_k,
     const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
-    const int32_t* __restrict__ block_idx, uint16_t* __restrict__ out, int N, int nb, int krow,
-    int nsb, float scale_log2, int total_wg, int f0, int f1) {
+    const int32_t* __restrict__ block_idx, const float* __restrict__ st_o,
+    const float* __restrict__ st_ml, uint16_t* __restrict__ out, int N, int nb, int krow, int nsb,
+    float scale_log2, int total_wg, int f0, int f1) {
   // LDS buffers as distinct variables, so the compiler can tell the DMA
   // targets from the buffers being read
   __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
@@ -773,6 +774,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  if (st_o && qi < N) {
+    // start from the softmax state of the extra tokens (O unnormalised, max
+    // and sum in base-2 units; the sum counts once, in the lower half)
+    const float* so = st_o + (bh * (size_t)N + qi) * HD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 t = *(const float4*)(so + 32 * db + 8 * r4 + 4 * g);
+        o[db][4 * r4 + 0] = t.x;
+        o[db][4 * r4 + 1] = t.y;
+        o[db][4 * r4 + 2] = t.z;
+        o[db][4 * r4 + 3] = t.w;
+      }
+    const float2 ml = *(const float2*)(st_ml + (bh * (size_t)N + qi) * 2);
+    m_run = ml.x;
+    l_run = g == 0 ? ml.y : 0.f;
+  }
   f32x16 sA[2], sB[2];
 
   // ---------------------------------------------------------------------
@@ -964,6 +983,383 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------- extra tokens ---
+// Besides its kept blocks, each query block r reads exactly the E tokens j of
+// the blocks it skipped with the largest q_pool[r] . k_j, equal scores going
+// to the lower token; every skipped block keeps its summary row.
+// Source: "H3 Sparse Attention" (WAS Node Suite node page), section "The
+// inputs that matter" (extra_tokens: the top-scoring tokens each query block
+// reads beyond its chosen blocks, 256 by default).
+//
+// token_select_kernel: one workgroup of 4 wavefronts per 32 query blocks of
+// one (b, h), on a 1-D grid remapped like the select kernel.
+//  - Scores on the matrix cores: C^T = K Qs^T, Qs holding every pooled query
+//    split exactly into three bfloat16 terms (hi + mid + lo equals the float32
+//    value), so each product is exact and the sums are float32.  Lane l of the
+//    accumulator holds query block l % 32 and 16 of the 32 tokens of a tile;
+//    the feature order inside the products is free, so a lane's K operand is
+//    128 contiguous bytes of its token row.
+//  - Each query block keeps a candidate list in LDS of 64-bit keys: the
+//    order-preserving float32 score above, the complemented token index below
+//    (so equal scores rank the lower token higher).  A token enters when the
+//    upper half of its key reaches the row's threshold.  Before a step whose
+//    128 new tokens could overflow a list, the list is cut to its E largest
+//    keys and the threshold rises to the E-th; every key dropped is below E
+//    kept ones, so it cannot be among the final E.
+//  - The blocks are walked in order, one block (32 tokens per wavefront) per
+//    step.  At the end each list is cut to E and written in ascending token
+//    order (each token's slot is the number of kept tokens below it), -1 after.
+
+constexpr int TS_ROWS = 32;   // query blocks per workgroup
+constexpr int TS_CAP = 512;   // candidate keys per query block
+
+__device__ __forceinline__ uint32_t order_key32(float s) {
+  if (s == 0.f) s = 0.f;  // -0 ties with +0
+  const uint32_t u = __float_as_uint(s);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+
+// Cuts a candidate list (n distinct nonzero keys, n <= TS_CAP) to its `keep`
+// largest keys, keeping their order, and returns the smallest kept key.  One
+// wavefront; MSB-first bitwise search that stops once exactly `keep` keys
+// reach the candidate threshold.
+__device__ uint64_t cut_list(uint64_t* list, int n, int keep, int lane) {
+  constexpr int PER = TS_CAP / 64;
+  uint64_t key[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int x = lane + 64 * j;
+    key[j] = x < n ? list[x] : 0ull;
+  }
+  uint64_t T = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t cand = T | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (cnt >= keep) {
+      T = cand;
+      if (cnt == keep) break;
+    }
+  }
+  // distinct keys: exactly `keep` of them are >= T
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int before = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool sel = key[j] >= T && key[j] != 0ull;
+    const uint64_t m = __ballot(sel);
+    if (sel) list[before + __popcll(m & lt)] = key[j];
+    before += __popcll(m);
+  }
+  return T;
+}
+
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(256, 1) void token_select_kernel(
+    const float* __restrict__ q_pool, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ block_idx, int32_t* __restrict__ token_idx, int N, int nb, int krow,
+    int E, int f0, int f1, int total_wg) {
+  __shared__ uint64_t list[TS_ROWS][TS_CAP];
+  __shared__ uint32_t skip[TS_ROWS][BSA_MAX_BLOCKS / 32];  // bit c: row skipped block c
+  __shared__ int cnt[TS_ROWS];
+  __shared__ uint32_t thr[TS_ROWS];
+
+  const int ngrp = (nb + TS_ROWS - 1) / TS_ROWS;
+  const int logical = xcd_remap(blockIdx.x, total_wg);
+  const int r0 = (logical % ngrp) * TS_ROWS;
+  const size_t bh = (size_t)(logical / ngrp);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ln = lane & 31;
+  const int nwords = (nb + 31) >> 5;
+
+  // candidates of row r0 + i: the blocks it did not keep; none for a sink
+  // query block (it attends to every block exactly) or past the last row
+  for (int x = tid; x < TS_ROWS * nwords; x += 256) {
+    const int i = x / nwords, wd = x % nwords, r = r0 + i;
+    uint32_t m = 0u;
+    if (r < nb && !(r >= f0 && r <= f1)) {
+      const int left = nb - 32 * wd;
+      m = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+    }
+    skip[i][wd] = m;
+  }
+  if (tid < TS_ROWS) {
+    cnt[tid] = 0;
+    thr[tid] = 0u;
+  }
+  __syncthreads();
+  for (int x = tid; x < TS_ROWS * krow; x += 256) {
+    const int i = x / krow, r = r0 + i;
+    if (r < nb) {
+      const int c = block_idx[(bh * nb + r) * (size_t)krow + (x - i * krow)];
+      if (c >= 0) atomicAnd(&skip[i][c >> 5], ~(1u << (c & 31)));
+    }
+  }
+
+  // B operand: query block r0 + ln, features 64g + 8s + [0, 8) for k-step s,
+  // as three exact bfloat16 terms
+  bf16x8 qs[3][8];
+  {
+    const float* qp = q_pool + (bh * nb + min(r0 + ln, nb - 1)) * HD + 64 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u16x8 hi, mid, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = qp[8 * s + e];
+        const uint16_t h = f2bf(x);
+        const float r1 = x - bf2f(h);  // exact
+        const uint16_t m = f2bf(r1);
+        const float r2 = r1 - bf2f(m);  // exact, at most 8 significant bits
+        hi[e] = h;
+        mid[e] = m;
+        lo[e] = f2bf(r2);
+      }
+      qs[0][s] = __builtin_bit_cast(bf16x8, hi);
+      qs[1][s] = __builtin_bit_cast(bf16x8, mid);
+      qs[2][s] = __builtin_bit_cast(bf16x8, lo);
+    }
+  }
+
+  // A operand: token c * 128 + 32 wave + ln, the 128 bytes of features
+  // [64g, 64g + 64).  Past the end of the sequence the last row is read
+  // again: such a token's scores fill only its own accumulator row and it is
+  // never inserted, so the loaded data needs no zeroing (and the prefetch
+  // needs no wait until its MFMAs).
+  const uint16_t* kb = k + bh * (size_t)N * HD;
+  auto load_tile = [&](int c, uint4* kt) {
+    const int t = c * BLK + 32 * wave + ln;
+    const uint4* src = (const uint4*)(kb + (size_t)min(t, N - 1) * HD + 64 * g);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kt[s] = src[s];
+  };
+
+  uint32_t thr_reg = 0u;
+  // one block per step: scores of its 32 tokens per wavefront, then (between
+  // two barriers, so every wavefront reads the same counts) the cut of the
+  // lists that the step could overflow, then the inserts
+  auto step = [&](int c, const uint4* ka, uint4* kn2) {
+    const int tbase = c * BLK + 32 * wave;
+    const bool row_skips = (skip[ln][c >> 5] >> (c & 31)) & 1u;
+    // always computed (no branch around the waits for a tile's loads)
+    f32x16 ch = {}, cm = {}, cl = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, ka[s]);
+      ch = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qs[0][s], ch, 0, 0, 0);
+      cm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qs[1][s], cm, 0, 0, 0);
+      cl = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qs[2][s], cl, 0, 0, 0);
+    }
+    // tiles are loaded two steps ahead, each after the MFMAs of the step
+    // before it, so a tile's MFMAs wait only for that tile's own loads
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(min(c + 2, nb - 1), kn2);  // unconditional: no branch around loads in flight
+    // a list holds at most TS_CAP - 128 keys before a step's inserts
+    __syncthreads();
+    // a wavefront cuts only its own rows (i = wave mod 4), whose counts no
+    // other wavefront changes, so reading the others' counts mid-cut is safe
+    const uint64_t full = __ballot(ln == lane && cnt[ln] > TS_CAP - BLK);
+    if (full) {
+      for (int i = wave; i < TS_ROWS; i += 4) {
+        if ((full >> i) & 1ull) {
+          const uint64_t T = cut_list(list[i], cnt[i], E, lane);
+          if (lane == 0) {
+            cnt[i] = E;
+            thr[i] = (uint32_t)(T >> 32);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    thr_reg = thr[ln];
+    if (row_skips && tbase < N) {
+      uint32_t mask = 0u;
+      uint32_t k32[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = tbase + 8 * (v >> 2) + 4 * g + (v & 3);
+        k32[v] = order_key32((cl[v] + cm[v]) + ch[v]);
+        if (t < N && k32[v] >= thr_reg) mask |= 1u << v;
+      }
+      if (mask) {
+        int pos = atomicAdd(&cnt[ln], __popc(mask));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if ((mask >> v) & 1u) {
+            const uint32_t t = (uint32_t)(tbase + 8 * (v >> 2) + 4 * g + (v & 3));
+            list[ln][pos++] = ((uint64_t)k32[v] << 32) | (uint64_t)(0xFFFFFFFFu - t);
+          }
+        }
+      }
+    }
+  };
+
+  uint4 kA[8], kB[8], kC[8];
+  load_tile(0, kA);
+  load_tile(min(1, nb - 1), kB);
+  __syncthreads();
+  for (int c = 0; c < nb; c += 3) {
+    step(c, kA, kC);
+    if (c + 1 < nb) step(c + 1, kB, kA);
+    if (c + 2 < nb) step(c + 2, kC, kB);
+  }
+  __syncthreads();
+
+  for (int i = wave; i < TS_ROWS; i += 4) {
+    const int r = r0 + i;
+    if (r >= nb) break;
+    int32_t* orow = token_idx + (bh * nb + r) * (size_t)E;
+    int n = cnt[i];
+    if (n > E) {
+      cut_list(list[i], n, E, lane);
+      n = E;
+    }
+    // output slot of a kept token = number of kept tokens below it, i.e. of
+    // kept keys with a larger lower half
+    uint32_t lo[BSA_MAX_EXTRA / 64];
+    int rank[BSA_MAX_EXTRA / 64];
+#pragma unroll
+    for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) {
+      const int x = lane + 64 * j;
+      lo[j] = x < n ? (uint32_t)list[i][x] : 0u;
+      rank[j] = 0;
+    }
+    for (int x = 0; x < n; ++x) {
+      const uint32_t o = (uint32_t)list[i][x];
+#pragma unroll
+      for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) rank[j] += o > lo[j];
+    }
+#pragma unroll
+    for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) {
+      const int x = lane + 64 * j;
+      if (x < n) orow[rank[j]] = (int32_t)(0xFFFFFFFFu - lo[j]);
+    }
+    for (int x = n + lane; x < E; x += 64) orow[x] = -1;
+  }
+}
+
+// extra_attn_kernel: the attention of each query block to its extra tokens,
+// left as softmax state for the attention kernel to start from: O
+// (unnormalised, float32), and the max m and sum l of the probabilities
+// (base-2 units), per query row.  Both parts then share one online softmax.
+// One workgroup (4 wavefronts of 32 queries) per (b, h, query block); the
+// extra tokens are taken 64 at a time: their K rows gathered into LDS in the
+// attention kernel's K layout, their V rows gathered and transposed into its
+// V^T layout, then S^T = K Q^T, the softmax update and O^T += V^T P^T on the
+// matrix cores.  A query block without extra tokens (a sink query block, or
+// one with no candidates) gets the empty state: O = 0, m = -inf, l = 0.
+__global__ __launch_bounds__(256, 2) void extra_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ token_idx, float* __restrict__ st_o, float* __restrict__ st_ml, int N,
+    int nb, int E, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[HT * HD], vs[HD * HT];
+  __shared__ int tok[BSA_MAX_EXTRA];
+  const int r = blockIdx.x;
+  const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, ln = lane & 31;
+
+  // the row's tokens: ascending, -1 padding after them
+  const int32_t t_in = tid < E ? token_idx[(bh * nb + r) * (size_t)E + tid] : -1;
+  tok[tid] = t_in;
+  const int nval = __syncthreads_count(t_in >= 0);
+
+  const int qi = r * BLK + 32 * wave + ln;
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  if (nval > 0) {
+    bf16x8 qf[8];
+    const uint16_t* qrow = q + (bh * (size_t)N + (size_t)min(qi, N - 1)) * HD;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      bf16x8 t = ld_bf16x8(qrow + 16 * kk + 8 * g);
+      if (qi >= N) t = bf16x8{};
+      qf[kk] = t;
+    }
+    const uint16_t* kb = k + bh * (size_t)N * HD;
+    const uint16_t* vb = v + bh * (size_t)N * HD;
+    for (int base = 0; base < nval; base += HT) {
+      // gather: 16-byte chunk x = tid + 256 j is chunk x % 16 of row x / 16
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = tid + 256 * j, row = x >> 4, ch = x & 15;
+        const int t = base + row < nval ? tok[base + row] : -1;
+        uint4 kd = make_uint4(0u, 0u, 0u, 0u), vd = kd;
+        if (t >= 0) {
+          kd = *(const uint4*)(kb + (size_t)t * HD + 8 * ch);
+          vd = *(const uint4*)(vb + (size_t)t * HD + 8 * ch);
+        }
+        *(uint4*)(ks + swz_k(row, ch)) = kd;
+        const int pos = vt_pos(row);
+        const uint32_t w[4] = {vd.x, vd.y, vd.z, vd.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vs[swz_v(8 * ch + e, pos >> 3) + (pos & 7)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+      __syncthreads();
+      // S^T: s[mb] element ii is key base + 32 mb + 8 (ii / 4) + 4 g + ii % 4
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ld_bf16x8(ks + swz_k(32 * (i & 1) + ln, 2 * (i >> 1) + g)), qf[i >> 1], s[i & 1], 0, 0, 0);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int key = base + 32 * mb + 8 * (ii >> 2) + 4 * g + (ii & 3);
+          const float x = key < nval ? s[mb][ii] * scale_log2 : -INFINITY;
+          s[mb][ii] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, other_half(mx));
+      const float m_new = fmaxf(m_run, mx);  // finite: the group holds a token
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      // P slice kk (keys 16 kk .. 16 kk + 15) in the V^T key order
+      bf16x8 pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u16x8 pu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t pbits = f2bf(__builtin_amdgcn_exp2f(s[kk >> 1][8 * (kk & 1) + e] - m_new));
+          pu[e] = pbits;
+          psum += bf2f(pbits);
+        }
+        pb[kk] = __builtin_bit_cast(bf16x8, pu);
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ld_bf16x8(vs + swz_v(32 * (i & 3) + ln, 2 * (i >> 2) + g)), pb[i >> 2], o[i & 3], 0, 0, 0);
+      __syncthreads();
+    }
+  }
+  if (qi < N) {
+    float* so = st_o + (bh * (size_t)N + qi) * HD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(float4*)(so + 32 * db + 8 * r4 + 4 * g) =
+            make_float4(o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]);
+    const float l_tot = l_run + other_half(l_run);
+    if (g == 0) *(float2*)(st_ml + (bh * (size_t)N + qi) * 2) = make_float2(m_run, l_tot);
+  }
+}
+
 // ------------------------------------------------------------------ host ---
 struct Geometry {
   int64_t B, H, N, nb, nsb, k;
@@ -973,10 +1369,11 @@ struct Geometry {
   bool reweight;
   int anchor_rows;
   double scale;
+  int E;  // extra tokens per query block
 };
 
 struct WsLayout {
-  size_t vt, svt, apart, anchor, total;
+  size_t vt, svt, apart, anchor, sto, stml, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -993,6 +1390,8 @@ int make_geometry(const bsa_problem* p, Geometry* g) {
     return BSA_ERR_INVALID;
   if (p->select_mode != BSA_SELECT_TOPK && p->select_mode != BSA_SELECT_THRESHOLD) return BSA_ERR_INVALID;
   if (!isfinite(p->select_tau)) return BSA_ERR_INVALID;
+  if (p->extra_tokens < 0 || p->extra_tokens > BSA_MAX_EXTRA) return BSA_ERR_INVALID;
+  g->E = p->extra_tokens;
   g->threshold = p->select_mode == BSA_SELECT_THRESHOLD;
   g->tau = (double)p->select_tau;
   g->B = p->batch;
@@ -1032,6 +1431,13 @@ WsLayout ws_layout(const Geometry& g) {
     w.anchor = off;
     off = align256(off + bh * HD * sizeof(double));
   }
+  if (g.E > 0) {
+    // softmax state of every query row over its extra tokens
+    w.sto = off;
+    off = align256(off + bh * g.N * HD * sizeof(float));
+    w.stml = off;
+    off = align256(off + bh * g.N * 2 * sizeof(float));
+  }
   w.total = off;
   return w;
 }
@@ -1053,6 +1459,32 @@ int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, i
   }
   hipLaunchKernelGGL((select_kernel<NKT, RB, ROWSPLIT>), grid, dim3(256), lds, stream, q_pool, k_pool, block_idx,
                      (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1, g.threshold ? 1 : 0, g.tau);
+  return launch_status();
+}
+
+int check_forward(const Geometry& g, const void* q, const void* k, const void* sum_k,
+                  const float* sum_bias, const int32_t* block_idx, const void* workspace,
+                  size_t workspace_bytes, const void* out) {
+  if (!q || !k || !out) return BSA_ERR_INVALID;
+  if (g.k > 0 && !block_idx) return BSA_ERR_INVALID;
+  if (g.k < g.nb && (!sum_k || !sum_bias)) return BSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(out) || (sum_k && !aligned16(sum_k)))
+    return BSA_ERR_INVALID;
+  if (!workspace || workspace_bytes < ws_layout(g).total || ((uintptr_t)workspace & 255u))
+    return BSA_ERR_WORKSPACE;
+  return BSA_OK;
+}
+
+int launch_attention(const Geometry& g, const void* q, const void* k, const void* sum_k,
+                     const float* sum_bias, const int32_t* block_idx, const char* ws, const float* st_o,
+                     const float* st_ml, void* out, hipStream_t stream) {
+  const WsLayout w = ws_layout(g);
+  const int total = (int)(g.B * g.H * g.nb);
+  const float scale_log2 = (float)(g.scale * 1.4426950408889634);
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, stream, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)(ws + w.vt), (const uint16_t*)sum_k,
+                     (const uint16_t*)(ws + w.svt), sum_bias, block_idx, st_o, st_ml, (uint16_t*)out,
+                     (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, (int)g.f0, (int)g.f1);
   return launch_status();
 }
 
@@ -1154,22 +1586,50 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
   Geometry g;
   int st = make_geometry(p, &g);
   if (st != BSA_OK) return st;
-  if (!q || !k || !out) return BSA_ERR_INVALID;
-  if (g.k > 0 && !block_idx) return BSA_ERR_INVALID;
-  if (g.k < g.nb && (!sum_k || !sum_bias)) return BSA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(out) || (sum_k && !aligned16(sum_k)))
-    return BSA_ERR_INVALID;
-  const WsLayout w = ws_layout(g);
-  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return BSA_ERR_WORKSPACE;
-  const char* ws = (const char*)workspace;
-  const int total = (int)(g.B * g.H * g.nb);
-  const float scale_log2 = (float)(g.scale * 1.4426950408889634);
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, (hipStream_t)hip_stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)(ws + w.vt),
-                     (const uint16_t*)sum_k, (const uint16_t*)(ws + w.svt), sum_bias, block_idx,
-                     (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total,
-                     (int)g.f0, (int)g.f1);
+  if (g.E > 0) return BSA_ERR_INVALID;  // extra tokens go through bsa_forward_tokens
+  if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
+    return st;
+  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, (const char*)workspace, nullptr, nullptr,
+                          out, (hipStream_t)hip_stream);
+}
+
+int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
+                      const int32_t* block_idx, int32_t* token_idx, void* hip_stream) {
+  Geometry g;
+  const int st = make_geometry(p, &g);
+  if (st != BSA_OK) return st;
+  if (g.E == 0) return BSA_OK;
+  if (!q_pool || !k || !token_idx || (g.k > 0 && !block_idx)) return BSA_ERR_INVALID;
+  if (!aligned16(q_pool) || !aligned16(k)) return BSA_ERR_INVALID;
+  const int total = (int)(((g.nb + TS_ROWS - 1) / TS_ROWS) * g.H * g.B);
+  hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)total), dim3(256), 0, (hipStream_t)hip_stream,
+                     q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx, (int)g.N,
+                     (int)g.nb, (int)g.k, g.E, (int)g.f0, (int)g.f1, total);
   return launch_status();
+}
+
+int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
+                       const void* sum_k, const float* sum_bias, const int32_t* block_idx,
+                       const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
+                       void* hip_stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st != BSA_OK) return st;
+  if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
+    return st;
+  hipStream_t s = (hipStream_t)hip_stream;
+  char* ws = (char*)workspace;
+  if (g.E == 0)
+    return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, out, s);
+  if (!v || !token_idx || !aligned16(v)) return BSA_ERR_INVALID;
+  const WsLayout w = ws_layout(g);
+  const float scale_log2 = (float)(g.scale * 1.4426950408889634);
+  hipLaunchKernelGGL(extra_attn_kernel, dim3((unsigned)g.nb, (unsigned)g.H, (unsigned)g.B), dim3(256), 0, s,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, token_idx,
+                     (float*)(ws + w.sto), (float*)(ws + w.stml), (int)g.N, (int)g.nb, g.E, scale_log2);
+  if ((st = launch_status()) != BSA_OK) return st;
+  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, (const float*)(ws + w.sto),
+                          (const float*)(ws + w.stml), out, s);
 }
 
 }  // extern "C"

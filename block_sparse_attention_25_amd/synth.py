@@ -51,6 +51,7 @@ class Workload:
     seed: int = 0
     sinks: bool = False    # route the conditioning rows as sinks
     tau: float | None = None  # threshold selection (top_k is then the cap)
+    extra: int = 0         # extra tokens per query block
 
     @property
     def sink_start(self) -> int:
@@ -81,6 +82,8 @@ WORKLOADS = {
     "768p_5s_sinks": Workload("768p_5s_sinks", 1, 56, (9, 48, 84), 36288, 1452, 64, sinks=True),
     # the 768p 5s shape with threshold selection at tau 1.0, uncapped
     "768p_5s_tau1": Workload("768p_5s_tau1", 1, 56, (9, 48, 84), 36288, 1452, 295, tau=1.0),
+    # the 768p 5s shape with 256 extra tokens per query block (the node's default)
+    "768p_5s_extra256": Workload("768p_5s_extra256", 1, 56, (9, 48, 84), 36288, 1452, 64, extra=256),
 }
 
 

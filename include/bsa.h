@@ -44,6 +44,8 @@ extern "C" {
 #define BSA_HEAD_DIM 128
 /* largest supported number of blocks per sequence (N <= 262144 tokens) */
 #define BSA_MAX_BLOCKS 2048
+/* largest supported number of extra tokens per query block */
+#define BSA_MAX_EXTRA 256
 
 enum {
   BSA_OK = 0,
@@ -90,6 +92,16 @@ typedef struct bsa_problem {
    * the normal tail beyond tau standard deviations). */
   int32_t select_mode;
   float select_tau;    /* threshold mode only; finite */
+  /* Extra tokens, in [0, BSA_MAX_EXTRA]: besides its kept blocks, each query
+   * block attends exactly to the extra_tokens tokens of the blocks it skipped
+   * whose keys score highest against its pooled query (q_pool[r] . k_j);
+   * those blocks keep their summary rows.  0 turns the option off.  Used by
+   * bsa_select_tokens and bsa_forward_tokens; bsa_forward rejects a problem
+   * with extra tokens.  Source: "H3 Sparse Attention" (WAS Node Suite node
+   * page), section "The inputs that matter" (extra_tokens, the top-scoring
+   * tokens each query block reads beyond its chosen blocks; 256 by default,
+   * 0 fastest). */
+  int32_t extra_tokens;
 } bsa_problem;
 
 enum { BSA_SELECT_TOPK = 0, BSA_SELECT_THRESHOLD = 1 };
@@ -105,7 +117,9 @@ int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff);
  * to *bytes.  The workspace holds, for every (b, h): V of each key block
  * transposed (feature-major, key order interleaved for the matrix cores, zero
  * past the end of a short block), the summary values transposed in groups of
- * 128 blocks, and in reweight mode the anchor and its per-block partial sums.
+ * 128 blocks, in reweight mode the anchor and its per-block partial sums, and
+ * with extra tokens the softmax state of every query row over its extra
+ * tokens (130 floats per row, written by bsa_forward_tokens).
  * Its contents are private to this library; it must be 256-byte aligned.
  */
 int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes);
@@ -178,10 +192,61 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
  * float32 accumulation and one final bf16 rounding.  V and the summary values
  * are read from the workspace.  A query block that is a conditioning sink
  * block attends to every key block exactly and ignores its block_idx row.
+ * A problem with extra tokens is rejected (BSA_ERR_INVALID): use
+ * bsa_forward_tokens.
  */
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
                 const float* sum_bias, const int32_t* block_idx, const void* workspace,
                 size_t workspace_bytes, void* out, void* hip_stream);
+
+/*
+ * Extra tokens, selection.
+ * Source: "H3 Sparse Attention" (WAS Node Suite node page), section "The
+ * inputs that matter" (extra_tokens: the top-scoring tokens each query block
+ * reads beyond its chosen blocks).
+ *
+ *   q_pool     in   fp32 [B, H, nb, 128] (from bsa_pool)
+ *   k          in   bf16 [B, H, N, 128]
+ *   block_idx  in   int32 [B, H, nb, k] (from bsa_select; may be NULL iff k == 0)
+ *   token_idx  out  int32 [B, H, nb, E], E = p->extra_tokens
+ *
+ * Candidates of query block r: every token j of the blocks not in
+ * block_idx[r].  Score: q_pool[r] . k_j, with q_pool[r] split exactly into
+ * three bfloat16 terms so that every product is exact and the sums are
+ * float32.  Row r of token_idx holds the E candidates of largest score,
+ * equal scores going to the lower token, in strictly ascending order, then
+ * -1 in the unused slots (fewer than E candidates).  A conditioning sink
+ * query block has no candidates (its row is all -1).  Returns BSA_OK and
+ * does nothing when E == 0 (token_idx may then be NULL).
+ */
+int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
+                      const int32_t* block_idx, int32_t* token_idx, void* hip_stream);
+
+/*
+ * Stages 3 and 4 with extra tokens: bsa_forward's result where the logits of
+ * query i of block r also hold scale * q_i . k_j for every token j of
+ * token_idx[r] (value v_j), all in one softmax.
+ * Sources: as for bsa_forward and bsa_select_tokens.
+ *
+ *   q, k, v    in   bf16 [B, H, N, 128]
+ *   sum_k, sum_bias, block_idx   in   as for bsa_forward
+ *   token_idx  in   int32 [B, H, nb, E], E = p->extra_tokens (may be NULL iff
+ *                   E == 0): tokens in [0, N), distinct, none in a block of
+ *                   block_idx[r], valid entries first, then -1 padding; the
+ *                   kernels trust this (bsa_select_tokens' output)
+ *   workspace  in/out  as filled by bsa_pool for the same q, k, v and
+ *                   problem; this call also writes its extra-token state
+ *   out        out  bf16 [B, H, N, 128]
+ *
+ * The extra tokens' part of each row's softmax (unnormalised output, max and
+ * sum) is computed first and left in the workspace; the attention kernel then
+ * starts each row from it.  With E == 0 this is bsa_forward (v and
+ * token_idx unused).
+ */
+int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
+                       const void* sum_k, const float* sum_bias, const int32_t* block_idx,
+                       const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
+                       void* hip_stream);
 
 #ifdef __cplusplus
 }

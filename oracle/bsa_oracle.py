@@ -189,10 +189,12 @@ def select_threshold(scores: np.ndarray, tau: float, top_k: int, forced=()) -> n
     return idx
 
 
-def select_extra_tokens(q_pool, k, idx, extra: int, block: int = BLOCK, dense_blocks=()):
+def select_extra_tokens(q_pool, k, idx, extra: int, block: int = BLOCK, dense_blocks=(),
+                        query_blocks=None):
     """Extra tokens (R15): for each query block r, the `extra` tokens of the
     blocks not in idx[r] with the largest q_pool[r] . k_j (float64), ties to
-    the lower token index; ascending, padded with -1.  int32 [nb, extra]."""
+    the lower token index; ascending, padded with -1.  int32 [nb, extra].
+    query_blocks restricts the work to those rows (the others stay -1)."""
     qp = np.asarray(q_pool, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     rows = block_rows(k.shape[0], block)
@@ -201,9 +203,12 @@ def select_extra_tokens(q_pool, k, idx, extra: int, block: int = BLOCK, dense_bl
     for r in range(nb):
         if r in set(dense_blocks) or extra == 0:
             continue
+        if query_blocks is not None and r not in query_blocks:
+            continue
         chosen = set(int(c) for c in idx[r] if c >= 0)
         cand = [j for c in range(nb) if c not in chosen for j in range(rows[c][0], rows[c][1])]
-        s = np.array([float(np.dot(qp[r], k[j])) for j in cand])
+        # the float64 dot products of every candidate key with the pooled query
+        s = k[cand] @ qp[r] if cand else np.zeros(0)
         order = sorted(range(len(cand)), key=lambda i: (-s[i], cand[i]))[:extra]
         kept = sorted(cand[i] for i in order)
         out[r, :len(kept)] = kept
@@ -290,11 +295,11 @@ def attention(q, k, v, idx, sum_k, sum_v, bias, scale: float, block: int = BLOCK
     "What Spark-Attn changes" (exact and compressed branches of one pass).
 
     idx may be any [nb, k] array of distinct valid block indices per row (the
-    output is unique given idx); entries of -1 are padding and ignored.  Query blocks listed in dense_blocks attend to
-    every key block exactly, whatever idx holds for them (R13).  extra [nb, E]
-    lists tokens each query block also reads exactly (R15; -1 is padding).
-    query_blocks
-    restricts the work to those query blocks (other output rows stay zero).
+    output is unique given idx); entries of -1 are padding and ignored.  Query
+    blocks listed in dense_blocks attend to every key block exactly, whatever
+    idx holds for them (R13).  extra [nb, E] lists tokens each query block
+    also reads exactly (R15; -1 is padding).  query_blocks restricts the work
+    to those query blocks (other output rows stay zero).
     Returns float64 [N, d]."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)

@@ -106,6 +106,25 @@ def check_idx_row_threshold(gpu_row, scores_row, want_row, forced, tau):
     return True, True
 
 
+def check_tokens_row(gpu_row, cand, cand_scores, E):
+    """An extra-token row: the E candidate tokens of largest float64 score
+    (ties to the lower token), ascending, then -1 padding when there are fewer
+    than E candidates; equal to the oracle's choice except inside the tie zone
+    at the E-th score (the GPU ranks float32 sums of exact products).
+    cand lists the candidate tokens ascending, cand_scores their scores.
+    Returns (ok, in_tie_zone)."""
+    g = [int(x) for x in gpu_row]
+    n = min(E, len(cand))
+    if len(g) != E or any(x != -1 for x in g[n:]):
+        return False, False
+    pos = {t: i for i, t in enumerate(cand)}
+    if any(t not in pos for t in g[:n]):
+        return False, False
+    if n == 0:
+        return True, False
+    return check_idx_row([pos[t] for t in g[:n]], np.asarray(cand_scores, dtype=np.float64), n)
+
+
 def check_output(gpu_out, ref_out):
     d = np.abs(np.asarray(gpu_out, dtype=np.float64) - ref_out)
     return float(d.max()), float(d.mean())

@@ -21,7 +21,7 @@ def test_library_exports_every_declared_symbol():
     L = bsa.lib()
     names = _declared_functions()
     assert {"bsa_pool", "bsa_select", "bsa_forward", "bsa_workspace_bytes",
-            "bsa_status_str"} <= set(names)
+            "bsa_status_str", "bsa_select_tokens", "bsa_forward_tokens"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -55,13 +55,13 @@ def test_blocks_and_workspace():
 
 def test_struct_layout_matches_header():
     """The ctypes mirror has the header's fields, in order, with the
-    header's size (13 four-byte fields)."""
+    header's size (14 four-byte fields)."""
     text = open(os.path.join(ROOT, "include", "bsa.h")).read()
     body = text[text.index("typedef struct bsa_problem {"):text.index("} bsa_problem;")]
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     fields = re.findall(r"\b(?:int32_t|float)\s+(\w+);", body)
     assert fields == [f for f, _ in bsa.Problem._fields_]
-    assert ctypes.sizeof(bsa.Problem) == 4 * len(fields) == 52
+    assert ctypes.sizeof(bsa.Problem) == 4 * len(fields) == 56
 
 
 def test_sink_blocks_and_k():
@@ -98,6 +98,7 @@ def test_ratio_budget():
     ("top_k", -1, ValueError), ("summary", 7, ValueError), ("anchor_rows", 5000, ValueError),
     ("anchor_rows", -2, ValueError), ("scale", -1.0, ValueError), ("scale", float("inf"), ValueError),
     ("scale", float("nan"), ValueError), ("seq_len", 2049 * 128, NotImplementedError),
+    ("extra_tokens", -1, ValueError), ("extra_tokens", 257, ValueError),
 ])
 def test_invalid_problems_rejected_before_launch(field, value, err):
     p = _prob()
@@ -135,6 +136,34 @@ def test_null_pointers_and_small_workspace_rejected():
     # top_k = 0: select has nothing to do and needs no pointers
     p0 = _prob(top_k=0)
     assert L.bsa_select(ctypes.byref(p0), None, None, None, None) == bsa.BSA_OK
+
+
+def test_extra_token_entry_points_validate():
+    L = bsa.lib()
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    p = _prob()
+    pe = _prob(extra_tokens=256)
+    # no extra tokens: token selection has nothing to do
+    assert L.bsa_select_tokens(ctypes.byref(p), None, None, None, None, None) == bsa.BSA_OK
+    # with extra tokens: every tensor is needed (block_idx unless k == 0)
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, fake, None, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, None, fake, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_select_tokens(ctypes.byref(pe), None, fake, fake, fake, None) == bsa.BSA_ERR_INVALID
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, odd, fake, fake, None) == bsa.BSA_ERR_INVALID
+    # bsa_forward refuses a problem with extra tokens; bsa_forward_tokens needs v and token_idx
+    big = 1 << 40
+    assert L.bsa_forward(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, big, fake,
+                         None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, None, fake, fake, fake, fake, fake, big,
+                                fake, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, None, fake, big,
+                                fake, None) == bsa.BSA_ERR_INVALID
+    # the extra-token state enlarges the workspace: 130 floats per query row
+    n = bsa.bsa_workspace_bytes(pe) - bsa.bsa_workspace_bytes(p)
+    assert 2 * 4096 * 130 * 4 <= n <= 2 * 4096 * 130 * 4 + 512
+    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, fake, fake,
+                                bsa.bsa_workspace_bytes(p), fake, None) == bsa.BSA_ERR_WORKSPACE
 
 
 def test_binding_rejects_bad_tensors():

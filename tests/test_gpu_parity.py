@@ -17,7 +17,8 @@ import block_sparse_attention_25_amd as bsa
 from block_sparse_attention_25_amd.synth import WORKLOADS, custom, generate
 from oracle import bsa_oracle as O
 from tests.parity import (MAX_ABS, MEAN_ABS, check_idx_row, check_idx_row_forced,
-                          check_idx_row_threshold, check_output, tensor_bits, to_device, widen)
+                          check_idx_row_threshold, check_output, check_tokens_row, tensor_bits,
+                          to_device, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,12 +41,36 @@ def _run_gpu(torch, qb, kb, vb, **kw):
     out, aux = bsa.attention(q, k, v, return_aux=True, **kw)
     torch.cuda.synchronize()
     host = {n: aux[n].cpu() for n in ("q_pool", "k_pool", "sum_k", "sum_v", "sum_bias", "block_idx")}
+    host["token_idx"] = None if aux["token_idx"] is None else aux["token_idx"].cpu()
     host["out"] = out
     return host
 
 
+def _check_tokens(host, qp, K, gidx, b, h, E, rows, sinks, label):
+    """Extra-token rows of one (b, h) against the oracle's float64 ranking."""
+    gtok = host["token_idx"][b, h].numpy()
+    nb = gidx.shape[0]
+    assert gtok.shape == (nb, E)
+    want = O.select_extra_tokens(qp, K, gidx, E, dense_blocks=sinks, query_blocks=rows)
+    ties = 0
+    for r in rows:
+        if r in sinks:
+            assert np.all(gtok[r] == -1), "%s sink row %d has extra tokens" % (label, r)
+            continue
+        chosen = set(int(c) for c in gidx[r] if c >= 0)
+        cand = [j for c in range(nb) if c not in chosen
+                for j in range(c * 128, min(c * 128 + 128, K.shape[0]))]
+        sc = K[cand] @ qp[r] if cand else np.zeros(0)
+        ok, tie = check_tokens_row(gtok[r], cand, sc, E)
+        assert ok, "%s token row %d: gpu %s want %s" % (label, r, list(gtok[r][:8]), list(want[r][:8]))
+        if not tie:
+            assert np.array_equal(gtok[r], want[r]), "%s token row %d" % (label, r)
+        ties += tie
+    return gtok, ties
+
+
 def _check_head(host, qb, kb, vb, b, h, top_k, summary="mean", anchor_rows=0,
-                query_blocks=None, label="", sink_start=0, sink_rows=0, tau=None):
+                query_blocks=None, label="", sink_start=0, sink_rows=0, tau=None, extra=0):
     """Compare one (b, h) of a GPU run with the oracle; returns tie-zone rows."""
     Q, K, V = (widen(x[b, h]) for x in (qb, kb, vb))
     N = Q.shape[0]
@@ -86,9 +111,16 @@ def _check_head(host, qb, kb, vb, b, h, top_k, summary="mean", anchor_rows=0,
                 ok, tie = check_idx_row(gidx[r], s[r], k)
             assert ok, "%s idx row %d: gpu %s" % (label, r, list(gidx[r]))
             ties += tie
+    # extra tokens: the rows checked below, against the float64 ranking
+    gtok = None
+    if extra:
+        rows_t = list(range(nb)) if query_blocks is None else list(query_blocks)
+        gtok, tties = _check_tokens(host, qp, K, gidx if k > 0 else np.zeros((nb, 0), np.int32),
+                                    b, h, extra, rows_t, sinks, label)
+        ties += tties
     # stages 3+4: output with the GPU's (validated) selection
     ref = O.attention(Q, K, V, gidx if k > 0 else np.zeros((nb, 0), np.int32), sk, sv, bias, sc,
-                      query_blocks=query_blocks, dense_blocks=sinks)
+                      query_blocks=query_blocks, dense_blocks=sinks, extra=gtok)
     gout = widen(tensor_bits(host["out"][b, h].cpu()))
     if query_blocks is None:
         rows = np.arange(N)
@@ -366,9 +398,97 @@ def test_guard_bands_untouched(torch_cuda):
             assert bool(torch.isnan(guard.float()).all()), name
 
 
+# --------------------------------------------------------- extra tokens ---
+@pytest.mark.parametrize("N,top_k,E,sink,summary,tau", [
+    (4096, 8, 64, 0, "mean", None),      # the tiny shape
+    (4096, 8, 256, 64, "mean", None),    # with its conditioning rows as sinks
+    (1000, 3, 100, 0, "mean", None),     # E not a multiple of 64, short last block
+    (1000, 7, 256, 0, "mean", None),     # one skipped block: fewer candidates than E
+    (1000, 0, 200, 0, "mean", None),     # top_k 0: every token a candidate
+    (1000, 8, 50, 0, "mean", None),      # every block kept: no candidates
+    (2000, 5, 256, 0, "reweight", None),
+    (2000, 10, 128, 0, "mean", 0.5),     # threshold selection (rows keep different counts)
+    (300, 1, 1, 0, "mean", None),        # one extra token
+    (1, 0, 5, 0, "mean", None),          # one token, a candidate
+    (129, 1, 10, 0, "mean", None),       # two blocks, the second of one row
+    (9000, 16, 256, 0, "mean", None),    # several row groups of 32 query blocks
+])
+def test_extra_tokens(torch_cuda, N, top_k, E, sink, summary, tau):
+    _log("case extra tokens N=%d top_k=%d E=%d sink=%d %s tau=%s" % (N, top_k, E, sink, summary, tau))
+    w = custom(N, heads=2, seed=N + E + top_k)
+    qb, kb, vb = generate(w)
+    anchor = N // 2 if summary == "reweight" else 0
+    host = _run_gpu(torch_cuda, qb, kb, vb, top_k=top_k, summary=summary, anchor_rows=anchor,
+                    sink_rows=sink, tau=tau, extra_tokens=E)
+    for h in range(2):
+        _check_head(host, qb, kb, vb, 0, h, top_k, summary, anchor, label="extra%d-%d" % (N, E),
+                    sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau, extra=E)
+
+
+def test_extra_token_ties_take_lower_index(torch_cuda):
+    """300 copies of one strong key row in blocks 20..31 tie bit-exactly: where
+    the E-th place falls among the copies, the lowest copies must win."""
+    _log("case extra-token ties")
+    from block_sparse_attention_25_amd.synth import bf16_bits
+    N, E = 4096, 256
+    w = custom(N, heads=1, seed=23)
+    qb, kb, vb = generate(w)
+    K0 = widen(kb[0, 0])
+    qm = widen(qb[0, 0])[:128].mean(axis=0)
+    src = bf16_bits((3.0 * K0[128 + int(np.argmax(K0[128:256] @ qm))]).astype(np.float32))
+    rng = np.random.default_rng(1)
+    dst = np.sort(rng.choice(np.arange(20 * 128, 32 * 128), 300, replace=False))
+    kb = kb.copy()
+    kb[0, 0, dst] = src
+    host = _run_gpu(torch_cuda, qb, kb, vb, top_k=2, extra_tokens=E)
+    _check_head(host, qb, kb, vb, 0, 0, 2, label="extra-ties", extra=E)
+    Q, K = widen(qb[0, 0]), widen(kb[0, 0])
+    qp = O.pool_mean(Q)
+    gidx = host["block_idx"][0, 0].numpy()
+    gtok = host["token_idx"][0, 0].numpy()
+    want = O.select_extra_tokens(qp, K, gidx, E)
+    copies = set(int(t) for t in dst)
+    exact_rows = 0
+    for r in range(gidx.shape[0]):
+        chosen = set(int(c) for c in gidx[r])
+        cand = [j for c in range(32) if c not in chosen for j in range(c * 128, c * 128 + 128)]
+        sc = K[cand] @ qp[r]
+        order = sorted(range(len(cand)), key=lambda i: (-sc[i], cand[i]))
+        if len(cand) > E and cand[order[E - 1]] in copies and cand[order[E]] in copies:
+            assert np.array_equal(gtok[r], want[r]), "row %d" % r
+            exact_rows += 1
+    _log("  rows whose E-th place falls among the copies: %d" % exact_rows)
+    assert exact_rows > 0
+
+
+def test_forward_tokens_matches_forward_without_tokens(torch_cuda):
+    """bsa_forward_tokens with every token row empty (-1) gives bsa_forward's
+    output bit for bit: the empty softmax state is the plain start."""
+    torch = torch_cuda
+    _log("case forward_tokens with empty rows")
+    N, H = 3000, 2
+    w = custom(N, heads=H, seed=41)
+    qb, kb, vb = generate(w)
+    q, k, v = (to_device(x) for x in (qb, kb, vb))
+    out, aux = bsa.attention(q, k, v, top_k=5, return_aux=True)
+    pe = bsa.make_problem(1, H, N, 5, extra_tokens=64)
+    ws = torch.empty(bsa.bsa_workspace_bytes(pe), dtype=torch.uint8, device="cuda")
+    nb = O.n_blocks(N)
+    q_pool = torch.empty((1, H, nb, 128), dtype=torch.float32, device="cuda")
+    k_pool, sum_bias = torch.empty_like(q_pool), torch.empty((1, H, nb), dtype=torch.float32, device="cuda")
+    sum_k = torch.empty((1, H, nb, 128), dtype=torch.bfloat16, device="cuda")
+    sum_v = torch.empty_like(sum_k)
+    bsa.bsa_pool(pe, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws)
+    tok = torch.full((1, H, nb, 64), -1, dtype=torch.int32, device="cuda")
+    out2 = torch.empty_like(q)
+    bsa.bsa_forward_tokens(pe, q, k, v, sum_k, sum_bias, aux["block_idx"], tok, ws, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
 # ---------------------------------------------------------- full sizes ---
 FULL = [("768p_5s", [0, 37]), ("768p_10s", [5]), ("2k_5s", [55]), ("768p_15s_reweight", [0, 21]),
-        ("768p_5s_sinks", [9]), ("768p_5s_tau1", [17])]
+        ("768p_5s_sinks", [9]), ("768p_5s_tau1", [17]), ("768p_5s_extra256", [3, 50])]
 
 
 @pytest.mark.parametrize("name,heads", FULL)
@@ -382,7 +502,7 @@ def test_full_size_workloads_sampled(torch_cuda, name, heads):
     nb = O.n_blocks(w.seq_len)
     top_k = w.top_k if w.top_k is not None else O.k_from_ratio(w.top_k_ratio, nb)
     kw = dict(top_k=top_k, summary=w.summary, sink_start=w.sink_start, sink_rows=w.sink_rows,
-              tau=w.tau)
+              tau=w.tau, extra_tokens=w.extra)
     if w.summary == "reweight":
         kw["anchor_rows"] = w.anchor_rows
     host = _run_gpu(torch_cuda, qb, kb, vb, **kw)
@@ -403,4 +523,4 @@ def test_full_size_workloads_sampled(torch_cuda, name, heads):
     for h in heads:
         _check_head(host, qb, kb, vb, 0, h, top_k, w.summary, w.anchor_rows if w.summary ==
                     "reweight" else 0, query_blocks=qbs, label=name, sink_start=w.sink_start,
-                    sink_rows=w.sink_rows, tau=w.tau)
+                    sink_rows=w.sink_rows, tau=w.tau, extra=w.extra)
