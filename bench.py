@@ -276,7 +276,7 @@ def main():
         "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
         "select_gbs": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma",
-                     "kernel": "attn_fwd_kernel" if tok is None else "extra_attn_kernel + attn_fwd_kernel",
+                     "kernel": "attn_fwd_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name),

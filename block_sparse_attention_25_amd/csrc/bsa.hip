@@ -613,9 +613,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ sum_k,
     const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
-    const int32_t* __restrict__ block_idx, const float* __restrict__ st_o,
-    const float* __restrict__ st_ml, uint16_t* __restrict__ out, int N, int nb, int krow, int nsb,
-    float scale_log2, int total_wg, int f0, int f1) {
+    const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ tok_idx, uint16_t* __restrict__ out, int N, int nb, int krow, int nsb,
+    float scale_log2, int total_wg, int f0, int f1, int E) {
   // LDS buffers as distinct variables, so the compiler can tell the DMA
   // targets from the buffers being read
   __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
@@ -776,25 +776,85 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  if (st_o && qi < N) {
-    // start from the softmax state of the extra tokens (O unnormalised, max
-    // and sum in base-2 units; the sum counts once, in the lower half)
-    const float* so = st_o + (bh * (size_t)N + qi) * HD;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 t = *(const float4*)(so + 32 * db + 8 * r4 + 4 * g);
-        o[db][4 * r4 + 0] = t.x;
-        o[db][4 * r4 + 1] = t.y;
-        o[db][4 * r4 + 2] = t.z;
-        o[db][4 * r4 + 3] = t.w;
-      }
-    const float2 ml = *(const float2*)(st_ml + (bh * (size_t)N + qi) * 2);
-    m_run = ml.x;
-    l_run = g == 0 ? ml.y : 0.f;
-  }
   f32x16 sA[2], sB[2];
+  if (E > 0 && !dense_row) {
+    // Extra tokens first, 64 at a time: their K rows gathered into ks0 (this
+    // kernel's K layout) and their V rows transposed into vs0 (its V^T
+    // layout), then S^T = K Q^T, a softmax update with the exact max and
+    // O^T += V^T P^T.  The state (o, m_run, l_run) carries into the online
+    // softmax of the main loop.  ks1 holds the row's token list until the
+    // main loop's first loads.
+    int* tok = (int*)ks1;
+    const int t_in = tid < E ? tok_idx[(bh * nb + r) * (size_t)E + tid] : -1;
+    tok[tid] = t_in;
+    const int nval = __syncthreads_count(t_in >= 0);  // valid tokens come first
+    const uint16_t* kb = k + bh * (size_t)N * HD;
+    const uint16_t* vb = v + bh * (size_t)N * HD;
+    for (int base = 0; base < nval; base += HT) {
+      // 16-byte chunk x = tid + 256 j is chunk x % 16 of gathered row x / 16
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = tid + 256 * j, row = x >> 4, ch = x & 15;
+        const int t = base + row < nval ? tok[base + row] : -1;
+        uint4 kd = make_uint4(0u, 0u, 0u, 0u), vd = kd;
+        if (t >= 0) {
+          kd = *(const uint4*)(kb + (size_t)t * HD + 8 * ch);
+          vd = *(const uint4*)(vb + (size_t)t * HD + 8 * ch);
+        }
+        *(uint4*)(ks0 + swz_k(row, ch)) = kd;
+        const int pos = vt_pos(row);
+        const uint32_t w[4] = {vd.x, vd.y, vd.z, vd.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vs0[swz_v(8 * ch + e, pos >> 3) + (pos & 7)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+      __syncthreads();
+      // S^T: sA[mb] element ii is key base + 32 mb + 8 (ii / 4) + 4 g + ii % 4
+      sA[0] = f32x16{};
+      sA[1] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        sA[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ld_bf16x8(ks0 + swz_k(32 * (i & 1) + ln, 2 * (i >> 1) + g)), qf[i >> 1], sA[i & 1], 0, 0, 0);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          const int key = base + 32 * mb + 8 * (ii >> 2) + 4 * g + (ii & 3);
+          const float x = key < nval ? sA[mb][ii] * scale_log2 : -INFINITY;
+          sA[mb][ii] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, other_half(mx));
+      const float m_new = fmaxf(m_run, mx);  // finite: the group holds a token
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      // P slice kk (keys 16 kk .. 16 kk + 15) in the V^T key order
+      bf16x8 pb[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+        u16x8_t pu;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t pbits = f2bf(__builtin_amdgcn_exp2f(sA[kk >> 1][8 * (kk & 1) + e] - m_new));
+          pu[e] = pbits;
+          psum += bf2f(pbits);
+        }
+        pb[kk] = __builtin_bit_cast(bf16x8, pu);
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ld_bf16x8(vs0 + swz_v(32 * (i & 3) + ln, 2 * (i >> 2) + g)), pb[i >> 2], o[i & 3], 0, 0, 0);
+      __syncthreads();
+    }
+  }
 
   // ---------------------------------------------------------------------
   // S^T(t) = K Q^T : s[mb] holds keys 32mb + 8(i/4) + 4g + i%4 of the half
@@ -1409,125 +1469,6 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   }
 }
 
-// extra_attn_kernel: the attention of each query block to its extra tokens,
-// left as softmax state for the attention kernel to start from: O
-// (unnormalised, float32), and the max m and sum l of the probabilities
-// (base-2 units), per query row.  Both parts then share one online softmax.
-// One workgroup (4 wavefronts of 32 queries) per (b, h, query block); the
-// extra tokens are taken 64 at a time: their K rows gathered into LDS in the
-// attention kernel's K layout, their V rows gathered and transposed into its
-// V^T layout, then S^T = K Q^T, the softmax update and O^T += V^T P^T on the
-// matrix cores.  A query block without extra tokens (a sink query block, or
-// one with no candidates) gets the empty state: O = 0, m = -inf, l = 0.
-__global__ __launch_bounds__(256, 2) void extra_attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ token_idx, float* __restrict__ st_o, float* __restrict__ st_ml, int N,
-    int nb, int E, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks[HT * HD], vs[HD * HT];
-  __shared__ int tok[BSA_MAX_EXTRA];
-  const int r = blockIdx.x;
-  const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5, ln = lane & 31;
-
-  // the row's tokens: ascending, -1 padding after them
-  const int32_t t_in = tid < E ? token_idx[(bh * nb + r) * (size_t)E + tid] : -1;
-  tok[tid] = t_in;
-  const int nval = __syncthreads_count(t_in >= 0);
-
-  const int qi = r * BLK + 32 * wave + ln;
-  f32x16 o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  if (nval > 0) {
-    bf16x8 qf[8];
-    const uint16_t* qrow = q + (bh * (size_t)N + (size_t)min(qi, N - 1)) * HD;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      bf16x8 t = ld_bf16x8(qrow + 16 * kk + 8 * g);
-      if (qi >= N) t = bf16x8{};
-      qf[kk] = t;
-    }
-    const uint16_t* kb = k + bh * (size_t)N * HD;
-    const uint16_t* vb = v + bh * (size_t)N * HD;
-    for (int base = 0; base < nval; base += HT) {
-      // gather: 16-byte chunk x = tid + 256 j is chunk x % 16 of row x / 16
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int x = tid + 256 * j, row = x >> 4, ch = x & 15;
-        const int t = base + row < nval ? tok[base + row] : -1;
-        uint4 kd = make_uint4(0u, 0u, 0u, 0u), vd = kd;
-        if (t >= 0) {
-          kd = *(const uint4*)(kb + (size_t)t * HD + 8 * ch);
-          vd = *(const uint4*)(vb + (size_t)t * HD + 8 * ch);
-        }
-        *(uint4*)(ks + swz_k(row, ch)) = kd;
-        const int pos = vt_pos(row);
-        const uint32_t w[4] = {vd.x, vd.y, vd.z, vd.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vs[swz_v(8 * ch + e, pos >> 3) + (pos & 7)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-      }
-      __syncthreads();
-      // S^T: s[mb] element ii is key base + 32 mb + 8 (ii / 4) + 4 g + ii % 4
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ld_bf16x8(ks + swz_k(32 * (i & 1) + ln, 2 * (i >> 1) + g)), qf[i >> 1], s[i & 1], 0, 0, 0);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-          const int key = base + 32 * mb + 8 * (ii >> 2) + 4 * g + (ii & 3);
-          const float x = key < nval ? s[mb][ii] * scale_log2 : -INFINITY;
-          s[mb][ii] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m_run, mx);  // finite: the group holds a token
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      // P slice kk (keys 16 kk .. 16 kk + 15) in the V^T key order
-      bf16x8 pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        u16x8 pu;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint16_t pbits = f2bf(__builtin_amdgcn_exp2f(s[kk >> 1][8 * (kk & 1) + e] - m_new));
-          pu[e] = pbits;
-          psum += bf2f(pbits);
-        }
-        pb[kk] = __builtin_bit_cast(bf16x8, pu);
-      }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ld_bf16x8(vs + swz_v(32 * (i & 3) + ln, 2 * (i >> 2) + g)), pb[i >> 2], o[i & 3], 0, 0, 0);
-      __syncthreads();
-    }
-  }
-  if (qi < N) {
-    float* so = st_o + (bh * (size_t)N + qi) * HD;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *(float4*)(so + 32 * db + 8 * r4 + 4 * g) =
-            make_float4(o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]);
-    const float l_tot = l_run + other_half(l_run);
-    if (g == 0) *(float2*)(st_ml + (bh * (size_t)N + qi) * 2) = make_float2(m_run, l_tot);
-  }
-}
-
 // ------------------------------------------------------------------ host ---
 struct Geometry {
   int64_t B, H, N, nb, nsb, k;
@@ -1541,7 +1482,7 @@ struct Geometry {
 };
 
 struct WsLayout {
-  size_t vt, svt, apart, anchor, sto, stml, total;
+  size_t vt, svt, apart, anchor, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1599,13 +1540,6 @@ WsLayout ws_layout(const Geometry& g) {
     w.anchor = off;
     off = align256(off + bh * HD * sizeof(double));
   }
-  if (g.E > 0) {
-    // softmax state of every query row over its extra tokens
-    w.sto = off;
-    off = align256(off + bh * g.N * HD * sizeof(float));
-    w.stml = off;
-    off = align256(off + bh * g.N * 2 * sizeof(float));
-  }
   w.total = off;
   return w;
 }
@@ -1644,15 +1578,16 @@ int check_forward(const Geometry& g, const void* q, const void* k, const void* s
 }
 
 int launch_attention(const Geometry& g, const void* q, const void* k, const void* sum_k,
-                     const float* sum_bias, const int32_t* block_idx, const char* ws, const float* st_o,
-                     const float* st_ml, void* out, hipStream_t stream) {
+                     const float* sum_bias, const int32_t* block_idx, const char* ws, const void* v,
+                     const int32_t* tok_idx, void* out, hipStream_t stream) {
   const WsLayout w = ws_layout(g);
   const int total = (int)(g.B * g.H * g.nb);
   const float scale_log2 = (float)(g.scale * 1.4426950408889634);
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, stream, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)(ws + w.vt), (const uint16_t*)sum_k,
-                     (const uint16_t*)(ws + w.svt), sum_bias, block_idx, st_o, st_ml, (uint16_t*)out,
-                     (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, (int)g.f0, (int)g.f1);
+                     (const uint16_t*)(ws + w.svt), sum_bias, block_idx, (const uint16_t*)v, tok_idx,
+                     (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, (int)g.f0,
+                     (int)g.f1, tok_idx ? g.E : 0);
   return launch_status();
 }
 
@@ -1781,7 +1716,7 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
 
 int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
                        const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                       const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
+                       const int32_t* token_idx, const void* workspace, size_t workspace_bytes, void* out,
                        void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
@@ -1789,18 +1724,10 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
   if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
     return st;
   hipStream_t s = (hipStream_t)hip_stream;
-  char* ws = (char*)workspace;
-  if (g.E == 0)
-    return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, out, s);
+  const char* ws = (const char*)workspace;
+  if (g.E == 0) return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, out, s);
   if (!v || !token_idx || !aligned16(v)) return BSA_ERR_INVALID;
-  const WsLayout w = ws_layout(g);
-  const float scale_log2 = (float)(g.scale * 1.4426950408889634);
-  hipLaunchKernelGGL(extra_attn_kernel, dim3((unsigned)g.nb, (unsigned)g.H, (unsigned)g.B), dim3(256), 0, s,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, token_idx,
-                     (float*)(ws + w.sto), (float*)(ws + w.stml), (int)g.N, (int)g.nb, g.E, scale_log2);
-  if ((st = launch_status()) != BSA_OK) return st;
-  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, (const float*)(ws + w.sto),
-                          (const float*)(ws + w.stml), out, s);
+  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, v, token_idx, out, s);
 }
 
 }  // extern "C"

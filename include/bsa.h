@@ -117,9 +117,7 @@ int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff);
  * to *bytes.  The workspace holds, for every (b, h): V of each key block
  * transposed (feature-major, key order interleaved for the matrix cores, zero
  * past the end of a short block), the summary values transposed in groups of
- * 128 blocks, in reweight mode the anchor and its per-block partial sums, and
- * with extra tokens the softmax state of every query row over its extra
- * tokens (130 floats per row, written by bsa_forward_tokens).
+ * 128 blocks, and in reweight mode the anchor and its per-block partial sums.
  * Its contents are private to this library; it must be 256-byte aligned.
  */
 int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes);
@@ -234,19 +232,18 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
  *                   E == 0): tokens in [0, N), distinct, none in a block of
  *                   block_idx[r], valid entries first, then -1 padding; the
  *                   kernels trust this (bsa_select_tokens' output)
- *   workspace  in/out  as filled by bsa_pool for the same q, k, v and
- *                   problem; this call also writes its extra-token state
+ *   workspace  in   as filled by bsa_pool for the same q, k, v and problem
  *   out        out  bf16 [B, H, N, 128]
  *
- * The extra tokens' part of each row's softmax (unnormalised output, max and
- * sum) is computed first and left in the workspace; the attention kernel then
- * starts each row from it.  With E == 0 this is bsa_forward (v and
+ * The attention kernel takes each query block's extra tokens first (their K
+ * and V rows gathered on chip) and continues the same online softmax over
+ * its blocks and summary rows.  With E == 0 this is bsa_forward (v and
  * token_idx unused).
  */
 int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
                        const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                       const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
-                       void* hip_stream);
+                       const int32_t* token_idx, const void* workspace, size_t workspace_bytes,
+                       void* out, void* hip_stream);
 
 #ifdef __cplusplus
 }
