@@ -10,8 +10,13 @@
 //   select_kernel     float64 block scores and a wavefront top-k with
 //                     lowest-index ties, ascending output
 //   attn_fwd_kernel   fused gather attention: bf16 MFMA 32x32x16, K and V^T
-//                     tiles staged in LDS, one online softmax over the selected
-//                     blocks and the summary rows
+//                     tiles staged in LDS, one online softmax over the extra
+//                     tokens (if any), the selected blocks and the summary rows
+//   token_select_kernel  extra tokens: scores of every token of the skipped
+//                     blocks on the matrix cores, the E best per query block
+//
+// Sources of the extra tokens: "H3 Sparse Attention" (WAS Node Suite node
+// page), section "The inputs that matter".
 //
 // Sources: "h3-sparse-attn 0.1.0" (PyPI page), opening paragraph and "Use";
 // "Spark-H3: Block Sparse Attention Speeds Up MiniMax-H3 in ComfyUI",
