@@ -337,14 +337,20 @@ def test_exact_ties_take_lower_index(torch_cuda):
     _check_head(host, qb, kb, vb, 0, 0, 3, label="ties")
 
 
-def test_deterministic_repeats(torch_cuda):
-    _log("case determinism")
+@pytest.mark.parametrize("extra", [0, 256])
+def test_deterministic_repeats(torch_cuda, extra):
+    _log("case determinism, extra tokens %d" % extra)
     w = custom(3000, heads=2, seed=5)
     qb, kb, vb = generate(w)
-    a = _run_gpu(torch_cuda, qb, kb, vb, top_k=6, summary="reweight", anchor_rows=2500)
-    b = _run_gpu(torch_cuda, qb, kb, vb, top_k=6, summary="reweight", anchor_rows=2500)
+    a = _run_gpu(torch_cuda, qb, kb, vb, top_k=6, summary="reweight", anchor_rows=2500,
+                 extra_tokens=extra)
+    b = _run_gpu(torch_cuda, qb, kb, vb, top_k=6, summary="reweight", anchor_rows=2500,
+                 extra_tokens=extra)
     for n in a:
         x, y = a[n], b[n]
+        if x is None:
+            assert y is None, n
+            continue
         if hasattr(x, "is_cuda") and x.is_cuda:
             x, y = x.cpu(), y.cpu()
         assert torch_cuda.equal(x.view(torch_cuda.uint8) if x.dtype == torch_cuda.bfloat16 else x,
