@@ -1276,21 +1276,30 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   // own accumulator row and it is never inserted, so the loaded data needs no
   // zeroing (and a load needs no wait until the MFMAs that read it).
   const uint16_t* kb = k + bh * (size_t)N * HD;
-  // the 12 MFMAs of a tile chain into its accumulator (an MFMA reading the
-  // previous one's result as its accumulator issues back to back), small
-  // terms first; the two tiles are independent chains
+  // the 12 MFMAs of a tile chain into its accumulator, small terms first;
+  // the two tiles' chains alternate, so each MFMA's predecessor in its chain
+  // has finished by the time it issues
   auto mfma_tile = [&](const uint4* kt, f32x4* acc) {
+    acc[0] = f32x4{};
+    acc[1] = f32x4{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      acc[t] = f32x4{};
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, kt[4 * t + s]);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qs[2][s], acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qs[1][s], acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qs[0][s], acc[t], 0, 0, 0);
-      }
-    }
+      for (int term = 2; term >= 0; --term)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[4 * t + s]),
+                                                           qs[term][s], acc[t], 0, 0, 0);
+  };
+
+  // value of lane l ^ 16 and of lane l ^ 32 (VALU lane swaps)
+  auto lane_x16 = [&](int x) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)((lane & 16) ? r[0] : r[1]);
+  };
+  auto lane_x32 = [&](int x) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)((lane & 32) ? r[0] : r[1]);
   };
 
   // One sweep over order[i0, i1), lists cut to `keep`; with `count` set, the
@@ -1323,31 +1332,27 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       mfma_tile(kn, accn);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(i + 3, kl);
-      // keys of tile i: value v of tile t is token tb + 16 t + v
+      // keys of tile i: value v of tile t is token tb + 16 t + v.  A score's
+      // key reaches the threshold key exactly when the score reaches the
+      // float with that key (the key map is monotone; -0 counts as +0)
       const int c = order[min(i, i1 - 1)];
       const int tb = c * BLK + 32 * tq + 4 * q4;
       const bool live = i < i1 && ((skip[row][c >> 5] >> (c & 31)) & 1u);
+      const float thr_f = thr_reg == 0u ? -INFINITY
+                          : (thr_reg >> 31) ? __uint_as_float(thr_reg & 0x7FFFFFFFu)
+                                            : __uint_as_float(~thr_reg);
       uint32_t mask = 0u;
-      uint32_t k32[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int j = 4 * t + v;
-          k32[j] = order_key32(acc[t][v]);
-          if (live && tb + 16 * t + v < N && k32[j] >= thr_reg) mask |= 1u << j;
-        }
-      // the row's four lanes of this wavefront (q4 = 0..3): their counts and
-      // this lane's offset among them
+        for (int v = 0; v < 4; ++v)
+          if (live && tb + 16 * t + v < N && acc[t][v] >= thr_f) mask |= 1u << (4 * t + v);
+      // the row's four lanes of this wavefront (q4 = 0..3): their total and
+      // this lane's offset among them (lane swaps across 16 and 32)
       const int pc = __popc(mask);
-      int before = 0, quarter = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int o = __shfl(pc, l16 + 16 * q, 64);
-        before += q < q4 ? o : 0;
-        quarter += o;
-      }
-      if (q4 == 0) cw[par][tq][row] = quarter;
+      const int p16 = lane_x16(pc), pair = pc + p16, p32 = lane_x32(pair);
+      const int before = ((q4 & 1) ? p16 : 0) + ((q4 & 2) ? p32 : 0);
+      if (q4 == 0) cw[par][tq][row] = pair + p32;
       __syncthreads();
       // a list whose keys this step could overflow is cut first; a wavefront
       // cuts only its own rows (x = wave mod 8)
@@ -1378,7 +1383,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       for (int j = 0; j < 8; ++j) {
         if ((mask >> j) & 1u) {
           const uint32_t t = (uint32_t)(tb + 16 * (j >> 2) + (j & 3));
-          const uint64_t kv = ((uint64_t)k32[j] << 32) | (uint64_t)(0xFFFFFFFFu - t);
+          const uint64_t kv = ((uint64_t)order_key32(acc[j >> 2][j & 3]) << 32) | (uint64_t)(0xFFFFFFFFu - t);
           list[row][pos++] = kv;
           nc += kv >= tm_reg;
         }
