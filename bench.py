@@ -210,7 +210,7 @@ def main():
         bsa.bsa_select(p, q_pool, k_pool, idx)
         if e: e[2].record()
         if tok is not None:
-            bsa.bsa_select_tokens(p, q_pool, k, idx, tok)
+            bsa.bsa_select_tokens(p, q_pool, k, idx, tok, ws)
         if e: e[3].record()
         if tok is not None:
             bsa.bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx, tok, ws, out)

@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
         L.bsa_select.restype = ctypes.c_int
         L.bsa_forward.argtypes = [_P] + [_vp] * 6 + [ctypes.c_size_t, _vp, _vp]
         L.bsa_forward.restype = ctypes.c_int
-        L.bsa_select_tokens.argtypes = [_P] + [_vp] * 5
+        L.bsa_select_tokens.argtypes = [_P] + [_vp] * 5 + [ctypes.c_size_t, _vp]
         L.bsa_select_tokens.restype = ctypes.c_int
         L.bsa_forward_tokens.argtypes = [_P] + [_vp] * 8 + [ctypes.c_size_t, _vp, _vp]
         L.bsa_forward_tokens.restype = ctypes.c_int
@@ -146,9 +146,11 @@ def bsa_forward(p: Problem, q, k, sum_k, sum_bias, block_idx, workspace, out, st
                              _ptr(out), _stream(stream)), "bsa_forward")
 
 
-def bsa_select_tokens(p: Problem, q_pool, k, block_idx, token_idx, stream=None):
+def bsa_select_tokens(p: Problem, q_pool, k, block_idx, token_idx, workspace, stream=None):
     _raise(lib().bsa_select_tokens(ctypes.byref(p), _ptr(q_pool), _ptr(k), _ptr(block_idx),
-                                   _ptr(token_idx), _stream(stream)), "bsa_select_tokens")
+                                   _ptr(token_idx), _ptr(workspace),
+                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "bsa_select_tokens")
 
 
 def bsa_forward_tokens(p: Problem, q, k, v, sum_k, sum_bias, block_idx, token_idx, workspace, out,
@@ -247,7 +249,7 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     tok = None
     if p.extra_tokens > 0:
         tok = torch.empty((B, H, nb, p.extra_tokens), dtype=torch.int32, device=dev)
-        bsa_select_tokens(p, q_pool, k, idx if kk > 0 else None, tok, stream)
+        bsa_select_tokens(p, q_pool, k, idx if kk > 0 else None, tok, ws, stream)
         bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx if kk > 0 else None, tok, ws, out,
                            stream)
     else:

@@ -1074,24 +1074,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 //    largest keys and the threshold rises to the smallest kept one; every key
 //    dropped is below `keep` kept ones.
 //  - Two phases.  First the sample blocks (one in TS_STRIDE), keeping the m
-//    best: their m-th key T_m is a lower bound of the row's E-th key whenever
-//    at least E candidates reach T_m, and then it is a safe starting
-//    threshold for the other blocks, which keep the E best.  The kernel
-//    counts the candidates reaching T_m; a row with fewer than E of them
-//    (its sample was unrepresentative) is redone over every block from an
-//    empty list.  m = E/8 + 8 sqrt(E/8) sets T_m near the 2E- to 3E-th
-//    score (for E = 256 the fewest candidates reaching T_m measured on the
-//    768p inputs is 1.6 E), so a row inserts about 3E tokens instead of
-//    E (1 + ln(candidates / E)) and is cut about three times instead of ten.
-//  - A step's inserts need no atomics: each token quarter publishes its
-//    per-row counts, and after a barrier every lane derives its positions.
-//  - Each step handles one key block (32 tokens per wavefront).  At the end
-//    each list is cut to E and written in ascending token order (a token's
-//    slot is the number of kept tokens below it), -1 after.
+//    best of each row in its list: the m-th key T_m is a lower bound of the
+//    row's E-th key whenever at least E candidates reach T_m.  Then the
+//    other blocks with the threshold fixed at T_m: each wavefront appends
+//    the keys reaching it to its own workspace segment per (query block,
+//    token quarter), with no lists, atomics or barriers, and a merge takes
+//    the E best of a row's phase-1 keys and segments.  A row with fewer than
+//    E keys reaching T_m (an unrepresentative sample) or with an overflowing
+//    segment is redone from an empty list over every block by the
+//    list-and-cut sweep.  m = E/8 + 8 sqrt(E/8) sets T_m near the 2E- to
+//    3E-th score (for E = 256 the fewest candidates reaching T_m measured on
+//    the 768p inputs is 1.6 E, the most 5 E).  Small E (< 64) runs the
+//    list-and-cut sweep over every block directly.
+//  - In the list-and-cut sweep each step handles one key block (32 tokens
+//    per wavefront); inserts need no atomics: each token quarter publishes
+//    its per-row counts, and after a barrier every lane derives positions.
+//  - At the end each list is cut to E and written in ascending token order
+//    (a token's slot is the number of kept tokens below it), -1 after.
 
 constexpr int TS_ROWS = 32;    // query blocks per workgroup
 constexpr int TS_CAP = 512;    // candidate keys per query block
 constexpr int TS_STRIDE = 8;   // blocks c with c % TS_STRIDE == 3 form the sample
+constexpr int SEG_CAP = 512;   // workspace keys per (query block, token quarter) in phase 2
 
 __device__ __forceinline__ uint32_t order_key32(float s) {
   if (s == 0.f) s = 0.f;  // -0 ties with +0
@@ -1099,24 +1103,18 @@ __device__ __forceinline__ uint32_t order_key32(float s) {
   return (u >> 31) ? ~u : (u | 0x80000000u);
 }
 
-// Cuts a candidate list (n distinct keys, each with a nonzero upper half;
-// keep <= n <= TS_CAP) to its `keep` largest keys, keeping their order, and
-// returns the smallest kept key.  One wavefront.  An MSB-first bitwise search
-// on the upper halves (the score keys) stops as soon as exactly `keep` keys
-// reach the candidate; only when several keys share the upper half at the
-// boundary does a second search order those by their lower halves.
-__device__ uint64_t cut_list(uint64_t* list, int n, int keep, int lane) {
-  constexpr int PER = TS_CAP / 64;
-  uint32_t hi[PER], lo[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int x = lane + 64 * j;
-    const uint64_t kv = x < n ? list[x] : 0ull;
-    hi[j] = (uint32_t)(kv >> 32);
-    lo[j] = (uint32_t)kv;
-  }
-  uint32_t T = 0u;
-  bool exact = false;
+// The `keep` largest of the distinct keys (hi, lo) a wavefront holds, PER
+// per lane (empty slots hi = 0, real keys have hi != 0; keep <= number of
+// real keys): kept are those with hi > T, or hi == T and (exact or lo >= L).
+// An MSB-first bitwise search on the upper halves (the score keys) stops as
+// soon as exactly `keep` keys reach the candidate; only when several keys
+// share the upper half at the boundary does a second search order those by
+// their lower halves (larger = lower token).
+template <int PER>
+__device__ void top_keys(const uint32_t (&hi)[PER], const uint32_t (&lo)[PER], int keep, uint32_t& T,
+                         uint32_t& L, bool& exact) {
+  T = 0u;
+  exact = false;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
@@ -1130,7 +1128,7 @@ __device__ uint64_t cut_list(uint64_t* list, int n, int keep, int lane) {
       }
     }
   }
-  uint32_t L = 0u;  // boundary keys (upper half T): keep those with lower half >= L
+  L = 0u;
   if (!exact) {
     int gt = 0;
 #pragma unroll
@@ -1147,6 +1145,13 @@ __device__ uint64_t cut_list(uint64_t* list, int n, int keep, int lane) {
       }
     }
   }
+}
+
+// Writes the kept keys to list[0, keep) in (slot, lane) order and returns
+// the smallest kept key.
+template <int PER>
+__device__ uint64_t write_kept(uint64_t* list, const uint32_t (&hi)[PER], const uint32_t (&lo)[PER],
+                               uint32_t T, uint32_t L, bool exact, int lane) {
   const uint64_t lt = (1ull << lane) - 1ull;
   int before = 0;
   uint64_t kmin = ~0ull;
@@ -1169,6 +1174,25 @@ __device__ uint64_t cut_list(uint64_t* list, int n, int keep, int lane) {
   return kmin;
 }
 
+// Cuts a candidate list (n distinct keys, each with a nonzero upper half;
+// keep <= n <= TS_CAP) to its `keep` largest keys and returns the smallest
+// kept key.  One wavefront.
+__device__ uint64_t cut_list(uint64_t* list, int n, int keep, int lane) {
+  constexpr int PER = TS_CAP / 64;
+  uint32_t hi[PER], lo[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int x = lane + 64 * j;
+    const uint64_t kv = x < n ? list[x] : 0ull;
+    hi[j] = (uint32_t)(kv >> 32);
+    lo[j] = (uint32_t)kv;
+  }
+  uint32_t T, L;
+  bool exact;
+  top_keys<PER>(hi, lo, keep, T, L, exact);
+  return write_kept<PER>(list, hi, lo, T, L, exact, lane);
+}
+
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1181,8 +1205,8 @@ constexpr int TS_THREADS = 512;
 
 __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     const float* __restrict__ q_pool, const uint16_t* __restrict__ k,
-    const int32_t* __restrict__ block_idx, int32_t* __restrict__ token_idx, int N, int nb, int krow,
-    int E, int m, int f0, int f1, int total_wg) {
+    const int32_t* __restrict__ block_idx, int32_t* __restrict__ token_idx,
+    uint64_t* __restrict__ gseg, int N, int nb, int krow, int E, int m, int f0, int f1, int total_wg) {
   // row strides padded by one element, so that lanes of different rows at
   // equal positions fall into different LDS banks
   __shared__ uint64_t list[TS_ROWS][TS_CAP + 1];
@@ -1194,7 +1218,8 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   // other, so no wavefront overwrites a value another still reads
   __shared__ int cnt[2][TS_ROWS];
   __shared__ int cw[2][4][TS_ROWS];
-  __shared__ int nge[TS_ROWS];
+  __shared__ int nge[TS_ROWS];        // rows to redo (phase 2 could not decide them)
+  __shared__ int segcnt[4][TS_ROWS];  // keys per workspace segment, -1 when it overflowed
   __shared__ uint32_t thr[TS_ROWS];
   __shared__ int redo;
 
@@ -1302,10 +1327,9 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     return (int)((lane & 32) ? r[0] : r[1]);
   };
 
-  // One sweep over order[i0, i1), lists cut to `keep`; with `count` set, the
-  // inserted keys >= T_m of each row are counted.  List sizes start and end
-  // in cnt[0] (a sweep runs a multiple of 4 steps).
-  auto sweep = [&](int i0, int i1, int keep, bool count) {
+  // One sweep over order[i0, i1) with lists cut to `keep`.  List sizes start
+  // and end in cnt[0] (a sweep runs a multiple of 4 steps).
+  auto sweep = [&](int i0, int i1, int keep) {
     auto load_tile = [&](int i, uint4* kt) {
       const int tb = (int)order[min(i, i1 - 1)] * BLK + 32 * tq + l16;
 #pragma unroll
@@ -1316,8 +1340,6 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       }
     };
     uint32_t thr_reg = thr[row];
-    const uint64_t tm_reg = tm[row];
-    int nc = 0;  // this lane's inserted keys >= T_m
     // Step i (software pipeline): the MFMAs of tile i+1 and the loads of tile
     // i+3 go out first; the keys of tile i (scored by the previous step) are
     // filtered by the row threshold and each token quarter publishes how many
@@ -1383,9 +1405,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       for (int j = 0; j < 8; ++j) {
         if ((mask >> j) & 1u) {
           const uint32_t t = (uint32_t)(tb + 16 * (j >> 2) + (j & 3));
-          const uint64_t kv = ((uint64_t)order_key32(acc[j >> 2][j & 3]) << 32) | (uint64_t)(0xFFFFFFFFu - t);
-          list[row][pos++] = kv;
-          nc += kv >= tm_reg;
+          list[row][pos++] = ((uint64_t)order_key32(acc[j >> 2][j & 3]) << 32) | (uint64_t)(0xFFFFFFFFu - t);
         }
       }
     };
@@ -1401,20 +1421,18 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       step(i + 2, accA, accB, kD, kB);
       step(i + 3, accB, accA, kA, kC);
     }
-    if (count && tm_reg != 0ull && nc) atomicAdd(&nge[row], nc);
     __syncthreads();
   };
 
   if (n1 > 0) {
     // phase 1: the sample, keeping the m best of each row
-    sweep(0, n1, m, false);
+    sweep(0, n1, m);
     for (int x = wave; x < TS_ROWS; x += TS_THREADS / 64) {
       const int n = cnt[0][x];
       if (n >= m) {
         const uint64_t T = cut_list(list[x], n, m, lane);
         if (lane == 0) {
           cnt[0][x] = m;
-          nge[x] = m;
           tm[x] = T;
           thr[x] = (uint32_t)(T >> 32);
         }
@@ -1422,28 +1440,154 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     }
     __syncthreads();
   }
-  // phase 2: the other blocks, keeping the E best
-  sweep(n1, nb, E, true);
   if (n1 > 0) {
-    // a row whose T_m fewer than E candidates reach may have lost tokens
-    // below T_m: redo it from an empty list over every block
-    if (tid < TS_ROWS && tm[tid] != 0ull && nge[tid] < E) atomicOr(&redo, 1);
+    // Phase 2 (filter): with the rows' thresholds fixed at T_m, every key
+    // reaching it goes to this wavefront's own workspace segment for its
+    // row, at positions the row's four lanes agree on; no lists, no atomics,
+    // no barriers.
+    {
+      auto load_tile = [&](int i, uint4* kt) {
+        const int tb = (int)order[min(max(i, n1), nb - 1)] * BLK + 32 * tq + l16;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint4* src = (const uint4*)(kb + (size_t)min(tb + 16 * t, N - 1) * HD + 32 * q4);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) kt[4 * t + s] = src[s];
+        }
+      };
+      const uint32_t th = (uint32_t)(tm[row] >> 32);
+      const float thr_f = th == 0u ? -INFINITY
+                          : (th >> 31) ? __uint_as_float(th & 0x7FFFFFFFu)
+                                       : __uint_as_float(~th);
+      uint64_t* seg = gseg + ((bh * nb + (size_t)min(r0 + row, nb - 1)) * 4 + tq) * SEG_CAP;
+      int scount = 0;  // the same in the row's four lanes
+      auto fstep = [&](int i, const f32x4* acc, f32x4* accn, const uint4* kn, uint4* kl) {
+        mfma_tile(kn, accn);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(i + 3, kl);
+        const int c = order[min(max(i, n1), nb - 1)];
+        const int tb = c * BLK + 32 * tq + 4 * q4;
+        const bool live = i >= n1 && i < nb && ((skip[row][c >> 5] >> (c & 31)) & 1u);
+        uint32_t mask = 0u;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (live && tb + 16 * t + v < N && acc[t][v] >= thr_f) mask |= 1u << (4 * t + v);
+        const int pc = __popc(mask);
+        const int p16 = lane_x16(pc), pair = pc + p16, p32 = lane_x32(pair);
+        int pos = scount + ((q4 & 1) ? p16 : 0) + ((q4 & 2) ? p32 : 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if ((mask >> j) & 1u) {
+            const uint32_t t = (uint32_t)(tb + 16 * (j >> 2) + (j & 3));
+            if (pos < SEG_CAP)
+              seg[pos] = ((uint64_t)order_key32(acc[j >> 2][j & 3]) << 32) | (uint64_t)(0xFFFFFFFFu - t);
+            ++pos;
+          }
+        }
+        scount += pair + p32;
+      };
+      // the pipeline fills inside the loop (three steps on zeroed buffers
+      // before tile n1), so no load is in flight when the loop is entered
+      // and every tile's MFMAs wait only for that tile's own loads
+      f32x4 accA[2] = {f32x4{}, f32x4{}}, accB[2] = {f32x4{}, f32x4{}};
+      uint4 kA[8], kB[8], kC[8], kD[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kA[j] = kB[j] = kC[j] = kD[j] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = n1 - 3; i < nb; i += 4) {
+        fstep(i, accA, accB, kB, kD);
+        fstep(i + 1, accB, accA, kC, kA);
+        fstep(i + 2, accA, accB, kD, kB);
+        fstep(i + 3, accB, accA, kA, kC);
+      }
+      if (q4 == 0) segcnt[tq][row] = scount <= SEG_CAP ? scount : -1;
+    }
+    __syncthreads();
+    // Merge: each row's phase-1 keys and its four segments; the E best of
+    // them are the row's answer when at least E keys reach T_m (then no key
+    // below T_m can be among the E best) and no segment overflowed.
+    for (int x = wave; x < TS_ROWS; x += TS_THREADS / 64) {
+      const int r = r0 + x;
+      bool bad = false;
+      if (r < nb) {
+        int c[4], total = cnt[0][x];
+        const int n0 = total;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = segcnt[q][x];
+          bad |= c[q] < 0;
+          total += max(c[q], 0);
+        }
+        if (!bad) {
+          constexpr int PER = TS_CAP / 64 + 4 * SEG_CAP / 64;
+          uint32_t hi[PER], lo[PER];
+          const uint64_t tmx = tm[x];
+          const uint64_t* sb = gseg + (bh * nb + (size_t)r) * 4 * SEG_CAP;
+          int nge_l = 0;
+#pragma unroll
+          for (int j = 0; j < PER; ++j) {
+            const int y = lane + 64 * j;
+            uint64_t kv = 0ull;
+            if (y < n0) {
+              kv = list[x][y];
+            } else if (y < total) {
+              int rest = y - n0, q = 0;
+#pragma unroll
+              for (int u = 0; u < 3; ++u)
+                if (q == u && rest >= c[u]) {
+                  rest -= c[u];
+                  q = u + 1;
+                }
+              kv = sb[q * SEG_CAP + rest];
+            }
+            hi[j] = (uint32_t)(kv >> 32);
+            lo[j] = (uint32_t)kv;
+            nge_l += (kv != 0ull && kv >= tmx);
+          }
+          int nge_w = nge_l;
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) nge_w += __shfl_xor(nge_w, off, 64);
+          if (tmx != 0ull && nge_w < E) {
+            bad = true;
+          } else {
+            const int keep = min(E, total);
+            if (keep > 0) {
+              uint32_t T, L;
+              bool exact;
+              top_keys<PER>(hi, lo, keep, T, L, exact);
+              write_kept<PER>(list[x], hi, lo, T, L, exact, lane);
+            }
+            if (lane == 0) cnt[0][x] = keep;
+          }
+        }
+      }
+      if (lane == 0) nge[x] = bad ? 1 : 0;
+    }
+    __syncthreads();
+    // rows phase 2 could not decide are redone from an empty list over
+    // every block with the list-and-cut sweep
+    if (tid < TS_ROWS && nge[tid]) atomicOr(&redo, 1);
     __syncthreads();
     if (redo) {
       for (int x = tid; x < TS_ROWS * nwords; x += TS_THREADS) {
         const int i = x / nwords;
-        if (!(tm[i] != 0ull && nge[i] < E)) skip[i][x % nwords] = 0u;
+        if (!nge[i]) skip[i][x % nwords] = 0u;
       }
       __syncthreads();
-      if (tid < TS_ROWS && tm[tid] != 0ull && nge[tid] < E) {
-        cnt[0][tid] = 0;
-        thr[tid] = 0u;
+      if (tid < TS_ROWS) {
+        if (nge[tid]) {
+          cnt[0][tid] = 0;
+          thr[tid] = 0u;
+        }
+        tm[tid] = 0ull;
       }
       __syncthreads();
-      if (tid < TS_ROWS) tm[tid] = 0ull;
-      __syncthreads();
-      sweep(0, nb, E, false);
+      sweep(0, nb, E);
     }
+  } else {
+    // small E: no sample, one list-and-cut sweep over every block
+    sweep(0, nb, E);
   }
 
   for (int x = wave; x < TS_ROWS; x += TS_THREADS / 64) {
@@ -1492,7 +1636,7 @@ struct Geometry {
 };
 
 struct WsLayout {
-  size_t vt, svt, apart, anchor, total;
+  size_t vt, svt, apart, anchor, tsel, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1549,6 +1693,11 @@ WsLayout ws_layout(const Geometry& g) {
     off = align256(off + bh * g.nb * HD * sizeof(double));
     w.anchor = off;
     off = align256(off + bh * HD * sizeof(double));
+  }
+  if (g.E > 0) {
+    // extra-token selection: a key segment per (query block, token quarter)
+    w.tsel = off;
+    off = align256(off + bh * g.nb * 4 * SEG_CAP * sizeof(uint64_t));
   }
   w.total = off;
   return w;
@@ -1707,20 +1856,24 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
 }
 
 int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
-                      const int32_t* block_idx, int32_t* token_idx, void* hip_stream) {
+                      const int32_t* block_idx, int32_t* token_idx, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
   Geometry g;
   const int st = make_geometry(p, &g);
   if (st != BSA_OK) return st;
   if (g.E == 0) return BSA_OK;
   if (!q_pool || !k || !token_idx || (g.k > 0 && !block_idx)) return BSA_ERR_INVALID;
   if (!aligned16(q_pool) || !aligned16(k)) return BSA_ERR_INVALID;
+  const WsLayout w = ws_layout(g);
+  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return BSA_ERR_WORKSPACE;
   // sample size of the first phase: T_m lands near the 2E- to 3E-th score,
   // with a margin for samples that are not random (small E: no sample)
   const int m = g.E >= 64 ? std::min(g.E, (int)ceil(g.E / 8.0 + 8.0 * sqrt(g.E / 8.0))) : 0;
   const int total = (int)(((g.nb + TS_ROWS - 1) / TS_ROWS) * g.H * g.B);
   hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)total), dim3(TS_THREADS), 0, (hipStream_t)hip_stream,
-                     q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx, (int)g.N,
-                     (int)g.nb, (int)g.k, g.E, m, (int)g.f0, (int)g.f1, total);
+                     q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx,
+                     (uint64_t*)((char*)workspace + w.tsel), (int)g.N, (int)g.nb, (int)g.k, g.E, m,
+                     (int)g.f0, (int)g.f1, total);
   return launch_status();
 }
 

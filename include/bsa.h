@@ -117,8 +117,10 @@ int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff);
  * to *bytes.  The workspace holds, for every (b, h): V of each key block
  * transposed (feature-major, key order interleaved for the matrix cores, zero
  * past the end of a short block), the summary values transposed in groups of
- * 128 blocks, and in reweight mode the anchor and its per-block partial sums.
- * Its contents are private to this library; it must be 256-byte aligned.
+ * 128 blocks, in reweight mode the anchor and its per-block partial sums,
+ * and with extra tokens the candidate keys of bsa_select_tokens (16 KB per
+ * query block).  Its contents are private to this library; it must be
+ * 256-byte aligned.
  */
 int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes);
 
@@ -207,6 +209,8 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
  *   k          in   bf16 [B, H, N, 128]
  *   block_idx  in   int32 [B, H, nb, k] (from bsa_select; may be NULL iff k == 0)
  *   token_idx  out  int32 [B, H, nb, E], E = p->extra_tokens
+ *   workspace  in/out  bsa_workspace_bytes() bytes (the region bsa_pool and
+ *                   bsa_forward use is left as it is)
  *
  * Candidates of query block r: every token j of the blocks not in
  * block_idx[r].  Score: q_pool[r] . k_j, with q_pool[r] split exactly into
@@ -218,7 +222,8 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
  * does nothing when E == 0 (token_idx may then be NULL).
  */
 int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
-                      const int32_t* block_idx, int32_t* token_idx, void* hip_stream);
+                      const int32_t* block_idx, int32_t* token_idx, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
 
 /*
  * Stages 3 and 4 with extra tokens: bsa_forward's result where the logits of

@@ -141,34 +141,28 @@ def test_null_pointers_and_small_workspace_rejected():
 def test_extra_token_entry_points_validate():
     L = bsa.lib()
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    big = 1 << 40
     p = _prob()
     pe = _prob(extra_tokens=256)
     # no extra tokens: token selection has nothing to do
-    assert L.bsa_select_tokens(ctypes.byref(p), None, None, None, None, None) == bsa.BSA_OK
+    assert L.bsa_select_tokens(ctypes.byref(p), None, None, None, None, None, 0, None) == bsa.BSA_OK
     # with extra tokens: every tensor is needed (block_idx unless k == 0)
-    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, fake, None, None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, None, fake, None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_select_tokens(ctypes.byref(pe), None, fake, fake, fake, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, fake, None, fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, None, fake, fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_select_tokens(ctypes.byref(pe), None, fake, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID
     odd = ctypes.c_void_p((1 << 20) + 2)
-    assert L.bsa_select_tokens(ctypes.byref(pe), fake, odd, fake, fake, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, odd, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID
+    # and the workspace, which holds a key segment per (query block, token quarter)
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, fake, fake, None, big, None) == bsa.BSA_ERR_WORKSPACE
+    assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, 16, None) == bsa.BSA_ERR_WORKSPACE
+    n = bsa.bsa_workspace_bytes(pe) - bsa.bsa_workspace_bytes(p)
+    assert 2 * 32 * 4 * 512 * 8 <= n <= 2 * 32 * 4 * 512 * 8 + 256
     # bsa_forward refuses a problem with extra tokens; bsa_forward_tokens needs v and token_idx
-    big = 1 << 40
     assert L.bsa_forward(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, big, fake,
                          None) == bsa.BSA_ERR_INVALID
     assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, None, fake, fake, fake, fake, fake, big,
                                 fake, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, None, fake, big,
                                 fake, None) == bsa.BSA_ERR_INVALID
-    # extra tokens need no workspace of their own
-    assert bsa.bsa_workspace_bytes(pe) == bsa.bsa_workspace_bytes(p)
     assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, fake, fake,
                                 16, fake, None) == bsa.BSA_ERR_WORKSPACE
-
-
-def test_binding_rejects_bad_tensors():
-    import torch
-    x = torch.zeros(1, 1, 256, 128, dtype=torch.float32)
-    with pytest.raises(ValueError):
-        bsa.attention(x, x, x, top_k=1)
-    with pytest.raises(ValueError):
-        bsa.make_problem(1, 1, 256, top_k=1, top_k_ratio=0.5)
