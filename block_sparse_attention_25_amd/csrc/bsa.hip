@@ -1269,17 +1269,17 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     }
   }
 
-  // B operand: query block r0 + row, features 32 q4 + 8s + [0, 8) for k-step
-  // s, as three exact bfloat16 terms
+  // B operand: query block r0 + row, features 32 s + 8 q4 + [0, 8) for
+  // k-step s, as three exact bfloat16 terms
   bf16x8 qs[3][4];
   {
-    const float* qp = q_pool + (bh * nb + min(r0 + row, nb - 1)) * HD + 32 * q4;
+    const float* qp = q_pool + (bh * nb + min(r0 + row, nb - 1)) * HD + 8 * q4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u16x8 hi, mid, lo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = qp[8 * s + e];
+        const float x = qp[32 * s + e];
         const uint16_t h = f2bf(x);
         const float r1 = x - bf2f(h);  // exact
         const uint16_t md = f2bf(r1);
@@ -1296,7 +1296,8 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   __syncthreads();
 
   // A operand of tile t: token c * 128 + 32 tq + 16 t + l16 of key block c,
-  // the 64 bytes of features [32 q4, 32 q4 + 32).  Past the end of the
+  // features 32 s + 8 q4 + [0, 8) for k-step s (so each load instruction
+  // reads 64 contiguous bytes of every row it touches).  Past the end of the
   // sequence the last row is read again: such a token's scores fill only its
   // own accumulator row and it is never inserted, so the loaded data needs no
   // zeroing (and a load needs no wait until the MFMAs that read it).
@@ -1334,9 +1335,9 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       const int tb = (int)order[min(i, i1 - 1)] * BLK + 32 * tq + l16;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const uint4* src = (const uint4*)(kb + (size_t)min(tb + 16 * t, N - 1) * HD + 32 * q4);
+        const uint16_t* src = kb + (size_t)min(tb + 16 * t, N - 1) * HD + 8 * q4;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kt[4 * t + s] = src[s];
+        for (int s = 0; s < 4; ++s) kt[4 * t + s] = *(const uint4*)(src + 32 * s);
       }
     };
     uint32_t thr_reg = thr[row];
@@ -1450,9 +1451,9 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
         const int tb = (int)order[min(max(i, n1), nb - 1)] * BLK + 32 * tq + l16;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const uint4* src = (const uint4*)(kb + (size_t)min(tb + 16 * t, N - 1) * HD + 32 * q4);
+          const uint16_t* src = kb + (size_t)min(tb + 16 * t, N - 1) * HD + 8 * q4;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) kt[4 * t + s] = src[s];
+          for (int s = 0; s < 4; ++s) kt[4 * t + s] = *(const uint4*)(src + 32 * s);
         }
       };
       const uint32_t th = (uint32_t)(tm[row] >> 32);
