@@ -75,6 +75,30 @@ Readings taken where the pages are silent (each is exercised by a test):
      (extra_tokens, the top-scoring tokens each query block reads beyond its
      chosen blocks).
 
+  R17 Spark-Reblock (the "q_reuse_k" layout).  Sources: "Spark-H3: Block
+     Sparse Attention Speeds Up MiniMax-H3 in ComfyUI", section "What
+     Spark-Attn changes" (queries are grouped by the similarity of their score
+     patterns over the keys, a cosine distance in the metric of the keys'
+     second moment; a hierarchical partitioner splits groups until each leaf
+     is one block, in O(N log N)), and section "Workflows" (every shipped
+     workflow sets reblock_layout=q_reuse_k: the query partition is reused for
+     the keys).  Per (batch, head): M = (1/N) sum_j k_j k_j^T over all rows;
+     L is the Cholesky factor of M + eps (trace(M)/d) I + 1e-30 I with
+     eps = 1e-6 (the small ridge keeps L defined for rank-deficient keys);
+     each query row becomes the unit vector z_i = L^T q_i / |L^T q_i| (zero
+     stays zero), so z_i . z_j is the cosine of q_i and q_j in the metric M.
+     A group of n rows (m = ceil(n / 128) blocks, m >= 2) splits on the
+     coordinate of z with the largest population variance over the group
+     (the lowest coordinate on ties): the 128 * ceil(m / 2) rows with the
+     smallest value of that coordinate (ties to the lower row index) form the
+     left group, the rest the right one, each in ascending row order.  The
+     leaves, left to right, give the permutation; Q, K and V are all permuted
+     by it, the block-sparse path runs on the permuted rows, and the output
+     rows are put back in their original places.  The pages name neither the
+     split rule nor its direction: a split on one coordinate of the whitened
+     unit vectors is the simplest hierarchical partitioner of that metric that
+     runs in O(N log N) with no iteration.
+
 Precision: pooled vectors are summed in float64 and stored as float32 (the
 precision in which a block ranking is decided); block scores are float64 dot
 products of those float32 vectors; everything else is float64.
@@ -370,3 +394,82 @@ def run_head(q, k, v, top_k: int, summary: str = "mean", anchor_rows: int = 0,
     out = attention(q, k, v, idx, sk, sv, b, sc, block, dense_blocks=sinks, extra=extra)
     return dict(q_pool=q_pool, k_pool=k_pool, scores=s, idx=idx, sum_k=sk,
                 sum_v=sv, bias=b, out=out, scale=sc, sinks=sinks, extra=extra)
+
+
+# ---------------------------------------------------------- Spark-Reblock ---
+REBLOCK_EPS = 1e-6
+
+
+def key_second_moment(k: np.ndarray) -> np.ndarray:
+    """M = (1/N) sum_j k_j k_j^T, the second moment of the key rows that
+    defines the query metric (R17; "What Spark-Attn changes", the Spark-Reblock
+    item: the metric comes from the opposite side's second moment)."""
+    k = np.asarray(k, dtype=np.float64)
+    return k.T @ k / k.shape[0]
+
+
+def mahalanobis_embedding(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Unit rows z_i = L^T q_i / |L^T q_i| with L L^T = M + ridge (R17), so
+    that z_i . z_j = q_i^T M q_j / (|q_i|_M |q_j|_M) up to the ridge."""
+    q = np.asarray(q, dtype=np.float64)
+    M = key_second_moment(k)
+    d = M.shape[0]
+    ridge = REBLOCK_EPS * (np.trace(M) / d) + 1e-30
+    L = np.linalg.cholesky(M + ridge * np.eye(d))
+    z = q @ L  # row i holds (L^T q_i)^T
+    norm = np.sqrt((z * z).sum(axis=1))
+    out = np.zeros_like(z)
+    nz = norm > 0
+    out[nz] = z[nz] / norm[nz, None]
+    return out
+
+
+def reblock_left_rows(n: int, block: int = BLOCK) -> int:
+    """Rows of the left group when a group of n rows splits: 128 * ceil(m / 2)
+    for its m = ceil(n / 128) blocks, so every leaf but the last is full (R17)."""
+    m = n_blocks(n, block)
+    return block * (-(-m // 2))
+
+
+def split_coordinate(zg: np.ndarray) -> int:
+    """The coordinate with the largest population variance over the group's
+    rows, the lowest one on ties (R17)."""
+    var = zg.var(axis=0)
+    return int(np.argmax(var))
+
+
+def reblock_permutation(q: np.ndarray, k: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """Spark-Reblock permutation of one (batch, head) (R17): perm[p] is the
+    original row placed at position p; int64 [N]."""
+    z = mahalanobis_embedding(q, k)
+    N = z.shape[0]
+    leaves = []
+
+    def split(rows: np.ndarray):
+        n = len(rows)
+        if n_blocks(n, block) <= 1:
+            leaves.append(rows)
+            return
+        c = split_coordinate(z[rows])
+        # rows ordered by that coordinate, ties to the lower row index
+        order = rows[np.lexsort((rows, z[rows, c]))]
+        nl = reblock_left_rows(n, block)
+        split(np.sort(order[:nl]))
+        split(np.sort(order[nl:]))
+
+    split(np.arange(N, dtype=np.int64))
+    return np.concatenate(leaves) if leaves else np.zeros(0, dtype=np.int64)
+
+
+def run_head_reblocked(q, k, v, perm, **kw):
+    """The block-sparse path on rows permuted by perm (Q, K and V alike, the
+    q_reuse_k layout), with the output rows put back in place (R17).  kw as
+    for run_head; the result's 'out' is in the original row order."""
+    perm = np.asarray(perm, dtype=np.int64)
+    res = run_head(np.asarray(q)[perm], np.asarray(k)[perm], np.asarray(v)[perm], **kw)
+    out = np.empty_like(res["out"])
+    out[perm] = res["out"]
+    res["out_permuted"] = res["out"]
+    res["out"] = out
+    return res
+

@@ -880,3 +880,307 @@ def test_planted_tie_rule_mistake_is_caught(monkeypatch):
         return idx
     monkeypatch.setattr(O, "select_topk", select_high_index)
     assert not _all_pins_pass()
+
+
+# ---------------------------------------------------------- Spark-Reblock ---
+def _iso_keys(N, scales=None, d=D):
+    """Key rows a_j e_(j mod d): the second moment is diag(a^2 N_j / N), the
+    identity for a_j = sqrt(d) when d divides N."""
+    s = np.ones(d) if scales is None else np.asarray(scales, dtype=np.float64)
+    k = np.zeros((N, d))
+    for j in range(N):
+        k[j, j % d] = math.sqrt(d * s[j % d])
+    return k
+
+
+_CENTERS = {0: (1.0, 0.5), 1: (1.0, -0.5), 2: (-1.0, 0.5), 3: (-1.0, -0.5)}
+
+
+def _cluster_rows(N, seed, d=D):
+    """Row i lies near the unit vector of _CENTERS[i % 4] in coordinates 0, 1,
+    with a positive row scale and 1e-3 noise elsewhere."""
+    rng = np.random.default_rng(seed)
+    c = np.zeros((N, d))
+    for i in range(N):
+        a, b = _CENTERS[i % 4]
+        c[i, 0], c[i, 1] = a / math.hypot(a, b), b / math.hypot(a, b)
+    c += 1e-3 * rng.standard_normal((N, d))
+    return c * rng.uniform(0.5, 2.0, size=(N, 1))
+
+
+def _cluster_expected(N):
+    """Hand-derived partition of _cluster_rows: the first split is on
+    coordinate 0 (variance 0.8 against 0.2), negative values left; each half
+    then splits on coordinate 1, negative values left."""
+    return np.concatenate([np.arange(N)[np.arange(N) % 4 == c] for c in (3, 2, 1, 0)])
+
+
+def test_reblock_embedding_is_metric_cosine():
+    rng = np.random.default_rng(40)
+    N = 200
+    q = rng.standard_normal((N, D))
+    k = rng.standard_normal((N, D)) * rng.uniform(0.2, 3.0, size=D)
+    z = O.mahalanobis_embedding(q, k)
+    # M written out as a sum of outer products, pair by pair
+    M = np.zeros((D, D))
+    for j in range(N):
+        M += np.outer(k[j], k[j])
+    M /= N
+    for i, j in [(0, 1), (3, 77), (150, 199), (10, 10)]:
+        cos = q[i] @ M @ q[j] / math.sqrt((q[i] @ M @ q[i]) * (q[j] @ M @ q[j]))
+        assert abs(z[i] @ z[j] - cos) < 1e-5
+    assert np.abs(np.linalg.norm(z, axis=1) - 1.0).max() < 1e-12
+
+
+def test_reblock_embedding_zero_rows_and_zero_keys():
+    q = np.random.default_rng(41).standard_normal((300, D))
+    q[5] = 0.0
+    z = O.mahalanobis_embedding(q, np.zeros((300, D)))
+    assert np.all(z[5] == 0.0)
+    # zero keys leave only the ridge: the embedding is the normalised query
+    assert np.abs(z[6] - q[6] / np.linalg.norm(q[6])).max() < 1e-12
+
+
+@pytest.mark.parametrize("N", [512, 1024])
+def test_reblock_clusters_hand_partition(N):
+    q = _cluster_rows(N, seed=42)
+    perm = O.reblock_permutation(q, _iso_keys(N))
+    if N == 512:
+        assert np.array_equal(perm, _cluster_expected(N))
+    else:
+        # 256 rows per cluster: the first two splits are the hand partition,
+        # then each cluster splits in two leaves on its noise
+        leaves = [perm[b * 128:(b + 1) * 128] for b in range(8)]
+        assert [sorted(set((l % 4).tolist())) for l in leaves] == [[c] for c in (3, 3, 2, 2, 1, 1, 0, 0)]
+
+
+def test_reblock_whitening_by_key_moment():
+    # M = diag(s): queries c / sqrt(s) embed to the cluster vectors c, so the
+    # hand partition holds; the unwhitened queries would split on coordinate 1
+    N = 512
+    s = np.ones(D)
+    s[0], s[1] = 100.0, 0.01
+    c = _cluster_rows(N, seed=43)
+    q = c / np.sqrt(s)
+    assert np.array_equal(O.reblock_permutation(q, _iso_keys(N, s)), _cluster_expected(N))
+    assert not np.array_equal(O.reblock_permutation(q, _iso_keys(N)), _cluster_expected(N))
+
+
+def test_reblock_exact_ties_go_left_in_row_order():
+    # identical rows: every coordinate has zero variance and every value ties,
+    # so each split keeps the lower rows on the left: the identity
+    N = 700
+    q = np.tile(np.random.default_rng(44).standard_normal(D), (N, 1))
+    k = np.random.default_rng(45).standard_normal((N, D))
+    assert np.array_equal(O.reblock_permutation(q, k), np.arange(N))
+
+
+def test_split_coordinate_rule():
+    zg = np.random.default_rng(46).standard_normal((50, 6)) * 0.1
+    zg[:, 4] = np.linspace(-1, 1, 50)
+    assert O.split_coordinate(zg) == 4
+    zg[:, 2] = zg[:, 4]                # the same variance: the lower coordinate
+    assert O.split_coordinate(zg) == 2
+
+
+@pytest.mark.parametrize("N", [1, 100, 128, 129, 300, 1000, 4097])
+def test_reblock_structure(N):
+    q, k, _ = _rand_head(N, seed=47)
+    perm = O.reblock_permutation(q, k)
+    assert np.array_equal(np.sort(perm), np.arange(N))
+    if N <= 128:
+        assert np.array_equal(perm, np.arange(N))
+    # leaves are the 128-row blocks of the new order, each in row order
+    for b0 in range(0, N, 128):
+        leaf = perm[b0:b0 + 128]
+        assert np.all(np.diff(leaf) > 0)
+
+
+def test_reblock_left_rows_closed_form():
+    assert O.reblock_left_rows(129) == 128
+    assert O.reblock_left_rows(256) == 128
+    assert O.reblock_left_rows(257) == 256
+    assert O.reblock_left_rows(37740) == 128 * 148     # 295 blocks
+    assert O.reblock_left_rows(37740 - 18944) == 128 * 74
+
+
+def test_reblock_root_split_brute_force():
+    # the first split recomputed with plain loops: variances of every
+    # coordinate, then the 256 smallest values, ties to the lower row
+    N = 434
+    q, k, _ = _rand_head(N, seed=48)
+    z = O.mahalanobis_embedding(q, k)
+    best, bc = -1.0, -1
+    for c in range(D):
+        col = [float(z[i, c]) for i in range(N)]
+        mu = sum(col) / N
+        var = sum((x - mu) ** 2 for x in col) / N
+        if var > best:
+            best, bc = var, c
+    left = sorted(sorted(range(N), key=lambda i: (z[i, bc], i))[:256])
+    perm = O.reblock_permutation(q, k)
+    assert sorted(perm[:256].tolist()) == left
+
+
+def test_reblock_invariances():
+    q, k, _ = _rand_head(700, seed=49)
+    perm = O.reblock_permutation(q, k)
+    rng = np.random.default_rng(50)
+    assert np.array_equal(O.reblock_permutation(q, 3.0 * k), perm)
+    assert np.array_equal(O.reblock_permutation(q, k[rng.permutation(700)]), perm)
+    assert np.array_equal(O.reblock_permutation(q * rng.uniform(0.1, 5, (700, 1)), k), perm)
+
+
+@pytest.mark.parametrize("N", [300, 1000])
+def test_reblock_all_blocks_is_dense_attention(N):
+    q, k, v = _synth_head(N, seed=51)
+    perm = O.reblock_permutation(q, k)
+    res = O.run_head_reblocked(q, k, v, perm, top_k=O.n_blocks(N))
+    assert np.abs(res["out"] - _sdpa(q, k, v)).max() < 1e-10
+
+
+def test_reblock_leaf_mask_formulation():
+    # the reblocked path written over the original rows: blocks are the row
+    # sets of the leaves, pooled and selected as row sets, then one masked
+    # dense attention per leaf
+    N, top_k = 900, 2
+    q, k, v = _synth_head(N, seed=52)
+    perm = O.reblock_permutation(q, k)
+    leaves = [perm[b:b + 128] for b in range(0, N, 128)]
+    nb = len(leaves)
+    qp = np.array([q[l].sum(0) / len(l) for l in leaves]).astype(np.float32)
+    kp = np.array([k[l].sum(0) / len(l) for l in leaves]).astype(np.float32)
+    idx = O.select_topk(qp.astype(np.float64) @ kp.astype(np.float64).T, top_k)
+    sk = np.array([k[l].mean(0) for l in leaves])
+    sv = np.array([v[l].mean(0) for l in leaves])
+    Kc, Vc = np.concatenate([k, sk]), np.concatenate([v, sv])
+    out = np.zeros_like(q)
+    for r, l in enumerate(leaves):
+        m = np.full(N + nb, -np.inf)
+        for c in range(nb):
+            if c in set(idx[r].tolist()):
+                m[leaves[c]] = 0.0
+            else:
+                m[N + c] = 0.0
+        out[l] = _sdpa(q[l], Kc, Vc, mask=np.repeat(m[None, :], len(l), axis=0))
+    res = O.run_head_reblocked(q, k, v, perm, top_k=top_k)
+    assert np.array_equal(res["idx"], idx)
+    assert np.abs(res["out"] - out).max() < 1e-10
+
+
+def _reblock_pins_pass():
+    try:
+        test_reblock_embedding_is_metric_cosine()
+        test_reblock_embedding_zero_rows_and_zero_keys()
+        test_reblock_clusters_hand_partition(512)
+        test_reblock_whitening_by_key_moment()
+        test_reblock_exact_ties_go_left_in_row_order()
+        test_split_coordinate_rule()
+        test_reblock_structure(1000)
+        test_reblock_left_rows_closed_form()
+        test_reblock_root_split_brute_force()
+        test_reblock_all_blocks_is_dense_attention(300)
+        test_reblock_leaf_mask_formulation()
+    except AssertionError:
+        return False
+    return True
+
+
+def test_reblock_pins_pass_on_the_oracle():
+    assert _reblock_pins_pass()
+
+
+_orig_embed = O.mahalanobis_embedding
+_orig_run_reblocked = O.run_head_reblocked
+
+
+def _embed_untransposed(q, k):
+    # mistake: L q_i instead of L^T q_i
+    q = np.asarray(q, dtype=np.float64)
+    M = O.key_second_moment(k)
+    L = np.linalg.cholesky(M + (1e-6 * np.trace(M) / M.shape[0] + 1e-30) * np.eye(M.shape[0]))
+    z = q @ L.T
+    n = np.linalg.norm(z, axis=1)
+    return z / np.where(n > 0, n, 1.0)[:, None]
+
+
+def _embed_unnormalised(q, k):
+    z = _orig_embed(q, k)
+    return z * np.linalg.norm(np.asarray(q, dtype=np.float64), axis=1)[:, None]
+
+
+def _embed_unwhitened(q, k):
+    # mistake: the plain cosine of the queries (no key metric)
+    q = np.asarray(q, dtype=np.float64)
+    n = np.linalg.norm(q, axis=1)
+    return q / np.where(n > 0, n, 1.0)[:, None]
+
+
+def _moment_uncentred_sum(k):
+    k = np.asarray(k, dtype=np.float64)
+    return k.T @ k          # mistake: no 1/N (the ridge then differs in scale only)
+
+
+def _split_lowest_variance(zg):
+    return int(np.argmin(zg.var(axis=0)))
+
+
+def _split_high_index_ties(zg):
+    var = zg.var(axis=0)
+    return int(len(var) - 1 - np.argmax(var[::-1]))
+
+
+def _left_rows_floor(n, block=128):
+    m = O.n_blocks(n, block)
+    return block * max(1, m // 2)
+
+
+def _run_reblocked_wrong_inverse(q, k, v, perm, **kw):
+    res = _orig_run_reblocked(q, k, v, perm, **kw)
+    res["out"] = res["out_permuted"][perm]
+    return res
+
+
+def _run_reblocked_queries_only(q, k, v, perm, **kw):
+    perm = np.asarray(perm)
+    res = O.run_head(np.asarray(q)[perm], k, v, **kw)
+    out = np.empty_like(res["out"])
+    out[perm] = res["out"]
+    res["out"] = out
+    return res
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("mahalanobis_embedding", _embed_untransposed),
+    ("mahalanobis_embedding", _embed_unnormalised),
+    ("mahalanobis_embedding", _embed_unwhitened),
+    ("split_coordinate", _split_lowest_variance),
+    ("split_coordinate", _split_high_index_ties),
+    ("reblock_left_rows", _left_rows_floor),
+    ("run_head_reblocked", _run_reblocked_wrong_inverse),
+    ("run_head_reblocked", _run_reblocked_queries_only),
+])
+def test_planted_reblock_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    assert not _reblock_pins_pass()
+
+
+def test_planted_reblock_tie_rule_mistake_is_caught(monkeypatch):
+    def perm_high_ties(q, k, block=128):
+        z = O.mahalanobis_embedding(q, k)
+        leaves = []
+
+        def split(rows):
+            n = len(rows)
+            if O.n_blocks(n, block) <= 1:
+                leaves.append(rows)
+                return
+            c = O.split_coordinate(z[rows])
+            order = rows[np.lexsort((-rows, z[rows, c]))]
+            nl = O.reblock_left_rows(n, block)
+            split(np.sort(order[:nl]))
+            split(np.sort(order[nl:]))
+        split(np.arange(z.shape[0]))
+        return np.concatenate(leaves)
+    monkeypatch.setattr(O, "reblock_permutation", perm_high_ties)
+    assert not _reblock_pins_pass()
