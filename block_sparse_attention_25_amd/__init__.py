@@ -85,6 +85,14 @@ def lib() -> ctypes.CDLL:
         L.bsa_select_tokens.restype = ctypes.c_int
         L.bsa_forward_tokens.argtypes = [_P] + [_vp] * 8 + [ctypes.c_size_t, _vp, _vp]
         L.bsa_forward_tokens.restype = ctypes.c_int
+        L.bsa_reblock_workspace_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
+        L.bsa_reblock_workspace_bytes.restype = ctypes.c_int
+        L.bsa_reblock.argtypes = [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.bsa_reblock.restype = ctypes.c_int
+        L.bsa_permute_rows.argtypes = [_P] + [_vp] * 8
+        L.bsa_permute_rows.restype = ctypes.c_int
+        L.bsa_unpermute_rows.argtypes = [_P] + [_vp] * 4
+        L.bsa_unpermute_rows.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -162,6 +170,30 @@ def bsa_forward_tokens(p: Problem, q, k, v, sum_k, sum_bias, block_idx, token_id
                                     _ptr(out), _stream(stream)), "bsa_forward_tokens")
 
 
+def bsa_reblock_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t()
+    _raise(lib().bsa_reblock_workspace_bytes(ctypes.byref(p), ctypes.byref(n)),
+           "bsa_reblock_workspace_bytes")
+    return n.value
+
+
+def bsa_reblock(p: Problem, q, k, perm, workspace, stream=None):
+    _raise(lib().bsa_reblock(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(perm), _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _stream(stream)), "bsa_reblock")
+
+
+def bsa_permute_rows(p: Problem, perm, q, k, v, q_out, k_out, v_out, stream=None):
+    _raise(lib().bsa_permute_rows(ctypes.byref(p), _ptr(perm), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(q_out), _ptr(k_out), _ptr(v_out), _stream(stream)),
+           "bsa_permute_rows")
+
+
+def bsa_unpermute_rows(p: Problem, perm, x, out, stream=None):
+    _raise(lib().bsa_unpermute_rows(ctypes.byref(p), _ptr(perm), _ptr(x), _ptr(out),
+                                    _stream(stream)), "bsa_unpermute_rows")
+
+
 # ---------------------------------------------------------------- helpers ---
 def k_from_ratio(ratio, n_blocks: int) -> int:
     """Top-k ratio budget -> block count, ceil(ratio * n_blocks) computed on the
@@ -212,8 +244,8 @@ def _check_qkv(q, k, v):
 
 
 def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows=0, scale=None,
-              sink_rows=0, sink_start=None, tau=None, extra_tokens=0, return_aux=False,
-              stream=None):
+              sink_rows=0, sink_start=None, tau=None, extra_tokens=0, reblock=False,
+              return_aux=False, stream=None):
     """Block-sparse attention of bf16 q, k, v [B, H, N, 128] on the GPU.
 
     top_k counts 128-token key blocks (or give top_k_ratio, e.g. "0.1");
@@ -226,8 +258,12 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     at most top_k; rows of block_idx padded with -1).  extra_tokens > 0 lets
     each query block also read exactly that many tokens of the blocks it
     skipped, those scoring highest against its pooled query (token_idx in the
-    aux dict).  Returns out [B, H, N, 128] bf16, plus a dict of intermediate
-    tensors when return_aux is set."""
+    aux dict).  reblock=True runs the path on Spark-Reblock's row order (the
+    q_reuse_k layout: Q, K and V permuted alike, the output put back in
+    place; perm in the aux dict, the other aux tensors in the new order); it
+    rejects sink rows and an anchor over part of the rows.  Returns out
+    [B, H, N, 128] bf16, plus a dict of intermediate tensors when return_aux
+    is set."""
     import torch
     _check_qkv(q, k, v)
     B, H, N, _ = q.shape
@@ -235,6 +271,17 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
                      tau, extra_tokens)
     nb, kk = bsa_problem_blocks(p)
     dev = q.device
+    perm = None
+    if reblock:
+        if p.sink_rows or (summary == "reweight" and p.anchor_rows not in (0, N)):
+            raise ValueError("reblock reorders the rows: sink_rows, and an anchor over part of the "
+                             "rows, would name other rows")
+        perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+        rws = torch.empty(bsa_reblock_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        bsa_reblock(p, q, k, perm, rws, stream)
+        qo, ko, vo = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bsa_permute_rows(p, perm, q, k, v, qo, ko, vo, stream)
+        q, k, v = qo, ko, vo
     f32, bf = torch.float32, torch.bfloat16
     q_pool = torch.empty((B, H, nb, HEAD_DIM), dtype=f32, device=dev)
     k_pool = torch.empty_like(q_pool)
@@ -254,7 +301,12 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
                            stream)
     else:
         bsa_forward(p, q, k, sum_k, sum_bias, idx if kk > 0 else None, ws, out, stream)
+    if perm is not None:
+        back = torch.empty_like(out)
+        bsa_unpermute_rows(p, perm, out, back, stream)
+        out = back
     if return_aux:
         return out, dict(q_pool=q_pool, k_pool=k_pool, sum_k=sum_k, sum_v=sum_v,
-                         sum_bias=sum_bias, block_idx=idx, token_idx=tok, workspace=ws, problem=p)
+                         sum_bias=sum_bias, block_idx=idx, token_idx=tok, workspace=ws, problem=p,
+                         perm=perm)
     return out

@@ -52,6 +52,7 @@ class Workload:
     sinks: bool = False    # route the conditioning rows as sinks
     tau: float | None = None  # threshold selection (top_k is then the cap)
     extra: int = 0         # extra tokens per query block
+    reblock: bool = False  # run on the Spark-Reblock row order (q_reuse_k)
 
     @property
     def sink_start(self) -> int:
@@ -84,6 +85,10 @@ WORKLOADS = {
     "768p_5s_tau1": Workload("768p_5s_tau1", 1, 56, (9, 48, 84), 36288, 1452, 295, tau=1.0),
     # the 768p 5s shape with 256 extra tokens per query block (the node's default)
     "768p_5s_extra256": Workload("768p_5s_extra256", 1, 56, (9, 48, 84), 36288, 1452, 64, extra=256),
+    # the 768p 5s shape on the Spark-Reblock order, with the shipped workflows'
+    # ratio budget (0.2 of 295 blocks: 59)
+    "768p_5s_reblock": Workload("768p_5s_reblock", 1, 56, (9, 48, 84), 36288, 1452, None, "0.2",
+                                reblock=True),
 }
 
 

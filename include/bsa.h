@@ -250,6 +250,71 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
                        const int32_t* token_idx, const void* workspace, size_t workspace_bytes,
                        void* out, void* hip_stream);
 
+/*
+ * Spark-Reblock (the q_reuse_k layout): an adaptive order of the N rows of
+ * every (batch, head) whose consecutive 128-row blocks group queries with
+ * similar attention-score patterns.
+ * Sources: "Spark-H3: Block Sparse Attention Speeds Up MiniMax-H3 in
+ * ComfyUI", section "What Spark-Attn changes" (similarity is a cosine in the
+ * metric of the keys' second moment; a hierarchical partitioner splits groups
+ * until each leaf is one block) and section "Workflows" (reblock_layout =
+ * q_reuse_k: keys and values take the query layout).
+ *
+ * Use: bsa_reblock -> perm; bsa_permute_rows(q, k, v) -> q', k', v'; the
+ * block-sparse path (bsa_pool ... bsa_forward or bsa_forward_tokens) on q',
+ * k', v' with the same problem -> out'; bsa_unpermute_rows(out') -> out.
+ * Problems with conditioning sinks, or Spark-Reweight with an anchor over
+ * part of the rows, are rejected with BSA_ERR_UNSUPPORTED by all three calls:
+ * those options name rows by position, which the new order changes.  The
+ * other fields of the problem are not read.
+ *
+ * What bsa_reblock computes, per (b, h):
+ *   M = (1/N) sum_j k_j k_j^T;  L L^T = M + (1e-6 trace(M) / 128 + 1e-30) I;
+ *   z_i = L^T q_i / |L^T q_i| (zero rows stay zero).
+ *   A group of n rows, m = ceil(n / 128) >= 2 blocks, splits on the
+ *   coordinate c of z with the largest variance over the group (the lowest c
+ *   on ties): its 128 ceil(m / 2) rows with the smallest z_i[c] (ties to the
+ *   lower row) form the left group, the others the right group, both in
+ *   ascending row order; groups of one block are leaves.  perm lists the
+ *   leaves left to right, so every 128-row block of the new order but the
+ *   last is full, and its rows ascend.
+ * Precision: M as float32 sums of exact products over 2048-row chunks, the
+ * chunks and the factorisation in float64, z in float32.  Where two split
+ * values (or two coordinate variances) are within float32 rounding of each
+ * other, the order may differ from an exact evaluation's.
+ *
+ *   q, k       in   bf16 [B, H, N, 128]
+ *   perm       out  int32 [B, H, N]: perm[p] = the row placed at position p
+ *   workspace  in/out  bsa_reblock_workspace_bytes() bytes, 256-byte aligned
+ *                   (about N * 528 bytes per (b, h)); its contents are
+ *                   scratch and need no initialisation
+ */
+int bsa_reblock_workspace_bytes(const bsa_problem* p, size_t* bytes);
+int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* perm,
+                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Rows of Q, K and V in the new order (the q_reuse_k layout):
+ * x_out[b, h, p, :] = x[b, h, perm[b, h, p], :] for x = q, k, v.
+ *   perm             in   int32 [B, H, N], a permutation of 0..N-1 per (b, h)
+ *                         (as bsa_reblock writes it; other values are not
+ *                         checked and read out of bounds)
+ *   q, k, v          in   bf16 [B, H, N, 128]
+ *   q_out, k_out, v_out  out  bf16 [B, H, N, 128], not overlapping the inputs
+ */
+int bsa_permute_rows(const bsa_problem* p, const int32_t* perm, const void* q, const void* k,
+                     const void* v, void* q_out, void* k_out, void* v_out, void* hip_stream);
+
+/*
+ * Output rows back in their original places: out[b, h, perm[b, h, p], :] =
+ * x[b, h, p, :].
+ *   perm   in   int32 [B, H, N], as for bsa_permute_rows
+ *   x      in   bf16 [B, H, N, 128] (the block-sparse output in the new order)
+ *   out    out  bf16 [B, H, N, 128], not overlapping x
+ */
+int bsa_unpermute_rows(const bsa_problem* p, const int32_t* perm, const void* x, void* out,
+                       void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -128,3 +128,62 @@ def check_tokens_row(gpu_row, cand, cand_scores, E):
 def check_output(gpu_out, ref_out):
     d = np.abs(np.asarray(gpu_out, dtype=np.float64) - ref_out)
     return float(d.max()), float(d.mean())
+
+
+# Reblock rule: a GPU split is accepted when some coordinate whose variance is
+# within REBLOCK_VAR_REL (relative) of the group's largest separates the left
+# rows from the right ones up to REBLOCK_KEY_ABS.  z has unit rows; the GPU's
+# z differs from the float64 one by the float32 rounding of M, L and z,
+# measured at most 2.1e-7 (768p 5s and 4,173-row heads), a tenth of the key
+# tolerance
+REBLOCK_KEY_ABS = 2e-6
+REBLOCK_VAR_REL = 1e-4
+
+
+def reblock_splits(N, left_rows, block=128):
+    """(start, n, n_left) of every split of the bisection tree over N rows;
+    the tree's shape depends on N only."""
+    out, stack = [], [(0, N)]
+    while stack:
+        s, n = stack.pop()
+        if -(-n // block) <= 1:
+            continue
+        nl = left_rows(n, block)
+        out.append((s, n, nl))
+        stack += [(s, nl), (s + nl, n - nl)]
+    return out
+
+
+def check_partition(z, perm, left_rows, block=128):
+    """Validate a GPU permutation against the float64 embedding z of the same
+    head: a permutation; every 128-row block ascending; every split separated
+    on a coordinate of (near-)largest variance.  Returns (ok, message)."""
+    N = z.shape[0]
+    perm = np.asarray(perm, dtype=np.int64)
+    if perm.shape != (N,) or not np.array_equal(np.sort(perm), np.arange(N)):
+        return False, "not a permutation"
+    for b0 in range(0, N, block):
+        if np.any(np.diff(perm[b0:b0 + block]) <= 0):
+            return False, "block at %d not ascending" % b0
+    for s, n, nl in reblock_splits(N, left_rows, block):
+        rows, left, right = perm[s:s + n], perm[s:s + nl], perm[s + nl:s + n]
+        var = z[rows].var(axis=0)
+        cands = np.nonzero(var >= var.max() * (1 - REBLOCK_VAR_REL))[0]
+        if not any(z[left, c].max() <= z[right, c].min() + REBLOCK_KEY_ABS for c in cands):
+            return False, "split at %d (n %d) not separated on %s" % (s, n, list(cands))
+    return True, ""
+
+
+def reblock_margins(z, perm, left_rows, block=128):
+    """Smallest margins of the oracle's own splits: the relative gap between
+    the largest and second-largest coordinate variance, and the gap between
+    the left group's largest and the right group's smallest split value."""
+    vgap, kgap = np.inf, np.inf
+    for s, n, nl in reblock_splits(z.shape[0], left_rows, block):
+        rows, left, right = perm[s:s + n], perm[s:s + nl], perm[s + nl:s + n]
+        var = z[rows].var(axis=0)
+        order = np.argsort(-var, kind="stable")
+        c = order[0]
+        vgap = min(vgap, (var[c] - var[order[1]]) / var[c] if var[c] > 0 else 0.0)
+        kgap = min(kgap, z[right, c].min() - z[left, c].max())
+    return vgap, kgap

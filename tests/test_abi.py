@@ -21,7 +21,8 @@ def test_library_exports_every_declared_symbol():
     L = bsa.lib()
     names = _declared_functions()
     assert {"bsa_pool", "bsa_select", "bsa_forward", "bsa_workspace_bytes",
-            "bsa_status_str", "bsa_select_tokens", "bsa_forward_tokens"} <= set(names)
+            "bsa_status_str", "bsa_select_tokens", "bsa_forward_tokens", "bsa_reblock",
+            "bsa_reblock_workspace_bytes", "bsa_permute_rows", "bsa_unpermute_rows"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -166,3 +167,43 @@ def test_extra_token_entry_points_validate():
                                 fake, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, fake, fake,
                                 16, fake, None) == bsa.BSA_ERR_WORKSPACE
+
+
+def test_reblock_entry_points_validate():
+    L = bsa.lib()
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    big = 1 << 40
+    p = bsa.make_problem(1, 2, 4096, top_k=8)
+    # workspace: float32 chunk moments, the three terms of L, z (float32),
+    # keys and an order buffer
+    n = bsa.bsa_reblock_workspace_bytes(p)
+    expect = 2 * 2 * 128 * 128 * 4 + 2 * 3 * 128 * 128 * 2 + 2 * 4096 * 128 * 4 + 2 * 2 * 4096 * 4
+    assert expect <= n <= expect + 5 * 256
+    assert L.bsa_reblock(ctypes.byref(p), None, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_reblock(ctypes.byref(p), fake, fake, None, fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_reblock(ctypes.byref(p), odd, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_reblock(ctypes.byref(p), fake, fake, fake, None, big, None) == bsa.BSA_ERR_WORKSPACE
+    assert L.bsa_reblock(ctypes.byref(p), fake, fake, fake, fake, n - 1, None) == bsa.BSA_ERR_WORKSPACE
+    assert L.bsa_permute_rows(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake,
+                              None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_permute_rows(ctypes.byref(p), fake, fake, fake, odd, fake, fake, fake,
+                              None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_unpermute_rows(ctypes.byref(p), fake, None, fake, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_unpermute_rows(ctypes.byref(p), fake, fake, odd, None) == bsa.BSA_ERR_INVALID
+    # options that name rows by position are refused by all three calls
+    size = ctypes.c_size_t()
+    for q in (bsa.make_problem(1, 2, 4096, top_k=8, sink_rows=100),
+              bsa.make_problem(1, 2, 4096, top_k=8, summary="reweight", anchor_rows=4000)):
+        assert L.bsa_reblock_workspace_bytes(ctypes.byref(q), ctypes.byref(size)) == bsa.BSA_ERR_UNSUPPORTED
+        assert L.bsa_reblock(ctypes.byref(q), fake, fake, fake, fake, big, None) == bsa.BSA_ERR_UNSUPPORTED
+        assert L.bsa_permute_rows(ctypes.byref(q), fake, fake, fake, fake, fake, fake, fake,
+                                  None) == bsa.BSA_ERR_UNSUPPORTED
+        assert L.bsa_unpermute_rows(ctypes.byref(q), fake, fake, fake, None) == bsa.BSA_ERR_UNSUPPORTED
+    # an anchor over every row does not depend on the order
+    for rows in (0, 4096):
+        q = bsa.make_problem(1, 2, 4096, top_k=8, summary="reweight", anchor_rows=rows)
+        assert bsa.bsa_reblock_workspace_bytes(q) == n
+    bad = bsa.make_problem(1, 2, 4096, top_k=8)
+    bad.head_dim = 64
+    assert L.bsa_reblock_workspace_bytes(ctypes.byref(bad), ctypes.byref(size)) == bsa.BSA_ERR_UNSUPPORTED

@@ -1,0 +1,185 @@
+"""GPU parity of Spark-Reblock: the permutation against the float64 oracle,
+then the whole path on the GPU's order against the oracle run on that order.
+
+The permutation must equal the oracle's wherever the oracle's own splits are
+decided by more than the float32 rounding of the GPU's embedding; elsewhere
+every GPU split is checked for validity against the float64 embedding
+(tests/parity.py: check_partition).  Downstream of the permutation the
+checks are those of the other parity tests, on the permuted rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_25_amd as bsa
+from block_sparse_attention_25_amd.synth import WORKLOADS, custom, generate
+from oracle import bsa_oracle as O
+from tests.parity import (REBLOCK_KEY_ABS, REBLOCK_VAR_REL, check_partition, reblock_margins,
+                          to_device, widen)
+from tests.test_gpu_parity import _check_head
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    sys.stdout.write(msg + "\n")
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    bsa.lib()
+    return torch
+
+
+def _gpu_perm(torch, qb, kb):
+    q, k = to_device(qb), to_device(kb)
+    B, H, N, _ = q.shape
+    p = bsa.make_problem(B, H, N, top_k=0)
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    ws = torch.empty(bsa.bsa_reblock_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    bsa.bsa_reblock(p, q, k, perm, ws)
+    torch.cuda.synchronize()
+    return perm.cpu().numpy()
+
+
+def _check_perm(gperm, Q, K, label):
+    """One head: valid against the float64 embedding; equal to the oracle's
+    order when its margins exceed the tolerances.  Returns True if equal."""
+    z = O.mahalanobis_embedding(Q, K)
+    ok, msg = check_partition(z, gperm, O.reblock_left_rows)
+    assert ok, "%s: %s" % (label, msg)
+    want = O.reblock_permutation(Q, K)
+    vgap, kgap = reblock_margins(z, want, O.reblock_left_rows)
+    same = np.array_equal(gperm, want)
+    _log("  %s: equal %s, oracle margins: variance %.2g, split value %.2g" % (label, same, vgap, kgap))
+    if vgap > REBLOCK_VAR_REL and kgap > REBLOCK_KEY_ABS:
+        assert same, label + ": differs from the oracle's order away from near-ties"
+    return same
+
+
+@pytest.mark.parametrize("N", [100, 128, 129, 1000, 4173])
+def test_reblock_permutation(torch_cuda, N):
+    _log("case reblock perm N=%d" % N)
+    qb, kb, _ = generate(custom(N, heads=2, seed=60), threads=2)
+    gperm = _gpu_perm(torch_cuda, qb, kb)
+    for h in range(2):
+        _check_perm(gperm[0, h], widen(qb[0, h]), widen(kb[0, h]), "N=%d h%d" % (N, h))
+
+
+def test_reblock_hand_partition(torch_cuda):
+    # four clusters of unit vectors in coordinates 0, 1 and isotropic keys:
+    # the order is fixed by hand (the oracle's pin), here through bf16 inputs
+    N = 512
+    rng = np.random.default_rng(61)
+    centers = {0: (1.0, 0.5), 1: (1.0, -0.5), 2: (-1.0, 0.5), 3: (-1.0, -0.5)}
+    q = np.zeros((N, 128), dtype=np.float32)
+    for i in range(N):
+        a, b = centers[i % 4]
+        q[i, 0], q[i, 1] = a / np.hypot(a, b), b / np.hypot(a, b)
+    q += 1e-3 * rng.standard_normal((N, 128)).astype(np.float32)
+    k = np.zeros((N, 128), dtype=np.float32)
+    k[np.arange(N), np.arange(N) % 128] = np.sqrt(128.0)
+    from block_sparse_attention_25_amd.synth import bf16_bits
+    qb, kb = bf16_bits(q)[None, None], bf16_bits(k)[None, None]
+    gperm = _gpu_perm(torch_cuda, qb, kb)[0, 0]
+    want = np.concatenate([np.arange(N)[np.arange(N) % 4 == c] for c in (3, 2, 1, 0)])
+    assert np.array_equal(gperm, want)
+
+
+def test_reblock_zero_keys_and_rows(torch_cuda):
+    # zero keys leave only the ridge (z = q / |q|); a zero query row stays zero
+    N = 700
+    qb, _, _ = generate(custom(N, heads=1, seed=62), threads=1)
+    qb = qb.copy()
+    qb[0, 0, 5] = 0
+    kb = np.zeros_like(qb)
+    gperm = _gpu_perm(torch_cuda, qb, kb)
+    _check_perm(gperm[0, 0], widen(qb[0, 0]), widen(kb[0, 0]), "zero keys")
+
+
+def _permuted(torch, host, perm, qb, kb, vb):
+    """The inputs and the un-permuted GPU output in the GPU's order, per head."""
+    B, H = qb.shape[:2]
+    idx = [[perm[b, h] for h in range(H)] for b in range(B)]
+    qp, kp, vp = (np.stack([np.stack([x[b, h][idx[b][h]] for h in range(H)]) for b in range(B)])
+                  for x in (qb, kb, vb))
+    out = host["out"]
+    pt = torch.from_numpy(perm.astype(np.int64)).to(out.device)
+    host = dict(host)
+    host["out"] = torch.stack([torch.stack([out[b, h][pt[b, h]] for h in range(H)]) for b in range(B)])
+    return host, qp, kp, vp
+
+
+def _run_reblocked(torch, qb, kb, vb, **kw):
+    q, k, v = (to_device(x) for x in (qb, kb, vb))
+    out, aux = bsa.attention(q, k, v, return_aux=True, reblock=True, **kw)
+    torch.cuda.synchronize()
+    host = {n: aux[n].cpu() for n in ("q_pool", "k_pool", "sum_k", "sum_v", "sum_bias", "block_idx")}
+    host["token_idx"] = None if aux["token_idx"] is None else aux["token_idx"].cpu()
+    host["out"] = out
+    return host, aux["perm"].cpu().numpy()
+
+
+@pytest.mark.parametrize("N,top_k,summary,tau,extra", [
+    (4173, 8, "mean", None, 0),
+    (4173, 6, "reweight", None, 0),
+    (4096, 32, "mean", 1.0, 0),
+    (2000, 4, "mean", None, 64),
+])
+def test_reblock_attention(torch_cuda, N, top_k, summary, tau, extra):
+    _log("case reblock attention N=%d k=%d %s tau=%s extra=%d" % (N, top_k, summary, tau, extra))
+    qb, kb, vb = generate(custom(N, heads=2, seed=63), threads=2)
+    host, perm = _run_reblocked(torch_cuda, qb, kb, vb, top_k=top_k, summary=summary, tau=tau,
+                                extra_tokens=extra)
+    host_p, qp, kp, vp = _permuted(torch_cuda, host, perm, qb, kb, vb)
+    for h in range(2):
+        _check_perm(perm[0, h], widen(qb[0, h]), widen(kb[0, h]), "N=%d h%d" % (N, h))
+        _check_head(host_p, qp, kp, vp, 0, h, top_k, summary, 0, label="reblock", tau=tau,
+                    extra=extra)
+
+
+def test_reblock_rejects_position_options(torch_cuda):
+    qb, kb, vb = generate(custom(1000, heads=1, seed=64), threads=1)
+    q, k, v = (to_device(x) for x in (qb, kb, vb))
+    with pytest.raises(ValueError):
+        bsa.attention(q, k, v, top_k=2, sink_rows=100, reblock=True)
+    with pytest.raises(ValueError):
+        bsa.attention(q, k, v, top_k=2, summary="reweight", anchor_rows=900, reblock=True)
+    # an anchor over every row is the same in any order
+    bsa.attention(q, k, v, top_k=2, summary="reweight", anchor_rows=1000, reblock=True)
+
+
+def test_reblock_deterministic(torch_cuda):
+    qb, kb, vb = generate(custom(4173, heads=2, seed=65), threads=2)
+    a = _run_reblocked(torch_cuda, qb, kb, vb, top_k=8)
+    b = _run_reblocked(torch_cuda, qb, kb, vb, top_k=8)
+    assert np.array_equal(a[1], b[1])
+    assert torch_cuda.equal(a[0]["out"], b[0]["out"])
+
+
+@pytest.mark.parametrize("heads", [[0, 29]])
+def test_reblock_full_size_sampled(torch_cuda, heads):
+    """768p 5s on the Spark-Reblock order, every head in one launch as in the
+    benchmark: the permutation of two heads against the oracle, then their
+    indices and sampled query blocks."""
+    w = WORKLOADS["768p_5s_reblock"]
+    _log("case full %s (H=%d N=%d)" % (w.name, w.heads, w.seq_len))
+    qb, kb, vb = generate(w, threads=16)
+    nb = O.n_blocks(w.seq_len)
+    top_k = O.k_from_ratio(w.top_k_ratio, nb)
+    host, perm = _run_reblocked(torch_cuda, qb, kb, vb, top_k_ratio=w.top_k_ratio)
+    for h in range(w.heads):
+        assert np.array_equal(np.sort(perm[0, h]), np.arange(w.seq_len))
+    for h in heads:
+        _check_perm(perm[0, h], widen(qb[0, h]), widen(kb[0, h]), "768p h%d" % h)
+    # downstream checks on the selected heads, in the GPU's order
+    sel = {n: (None if t is None else t[:, heads]) for n, t in host.items()}
+    host_p, qp, kp, vp = _permuted(torch_cuda, sel, perm[:, heads], qb[:, heads], kb[:, heads],
+                                   vb[:, heads])
+    qbs = [0, 1, nb // 2, nb - 2, nb - 1]
+    for i, h in enumerate(heads):
+        _check_head(host_p, qp, kp, vp, 0, i, top_k, query_blocks=qbs, label="768p reblock h%d" % h)
