@@ -4,7 +4,9 @@
 One step = bsa_pool + bsa_select + bsa_forward over one batch of synthetic
 input already resident in HBM (the 768p 5s shape by default: 56 heads x
 37,740 tokens, head_dim 128, top_k 64 of 295 blocks, mean summaries); with
-extra tokens, bsa_select_tokens + bsa_forward_tokens in place of bsa_forward.
+extra tokens, bsa_select_tokens + bsa_forward_tokens in place of bsa_forward;
+on the Spark-Reblock order, bsa_reblock + bsa_permute_rows before and
+bsa_unpermute_rows after.
 
 Prints one JSON line.  `value` is the effective TFLOP/s of a whole step
 counting only the selected blocks' attention FLOPs, 4 * 128 * sum_r n_r *
@@ -126,6 +128,9 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
     t0 = time.perf_counter()
     for h in range(qb.shape[1]):
         Q, K, V = (bf16_to_f32(x[0, h]).astype(np.float64) for x in (qb, kb, vb))
+        if w.reblock:
+            perm = O.reblock_permutation(Q, K)
+            Q, K, V = Q[perm], K[perm], V[perm]
         qp, kp = O.pool_mean(Q), O.pool_mean(K)
         sc_ = O.block_scores(qp, kp)
         idx = O.select_topk(sc_, top_k, sinks) if w.tau is None else \
@@ -150,10 +155,10 @@ def cpu_baseline(w, qb, kb, vb, budget_s):
         heads_done += 1
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle", "host": host,
-            "sample": "%d query blocks (%d whole heads of %d, each with its pool, scores, top-k%s and "
+            "sample": "%d query blocks (%d whole heads of %d, each with its %spool, scores, top-k%s and "
                       "summaries) of the %s workload; %.1f s wall"
-                      % (blocks_done, heads_done, qb.shape[1], ", extra tokens" if w.extra else "",
-                         w.name, dt)}
+                      % (blocks_done, heads_done, qb.shape[1], "reblock order, " if w.reblock else "",
+                         ", extra tokens" if w.extra else "", w.name, dt)}
 
 
 def main():
@@ -200,23 +205,37 @@ def main():
     ws = torch.empty(bsa.bsa_workspace_bytes(p), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     tok = torch.empty((B, H, nb, w.extra), dtype=torch.int32, device=dev) if w.extra else None
+    if w.reblock:
+        perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+        rws = torch.empty(bsa.bsa_reblock_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        qr, kr, vr = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        out_r = torch.empty_like(q)
+    else:
+        qr, kr, vr, out_r = q, k, v, out
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
 
     def step(e=None):
         if e: e[0].record()
-        bsa.bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws)
+        if w.reblock:
+            bsa.bsa_reblock(p, q, k, perm, rws)
+            bsa.bsa_permute_rows(p, perm, q, k, v, qr, kr, vr)
         if e: e[1].record()
-        bsa.bsa_select(p, q_pool, k_pool, idx)
+        bsa.bsa_pool(p, qr, kr, vr, q_pool, k_pool, sum_k, sum_v, sum_bias, ws)
         if e: e[2].record()
-        if tok is not None:
-            bsa.bsa_select_tokens(p, q_pool, k, idx, tok, ws)
+        bsa.bsa_select(p, q_pool, k_pool, idx)
         if e: e[3].record()
         if tok is not None:
-            bsa.bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx, tok, ws, out)
-        else:
-            bsa.bsa_forward(p, q, k, sum_k, sum_bias, idx, ws, out)
+            bsa.bsa_select_tokens(p, q_pool, kr, idx, tok, ws)
         if e: e[4].record()
+        if tok is not None:
+            bsa.bsa_forward_tokens(p, qr, kr, vr, sum_k, sum_bias, idx, tok, ws, out_r)
+        else:
+            bsa.bsa_forward(p, qr, kr, sum_k, sum_bias, idx, ws, out_r)
+        if e: e[5].record()
+        if w.reblock:
+            bsa.bsa_unpermute_rows(p, perm, out_r, out)
+        if e: e[6].record()
 
     for _ in range(args.warmup):
         step()
@@ -226,12 +245,11 @@ def main():
         step(ev[i])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
-    pool_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    sel_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-    tok_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps
-    attn_ms = sum(e[3].elapsed_time(e[4]) for e in ev) / args.steps
-    step_ms = sum(e[0].elapsed_time(e[4]) for e in ev) / args.steps
-    step_med = float(np.median([e[0].elapsed_time(e[4]) for e in ev]))
+    def span(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in ev) / args.steps
+    reblock_ms, pool_ms, sel_ms, tok_ms, attn_ms, unperm_ms = (span(i, i + 1) for i in range(6))
+    step_ms = span(0, 6)
+    step_med = float(np.median([e[0].elapsed_time(e[6]) for e in ev]))
     flops, summary_flops = counted_flops(torch, idx, N, nb, H, B, dense, tok)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
@@ -264,11 +282,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": N, "head_dim": 128,
                    "n_blocks": nb, "top_k": kk, "summary": w.summary,
-                   "sink_rows": w.sink_rows, "tau": w.tau, "extra_tokens": w.extra},
+                   "sink_rows": w.sink_rows, "tau": w.tau, "extra_tokens": w.extra,
+                   "reblock": w.reblock},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"pool": round(pool_ms, 4), "select": round(sel_ms, 4),
                        "attention": round(attn_ms, 4),
-                       **({"select_tokens": round(tok_ms, 4)} if tok is not None else {})},
+                       **({"select_tokens": round(tok_ms, 4)} if tok is not None else {}),
+                       **({"reblock_and_permute": round(reblock_ms, 4),
+                           "unpermute": round(unperm_ms, 4)} if w.reblock else {})},
         "wall_ms_per_step": round(wall_ms, 4),
         "median_ms_per_step": round(step_med, 4),
         "counted_tflop_per_step": round(flops / 1e12, 4),
