@@ -22,14 +22,19 @@
 // Kernels:
 //   rb_moment_kernel    K^T K over 2048-row chunks on the matrix cores (bf16
 //                       products are exact; float32 sums within a chunk)
-//   rb_factor_kernel    the chunks summed in float64 (fixed order), the ridge,
-//                       Cholesky in LDS (float64), L split into three bf16
-//                       terms whose sum is the float32 value of each entry
+//   rb_msum_kernel      the chunks summed in float64 (fixed order)
+//   rb_factor_kernel    the ridge, Cholesky in LDS (float64), L split into
+//                       three bf16 terms whose sum is the float32 value of
+//                       each entry
 //   rb_embed_kernel     z = Q L on the matrix cores (three terms), each row
 //                       normalised (float32); the identity order
-//   rb_level_kernel     one level of the bisection, one workgroup per group:
-//                       float64 coordinate variances, a radix select of the
-//                       split value, a stable partition of the group's rows
+//   rb_stats_kernel     one level of the bisection, first half: float64 sums of
+//                       z and z^2 per coordinate over 128-position slices
+//   rb_split_*_kernel   second half, per group: the coordinate of largest
+//                       variance, the split value (a radix select, or a
+//                       bitwise search for small groups), a stable partition
+//                       of the group's rows (one wavefront per group up to
+//                       1024 rows, else one workgroup)
 //   rb_permute_kernel   rows of Q, K, V gathered into the new order
 //   rb_unpermute_kernel output rows put back in their original places
 #include <hip/hip_runtime.h>
@@ -68,7 +73,10 @@ __device__ __forceinline__ uint32_t rb_key(float x) {
 // One workgroup of 4 wavefronts per (chunk of 2048 key rows, batch x head).
 // Each 64-row step is staged in LDS transposed (feature-major), so that both
 // MFMA operands of K^T K read 8 consecutive rows of one feature in 16 bytes.
-// Wavefront w owns the 32 x 128 output stripe of features 32 w + [0, 32).
+// Thread t loads 8 features (piece t mod 16) of rows 4 (t / 16) + [0, 4) and
+// writes each feature's 4 values in one 8-byte store; the next step's rows
+// are loaded while this step's MFMAs run.  Wavefront w owns the 32 x 128
+// output stripe of features 32 w + [0, 32).
 constexpr int MT_STRIDE = 64 + 8;  // LDS row stride (elements) of the transposed step
 
 __global__ __launch_bounds__(256) void rb_moment_kernel(const uint16_t* __restrict__ k,
@@ -78,28 +86,38 @@ __global__ __launch_bounds__(256) void rb_moment_kernel(const uint16_t* __restri
   const size_t bh = blockIdx.x / nchunk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
+  const int c8 = tid & 15, tq = tid >> 4;
   const uint16_t* kb = k + bh * (size_t)N * RB_HD;
   const int r0 = chunk * RB_CHUNK, r1 = min(N, r0 + RB_CHUNK);
+  // rows past the chunk read its last row and are zeroed when staged
+  auto load = [&](int t0, uint4* pc) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      pc[u] = *(const uint4*)(kb + (size_t)min(t0 + 4 * tq + u, r1 - 1) * RB_HD + 8 * c8);
+  };
   f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  uint4 pc[4];
+  load(r0, pc);
   for (int t0 = r0; t0 < r1; t0 += 64) {
-    // 64 rows x 128 features = 1024 pieces of 8 features, four per thread
-    uint4 piece[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = tid + 256 * u, row = x >> 4, c8 = x & 15;
-      piece[u] = t0 + row < r1 ? *(const uint4*)(kb + (size_t)(t0 + row) * RB_HD + 8 * c8)
-                               : make_uint4(0u, 0u, 0u, 0u);
-    }
     __syncthreads();  // the previous step's operand reads are done
+    uint32_t w[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int x = tid + 256 * u, row = x >> 4, c8 = x & 15;
-      const uint32_t w[4] = {piece[u].x, piece[u].y, piece[u].z, piece[u].w};
+      const bool ok = t0 + 4 * tq + u < r1;
+      w[u][0] = ok ? pc[u].x : 0u;
+      w[u][1] = ok ? pc[u].y : 0u;
+      w[u][2] = ok ? pc[u].z : 0u;
+      w[u][3] = ok ? pc[u].w : 0u;
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        kt[(8 * c8 + e) * MT_STRIDE + row] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+    for (int e = 0; e < 8; ++e) {
+      uint32_t h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) h[u] = (e & 1) ? (w[u][e >> 1] >> 16) : (w[u][e >> 1] & 0xFFFFu);
+      *(uint2*)&kt[(8 * c8 + e) * MT_STRIDE + 4 * tq] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
     }
     __syncthreads();
+    load(t0 + 64, pc);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 a = *(const bf16x8*)&kt[(32 * wave + ln) * MT_STRIDE + 16 * s + 8 * g];
@@ -122,22 +140,43 @@ __global__ __launch_bounds__(256) void rb_moment_kernel(const uint16_t* __restri
     }
 }
 
+// M = (1/N) times the sum of the chunk partials, float64, added in chunk
+// order; one thread per entry, 64 workgroups per (batch, head).
+__global__ __launch_bounds__(256) void rb_msum_kernel(const float* __restrict__ part, double* __restrict__ msum,
+                                                      int N, int nchunk) {
+  const int x = (blockIdx.x & 63) * 256 + threadIdx.x;
+  const size_t bh = blockIdx.x >> 6;
+  const float* pb = part + bh * (size_t)nchunk * RB_HD * RB_HD + x;
+  double s = 0.0;
+  int c = 0;
+  for (; c + 4 <= nchunk; c += 4) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = pb[(size_t)(c + u) * RB_HD * RB_HD];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s += (double)v[u];
+  }
+  for (; c < nchunk; ++c) s += (double)pb[(size_t)c * RB_HD * RB_HD];
+  msum[bh * RB_HD * RB_HD + x] = s / (double)N;
+}
+
 // ------------------------------------------------------------ factor ---
 // One workgroup of 1024 threads per (batch, head): M in LDS (float64), the
 // ridge, a right-looking Cholesky on the lower triangle, then L^T written as
 // three bfloat16 terms per entry (rows d = output coordinate, columns e =
 // query feature), the B operand of z = q L.
-__global__ __launch_bounds__(1024) void rb_factor_kernel(const float* __restrict__ part,
-                                                         uint16_t* __restrict__ ltw, int N, int nchunk) {
+__global__ __launch_bounds__(1024) void rb_factor_kernel(const double* __restrict__ msum,
+                                                         uint16_t* __restrict__ ltw) {
   __shared__ double A[RB_HD][RB_HD + 1];
+  __shared__ double piv[RB_HD];
   __shared__ double ridge_s;
   const size_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
-  const float* pb = part + bh * (size_t)nchunk * RB_HD * RB_HD;
-  for (int x = tid; x < RB_HD * RB_HD; x += 1024) {
-    double s = 0.0;
-    for (int c = 0; c < nchunk; ++c) s += (double)pb[(size_t)c * RB_HD * RB_HD + x];
-    A[x / RB_HD][x % RB_HD] = s / (double)N;
+  const double* mb = msum + bh * RB_HD * RB_HD;
+#pragma unroll
+  for (int u = 0; u < RB_HD * RB_HD / 1024; ++u) {
+    const int x = tid + 1024 * u;
+    A[x / RB_HD][x % RB_HD] = mb[x];
   }
   __syncthreads();
   if (tid < 64) {
@@ -150,24 +189,33 @@ __global__ __launch_bounds__(1024) void rb_factor_kernel(const float* __restrict
   const double ridge = ridge_s;
   if (tid < RB_HD) A[tid][tid] += ridge;
   __syncthreads();
+  // Right-looking elimination on the unscaled Schur complements, one barrier
+  // a step: step j subtracts A[i][j] A[c][j] / d_j from every entry (i, c),
+  // j < c <= i, with d_j = A[j][j] (held at the ridge when float32 rounding
+  // of M pushed it below); L[j][j] = sqrt(d_j), L[i][j] = A[i][j] / sqrt(d_j).
+  // Entry x of the rows below j, counted row by row, is (i, c) with
+  // x = i (i + 1) / 2 + c, c <= i.
   for (int j = 0; j < RB_HD; ++j) {
-    // a pivot that float32 rounding of M pushed below the ridge is held at it
-    if (tid == 0) A[j][j] = sqrt(fmax(A[j][j], ridge));
-    __syncthreads();
-    const double piv = A[j][j];
-    if (tid > j && tid < RB_HD) A[tid][j] /= piv;
-    __syncthreads();
+    const double dj = fmax(A[j][j], ridge);
+    if (tid == 0) piv[j] = dj;
+    const double inv = 1.0 / dj;
     const int nr = RB_HD - 1 - j;
-    for (int x = tid; x < nr * nr; x += 1024) {
-      const int i = j + 1 + x / nr, c = j + 1 + x % nr;
-      if (c <= i) A[i][c] -= A[i][j] * A[c][j];
+    const int tot = nr * (nr + 1) / 2;
+    for (int x = tid; x < tot; x += 1024) {
+      int i = (int)((sqrtf(8.0f * (float)x + 1.0f) - 1.0f) * 0.5f);
+      if ((i + 1) * (i + 2) / 2 <= x) ++i;
+      if (i * (i + 1) / 2 > x) --i;
+      const int c = x - i * (i + 1) / 2;
+      A[j + 1 + i][j + 1 + c] -= A[j + 1 + i][j] * A[j + 1 + c][j] * inv;
     }
     __syncthreads();
   }
+  if (tid < RB_HD) piv[tid] = sqrt(piv[tid]);
+  __syncthreads();
   uint16_t* lb = ltw + bh * 3 * (size_t)RB_HD * RB_HD;
   for (int x = tid; x < RB_HD * RB_HD; x += 1024) {
     const int d = x / RB_HD, e = x % RB_HD;
-    const float f = e >= d ? (float)A[e][d] : 0.f;
+    const float f = e > d ? (float)(A[e][d] / piv[d]) : e == d ? (float)piv[d] : 0.f;
     const uint16_t hi = rb_f2bf(f);
     const float r1 = f - rb_bf2f(hi);  // exact
     const uint16_t mid = rb_f2bf(r1);
@@ -179,81 +227,166 @@ __global__ __launch_bounds__(1024) void rb_factor_kernel(const float* __restrict
 }
 
 // ------------------------------------------------------------- embed ---
-// One workgroup of 4 wavefronts per (256 rows, batch x head); wavefront w
-// takes rows 64 w + [0, 64) as two 32-row tiles against the four 32-column
-// tiles of z.  The three terms of L^T sit in LDS with the 16-byte piece c of
-// row d stored at piece c ^ (d mod 16), so that the 32 rows a B-operand read
-// touches fall into different banks.
-__global__ __launch_bounds__(256) void rb_embed_kernel(const uint16_t* __restrict__ q,
-                                                       const uint16_t* __restrict__ ltw,
-                                                       float* __restrict__ zh, int32_t* __restrict__ order0,
-                                                       int N, int ntile) {
+// One workgroup of 8 wavefronts per (1024 rows, batch x head).  The product
+// is taken transposed, z^T = L^T Q^T, so that lane l of a wavefront's 32-row
+// tile holds 64 of the 128 coordinates of row l (the other 64 in lane l ^ 32):
+// a row's squared norm is a local sum and one exchange.  The A operands (the
+// three terms of L^T) come from LDS, with the 16-byte piece c of row d stored
+// at piece c ^ (d mod 16); the B operands are the tile's Q rows, the next
+// tile's loaded during this tile's 96 MFMAs (four independent chains).
+constexpr int EM_ROWS = 1024;
+constexpr int EM_WAVES = 8;
+
+__global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ ltw,
+                                                                 float* __restrict__ zh,
+                                                                 int32_t* __restrict__ order0, int N,
+                                                                 int ntile) {
   __shared__ __attribute__((aligned(16))) uint16_t lb[3 * RB_HD * RB_HD];
   const int tile = blockIdx.x % ntile;
   const size_t bh = blockIdx.x / ntile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, ln = lane & 31;
-  const int row0 = tile * 256;
+  const int row0 = tile * EM_ROWS;
   {
     const uint4* src = (const uint4*)(ltw + bh * 3 * (size_t)RB_HD * RB_HD);
-    for (int x = tid; x < 3 * RB_HD * 16; x += 256) {
+    for (int x = tid; x < 3 * RB_HD * 16; x += 64 * EM_WAVES) {
       const int t = x / (RB_HD * 16), d = (x >> 4) % RB_HD, c = x & 15;
       *(uint4*)&lb[(t * RB_HD + d) * RB_HD + 8 * (c ^ (d & 15))] = src[x];
     }
   }
-  if (row0 + tid < N) order0[bh * N + row0 + tid] = row0 + tid;
+  for (int i = tid; i < EM_ROWS; i += 64 * EM_WAVES)
+    if (row0 + i < N) order0[bh * N + row0 + i] = row0 + i;
   __syncthreads();
-  f32x16 acc[2][4];
+  const int nrows = min(EM_ROWS, N - row0);
+  const int ntl = (nrows + 31) / 32;  // 32-row tiles; wavefront w takes w, w + 8, ...
+  // rows past N read row N - 1; nothing is stored for them
+  auto load_b = [&](int t, uint4* dst) {
+    const int qi = min(row0 + 32 * t + ln, N - 1);
+    const uint16_t* qr = q + (bh * (size_t)N + (size_t)qi) * RB_HD;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int tj = 0; tj < 4; ++tj) acc[rt][tj] = f32x16{};
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int qi = row0 + 64 * wave + 32 * rt + ln;
-    const uint16_t* qrow = q + (bh * (size_t)N + (size_t)min(qi, N - 1)) * RB_HD;
+    for (int s = 0; s < 8; ++s) dst[s] = *(const uint4*)(qr + 16 * s + 8 * g);
+  };
+  float* zb = zh + bh * (size_t)N * RB_HD;
+  uint4 bq[8], bn[8];
+  int t = wave;
+  if (t < ntl) load_b(t, bq);
+  for (; t < ntl; t += EM_WAVES) {
+    load_b(min(t + EM_WAVES, ntl - 1), bn);
+    f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      uint4 u = *(const uint4*)(qrow + 16 * s + 8 * g);
-      if (qi >= N) u = make_uint4(0u, 0u, 0u, 0u);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
       for (int term = 2; term >= 0; --term)
 #pragma unroll
-        for (int tj = 0; tj < 4; ++tj) {
-          const int d = 32 * tj + ln;
-          const bf16x8 b = *(const bf16x8*)&lb[(term * RB_HD + d) * RB_HD + 8 * ((2 * s + g) ^ (d & 15))];
-          acc[rt][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[rt][tj], 0, 0, 0);
+        for (int mt = 0; mt < 4; ++mt) {
+          const int d = 32 * mt + ln;
+          const bf16x8 av = *(const bf16x8*)&lb[(term * RB_HD + d) * RB_HD + 8 * ((2 * s + g) ^ (d & 15))];
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, bq[s]), acc[mt], 0, 0, 0);
         }
+      // keep each k-step's twelve operand reads next to its MFMAs (hoisting
+      // all of them would not fit the registers)
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // element e of tile mt: coordinate 32 mt + 8 (e / 4) + 4 g + e % 4 of row ln
+    float ss = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ss += acc[mt][e] * acc[mt][e];
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+    const int row = row0 + 32 * t + ln;
+    if (row < N) {
+      float* zr = zb + (size_t)row * RB_HD + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(float4*)(zr + 32 * mt + 8 * j) = make_float4(acc[mt][4 * j] * inv, acc[mt][4 * j + 1] * inv,
+                                                         acc[mt][4 * j + 2] * inv, acc[mt][4 * j + 3] * inv);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bq[s] = bn[s];
   }
-  // element a of tile (rt, tj): row 8 (a / 4) + 4 g + a % 4 of the row tile,
-  // coordinate 32 tj + ln; a row's 128 coordinates live in the 32 lanes of
-  // one half-wave
-  float* zb = zh + bh * (size_t)N * RB_HD;
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int a = 0; a < 16; ++a) {
-      float ss = 0.f;
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) ss += acc[rt][tj][a] * acc[rt][tj][a];
-#pragma unroll
-      for (int off = 16; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-      const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-      const int row = row0 + 64 * wave + 32 * rt + 8 * (a >> 2) + 4 * g + (a & 3);
-      if (row < N) {
-#pragma unroll
-        for (int tj = 0; tj < 4; ++tj) zb[(size_t)row * RB_HD + 32 * tj + ln] = acc[rt][tj][a] * inv;
-      }
-    }
 }
 
 // ------------------------------------------------------------- level ---
-constexpr int LV_THREADS = 1024;
-constexpr int LV_WAVES = LV_THREADS / 64;
+// One level of the bisection in two kernels.  rb_stats_kernel sums z and z^2
+// per coordinate over each 128-position slice of the current order (groups
+// start on multiples of 128, so a slice lies in one group); rb_split_kernel
+// takes one group per workgroup, adds its slices' sums in slice order, picks
+// the split coordinate, selects the split value and partitions the rows.
+
+// the group [s, s + n) that holds position pos after `level` splits (the
+// tree's shape depends on N only); a finished leaf keeps its range
+__device__ __forceinline__ void rb_group_of(int N, int level, int pos, int& s, int& n) {
+  s = 0;
+  n = N;
+  for (int t = 0; t < level; ++t) {
+    const int m = (n + RB_BLK - 1) / RB_BLK;
+    if (m <= 1) break;
+    const int nl = RB_BLK * ((m + 1) / 2);
+    if (pos >= s + nl) {
+      s += nl;
+      n -= nl;
+    } else {
+      n = nl;
+    }
+  }
+}
+
+// One workgroup of 4 wavefronts per (slice, batch x head); wavefront w sums
+// rows w + 4 i of the slice, lane l coordinates 2 l and 2 l + 1, with eight
+// row loads in flight.  stats[bh][slice][0 | 1][d]: sums of z_d and z_d^2.
+__global__ __launch_bounds__(256) void rb_stats_kernel(const float* __restrict__ zh,
+                                                       const int32_t* __restrict__ pin,
+                                                       double* __restrict__ stats, int N, int nb, int level) {
+  __shared__ double red[2][4][RB_HD];
+  const int c = blockIdx.x % nb;
+  const size_t bh = blockIdx.x / nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int s, n;
+  rb_group_of(N, level, c * RB_BLK, s, n);
+  if (n <= RB_BLK) return;  // a leaf: no split to prepare
+  const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
+  const float* zb = zh + bh * (size_t)N * RB_HD;
+  // lane i < 32 holds the row of slice position wave + 4 i; positions past
+  // the end of a short last slice read its last row and are weighted out, so
+  // every load is unconditional and all eight are in flight together
+  const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
+  double s1x = 0.0, s1y = 0.0, s2x = 0.0, s2y = 0.0;
+#pragma unroll
+  for (int i0 = 0; i0 < 32; i0 += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = __builtin_amdgcn_readlane(myrow, i0 + u);
+      v[u] = *(const float2*)(zb + (size_t)r * RB_HD + 2 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double w = wave + 4 * (i0 + u) < cnt ? 1.0 : 0.0;
+      const double x = (double)v[u].x, y = (double)v[u].y;
+      s1x += w * x;
+      s1y += w * y;
+      s2x += w * x * x;
+      s2y += w * y * y;
+    }
+  }
+  red[0][wave][2 * lane] = s1x;
+  red[0][wave][2 * lane + 1] = s1y;
+  red[1][wave][2 * lane] = s2x;
+  red[1][wave][2 * lane + 1] = s2y;
+  __syncthreads();
+  if (tid < 2 * RB_HD) {
+    const int a = tid >> 7, d = tid & (RB_HD - 1);
+    stats[((bh * nb + c) * 2 + a) * RB_HD + d] = red[a][0][d] + red[a][1][d] + red[a][2][d] + red[a][3][d];
+  }
+}
 
 // exclusive prefix over the workgroup of two counters (x, y) per thread
+template <int W>
 __device__ __forceinline__ void block_scan2(int& x, int& y, int (*wt)[2], int lane, int wave) {
   int ix = x, iy = y;
 #pragma unroll
@@ -278,28 +411,17 @@ __device__ __forceinline__ void block_scan2(int& x, int& y, int (*wt)[2], int la
   y = by + iy - y;
 }
 
-// One level of the bisection.  Workgroup (bh, g) follows the bits of g from
-// the root to its group [s, s + n) of the current order; a path that enters a
-// finished leaf with a 1 bit is empty, one with 0 bits carries the leaf over.
-__global__ __launch_bounds__(LV_THREADS) void rb_level_kernel(const float* __restrict__ zh,
-                                                              const int32_t* __restrict__ pin,
-                                                              int32_t* __restrict__ pout,
-                                                              uint32_t* __restrict__ keys, int N, int level) {
-  __shared__ double red[2][LV_WAVES][RB_HD];
-  __shared__ uint32_t hist[256];
-  __shared__ int wt[LV_WAVES][2];
-  __shared__ int sh_d, sh_digit, sh_want;
-  const int ng = 1 << level;
-  const int gi = blockIdx.x % ng;
-  const size_t bh = blockIdx.x / ng;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  int s = 0, n = N;
+// The group [s, s + n) of workgroup-or-wavefront g at `level`, following the
+// bits of g from the root: a path that enters a finished leaf with a 1 bit is
+// empty (returns false); one with 0 bits carries the leaf over.
+__device__ __forceinline__ bool rb_locate(int N, int level, int gi, int& s, int& n) {
+  s = 0;
+  n = N;
   for (int t = level - 1; t >= 0; --t) {
     const int m = (n + RB_BLK - 1) / RB_BLK;
     const int bit = (gi >> t) & 1;
     if (m <= 1) {
-      if (bit) return;
+      if (bit) return false;
       continue;
     }
     const int nl = RB_BLK * ((m + 1) / 2);
@@ -310,89 +432,347 @@ __global__ __launch_bounds__(LV_THREADS) void rb_level_kernel(const float* __res
       n = nl;
     }
   }
+  return true;
+}
+
+// the split coordinate of a wavefront that holds the variances of
+// coordinates lane and lane + 64: the largest variance, the lowest
+// coordinate on ties (the same in every lane)
+__device__ __forceinline__ int rb_argmax_wave(double v0, double v1, int lane) {
+  double best = v0;
+  int bd = lane;
+  if (v1 > best) {
+    best = v1;
+    bd = lane + 64;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ob = __shfl_xor(best, off, 64);
+    const int od = __shfl_xor(bd, off, 64);
+    if (ob > best || (ob == best && od < bd)) {
+      best = ob;
+      bd = od;
+    }
+  }
+  return bd;
+}
+
+// variance of coordinate d over the group [s, s + n) of m <= 8 slices from
+// its slice sums (added in slice order; eight loads in flight)
+__device__ __forceinline__ double rb_group_var8(const double* stats_bh, int s, int n, int d) {
+  const double* sp = stats_bh + (s / RB_BLK) * 2 * RB_HD + d;
+  const int m = (n + RB_BLK - 1) / RB_BLK;
+  double va[8], vb[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    va[c] = sp[(size_t)min(c, m - 1) * 2 * RB_HD];
+    vb[c] = sp[(size_t)min(c, m - 1) * 2 * RB_HD + RB_HD];
+  }
+  double a = 0.0, b = 0.0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    a += c < m ? va[c] : 0.0;
+    b += c < m ? vb[c] : 0.0;
+  }
+  const double mu = a / n;
+  return b / n - mu * mu;
+}
+
+// Split coordinate of a group of any size, all 1024 threads of the
+// workgroup: thread t adds the slices c = t / 128 (mod 8) of coordinate
+// t mod 128 in slice order, the eight partial sums are added in order, and
+// wavefront 0 takes the largest variance (the lowest coordinate on ties).
+__device__ __forceinline__ int rb_split_coord_block(const double* stats_bh, int s, int n, double (*part)[2][RB_HD],
+                                                    int* sh_d, int tid) {
+  const int d = tid & (RB_HD - 1), p = tid >> 7;
+  const int m = (n + RB_BLK - 1) / RB_BLK;
+  const double* sp = stats_bh + (s / RB_BLK) * 2 * RB_HD + d;
+  double a = 0.0, b = 0.0;
+  for (int c0 = p; c0 < m; c0 += 32) {
+    double va[4], vb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = min(c0 + 8 * u, m - 1);
+      va[u] = sp[(size_t)c * 2 * RB_HD];
+      vb[u] = sp[(size_t)c * 2 * RB_HD + RB_HD];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a += c0 + 8 * u < m ? va[u] : 0.0;
+      b += c0 + 8 * u < m ? vb[u] : 0.0;
+    }
+  }
+  part[p][0][d] = a;
+  part[p][1][d] = b;
+  __syncthreads();
+  if (tid < 64) {
+    double v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int dd = tid + 64 * h;
+      double sa = 0.0, sb = 0.0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        sa += part[q][0][dd];
+        sb += part[q][1][dd];
+      }
+      const double mu = sa / n;
+      v[h] = sb / n - mu * mu;
+    }
+    const int bd = rb_argmax_wave(v[0], v[1], tid);
+    if (tid == 0) *sh_d = bd;
+  }
+  __syncthreads();
+  return *sh_d;
+}
+
+// Groups of at most 1024 rows: one wavefront per group, four per workgroup,
+// no workgroup barriers.  Lane l owns positions [l C, l C + C), C <= 16, keys
+// and rows in registers; the split value is found bit by bit from the top
+// (the smallest key with at least n_left keys at or below it).
+constexpr int WS_KPT = 16;
+
+__global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restrict__ zh,
+                                                            const double* __restrict__ stats,
+                                                            const int32_t* __restrict__ pin,
+                                                            int32_t* __restrict__ pout, int N, int nb, int level,
+                                                            int total) {
+  const int lane = threadIdx.x & 63;
+  const int G = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (G >= total) return;
+  const int gi = G & ((1 << level) - 1);
+  const size_t bh = (size_t)(G >> level);
+  int s, n;
+  if (!rb_locate(N, level, gi, s, n)) return;
   const int32_t* pi = pin + bh * N + s;
   int32_t* po = pout + bh * N + s;
   const int m = (n + RB_BLK - 1) / RB_BLK;
   if (m <= 1) {
-    for (int j = tid; j < n; j += LV_THREADS) po[j] = pi[j];
+    for (int j = lane; j < n; j += 64) po[j] = pi[j];
     return;
   }
   const int nl = RB_BLK * ((m + 1) / 2);
+  const double* sb = stats + bh * nb * 2 * RB_HD;
+  const int dstar = rb_argmax_wave(rb_group_var8(sb, s, n, lane), rb_group_var8(sb, s, n, lane + 64), lane);
   const float* zb = zh + bh * (size_t)N * RB_HD;
-  uint32_t* kb = keys + bh * N + s;
+  const int C = (n + 63) / 64;
+  const int j0 = lane * C;
+  int32_t pr[WS_KPT];
+  uint32_t kr[WS_KPT];
+#pragma unroll
+  for (int u = 0; u < WS_KPT; ++u) pr[u] = pi[min(j0 + u, n - 1)];
+  float x[WS_KPT];
+#pragma unroll
+  for (int u = 0; u < WS_KPT; ++u) x[u] = zb[(size_t)pr[u] * RB_HD + dstar];
+#pragma unroll
+  for (int u = 0; u < WS_KPT; ++u) kr[u] = rb_key(x[u]);
+  auto valid = [&](int u) { return u < C && j0 + u < n; };
+  // counts by ballot: no cross-lane data movement
+  auto count_le = [&](uint32_t cand) {
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < WS_KPT; ++u) c += __popcll(__ballot(valid(u) && kr[u] <= cand));
+    return c;
+  };
+  uint32_t Tk = 0u;
+  for (int bit = 31; bit >= 0; --bit)
+    if (count_le(Tk | ((1u << bit) - 1u)) < nl) Tk |= 1u << bit;
+  int lt = 0, eq = 0;
+#pragma unroll
+  for (int u = 0; u < WS_KPT; ++u) {
+    lt += (valid(u) && kr[u] < Tk) ? 1 : 0;
+    eq += (valid(u) && kr[u] == Tk) ? 1 : 0;
+  }
+  const int need = nl - (Tk ? count_le(Tk - 1u) : 0);  // keys equal to Tk that go left, the first in order
+  int ilt = lt, ieq = eq;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ox = __shfl_up(ilt, off, 64), oy = __shfl_up(ieq, off, 64);
+    if (lane >= off) {
+      ilt += ox;
+      ieq += oy;
+    }
+  }
+  lt = ilt - lt;
+  eq = ieq - eq;
+#pragma unroll
+  for (int u = 0; u < WS_KPT; ++u) {
+    if (valid(u)) {
+      const uint32_t key = kr[u];
+      const int before_left = lt + min(eq, need);
+      const bool left = key < Tk || (key == Tk && eq < need);
+      po[min(left ? before_left : nl + (j0 + u - before_left), n - 1)] = pr[u];
+      lt += key < Tk;
+      eq += key == Tk;
+    }
+  }
+}
 
-  // (1) sums of z and z^2 per coordinate (float64): wavefront w takes rows
-  // w, w + 16, ...; lane l coordinates 2 l and 2 l + 1
+// Larger groups: one workgroup of 1024 threads per group, thread t owning
+// positions [t C, t C + C), C <= KPT, keys and rows in registers; the split
+// value by an MSB-first radix select, 8 bits a pass.
+template <int KPT>
+__global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restrict__ zh,
+                                                            const double* __restrict__ stats,
+                                                            const int32_t* __restrict__ pin,
+                                                            int32_t* __restrict__ pout, int N, int nb, int level) {
+  constexpr int T = 1024, W = T / 64;
+  __shared__ uint32_t hist[256];
+  __shared__ int wt[W][2];
+  __shared__ double part[8][2][RB_HD];
+  __shared__ int sh_d, sh_digit, sh_want;
+  const int ng = 1 << level;
+  const int gi = blockIdx.x % ng;
+  const size_t bh = blockIdx.x / ng;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int s, n;
+  if (!rb_locate(N, level, gi, s, n)) return;
+  const int32_t* pi = pin + bh * N + s;
+  int32_t* po = pout + bh * N + s;
+  const int m = (n + RB_BLK - 1) / RB_BLK;
+  if (m <= 1) {
+    for (int j = tid; j < n; j += T) po[j] = pi[j];
+    return;
+  }
+  const int nl = RB_BLK * ((m + 1) / 2);
+  const int dstar = rb_split_coord_block(stats + bh * nb * 2 * RB_HD, s, n, part, &sh_d, tid);
+  const float* zb = zh + bh * (size_t)N * RB_HD;
+  const int C = (n + T - 1) / T;
+  const int j0 = min(n, tid * C);
+  uint32_t kr[KPT];
   {
-    double s1x = 0.0, s1y = 0.0, s2x = 0.0, s2y = 0.0;
-    for (int j = wave; j < n; j += 4 * LV_WAVES) {
-      int r[4];
+    int32_t pr[KPT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) r[u] = j + u * LV_WAVES < n ? pi[j + u * LV_WAVES] : -1;
-      float2 v[4];
+    for (int u = 0; u < KPT; ++u) pr[u] = pi[(uint32_t)min(j0 + u, n - 1)];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        v[u] = r[u] >= 0 ? *(const float2*)(zb + (size_t)r[u] * RB_HD + 2 * lane) : make_float2(0.f, 0.f);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        s1x += (double)v[u].x;
-        s1y += (double)v[u].y;
-        s2x += (double)v[u].x * (double)v[u].x;
-        s2y += (double)v[u].y * (double)v[u].y;
-      }
-    }
-    red[0][wave][2 * lane] = s1x;
-    red[0][wave][2 * lane + 1] = s1y;
-    red[1][wave][2 * lane] = s2x;
-    red[1][wave][2 * lane + 1] = s2y;
+    for (int u = 0; u < KPT; ++u) kr[u] = rb_key(zb[(uint32_t)(pr[u] * RB_HD + dstar)]);
   }
-  __syncthreads();
-  if (wave == 0) {
-    double best = -1.0;
-    int bd = 0;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int d = lane + 64 * h;
-      double a = 0.0, b = 0.0;
-      for (int w = 0; w < LV_WAVES; ++w) {
-        a += red[0][w][d];
-        b += red[1][w][d];
-      }
-      const double mu = a / n;
-      const double var = b / n - mu * mu;
-      if (var > best) {
-        best = var;
-        bd = d;
-      }
-    }
-    // largest variance, the lowest coordinate on ties
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const double ob = __shfl_xor(best, off, 64);
-      const int od = __shfl_xor(bd, off, 64);
-      if (ob > best || (ob == best && od < bd)) {
-        best = ob;
-        bd = od;
-      }
-    }
-    if (lane == 0) sh_d = bd;
-  }
-  __syncthreads();
-  const int dstar = sh_d;
+  auto valid = [&](int u) { return u < C && j0 + u < n; };
 
-  // (2) keys of the split coordinate, in group order
-  for (int j = tid; j < n; j += LV_THREADS) kb[j] = rb_key(zb[(size_t)pi[j] * RB_HD + dstar]);
-  __syncthreads();
-
-  // (3) the key of rank nl - 1: MSB-first radix select, 8 bits a pass
   uint32_t prefix = 0u, pmask = 0u;
   int want = nl - 1;
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    for (int j = tid; j < n; j += LV_THREADS) {
-      const uint32_t key = kb[j];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (valid(u) && (kr[u] & pmask) == prefix) atomicAdd(&hist[(kr[u] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
+                     h3 = hist[4 * lane + 3];
+      const int c = (int)(h0 + h1 + h2 + h3);
+      int incl = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      int before = incl - c;
+      if (before <= want && want < incl) {
+        const uint32_t hh[4] = {h0, h1, h2, h3};
+        int dg = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (dg == e && before + (int)hh[e] <= want) {
+            before += (int)hh[e];
+            dg = e + 1;
+          }
+        }
+        sh_digit = 4 * lane + dg;
+        sh_want = want - before;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh_digit << shift;
+    pmask |= 255u << shift;
+    want = sh_want;
+  }
+  const uint32_t Tk = prefix;
+  const int need = want + 1;
+  int lt = 0, eq = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    lt += (valid(u) && kr[u] < Tk) ? 1 : 0;
+    eq += (valid(u) && kr[u] == Tk) ? 1 : 0;
+  }
+  block_scan2<W>(lt, eq, wt, lane, wave);
+  // the rows again (all loads in flight together), rather than held in
+  // registers through the select
+  int32_t pr[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) pr[u] = pi[(uint32_t)min(j0 + u, n - 1)];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    if (valid(u)) {
+      const uint32_t key = kr[u];
+      const int before_left = lt + min(eq, need);
+      const bool left = key < Tk || (key == Tk && eq < need);
+      po[min(left ? before_left : nl + (j0 + u - before_left), n - 1)] = pr[u];
+      lt += key < Tk;
+      eq += key == Tk;
+    }
+  }
+}
+
+// The largest groups (more than 20 rows per thread of 1024): one workgroup
+// per group, keys in the global key buffer (read from L2 in every pass, eight
+// loads in flight), the split value by an MSB-first radix select.
+__global__ __launch_bounds__(1024) void rb_split_big_kernel(const float* __restrict__ zh,
+                                                            const double* __restrict__ stats,
+                                                            const int32_t* __restrict__ pin,
+                                                            int32_t* __restrict__ pout,
+                                                            uint32_t* __restrict__ keys, int N, int nb, int level) {
+  constexpr int T = 1024, W = T / 64, U = 8;
+  __shared__ uint32_t hist[256];
+  __shared__ int wt[W][2];
+  __shared__ double part[8][2][RB_HD];
+  __shared__ int sh_d, sh_digit, sh_want;
+  const int ng = 1 << level;
+  const int gi = blockIdx.x % ng;
+  const size_t bh = blockIdx.x / ng;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int s, n;
+  if (!rb_locate(N, level, gi, s, n)) return;
+  const int32_t* pi = pin + bh * N + s;
+  int32_t* po = pout + bh * N + s;
+  const int m = (n + RB_BLK - 1) / RB_BLK;
+  if (m <= 1) {
+    for (int j = tid; j < n; j += T) po[j] = pi[j];
+    return;
+  }
+  const int nl = RB_BLK * ((m + 1) / 2);
+  const int dstar = rb_split_coord_block(stats + bh * nb * 2 * RB_HD, s, n, part, &sh_d, tid);
+  const float* zb = zh + bh * (size_t)N * RB_HD;
+  uint32_t* kb = keys + bh * N + s;
+
+  // keys of the split coordinate, in group order; positions past the end
+  // read the last row and store nothing
+  for (int j0 = tid; j0 < n; j0 += U * T) {
+    int r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = pi[(uint32_t)min(j0 + u * T, n - 1)];
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = zb[(uint32_t)(r[u] * RB_HD + dstar)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j0 + u * T < n) kb[j0 + u * T] = rb_key(x[u]);
+  }
+  __syncthreads();
+
+  uint32_t prefix = 0u, pmask = 0u;
+  int want = nl - 1;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    for (int j0 = tid; j0 < n; j0 += U * T) {
+      uint32_t k8[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) k8[u] = kb[(uint32_t)min(j0 + u * T, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (j0 + u * T < n && (k8[u] & pmask) == prefix) atomicAdd(&hist[(k8[u] >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -425,28 +805,47 @@ __global__ __launch_bounds__(LV_THREADS) void rb_level_kernel(const float* __res
     pmask |= 255u << shift;
     want = sh_want;
   }
-  const uint32_t T = prefix;
-  const int need = want + 1;  // keys equal to T that go left, the first in order
+  const uint32_t Tk = prefix;
+  const int need = want + 1;  // keys equal to Tk that go left, the first in order
 
-  // (4) stable partition: thread t takes positions [t C, t C + C)
-  const int C = (n + LV_THREADS - 1) / LV_THREADS;
+  // stable partition: thread t takes positions [t C, t C + C), read in
+  // batches of eight
+  const int C = (n + T - 1) / T;
   const int j0 = min(n, tid * C), j1 = min(n, j0 + C);
   int lt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = kb[j];
-    lt += key < T;
-    eq += key == T;
+  for (int j = j0; j < j1; j += U) {
+    uint32_t k8[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) k8[u] = kb[(uint32_t)min(j + u, j1 - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j + u < j1) {
+        lt += k8[u] < Tk;
+        eq += k8[u] == Tk;
+      }
   }
-  block_scan2(lt, eq, wt, lane, wave);
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = kb[j];
-    const int before_left = lt + min(eq, need);
-    const bool left = key < T || (key == T && eq < need);
-    // the counts place every row inside [0, n); the clamp only keeps a
-    // miscount from writing outside the group
-    po[min(left ? before_left : nl + (j - before_left), n - 1)] = pi[j];
-    lt += key < T;
-    eq += key == T;
+  block_scan2<W>(lt, eq, wt, lane, wave);
+  for (int j = j0; j < j1; j += U) {
+    uint32_t k8[U];
+    int32_t r8[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      k8[u] = kb[(uint32_t)min(j + u, j1 - 1)];
+      r8[u] = pi[(uint32_t)min(j + u, j1 - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (j + u < j1) {
+        const uint32_t key = k8[u];
+        const int before_left = lt + min(eq, need);
+        const bool left = key < Tk || (key == Tk && eq < need);
+        // the counts place every row inside [0, n); the clamp only keeps a
+        // miscount from writing outside the group
+        po[min(left ? before_left : nl + (j + u - before_left), n - 1)] = r8[u];
+        lt += key < Tk;
+        eq += key == Tk;
+      }
+    }
   }
 }
 
@@ -489,7 +888,7 @@ struct RbGeom {
 };
 
 struct RbLayout {
-  size_t part, ltw, zh, keys, perm, total;
+  size_t part, msum, ltw, zh, keys, perm, stats, total;
 };
 
 size_t rb_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -512,7 +911,8 @@ int rb_geometry(const bsa_problem* p, RbGeom* g) {
   g->nchunk = (int)((g->N + RB_CHUNK - 1) / RB_CHUNK);
   // 1-D grids: work-items per launch must fit 32 bits
   const int64_t lv_wg = g->levels > 0 ? (int64_t(1) << (g->levels - 1)) : 1;
-  if (g->BH * lv_wg * LV_THREADS >= (int64_t(1) << 32)) return BSA_ERR_UNSUPPORTED;
+  if (g->BH * lv_wg * 1024 >= (int64_t(1) << 32)) return BSA_ERR_UNSUPPORTED;
+  if (g->BH * g->nb * 256 >= (int64_t(1) << 32)) return BSA_ERR_UNSUPPORTED;
   if (g->BH * ((g->N + 15) / 16) * 256 >= (int64_t(1) << 32)) return BSA_ERR_UNSUPPORTED;
   return BSA_OK;
 }
@@ -522,6 +922,8 @@ RbLayout rb_layout(const RbGeom& g) {
   size_t off = 0;
   w.part = off;
   off = rb_align(off + (size_t)g.BH * g.nchunk * RB_HD * RB_HD * sizeof(float));
+  w.msum = off;
+  off = rb_align(off + (size_t)g.BH * RB_HD * RB_HD * sizeof(double));
   w.ltw = off;
   off = rb_align(off + (size_t)g.BH * 3 * RB_HD * RB_HD * sizeof(uint16_t));
   w.zh = off;
@@ -530,6 +932,8 @@ RbLayout rb_layout(const RbGeom& g) {
   off = rb_align(off + (size_t)g.BH * g.N * sizeof(uint32_t));
   w.perm = off;
   off = rb_align(off + (size_t)g.BH * g.N * sizeof(int32_t));
+  w.stats = off;
+  off = rb_align(off + (size_t)g.BH * g.nb * 2 * RB_HD * sizeof(double));
   w.total = off;
   return w;
 }
@@ -573,14 +977,40 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
   const int N = (int)g.N;
   hipLaunchKernelGGL(rb_moment_kernel, dim3((unsigned)(g.BH * g.nchunk)), dim3(256), 0, s,
                      (const uint16_t*)k, part, N, g.nchunk);
-  hipLaunchKernelGGL(rb_factor_kernel, dim3((unsigned)g.BH), dim3(1024), 0, s, (const float*)part, ltw, N,
+  double* msum = (double*)(ws + w.msum);
+  hipLaunchKernelGGL(rb_msum_kernel, dim3((unsigned)(g.BH * 64)), dim3(256), 0, s, (const float*)part, msum, N,
                      g.nchunk);
-  const int ntile = (N + 255) / 256;
-  hipLaunchKernelGGL(rb_embed_kernel, dim3((unsigned)(g.BH * ntile)), dim3(256), 0, s, (const uint16_t*)q,
+  hipLaunchKernelGGL(rb_factor_kernel, dim3((unsigned)g.BH), dim3(1024), 0, s, (const double*)msum, ltw);
+  const int ntile = (N + EM_ROWS - 1) / EM_ROWS;
+  hipLaunchKernelGGL(rb_embed_kernel, dim3((unsigned)(g.BH * ntile)), dim3(64 * EM_WAVES), 0, s, (const uint16_t*)q,
                      (const uint16_t*)ltw, zh, buf[0], N, ntile);
-  for (int l = 0; l < g.levels; ++l)
-    hipLaunchKernelGGL(rb_level_kernel, dim3((unsigned)(g.BH << l)), dim3(LV_THREADS), 0, s, (const float*)zh,
-                       (const int32_t*)buf[l & 1], buf[(l + 1) & 1], keys, N, l);
+  double* stats = (double*)(ws + w.stats);
+  const int nb = (int)g.nb;
+  for (int l = 0; l < g.levels; ++l) {
+    hipLaunchKernelGGL(rb_stats_kernel, dim3((unsigned)(g.BH * nb)), dim3(256), 0, s, (const float*)zh,
+                       (const int32_t*)buf[l & 1], stats, N, nb, l);
+    // largest group at this level: 128 ceil(nb / 2^l) rows
+    const int64_t largest = (int64_t)RB_BLK * ((g.nb + (int64_t(1) << l) - 1) >> l);
+    const int64_t per = (largest + 1023) / 1024;  // rows per thread of a 1024-thread workgroup
+    const dim3 grid((unsigned)(g.BH << l));
+    const float* zc = zh;
+    const double* sc = stats;
+    const int32_t* pin = buf[l & 1];
+    int32_t* pout = buf[(l + 1) & 1];
+    if (largest <= 64 * WS_KPT) {
+      const int total = (int)(g.BH << l);
+      hipLaunchKernelGGL(rb_split_wave_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, zc, sc, pin,
+                         pout, N, nb, l, total);
+    } else if (per <= 4) {
+      hipLaunchKernelGGL((rb_split_reg_kernel<4>), grid, dim3(1024), 0, s, zc, sc, pin, pout, N, nb, l);
+    } else if (per <= 12) {
+      hipLaunchKernelGGL((rb_split_reg_kernel<12>), grid, dim3(1024), 0, s, zc, sc, pin, pout, N, nb, l);
+    } else if (per <= 20) {
+      hipLaunchKernelGGL((rb_split_reg_kernel<20>), grid, dim3(1024), 0, s, zc, sc, pin, pout, N, nb, l);
+    } else {
+      hipLaunchKernelGGL(rb_split_big_kernel, grid, dim3(1024), 0, s, zc, sc, pin, pout, keys, N, nb, l);
+    }
+  }
   return rb_status();
 }
 
