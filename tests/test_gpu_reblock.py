@@ -161,25 +161,42 @@ def test_reblock_deterministic(torch_cuda):
     assert torch_cuda.equal(a[0]["out"], b[0]["out"])
 
 
-@pytest.mark.parametrize("heads", [[0, 29]])
-def test_reblock_full_size_sampled(torch_cuda, heads):
-    """768p 5s on the Spark-Reblock order, every head in one launch as in the
-    benchmark: the permutation of two heads against the oracle, then their
-    indices and sampled query blocks."""
-    w = WORKLOADS["768p_5s_reblock"]
-    _log("case full %s (H=%d N=%d)" % (w.name, w.heads, w.seq_len))
+def test_reblock_batch_of_two(torch_cuda):
+    # rows of batch 1 must be ordered and attended within batch 1
+    w = custom(3000, heads=2, seed=66)
+    qb, kb, vb = generate(w, threads=2)
+    qb2, kb2, vb2 = generate(custom(3000, heads=2, seed=67), threads=2)
+    qb, kb, vb = (np.concatenate([a, b]) for a, b in ((qb, qb2), (kb, kb2), (vb, vb2)))
+    host, perm = _run_reblocked(torch_cuda, qb, kb, vb, top_k=5)
+    host_p, qp, kp, vp = _permuted(torch_cuda, host, perm, qb, kb, vb)
+    for b in range(2):
+        for h in range(2):
+            _check_perm(perm[b, h], widen(qb[b, h]), widen(kb[b, h]), "batch %d h%d" % (b, h))
+    _check_head(host_p, qp, kp, vp, 1, 1, 5, label="reblock batch 1")
+
+
+@pytest.mark.parametrize("name,heads", [("768p_5s_reblock", [0, 29]), ("2k_5s", [7])])
+def test_reblock_full_size_sampled(torch_cuda, name, heads):
+    """Full-size heads on the Spark-Reblock order, every head in one launch as
+    in the benchmark: the permutation of a few heads against the oracle, then
+    their indices and sampled query blocks (2K: 11 levels, the largest groups
+    through the global key buffer)."""
+    w = WORKLOADS[name]
+    _log("case full %s reblock (H=%d N=%d)" % (w.name, w.heads, w.seq_len))
     qb, kb, vb = generate(w, threads=16)
     nb = O.n_blocks(w.seq_len)
-    top_k = O.k_from_ratio(w.top_k_ratio, nb)
-    host, perm = _run_reblocked(torch_cuda, qb, kb, vb, top_k_ratio=w.top_k_ratio)
+    ratio = w.top_k_ratio
+    top_k = O.k_from_ratio(ratio, nb) if ratio is not None else w.top_k
+    kw = dict(top_k_ratio=ratio) if ratio is not None else dict(top_k=top_k)
+    host, perm = _run_reblocked(torch_cuda, qb, kb, vb, **kw)
     for h in range(w.heads):
         assert np.array_equal(np.sort(perm[0, h]), np.arange(w.seq_len))
     for h in heads:
-        _check_perm(perm[0, h], widen(qb[0, h]), widen(kb[0, h]), "768p h%d" % h)
+        _check_perm(perm[0, h], widen(qb[0, h]), widen(kb[0, h]), "%s h%d" % (name, h))
     # downstream checks on the selected heads, in the GPU's order
     sel = {n: (None if t is None else t[:, heads]) for n, t in host.items()}
     host_p, qp, kp, vp = _permuted(torch_cuda, sel, perm[:, heads], qb[:, heads], kb[:, heads],
                                    vb[:, heads])
     qbs = [0, 1, nb // 2, nb - 2, nb - 1]
     for i, h in enumerate(heads):
-        _check_head(host_p, qp, kp, vp, 0, i, top_k, query_blocks=qbs, label="768p reblock h%d" % h)
+        _check_head(host_p, qp, kp, vp, 0, i, top_k, query_blocks=qbs, label="%s reblock h%d" % (name, h))
