@@ -16,7 +16,7 @@ import block_sparse_attention_25_amd as bsa
 from block_sparse_attention_25_amd.synth import WORKLOADS, custom, generate
 from oracle import bsa_oracle as O
 from tests.parity import (REBLOCK_KEY_ABS, REBLOCK_VAR_REL, check_partition, reblock_margins,
-                          to_device, widen)
+                          tensor_bits, to_device, widen)
 from tests.test_gpu_parity import _check_head
 
 pytestmark = pytest.mark.gpu
@@ -151,6 +151,50 @@ def test_reblock_rejects_position_options(torch_cuda):
         bsa.attention(q, k, v, top_k=2, summary="reweight", anchor_rows=900, reblock=True)
     # an anchor over every row is the same in any order
     bsa.attention(q, k, v, top_k=2, summary="reweight", anchor_rows=1000, reblock=True)
+
+
+def test_reblock_all_zero_inputs(torch_cuda):
+    # zero keys leave only the ridge and zero queries embed to zero: every
+    # split value ties, so the order is the identity; every logit is 0 (the
+    # selection ties too: the three lowest blocks)
+    torch = torch_cuda
+    N = 1500
+    qb = np.zeros((1, 1, N, 128), dtype=np.uint16)
+    _, _, vb = generate(custom(N, heads=1, seed=68), threads=1)
+    host, perm = _run_reblocked(torch, qb, qb, vb, top_k=3)
+    assert np.array_equal(perm[0, 0], np.arange(N))
+    Q, V = widen(qb[0, 0]), widen(vb[0, 0])
+    want = O.run_head_reblocked(Q, Q, V, perm[0, 0], top_k=3)["out"]
+    got = widen(tensor_bits(host["out"][0, 0]))
+    assert np.abs(got - want).max() < 1e-2
+
+
+def test_reblock_guard_bands_untouched(torch_cuda):
+    """perm and the permuted and unpermuted rows written into poisoned
+    buffers: every element inside written, the guard regions after them
+    untouched."""
+    torch = torch_cuda
+    N, H, G = 1000, 2, 4096
+    qb, kb, vb = generate(custom(N, heads=H, seed=69), threads=2)
+    q, k, v = (to_device(x) for x in (qb, kb, vb))
+    p = bsa.make_problem(1, H, N, top_k=3)
+    n_rows = H * N * 128
+    perm = torch.full((H * N + G,), -7, dtype=torch.int32, device="cuda")
+    outs = [torch.full((n_rows + G,), float("nan"), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+            for _ in range(4)]
+    ws = torch.empty(bsa.bsa_reblock_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    bsa.bsa_reblock(p, q, k, perm, ws)
+    bsa.bsa_permute_rows(p, perm, q, k, v, outs[0], outs[1], outs[2])
+    bsa.bsa_unpermute_rows(p, perm, outs[0], outs[3])
+    torch.cuda.synchronize()
+    pc = perm.cpu()
+    assert bool((pc[:H * N] >= 0).all()) and bool((pc[H * N:] == -7).all())
+    for i, o in enumerate(outs):
+        oc = o.cpu().float()
+        assert not bool(torch.isnan(oc[:n_rows]).any()), i
+        assert bool(torch.isnan(oc[n_rows:]).all()), i
+    # permute then unpermute gives Q back, bit for bit
+    assert torch.equal(outs[3][:n_rows].view(1, H, N, 128), q)
 
 
 def test_reblock_deterministic(torch_cuda):
