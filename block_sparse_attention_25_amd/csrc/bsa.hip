@@ -1058,14 +1058,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 // inputs that matter" (extra_tokens: the top-scoring tokens each query block
 // reads beyond its chosen blocks, 256 by default).
 //
-// token_select_kernel: one workgroup of 4 wavefronts per 32 query blocks of
-// one (b, h), on a 1-D grid remapped like the select kernel.
-//  - Scores on the matrix cores: C^T = K Qs^T, Qs holding every pooled query
-//    split exactly into three bfloat16 terms (hi + mid + lo equals the float32
-//    value), so each product is exact and the sums are float32.  Lane l of the
-//    accumulator holds query block l % 32 and 16 of the 32 tokens of a tile;
-//    the feature order inside the products is free, so a lane's K operand is
-//    128 contiguous bytes of its token row.
+// token_select_kernel: one workgroup of 8 wavefronts (two per SIMD) per 32
+// query blocks of one (b, h), on a 1-D grid remapped like the select kernel.
+//  - Scores on the matrix cores (16x16x32 bf16): C^T = K Qs^T, Qs holding
+//    every pooled query split exactly into three bfloat16 terms (hi + mid +
+//    lo equals the float32 value), so each product is exact and the sums are
+//    float32.  Wavefront w scores tokens 32 (w % 4) + [0, 32) of every block
+//    against query blocks 16 (w / 4) + [0, 16); lane l of an accumulator
+//    holds query block l % 16 and 4 tokens.  The feature order inside the
+//    products is free, so each load reads 64 contiguous bytes of a token row.
 //  - Each query block keeps a candidate list in LDS of 64-bit keys: the
 //    order-preserving float32 score above, the complemented token index below
 //    (so equal scores rank the lower token higher).  A token enters when the
