@@ -118,6 +118,9 @@ __global__ __launch_bounds__(256) void rb_moment_kernel(const uint16_t* __restri
     }
     __syncthreads();
     load(t0 + 64, pc);
+    // keep the next step's loads ahead of this step's MFMAs (left to itself
+    // the scheduler sinks them past the MFMAs, next to their first use)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 a = *(const bf16x8*)&kt[(32 * wave + ln) * MT_STRIDE + 16 * s + 8 * g];
