@@ -544,8 +544,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
         } else {
           const bool is_eq = key[i] == T;
           const uint64_t em = __ballot(is_eq);
-          sel = key[i] > T || (is_eq && eq_before + __popcll(em & lt) < need_eq);
-          eq_before += __popcll(em);
+          sel = key[i] > T || (is_eq && eq_before + (int)__popcll(em & lt) < need_eq);
+          eq_before += (int)__popcll(em);
         }
         const uint64_t sm = __ballot(sel);
         if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
@@ -882,8 +882,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   };
 
   // Region A of a half tile: the 16 MFMAs of S(t+1) = K(t+1) Q^T, each
-  // followed by one slice of the softmax of S(t), in a fixed order (hard
-  // scheduling fences between slots).  Slot work:
+  // followed by one slice of the softmax of S(t).  Slot work:
   //   0-3   scale (+ additive term) and running max over 8 of the 32 values
   //   4     exchange the max with the partner lane (l ^ 32)
   //   5     new reference max, rescale factor
@@ -958,7 +957,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       }
       kop0 = kop1;
       kop1 = kop2;
-      __builtin_amdgcn_sched_barrier(0);
+      // no scheduling fence here: the compiler's own interleaving of the
+      // slots measures about 1.5% faster than a fixed slot order
     }
     l_run = psum;
     return alpha;
