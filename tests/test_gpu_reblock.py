@@ -197,6 +197,18 @@ def test_reblock_guard_bands_untouched(torch_cuda):
     assert torch.equal(outs[3][:n_rows].view(1, H, N, 128), q)
 
 
+def test_reblock_maximum_size(torch_cuda):
+    """The largest supported sequence, ragged: 2,048 blocks, 11 levels, the
+    top groups through the global key buffer (256 rows a thread)."""
+    N = 262100
+    _log("case reblock maximum size N=%d" % N)
+    qb, kb, vb = generate(custom(N, heads=1, seed=70), threads=16)
+    host, perm = _run_reblocked(torch_cuda, qb, kb, vb, top_k=64)
+    _check_perm(perm[0, 0], widen(qb[0, 0]), widen(kb[0, 0]), "max N")
+    host_p, qp, kp, vp = _permuted(torch_cuda, host, perm, qb, kb, vb)
+    _check_head(host_p, qp, kp, vp, 0, 0, 64, query_blocks=[0, 1024, 2046, 2047], label="reblock max")
+
+
 def test_reblock_deterministic(torch_cuda):
     qb, kb, vb = generate(custom(4173, heads=2, seed=65), threads=2)
     a = _run_reblocked(torch_cuda, qb, kb, vb, top_k=8)
