@@ -620,7 +620,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
     const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ tok_idx, uint16_t* __restrict__ out, int N, int nb, int krow, int nsb,
-    float scale_log2, int total_wg, int f0, int f1, int E) {
+    float scale_log2, int total_wg, int chunk, int f0, int f1, int E) {
   // LDS buffers as distinct variables, so the compiler can tell the DMA
   // targets from the buffers being read
   __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
@@ -629,12 +629,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ uint32_t selmask[BSA_MAX_BLOCKS / 32];
   __shared__ int32_t sidx[BSA_MAX_BLOCKS];  // this query block's selected blocks
 
-  const int logical = xcd_remap(blockIdx.x, total_wg);
-  // each head's query blocks in sequence order starting at the first sink
-  // block, so the longer dense sink rows are dispatched first (identity when
-  // there are no sinks, f0 = 0)
-  const int r = (logical % nb + f0) % nb;
-  const size_t bh = (size_t)(logical / nb);
+  // Workgroup -> (b, h, query block).  Workgroups are dealt to the 8 XCDs
+  // round-robin.  With chunk = 0 each XCD takes a contiguous range of (head,
+  // query block), each head's query blocks in sequence order starting at the
+  // first sink block (so the longer dense sink rows are dispatched first).
+  // With chunk > 0 XCD x takes query blocks [x chunk, x chunk + chunk) of
+  // every head in turn, so the XCDs all work on the same one or two heads at
+  // a time and their L2 misses meet in the memory-side cache, while each L2
+  // still sees neighbouring query blocks; padding workgroups past nb leave at
+  // once.
+  int rr;
+  size_t bh;
+  if (chunk > 0) {
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    rr = x * chunk + j % chunk;
+    bh = (size_t)(j / chunk);
+    if (rr >= nb) return;  // uniform over the workgroup, before any barrier
+  } else {
+    const int logical = xcd_remap(blockIdx.x, total_wg);
+    rr = logical % nb;
+    bh = (size_t)(logical / nb);
+  }
+  const int r = (rr + f0) % nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
   const int g = lane >> 5, ln = lane & 31;
@@ -1677,9 +1693,9 @@ int make_geometry(const bsa_problem* p, Geometry* g) {
   g->reweight = p->summary == BSA_SUMMARY_REWEIGHT;
   g->anchor_rows = p->anchor_rows == 0 ? p->seq_len : p->anchor_rows;
   g->scale = p->scale == 0.f ? 1.0 / sqrt((double)HD) : (double)p->scale;
-  // the attention launch is a 1-D grid of 256-thread workgroups, and a grid
-  // dimension counts work-items in 32 bits
-  if (g->B * g->H * g->nb * 256 >= (1ll << 32)) return BSA_ERR_UNSUPPORTED;
+  // the attention launch is a 1-D grid of 256-thread workgroups (at most
+  // 8 ceil(nb / 8) per head), and a grid dimension counts work-items in 32 bits
+  if (g->B * g->H * (8 * ((g->nb + 7) / 8)) * 256 >= (1ll << 32)) return BSA_ERR_UNSUPPORTED;
   return BSA_OK;
 }
 
@@ -1742,13 +1758,20 @@ int launch_attention(const Geometry& g, const void* q, const void* k, const void
                      const float* sum_bias, const int32_t* block_idx, const char* ws, const void* v,
                      const int32_t* tok_idx, void* out, hipStream_t stream) {
   const WsLayout w = ws_layout(g);
-  const int total = (int)(g.B * g.H * g.nb);
+  // The head-synchronous map (8 chunks of ceil(nb / 8) query blocks per head)
+  // once the K and V^T of eight heads, one per XCD, would pass 192 MiB
+  // (nb > 384); below that, and with sinks, one contiguous range per XCD.
+  // Measured inside whole steps: 4.9% faster at 1,045 blocks, 0.7% at 574,
+  // 0.7% slower at 295 (there the XCDs' own heads still share the
+  // memory-side cache, and a 37-block chunk puts two heads in each L2).
+  const int chunk = (g.f1 < g.f0 && g.nb > 384) ? (int)((g.nb + 7) / 8) : 0;
+  const int total = chunk > 0 ? (int)(g.B * g.H * 8 * chunk) : (int)(g.B * g.H * g.nb);
   const float scale_log2 = (float)(g.scale * 1.4426950408889634);
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, stream, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)(ws + w.vt), (const uint16_t*)sum_k,
                      (const uint16_t*)(ws + w.svt), sum_bias, block_idx, (const uint16_t*)v, tok_idx,
-                     (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, (int)g.f0,
-                     (int)g.f1, tok_idx ? g.E : 0);
+                     (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, chunk,
+                     (int)g.f0, (int)g.f1, tok_idx ? g.E : 0);
   return launch_status();
 }
 
