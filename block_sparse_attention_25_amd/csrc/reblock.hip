@@ -29,7 +29,9 @@
 //   rb_embed_kernel     z = Q L on the matrix cores (three terms), each row
 //                       normalised (float32); the identity order
 //   rb_stats_kernel     one level of the bisection, first half: float64 sums of
-//                       z and z^2 per coordinate over 128-position slices
+//                       z and z^2 per coordinate over 128-position slices of
+//                       the root and of left children (a right child's sums
+//                       are its parent's less its left sibling's)
 //   rb_split_*_kernel   second half, per group: the coordinate of largest
 //                       variance, the split value (a radix select, or a
 //                       bitwise search for small groups), a stable partition
@@ -317,20 +319,26 @@ __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t*
 // ------------------------------------------------------------- level ---
 // One level of the bisection in two kernels.  rb_stats_kernel sums z and z^2
 // per coordinate over each 128-position slice of the current order (groups
-// start on multiples of 128, so a slice lies in one group); rb_split_kernel
-// takes one group per workgroup, adds its slices' sums in slice order, picks
-// the split coordinate, selects the split value and partitions the rows.
+// start on multiples of 128, so a slice lies in one group), for the root and
+// the left children only; rb_split_kernel takes one group per workgroup, adds
+// its slices' sums in slice order (a right child: its left sibling's, taken
+// from the parent's totals), keeps the group's totals for its own children,
+// picks the split coordinate, selects the split value and partitions the rows.
+// Reading only the left children's rows halves the level's traffic.
 
 // the group [s, s + n) that holds position pos after `level` splits (the
-// tree's shape depends on N only); a finished leaf keeps its range
-__device__ __forceinline__ void rb_group_of(int N, int level, int pos, int& s, int& n) {
+// tree's shape depends on N only); a finished leaf keeps its range.  right:
+// the last split sent the group right.
+__device__ __forceinline__ void rb_group_of(int N, int level, int pos, int& s, int& n, bool& right) {
   s = 0;
   n = N;
+  right = false;
   for (int t = 0; t < level; ++t) {
     const int m = (n + RB_BLK - 1) / RB_BLK;
     if (m <= 1) break;
     const int nl = RB_BLK * ((m + 1) / 2);
-    if (pos >= s + nl) {
+    right = pos >= s + nl;
+    if (right) {
       s += nl;
       n -= nl;
     } else {
@@ -350,8 +358,9 @@ __global__ __launch_bounds__(256) void rb_stats_kernel(const float* __restrict__
   const size_t bh = blockIdx.x / nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int s, n;
-  rb_group_of(N, level, c * RB_BLK, s, n);
-  if (n <= RB_BLK) return;  // a leaf: no split to prepare
+  bool right;
+  rb_group_of(N, level, c * RB_BLK, s, n, right);
+  if (n <= RB_BLK || right) return;  // a leaf, or sums the split kernel derives
   const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
   const float* zb = zh + bh * (size_t)N * RB_HD;
   // lane i < 32 holds the row of slice position wave + 4 i; positions past
@@ -416,10 +425,13 @@ __device__ __forceinline__ void block_scan2(int& x, int& y, int (*wt)[2], int la
 
 // The group [s, s + n) of workgroup-or-wavefront g at `level`, following the
 // bits of g from the root: a path that enters a finished leaf with a 1 bit is
-// empty (returns false); one with 0 bits carries the leaf over.
-__device__ __forceinline__ bool rb_locate(int N, int level, int gi, int& s, int& n) {
+// empty (returns false); one with 0 bits carries the leaf over.  sp: the start
+// of the group's parent when the last split sent it right (its left sibling
+// is [sp, s)), else s.
+__device__ __forceinline__ bool rb_locate(int N, int level, int gi, int& s, int& n, int& sp) {
   s = 0;
   n = N;
+  sp = 0;
   for (int t = level - 1; t >= 0; --t) {
     const int m = (n + RB_BLK - 1) / RB_BLK;
     const int bit = (gi >> t) & 1;
@@ -428,6 +440,7 @@ __device__ __forceinline__ bool rb_locate(int N, int level, int gi, int& s, int&
       continue;
     }
     const int nl = RB_BLK * ((m + 1) / 2);
+    sp = s;
     if (bit) {
       s += nl;
       n -= nl;
@@ -460,36 +473,61 @@ __device__ __forceinline__ int rb_argmax_wave(double v0, double v1, int lane) {
   return bd;
 }
 
-// variance of coordinate d over the group [s, s + n) of m <= 8 slices from
-// its slice sums (added in slice order; eight loads in flight)
-__device__ __forceinline__ double rb_group_var8(const double* stats_bh, int s, int n, int d) {
-  const double* sp = stats_bh + (s / RB_BLK) * 2 * RB_HD + d;
-  const int m = (n + RB_BLK - 1) / RB_BLK;
-  double va[8], vb[8];
+// sums of z_d and z_d^2 over the slices [c0, c0 + cnt) (cnt >= 1), added in
+// slice order with eight loads in flight
+__device__ __forceinline__ void rb_slice_sums(const double* stats_bh, int c0, int cnt, int d, double& a,
+                                              double& b) {
+  const double* sp = stats_bh + (size_t)c0 * 2 * RB_HD + d;
+  a = 0.0;
+  b = 0.0;
+  for (int base = 0; base < cnt; base += 8) {
+    double va[8], vb[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    va[c] = sp[(size_t)min(c, m - 1) * 2 * RB_HD];
-    vb[c] = sp[(size_t)min(c, m - 1) * 2 * RB_HD + RB_HD];
-  }
-  double a = 0.0, b = 0.0;
+    for (int c = 0; c < 8; ++c) {
+      va[c] = sp[(size_t)min(base + c, cnt - 1) * 2 * RB_HD];
+      vb[c] = sp[(size_t)min(base + c, cnt - 1) * 2 * RB_HD + RB_HD];
+    }
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    a += c < m ? va[c] : 0.0;
-    b += c < m ? vb[c] : 0.0;
+    for (int c = 0; c < 8; ++c) {
+      a += base + c < cnt ? va[c] : 0.0;
+      b += base + c < cnt ? vb[c] : 0.0;
+    }
   }
+}
+
+// variance of coordinate d over the group [s, s + n): its slices' sums, or
+// for a right child (sp < s) its parent's totals less its left sibling's
+// slices [sp, s); the group's totals go to tcur for its children
+__device__ __forceinline__ double rb_group_var(const double* stats_bh, const double* tprev_bh, double* tcur_bh,
+                                               int s, int n, int sp, int d) {
+  double a, b;
+  if (sp == s) {
+    rb_slice_sums(stats_bh, s / RB_BLK, (n + RB_BLK - 1) / RB_BLK, d, a, b);
+  } else {
+    double la, lb;
+    rb_slice_sums(stats_bh, sp / RB_BLK, (s - sp) / RB_BLK, d, la, lb);
+    a = tprev_bh[(size_t)(sp / RB_BLK) * 2 * RB_HD + d] - la;
+    b = tprev_bh[(size_t)(sp / RB_BLK) * 2 * RB_HD + RB_HD + d] - lb;
+  }
+  tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + d] = a;
+  tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + RB_HD + d] = b;
   const double mu = a / n;
   return b / n - mu * mu;
 }
 
 // Split coordinate of a group of any size, all 1024 threads of the
 // workgroup: thread t adds the slices c = t / 128 (mod 8) of coordinate
-// t mod 128 in slice order, the eight partial sums are added in order, and
-// wavefront 0 takes the largest variance (the lowest coordinate on ties).
-__device__ __forceinline__ int rb_split_coord_block(const double* stats_bh, int s, int n, double (*part)[2][RB_HD],
+// t mod 128 in slice order (a right child, sp < s: the slices of its left
+// sibling [sp, s), subtracted from the parent's totals), the eight partial
+// sums are added in order, the group's totals go to tcur, and wavefront 0
+// takes the largest variance (the lowest coordinate on ties).
+__device__ __forceinline__ int rb_split_coord_block(const double* stats_bh, const double* tprev_bh,
+                                                    double* tcur_bh, int s, int n, int sp_, double (*part)[2][RB_HD],
                                                     int* sh_d, int tid) {
   const int d = tid & (RB_HD - 1), p = tid >> 7;
-  const int m = (n + RB_BLK - 1) / RB_BLK;
-  const double* sp = stats_bh + (s / RB_BLK) * 2 * RB_HD + d;
+  const bool right = sp_ != s;
+  const int m = right ? (s - sp_) / RB_BLK : (n + RB_BLK - 1) / RB_BLK;
+  const double* sp = stats_bh + ((right ? sp_ : s) / RB_BLK) * 2 * RB_HD + d;
   double a = 0.0, b = 0.0;
   for (int c0 = p; c0 < m; c0 += 32) {
     double va[4], vb[4];
@@ -519,6 +557,12 @@ __device__ __forceinline__ int rb_split_coord_block(const double* stats_bh, int 
         sa += part[q][0][dd];
         sb += part[q][1][dd];
       }
+      if (right) {
+        sa = tprev_bh[(size_t)(sp_ / RB_BLK) * 2 * RB_HD + dd] - sa;
+        sb = tprev_bh[(size_t)(sp_ / RB_BLK) * 2 * RB_HD + RB_HD + dd] - sb;
+      }
+      tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + dd] = sa;
+      tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + RB_HD + dd] = sb;
       const double mu = sa / n;
       v[h] = sb / n - mu * mu;
     }
@@ -537,6 +581,8 @@ constexpr int WS_KPT = 16;
 
 __global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restrict__ zh,
                                                             const double* __restrict__ stats,
+                                                            const double* __restrict__ tprev,
+                                                            double* __restrict__ tcur,
                                                             const int32_t* __restrict__ pin,
                                                             int32_t* __restrict__ pout, int N, int nb, int level,
                                                             int total) {
@@ -545,8 +591,8 @@ __global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restr
   if (G >= total) return;
   const int gi = G & ((1 << level) - 1);
   const size_t bh = (size_t)(G >> level);
-  int s, n;
-  if (!rb_locate(N, level, gi, s, n)) return;
+  int s, n, sp;
+  if (!rb_locate(N, level, gi, s, n, sp)) return;
   const int32_t* pi = pin + bh * N + s;
   int32_t* po = pout + bh * N + s;
   const int m = (n + RB_BLK - 1) / RB_BLK;
@@ -555,8 +601,9 @@ __global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restr
     return;
   }
   const int nl = RB_BLK * ((m + 1) / 2);
-  const double* sb = stats + bh * nb * 2 * RB_HD;
-  const int dstar = rb_argmax_wave(rb_group_var8(sb, s, n, lane), rb_group_var8(sb, s, n, lane + 64), lane);
+  const size_t so = bh * nb * 2 * RB_HD;
+  const int dstar = rb_argmax_wave(rb_group_var(stats + so, tprev + so, tcur + so, s, n, sp, lane),
+                                   rb_group_var(stats + so, tprev + so, tcur + so, s, n, sp, lane + 64), lane);
   const float* zb = zh + bh * (size_t)N * RB_HD;
   const int C = (n + 63) / 64;
   const int j0 = lane * C;
@@ -617,6 +664,8 @@ __global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restr
 template <int KPT>
 __global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restrict__ zh,
                                                             const double* __restrict__ stats,
+                                                            const double* __restrict__ tprev,
+                                                            double* __restrict__ tcur,
                                                             const int32_t* __restrict__ pin,
                                                             int32_t* __restrict__ pout, int N, int nb, int level) {
   constexpr int T = 1024, W = T / 64;
@@ -628,8 +677,8 @@ __global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restr
   const int gi = blockIdx.x % ng;
   const size_t bh = blockIdx.x / ng;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int s, n;
-  if (!rb_locate(N, level, gi, s, n)) return;
+  int s, n, sp;
+  if (!rb_locate(N, level, gi, s, n, sp)) return;
   const int32_t* pi = pin + bh * N + s;
   int32_t* po = pout + bh * N + s;
   const int m = (n + RB_BLK - 1) / RB_BLK;
@@ -638,7 +687,8 @@ __global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restr
     return;
   }
   const int nl = RB_BLK * ((m + 1) / 2);
-  const int dstar = rb_split_coord_block(stats + bh * nb * 2 * RB_HD, s, n, part, &sh_d, tid);
+  const size_t so = bh * nb * 2 * RB_HD;
+  const int dstar = rb_split_coord_block(stats + so, tprev + so, tcur + so, s, n, sp, part, &sh_d, tid);
   const float* zb = zh + bh * (size_t)N * RB_HD;
   const int C = (n + T - 1) / T;
   const int j0 = min(n, tid * C);
@@ -723,6 +773,8 @@ __global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restr
 // loads in flight), the split value by an MSB-first radix select.
 __global__ __launch_bounds__(1024) void rb_split_big_kernel(const float* __restrict__ zh,
                                                             const double* __restrict__ stats,
+                                                            const double* __restrict__ tprev,
+                                                            double* __restrict__ tcur,
                                                             const int32_t* __restrict__ pin,
                                                             int32_t* __restrict__ pout,
                                                             uint32_t* __restrict__ keys, int N, int nb, int level) {
@@ -735,8 +787,8 @@ __global__ __launch_bounds__(1024) void rb_split_big_kernel(const float* __restr
   const int gi = blockIdx.x % ng;
   const size_t bh = blockIdx.x / ng;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int s, n;
-  if (!rb_locate(N, level, gi, s, n)) return;
+  int s, n, sp;
+  if (!rb_locate(N, level, gi, s, n, sp)) return;
   const int32_t* pi = pin + bh * N + s;
   int32_t* po = pout + bh * N + s;
   const int m = (n + RB_BLK - 1) / RB_BLK;
@@ -745,7 +797,8 @@ __global__ __launch_bounds__(1024) void rb_split_big_kernel(const float* __restr
     return;
   }
   const int nl = RB_BLK * ((m + 1) / 2);
-  const int dstar = rb_split_coord_block(stats + bh * nb * 2 * RB_HD, s, n, part, &sh_d, tid);
+  const size_t so = bh * nb * 2 * RB_HD;
+  const int dstar = rb_split_coord_block(stats + so, tprev + so, tcur + so, s, n, sp, part, &sh_d, tid);
   const float* zb = zh + bh * (size_t)N * RB_HD;
   uint32_t* kb = keys + bh * N + s;
 
@@ -891,7 +944,7 @@ struct RbGeom {
 };
 
 struct RbLayout {
-  size_t part, msum, ltw, zh, keys, perm, stats, total;
+  size_t part, msum, ltw, zh, keys, perm, stats, tot, total;
 };
 
 size_t rb_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -937,6 +990,8 @@ RbLayout rb_layout(const RbGeom& g) {
   off = rb_align(off + (size_t)g.BH * g.N * sizeof(int32_t));
   w.stats = off;
   off = rb_align(off + (size_t)g.BH * g.nb * 2 * RB_HD * sizeof(double));
+  w.tot = off;  // group totals, two levels (by level parity)
+  off = rb_align(off + 2 * (size_t)g.BH * g.nb * 2 * RB_HD * sizeof(double));
   w.total = off;
   return w;
 }
@@ -988,6 +1043,9 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
   hipLaunchKernelGGL(rb_embed_kernel, dim3((unsigned)(g.BH * ntile)), dim3(64 * EM_WAVES), 0, s, (const uint16_t*)q,
                      (const uint16_t*)ltw, zh, buf[0], N, ntile);
   double* stats = (double*)(ws + w.stats);
+  // level l writes its groups' totals to tot[l % 2] and reads its parents'
+  // from tot[(l + 1) % 2]
+  double* tot[2] = {(double*)(ws + w.tot), (double*)(ws + w.tot) + (size_t)g.BH * g.nb * 2 * RB_HD};
   const int nb = (int)g.nb;
   for (int l = 0; l < g.levels; ++l) {
     hipLaunchKernelGGL(rb_stats_kernel, dim3((unsigned)(g.BH * nb)), dim3(256), 0, s, (const float*)zh,
@@ -998,20 +1056,22 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
     const dim3 grid((unsigned)(g.BH << l));
     const float* zc = zh;
     const double* sc = stats;
+    const double* tp = tot[(l + 1) & 1];
+    double* tc = tot[l & 1];
     const int32_t* pin = buf[l & 1];
     int32_t* pout = buf[(l + 1) & 1];
     if (largest <= 64 * WS_KPT) {
       const int total = (int)(g.BH << l);
-      hipLaunchKernelGGL(rb_split_wave_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, zc, sc, pin,
-                         pout, N, nb, l, total);
+      hipLaunchKernelGGL(rb_split_wave_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, zc, sc, tp, tc,
+                         pin, pout, N, nb, l, total);
     } else if (per <= 4) {
-      hipLaunchKernelGGL((rb_split_reg_kernel<4>), grid, dim3(1024), 0, s, zc, sc, pin, pout, N, nb, l);
+      hipLaunchKernelGGL((rb_split_reg_kernel<4>), grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, N, nb, l);
     } else if (per <= 12) {
-      hipLaunchKernelGGL((rb_split_reg_kernel<12>), grid, dim3(1024), 0, s, zc, sc, pin, pout, N, nb, l);
+      hipLaunchKernelGGL((rb_split_reg_kernel<12>), grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, N, nb, l);
     } else if (per <= 20) {
-      hipLaunchKernelGGL((rb_split_reg_kernel<20>), grid, dim3(1024), 0, s, zc, sc, pin, pout, N, nb, l);
+      hipLaunchKernelGGL((rb_split_reg_kernel<20>), grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, N, nb, l);
     } else {
-      hipLaunchKernelGGL(rb_split_big_kernel, grid, dim3(1024), 0, s, zc, sc, pin, pout, keys, N, nb, l);
+      hipLaunchKernelGGL(rb_split_big_kernel, grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, keys, N, nb, l);
     }
   }
   return rb_status();
