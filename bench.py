@@ -5,8 +5,9 @@ One step = bsa_pool + bsa_select + bsa_forward over one batch of synthetic
 input already resident in HBM (the 768p 5s shape by default: 56 heads x
 37,740 tokens, head_dim 128, top_k 64 of 295 blocks, mean summaries); with
 extra tokens, bsa_select_tokens + bsa_forward_tokens in place of bsa_forward;
-on the Spark-Reblock order, bsa_reblock + bsa_permute_rows before and
-bsa_unpermute_rows after.
+on the Spark-Reblock order, bsa_reblock first and the reordered calls
+(bsa_pool_reordered, bsa_forward_reordered: rows read and written through the
+order) in place of bsa_pool and bsa_forward.
 
 Prints one JSON line.  `value` is the effective TFLOP/s of a whole step
 counting only the selected blocks' attention FLOPs, 4 * 128 * sum_r n_r *
@@ -208,34 +209,35 @@ def main():
     if w.reblock:
         perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
         rws = torch.empty(bsa.bsa_reblock_workspace_bytes(p), dtype=torch.uint8, device=dev)
-        qr, kr, vr = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        out_r = torch.empty_like(q)
+        kr = torch.empty_like(k)   # the keys in the new order
     else:
-        qr, kr, vr, out_r = q, k, v, out
+        kr = k
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
 
     def step(e=None):
         if e: e[0].record()
         if w.reblock:
             bsa.bsa_reblock(p, q, k, perm, rws)
-            bsa.bsa_permute_rows(p, perm, q, k, v, qr, kr, vr)
         if e: e[1].record()
-        bsa.bsa_pool(p, qr, kr, vr, q_pool, k_pool, sum_k, sum_v, sum_bias, ws)
+        if w.reblock:
+            bsa.bsa_pool_reordered(p, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, kr, ws)
+        else:
+            bsa.bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws)
         if e: e[2].record()
         bsa.bsa_select(p, q_pool, k_pool, idx)
         if e: e[3].record()
         if tok is not None:
             bsa.bsa_select_tokens(p, q_pool, kr, idx, tok, ws)
         if e: e[4].record()
-        if tok is not None:
-            bsa.bsa_forward_tokens(p, qr, kr, vr, sum_k, sum_bias, idx, tok, ws, out_r)
-        else:
-            bsa.bsa_forward(p, qr, kr, sum_k, sum_bias, idx, ws, out_r)
-        if e: e[5].record()
         if w.reblock:
-            bsa.bsa_unpermute_rows(p, perm, out_r, out)
-        if e: e[6].record()
+            bsa.bsa_forward_reordered(p, perm, q, kr, v if tok is not None else None, sum_k, sum_bias, idx,
+                                      tok, ws, out)
+        elif tok is not None:
+            bsa.bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx, tok, ws, out)
+        else:
+            bsa.bsa_forward(p, q, k, sum_k, sum_bias, idx, ws, out)
+        if e: e[5].record()
 
     for _ in range(args.warmup):
         step()
@@ -247,15 +249,17 @@ def main():
     wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
     def span(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in ev) / args.steps
-    reblock_ms, pool_ms, sel_ms, tok_ms, attn_ms, unperm_ms = (span(i, i + 1) for i in range(6))
-    step_ms = span(0, 6)
-    step_med = float(np.median([e[0].elapsed_time(e[6]) for e in ev]))
+    reblock_ms, pool_ms, sel_ms, tok_ms, attn_ms = (span(i, i + 1) for i in range(5))
+    step_ms = span(0, 5)
+    step_med = float(np.median([e[0].elapsed_time(e[5]) for e in ev]))
     flops, summary_flops = counted_flops(torch, idx, N, nb, H, B, dense, tok)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
     # pool: read Q, K, V once; write q_pool, k_pool (fp32), sum_k, sum_v (bf16),
     # the bias, V^T of every block (32 KiB) and one summary-V^T column (256 B)
     pool_bytes = 3 * B * H * N * 128 * 2 + B * H * nb * (2 * 512 + 2 * 256 + 4 + 32768 + 256)
+    if w.reblock:  # plus the keys in the new order, and each row's perm entry read twice
+        pool_bytes += B * H * N * (128 * 2 + 2 * 4)
     sel_bytes = 2 * B * H * nb * 128 * 4 + B * H * nb * kk * 4
 
     if args.calib_copy:
@@ -288,8 +292,7 @@ def main():
         "kernels_ms": {"pool": round(pool_ms, 4), "select": round(sel_ms, 4),
                        "attention": round(attn_ms, 4),
                        **({"select_tokens": round(tok_ms, 4)} if tok is not None else {}),
-                       **({"reblock_and_permute": round(reblock_ms, 4),
-                           "unpermute": round(unperm_ms, 4)} if w.reblock else {})},
+                       **({"reblock": round(reblock_ms, 4)} if w.reblock else {})},
         "wall_ms_per_step": round(wall_ms, 4),
         "median_ms_per_step": round(step_med, 4),
         "counted_tflop_per_step": round(flops / 1e12, 4),

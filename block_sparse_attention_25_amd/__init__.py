@@ -93,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.bsa_permute_rows.restype = ctypes.c_int
         L.bsa_unpermute_rows.argtypes = [_P] + [_vp] * 4
         L.bsa_unpermute_rows.restype = ctypes.c_int
+        L.bsa_pool_reordered.argtypes = [_P] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+        L.bsa_pool_reordered.restype = ctypes.c_int
+        L.bsa_forward_reordered.argtypes = [_P] + [_vp] * 9 + [ctypes.c_size_t, _vp, _vp]
+        L.bsa_forward_reordered.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -194,6 +198,24 @@ def bsa_unpermute_rows(p: Problem, perm, x, out, stream=None):
                                     _stream(stream)), "bsa_unpermute_rows")
 
 
+def bsa_pool_reordered(p: Problem, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out,
+                       workspace, stream=None):
+    _raise(lib().bsa_pool_reordered(ctypes.byref(p), _ptr(perm), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(q_pool), _ptr(k_pool), _ptr(sum_k), _ptr(sum_v),
+                                    _ptr(sum_bias), _ptr(k_out), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "bsa_pool_reordered")
+
+
+def bsa_forward_reordered(p: Problem, perm, q, k_r, v, sum_k, sum_bias, block_idx, token_idx, workspace,
+                          out, stream=None):
+    _raise(lib().bsa_forward_reordered(ctypes.byref(p), _ptr(perm), _ptr(q), _ptr(k_r), _ptr(v),
+                                       _ptr(sum_k), _ptr(sum_bias), _ptr(block_idx), _ptr(token_idx),
+                                       _ptr(workspace),
+                                       0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                       _ptr(out), _stream(stream)), "bsa_forward_reordered")
+
+
 # ---------------------------------------------------------------- helpers ---
 def k_from_ratio(ratio, n_blocks: int) -> int:
     """Top-k ratio budget -> block count, ceil(ratio * n_blocks) computed on the
@@ -260,8 +282,9 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     skipped, those scoring highest against its pooled query (token_idx in the
     aux dict).  reblock=True runs the path on Spark-Reblock's row order (the
     q_reuse_k layout: Q, K and V permuted alike, the output put back in
-    place; perm in the aux dict, the other aux tensors in the new order); it
-    rejects sink rows and an anchor over part of the rows.  Returns out
+    place; perm and k_r, the keys in the new order, in the aux dict, the
+    other aux tensors in the new order); it rejects sink rows and an anchor
+    over part of the rows.  Returns out
     [B, H, N, 128] bf16, plus a dict of intermediate tensors when return_aux
     is set."""
     import torch
@@ -279,9 +302,6 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
         perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
         rws = torch.empty(bsa_reblock_workspace_bytes(p), dtype=torch.uint8, device=dev)
         bsa_reblock(p, q, k, perm, rws, stream)
-        qo, ko, vo = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        bsa_permute_rows(p, perm, q, k, v, qo, ko, vo, stream)
-        q, k, v = qo, ko, vo
     f32, bf = torch.float32, torch.bfloat16
     q_pool = torch.empty((B, H, nb, HEAD_DIM), dtype=f32, device=dev)
     k_pool = torch.empty_like(q_pool)
@@ -291,22 +311,28 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     idx = torch.empty((B, H, nb, kk), dtype=torch.int32, device=dev)
     ws = torch.empty(bsa_workspace_bytes(p), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
-    bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws, stream)
+    k_r = None
+    if perm is not None:
+        # q and v are read through perm; K gets one copy in the new order
+        k_r = torch.empty_like(k)
+        bsa_pool_reordered(p, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_r, ws, stream)
+    else:
+        bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws, stream)
     bsa_select(p, q_pool, k_pool, idx if kk > 0 else None, stream)
     tok = None
     if p.extra_tokens > 0:
         tok = torch.empty((B, H, nb, p.extra_tokens), dtype=torch.int32, device=dev)
-        bsa_select_tokens(p, q_pool, k, idx if kk > 0 else None, tok, ws, stream)
+        bsa_select_tokens(p, q_pool, k if k_r is None else k_r, idx if kk > 0 else None, tok, ws, stream)
+    if perm is not None:
+        bsa_forward_reordered(p, perm, q, k_r, v if tok is not None else None, sum_k, sum_bias,
+                              idx if kk > 0 else None, tok, ws, out, stream)
+    elif tok is not None:
         bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx if kk > 0 else None, tok, ws, out,
                            stream)
     else:
         bsa_forward(p, q, k, sum_k, sum_bias, idx if kk > 0 else None, ws, out, stream)
-    if perm is not None:
-        back = torch.empty_like(out)
-        bsa_unpermute_rows(p, perm, out, back, stream)
-        out = back
     if return_aux:
         return out, dict(q_pool=q_pool, k_pool=k_pool, sum_k=sum_k, sum_v=sum_v,
                          sum_bias=sum_bias, block_idx=idx, token_idx=tok, workspace=ws, problem=p,
-                         perm=perm)
+                         perm=perm, k_r=k_r)
     return out

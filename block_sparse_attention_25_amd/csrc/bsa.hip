@@ -79,6 +79,8 @@ __device__ __forceinline__ void unpack8(const uint4& u, double* out) {
 // the 8 features [8*(t%16), +8) of the rows {t/16 + 16*i : i < 8} of the block.
 // Column sums are float64: sums of bfloat16 values are exact for these
 // magnitudes, so the order of summation does not change the result.
+// GATHER: the blocks are those of a row order perm (position p holds row
+// perm[p]); every row is read through it.
 
 __device__ __forceinline__ void lds_colsum(double (*red)[HD], const double* acc, int tid,
                                            double* col_out /* valid for tid < 128 */) {
@@ -95,8 +97,9 @@ __device__ __forceinline__ void lds_colsum(double (*red)[HD], const double* acc,
   __syncthreads();
 }
 
-template <bool REWEIGHT>
+template <bool REWEIGHT, bool GATHER>
 __global__ __launch_bounds__(256) void pool_q_kernel(const uint16_t* __restrict__ q,
+                                                     const int32_t* __restrict__ perm,
                                                      float* __restrict__ q_pool,
                                                      double* __restrict__ anchor_part, int N,
                                                      int nb, int anchor_rows) {
@@ -104,15 +107,21 @@ __global__ __launch_bounds__(256) void pool_q_kernel(const uint16_t* __restrict_
   const int c = blockIdx.x, tid = threadIdx.x;
   const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
   const int s = c * BLK, n = min(BLK, N - s);
-  const uint16_t* xb = q + (bh * N + s) * HD;
+  const uint16_t* xb = q + bh * N * HD;
   const int cc = tid & 15, rp = tid >> 4;
+  int src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pos = s + min(rp + 16 * i, n - 1);
+    src[i] = GATHER ? perm[bh * N + pos] : pos;
+  }
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, acc_a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = rp + 16 * i;
     if (row < n) {
       double vals[8];
-      unpack8(*(const uint4*)(xb + row * HD + cc * 8), vals);
+      unpack8(*(const uint4*)(xb + (size_t)src[i] * HD + cc * 8), vals);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += vals[e];
       if (REWEIGHT && s + row < anchor_rows) {
@@ -152,9 +161,11 @@ __global__ __launch_bounds__(1024) void anchor_kernel(const double* __restrict__
   }
 }
 
-template <bool REWEIGHT>
+// GATHER also writes the block's K rows in the order's positions to k_out.
+template <bool REWEIGHT, bool GATHER>
 __global__ __launch_bounds__(256) void pool_kv_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const double* __restrict__ anchor,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
+    uint16_t* __restrict__ k_out, const double* __restrict__ anchor,
     float* __restrict__ k_pool, uint16_t* __restrict__ sum_k, uint16_t* __restrict__ sum_v,
     float* __restrict__ sum_bias, uint16_t* __restrict__ vt, uint16_t* __restrict__ svt, int N,
     int nb, int nsb, double scale) {
@@ -165,21 +176,33 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
   const int c = blockIdx.x, tid = threadIdx.x;
   const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
   const int s = c * BLK, n = min(BLK, N - s);
-  const uint16_t* kb = k + (bh * N + s) * HD;
-  const uint16_t* vb = v + (bh * N + s) * HD;
+  const uint16_t* kb = k + bh * N * HD;
+  const uint16_t* vb = v + bh * N * HD;
   const int cc = tid & 15, rp = tid >> 4;
+  int src[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pos = s + min(rp + 16 * i, n - 1);
+    src[i] = GATHER ? perm[bh * N + pos] : pos;
+  }
 
   uint4 kr[8], vr[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = rp + 16 * i;
     // load a valid row (clamped) and zero it afterwards: no pointer select
-    const int rowc = min(row, n - 1);
-    kr[i] = zero_unless(*(const uint4*)(kb + rowc * HD + cc * 8), row < n);
-    vr[i] = zero_unless(*(const uint4*)(vb + rowc * HD + cc * 8), row < n);
+    kr[i] = zero_unless(*(const uint4*)(kb + (size_t)src[i] * HD + cc * 8), row < n);
+    vr[i] = zero_unless(*(const uint4*)(vb + (size_t)src[i] * HD + cc * 8), row < n);
     // stage V (zeros past the end of a short block) for the transpose below
     uint32_t* dst = (uint32_t*)&vl[row][cc * 8];
     dst[0] = vr[i].x; dst[1] = vr[i].y; dst[2] = vr[i].z; dst[3] = vr[i].w;
+  }
+  if (GATHER) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = rp + 16 * i;
+      if (row < n) *(uint4*)(k_out + (bh * N + s + row) * HD + cc * 8) = kr[i];
+    }
   }
 
   double acc[8], vals[8];
@@ -619,8 +642,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ sum_k,
     const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
     const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ tok_idx, uint16_t* __restrict__ out, int N, int nb, int krow, int nsb,
-    float scale_log2, int total_wg, int chunk, int f0, int f1, int E) {
+    const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ perm, uint16_t* __restrict__ out, int N,
+    int nb, int krow, int nsb, float scale_log2, int total_wg, int chunk, int f0, int f1, int E) {
   // LDS buffers as distinct variables, so the compiler can tell the DMA
   // targets from the buffers being read
   __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
@@ -667,11 +690,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       make_rsrc(sum_k ? sum_k + bh * (size_t)nb * HD : k, sum_k ? (uint32_t)nb * HD * 2 : 0u);
   const __amdgpu_buffer_rsrc_t rsv = make_rsrc(svt + bh * (size_t)nsb * BLK * HD, (uint32_t)nsb * BLK * HD * 2);
 
-  // Q fragments (B operand of S^T = K Q^T): query qi, features 16kk + 8g + [0, 8)
+  // Q fragments (B operand of S^T = K Q^T): query qi, features 16kk + 8g + [0, 8).
+  // With a row order perm, query qi (a position) is row perm[qi] of q and
+  // of out, and token t of the extra tokens is row perm[t] of v.
   const int qi = r * BLK + 32 * wave + ln;
   bf16x8 qf[8];
   {
-    const uint16_t* qrow = q + (bh * (size_t)N + (size_t)min(qi, N - 1)) * HD;
+    const int qpos = min(qi, N - 1);
+    const uint16_t* qrow = q + (bh * (size_t)N + (size_t)(perm ? perm[bh * N + qpos] : qpos)) * HD;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       bf16x8 t = ld_bf16x8(qrow + 16 * kk + 8 * g);
@@ -820,7 +846,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         uint4 kd = make_uint4(0u, 0u, 0u, 0u), vd = kd;
         if (t >= 0) {
           kd = *(const uint4*)(kb + (size_t)t * HD + 8 * ch);
-          vd = *(const uint4*)(vb + (size_t)t * HD + 8 * ch);
+          vd = *(const uint4*)(vb + (size_t)(perm ? perm[bh * N + t] : t) * HD + 8 * ch);
         }
         *(uint4*)(ks0 + swz_k(row, ch)) = kd;
         const int pos = vt_pos(row);
@@ -1050,7 +1076,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const float l_tot = l_run + other_half(l_run);
   const float inv = 1.f / l_tot;
   if (qi < N) {
-    uint16_t* orow = out + (bh * (size_t)N + qi) * HD;
+    uint16_t* orow = out + (bh * (size_t)N + (size_t)(perm ? perm[bh * N + qi] : qi)) * HD;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
 #pragma unroll
@@ -1756,7 +1782,7 @@ int check_forward(const Geometry& g, const void* q, const void* k, const void* s
 
 int launch_attention(const Geometry& g, const void* q, const void* k, const void* sum_k,
                      const float* sum_bias, const int32_t* block_idx, const char* ws, const void* v,
-                     const int32_t* tok_idx, void* out, hipStream_t stream) {
+                     const int32_t* tok_idx, const int32_t* perm, void* out, hipStream_t stream) {
   const WsLayout w = ws_layout(g);
   // The head-synchronous map (8 chunks of ceil(nb / 8) query blocks per head)
   // once the K and V^T of eight heads, one per XCD, would pass 192 MiB
@@ -1769,9 +1795,66 @@ int launch_attention(const Geometry& g, const void* q, const void* k, const void
   const float scale_log2 = (float)(g.scale * 1.4426950408889634);
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, stream, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)(ws + w.vt), (const uint16_t*)sum_k,
-                     (const uint16_t*)(ws + w.svt), sum_bias, block_idx, (const uint16_t*)v, tok_idx,
+                     (const uint16_t*)(ws + w.svt), sum_bias, block_idx, (const uint16_t*)v, tok_idx, perm,
                      (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, chunk,
                      (int)g.f0, (int)g.f1, tok_idx ? g.E : 0);
+  return launch_status();
+}
+
+int check_pool(const Geometry& g, const void* q, const void* k, const void* v, const float* q_pool,
+               const float* k_pool, const void* sum_k, const void* sum_v, const float* sum_bias,
+               const void* workspace, size_t workspace_bytes) {
+  if (!q || !k || !v || !q_pool || !k_pool || !sum_k || !sum_v || !sum_bias) return BSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_pool) || !aligned16(k_pool) ||
+      !aligned16(sum_k) || !aligned16(sum_v))
+    return BSA_ERR_INVALID;
+  if (!workspace || workspace_bytes < ws_layout(g).total || ((uintptr_t)workspace & 255u))
+    return BSA_ERR_WORKSPACE;
+  return BSA_OK;
+}
+
+// A row order is applied to Q, K and V alike, so options that name rows by
+// position (conditioning sinks, an anchor over part of the rows) are refused.
+int check_reorder(const bsa_problem* p) {
+  if (p->sink_rows != 0) return BSA_ERR_UNSUPPORTED;
+  if (p->summary == BSA_SUMMARY_REWEIGHT && p->anchor_rows != 0 && p->anchor_rows != p->seq_len)
+    return BSA_ERR_UNSUPPORTED;
+  return BSA_OK;
+}
+
+template <bool REWEIGHT, bool GATHER>
+void launch_pool_t(const Geometry& g, const int32_t* perm, const void* q, const void* k, const void* v,
+                   float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out, char* ws,
+                   hipStream_t s) {
+  const WsLayout w = ws_layout(g);
+  const dim3 grid((unsigned)g.nb, (unsigned)g.H, (unsigned)g.B);
+  double* apart = REWEIGHT ? (double*)(ws + w.apart) : nullptr;
+  double* anc = REWEIGHT ? (double*)(ws + w.anchor) : nullptr;
+  hipLaunchKernelGGL((pool_q_kernel<REWEIGHT, GATHER>), grid, dim3(256), 0, s, (const uint16_t*)q, perm, q_pool,
+                     apart, (int)g.N, (int)g.nb, REWEIGHT ? g.anchor_rows : 0);
+  if (REWEIGHT)
+    hipLaunchKernelGGL(anchor_kernel, dim3((unsigned)g.H, (unsigned)g.B), dim3(8 * HD), 0, s,
+                       (const double*)apart, anc, (int)g.nb, g.anchor_rows);
+  hipLaunchKernelGGL((pool_kv_kernel<REWEIGHT, GATHER>), grid, dim3(256), 0, s, (const uint16_t*)k,
+                     (const uint16_t*)v, perm, (uint16_t*)k_out, (const double*)anc, k_pool, (uint16_t*)sum_k,
+                     (uint16_t*)sum_v, sum_bias, (uint16_t*)(ws + w.vt), (uint16_t*)(ws + w.svt), (int)g.N,
+                     (int)g.nb, (int)g.nsb, g.scale);
+}
+
+int launch_pool(const Geometry& g, const int32_t* perm, const void* q, const void* k, const void* v,
+                float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out, char* ws,
+                hipStream_t s) {
+  if (g.reweight) {
+    if (perm)
+      launch_pool_t<true, true>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+    else
+      launch_pool_t<true, false>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+  } else {
+    if (perm)
+      launch_pool_t<false, true>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+    else
+      launch_pool_t<false, false>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+  }
   return launch_status();
 }
 
@@ -1814,38 +1897,24 @@ int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v, 
   Geometry g;
   int st = make_geometry(p, &g);
   if (st != BSA_OK) return st;
-  if (!q || !k || !v || !q_pool || !k_pool || !sum_k || !sum_v || !sum_bias) return BSA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_pool) || !aligned16(k_pool) ||
-      !aligned16(sum_k) || !aligned16(sum_v))
-    return BSA_ERR_INVALID;
-  const WsLayout w = ws_layout(g);
-  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return BSA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)hip_stream;
-  char* ws = (char*)workspace;
-  const dim3 grid((unsigned)g.nb, (unsigned)g.H, (unsigned)g.B);
-  double* apart = g.reweight ? (double*)(ws + w.apart) : nullptr;
-  double* anc = g.reweight ? (double*)(ws + w.anchor) : nullptr;
-  if (g.reweight) {
-    hipLaunchKernelGGL(pool_q_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)q, q_pool, apart,
-                       (int)g.N, (int)g.nb, g.anchor_rows);
-    if ((st = launch_status()) != BSA_OK) return st;
-    hipLaunchKernelGGL(anchor_kernel, dim3((unsigned)g.H, (unsigned)g.B), dim3(8 * HD), 0, s,
-                       (const double*)apart, anc, (int)g.nb, g.anchor_rows);
-    if ((st = launch_status()) != BSA_OK) return st;
-    hipLaunchKernelGGL(pool_kv_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)k,
-                       (const uint16_t*)v, (const double*)anc, k_pool, (uint16_t*)sum_k,
-                       (uint16_t*)sum_v, sum_bias, (uint16_t*)(ws + w.vt), (uint16_t*)(ws + w.svt),
-                       (int)g.N, (int)g.nb, (int)g.nsb, g.scale);
-  } else {
-    hipLaunchKernelGGL(pool_q_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)q, q_pool,
-                       (double*)nullptr, (int)g.N, (int)g.nb, 0);
-    if ((st = launch_status()) != BSA_OK) return st;
-    hipLaunchKernelGGL(pool_kv_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)k,
-                       (const uint16_t*)v, (const double*)nullptr, k_pool, (uint16_t*)sum_k,
-                       (uint16_t*)sum_v, sum_bias, (uint16_t*)(ws + w.vt), (uint16_t*)(ws + w.svt),
-                       (int)g.N, (int)g.nb, (int)g.nsb, g.scale);
-  }
-  return launch_status();
+  if ((st = check_pool(g, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, workspace_bytes)) != BSA_OK)
+    return st;
+  return launch_pool(g, nullptr, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, nullptr, (char*)workspace,
+                     (hipStream_t)hip_stream);
+}
+
+int bsa_pool_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k, const void* v,
+                       float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st != BSA_OK) return st;
+  if ((st = check_reorder(p)) != BSA_OK) return st;
+  if (!perm || ((uintptr_t)perm & 3u) || !k_out || !aligned16(k_out) || k_out == k) return BSA_ERR_INVALID;
+  if ((st = check_pool(g, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, workspace_bytes)) != BSA_OK)
+    return st;
+  return launch_pool(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, (char*)workspace,
+                     (hipStream_t)hip_stream);
 }
 
 int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, int32_t* block_idx,
@@ -1877,7 +1946,7 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
   if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
     return st;
   return launch_attention(g, q, k, sum_k, sum_bias, block_idx, (const char*)workspace, nullptr, nullptr,
-                          out, (hipStream_t)hip_stream);
+                          nullptr, out, (hipStream_t)hip_stream);
 }
 
 int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
@@ -1913,9 +1982,28 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
     return st;
   hipStream_t s = (hipStream_t)hip_stream;
   const char* ws = (const char*)workspace;
-  if (g.E == 0) return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, out, s);
+  if (g.E == 0) return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, nullptr, out, s);
   if (!v || !token_idx || !aligned16(v)) return BSA_ERR_INVALID;
-  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, v, token_idx, out, s);
+  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, v, token_idx, nullptr, out, s);
+}
+
+int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k_r,
+                          const void* v, const void* sum_k, const float* sum_bias, const int32_t* block_idx,
+                          const int32_t* token_idx, const void* workspace, size_t workspace_bytes, void* out,
+                          void* hip_stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st != BSA_OK) return st;
+  if ((st = check_reorder(p)) != BSA_OK) return st;
+  if (!perm || ((uintptr_t)perm & 3u)) return BSA_ERR_INVALID;
+  if ((st = check_forward(g, q, k_r, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
+    return st;
+  if (out == q || out == k_r) return BSA_ERR_INVALID;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const char* ws = (const char*)workspace;
+  if (g.E == 0) return launch_attention(g, q, k_r, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, perm, out, s);
+  if (!v || !token_idx || !aligned16(v) || out == v) return BSA_ERR_INVALID;
+  return launch_attention(g, q, k_r, sum_k, sum_bias, block_idx, ws, v, token_idx, perm, out, s);
 }
 
 }  // extern "C"

@@ -260,13 +260,18 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
  * until each leaf is one block) and section "Workflows" (reblock_layout =
  * q_reuse_k: keys and values take the query layout).
  *
- * Use: bsa_reblock -> perm; bsa_permute_rows(q, k, v) -> q', k', v'; the
- * block-sparse path (bsa_pool ... bsa_forward or bsa_forward_tokens) on q',
- * k', v' with the same problem -> out'; bsa_unpermute_rows(out') -> out.
- * Problems with conditioning sinks, or Spark-Reweight with an anchor over
- * part of the rows, are rejected with BSA_ERR_UNSUPPORTED by all three calls:
- * those options name rows by position, which the new order changes.  The
- * other fields of the problem are not read.
+ * Use: bsa_reblock -> perm, then either
+ *  - bsa_pool_reordered (-> k', the keys in the new order), bsa_select,
+ *    [bsa_select_tokens on k'], bsa_forward_reordered -> out, which read
+ *    q and v through perm and write out in the original row order, or
+ *  - bsa_permute_rows(q, k, v) -> q', k', v'; the block-sparse path
+ *    (bsa_pool ... bsa_forward or bsa_forward_tokens) on q', k', v' with the
+ *    same problem -> out'; bsa_unpermute_rows(out') -> out.
+ * Both give the same bits.  Problems with conditioning sinks, or
+ * Spark-Reweight with an anchor over part of the rows, are rejected with
+ * BSA_ERR_UNSUPPORTED by all of these calls: those options name rows by
+ * position, which the new order changes.  The reblock and row calls read no
+ * other field of the problem.
  *
  * What bsa_reblock computes, per (b, h):
  *   M = (1/N) sum_j k_j k_j^T;  L L^T = M + (1e-6 trace(M) / 128 + 1e-30) I;
@@ -286,12 +291,47 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
  *   q, k       in   bf16 [B, H, N, 128]
  *   perm       out  int32 [B, H, N]: perm[p] = the row placed at position p
  *   workspace  in/out  bsa_reblock_workspace_bytes() bytes, 256-byte aligned
- *                   (about N * 528 bytes per (b, h)); its contents are
+ *                   (about N * 568 bytes per (b, h)); its contents are
  *                   scratch and need no initialisation
  */
 int bsa_reblock_workspace_bytes(const bsa_problem* p, size_t* bytes);
 int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* perm,
                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * The block-sparse path on a row order without permuted copies of Q, V and
+ * the output.  Sources: as for bsa_pool, bsa_forward and bsa_reblock.
+ *
+ * bsa_pool_reordered: bsa_pool of q', k', v' where x'[b, h, p, :] =
+ * x[b, h, perm[b, h, p], :], every row read through perm, plus
+ *   k_out  out  bf16 [B, H, N, 128]: k', the keys in the new order, which
+ *               bsa_forward_reordered (and bsa_select_tokens) read as
+ *               contiguous tiles; not overlapping q, k or v
+ * The pooled vectors, summaries and block indices that follow are those of
+ * the new order (block c = positions [128 c, 128 c + 128)).
+ *
+ * bsa_forward_reordered: bsa_forward_tokens of q', k', v' (bsa_forward when
+ * p->extra_tokens == 0; v and token_idx may then be NULL), with its output
+ * row p written to out[b, h, perm[b, h, p], :]:
+ *   q, v       in   bf16 [B, H, N, 128], the original row order
+ *   k_r        in   bf16 [B, H, N, 128], k_out of bsa_pool_reordered
+ *   sum_k, sum_bias, block_idx, token_idx, workspace   in   as for
+ *              bsa_forward_tokens, from the calls on the new order
+ *   out        out  bf16 [B, H, N, 128], the original row order; not
+ *              overlapping any input
+ *
+ *   perm  in  int32 [B, H, N], a permutation of 0..N-1 per (b, h) (as
+ *             bsa_reblock writes it; other values are not checked and read
+ *             or write out of bounds); 4-byte aligned
+ */
+int bsa_pool_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k,
+                       const void* v, float* q_pool, float* k_pool, void* sum_k, void* sum_v,
+                       float* sum_bias, void* k_out, void* workspace, size_t workspace_bytes,
+                       void* hip_stream);
+int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k_r,
+                          const void* v, const void* sum_k, const float* sum_bias,
+                          const int32_t* block_idx, const int32_t* token_idx, const void* workspace,
+                          size_t workspace_bytes, void* out, void* hip_stream);
 
 /*
  * Rows of Q, K and V in the new order (the q_reuse_k layout):

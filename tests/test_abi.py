@@ -22,7 +22,8 @@ def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert {"bsa_pool", "bsa_select", "bsa_forward", "bsa_workspace_bytes",
             "bsa_status_str", "bsa_select_tokens", "bsa_forward_tokens", "bsa_reblock",
-            "bsa_reblock_workspace_bytes", "bsa_permute_rows", "bsa_unpermute_rows"} <= set(names)
+            "bsa_reblock_workspace_bytes", "bsa_permute_rows", "bsa_unpermute_rows",
+            "bsa_pool_reordered", "bsa_forward_reordered"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -193,7 +194,19 @@ def test_reblock_entry_points_validate():
                               None) == bsa.BSA_ERR_INVALID
     assert L.bsa_unpermute_rows(ctypes.byref(p), fake, None, fake, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_unpermute_rows(ctypes.byref(p), fake, fake, odd, None) == bsa.BSA_ERR_INVALID
-    # options that name rows by position are refused by all three calls
+    # the reordered calls: a missing or misaligned perm, k_out on k, out on q
+    f = fake
+    assert L.bsa_pool_reordered(ctypes.byref(p), None, f, f, f, f, f, f, f, f, odd, f, big,
+                                None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_pool_reordered(ctypes.byref(p), odd, f, f, f, f, f, f, f, f, f, f, big,
+                                None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_pool_reordered(ctypes.byref(p), f, f, f, f, f, f, f, f, f, f, f, big,
+                                None) == bsa.BSA_ERR_INVALID       # k_out == k
+    assert L.bsa_forward_reordered(ctypes.byref(p), None, f, f, f, f, f, f, None, f, big, odd,
+                                   None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_forward_reordered(ctypes.byref(p), f, f, f, f, f, f, f, None, f, big, f,
+                                   None) == bsa.BSA_ERR_INVALID    # out == q
+    # options that name rows by position are refused by all the reblock calls
     size = ctypes.c_size_t()
     for q in (bsa.make_problem(1, 2, 4096, top_k=8, sink_rows=100),
               bsa.make_problem(1, 2, 4096, top_k=8, summary="reweight", anchor_rows=4000)):
@@ -202,6 +215,10 @@ def test_reblock_entry_points_validate():
         assert L.bsa_permute_rows(ctypes.byref(q), fake, fake, fake, fake, fake, fake, fake,
                                   None) == bsa.BSA_ERR_UNSUPPORTED
         assert L.bsa_unpermute_rows(ctypes.byref(q), fake, fake, fake, None) == bsa.BSA_ERR_UNSUPPORTED
+        assert L.bsa_pool_reordered(ctypes.byref(q), f, f, f, f, f, f, f, f, f, odd, f, big,
+                                    None) == bsa.BSA_ERR_UNSUPPORTED
+        assert L.bsa_forward_reordered(ctypes.byref(q), f, f, f, f, f, f, f, None, f, big, odd,
+                                       None) == bsa.BSA_ERR_UNSUPPORTED
     # an anchor over every row does not depend on the order
     for rows in (0, 4096):
         q = bsa.make_problem(1, 2, 4096, top_k=8, summary="reweight", anchor_rows=rows)

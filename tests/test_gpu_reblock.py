@@ -142,6 +142,48 @@ def test_reblock_attention(torch_cuda, N, top_k, summary, tau, extra):
                     extra=extra)
 
 
+@pytest.mark.parametrize("N,top_k,summary,tau,extra", [
+    (4173, 8, "mean", None, 0),
+    (4173, 6, "reweight", None, 0),
+    (4096, 32, "mean", 1.0, 0),
+    (2000, 4, "mean", None, 64),
+    (50000, 4, "mean", None, 0),   # 391 blocks: the head-synchronous attention grid
+])
+def test_reordered_calls_equal_permuted_copies(torch_cuda, N, top_k, summary, tau, extra):
+    """bsa_pool_reordered / bsa_forward_reordered (rows read through perm, the
+    output written back through it) against the permuted-copy path
+    (bsa_permute_rows, the plain calls, bsa_unpermute_rows): the same bits in
+    every output, and k_r equal to the permuted K."""
+    torch = torch_cuda
+    _log("case reordered calls N=%d k=%d %s tau=%s extra=%d" % (N, top_k, summary, tau, extra))
+    qb, kb, vb = generate(custom(N, heads=2, seed=71), threads=2)
+    q, k, v = (to_device(x) for x in (qb, kb, vb))
+    kw = dict(top_k=top_k, summary=summary, tau=tau, extra_tokens=extra)
+    out_a, aux_a = bsa.attention(q, k, v, reblock=True, return_aux=True, **kw)
+    perm = aux_a["perm"]
+    p = aux_a["problem"]
+    qr, kr, vr = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bsa.bsa_permute_rows(p, perm, q, k, v, qr, kr, vr)
+    out_r, aux_b = bsa.attention(qr, kr, vr, return_aux=True, **kw)
+    out_b = torch.empty_like(out_r)
+    bsa.bsa_unpermute_rows(p, perm, out_r, out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(aux_a["k_r"], kr)
+    for name in ("q_pool", "k_pool", "sum_k", "sum_v", "sum_bias", "block_idx", "token_idx"):
+        if aux_a[name] is not None:
+            assert torch.equal(aux_a[name], aux_b[name]), name
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    # k_out is written row by row: every element of it, nothing past it
+    G = 4096
+    n_el = 2 * N * 128
+    k_out = torch.full((n_el + G,), float("nan"), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    bsa.bsa_pool_reordered(p, perm, q, k, v, aux_a["q_pool"], aux_a["k_pool"], aux_a["sum_k"],
+                           aux_a["sum_v"], aux_a["sum_bias"], k_out, aux_a["workspace"])
+    torch.cuda.synchronize()
+    assert torch.equal(k_out[:n_el].view(1, 2, N, 128), kr)
+    assert bool(torch.isnan(k_out[n_el:].float()).all())
+
+
 def test_reblock_rejects_position_options(torch_cuda):
     qb, kb, vb = generate(custom(1000, heads=1, seed=64), threads=1)
     q, k, v = (to_device(x) for x in (qb, kb, vb))
