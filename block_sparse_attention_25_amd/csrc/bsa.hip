@@ -579,6 +579,48 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
   }
 }
 
+// ------------------------------------------------------------ row order ---
+// The order in which the attention grid visits one head's query blocks: by
+// their first three kept blocks, then by block (a bitonic sort of 64-bit keys
+// in LDS, one workgroup per head).  Every query block walks its kept blocks
+// in ascending order, so workgroups that run at the same time on an XCD then
+// start on the same key blocks and meet in its L2 (measured at 295 blocks:
+// attention 2% faster than in sequence order).
+__global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restrict__ block_idx,
+                                                         int32_t* __restrict__ order, int nb, int krow) {
+  __shared__ uint64_t key[BSA_MAX_BLOCKS];
+  const size_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  int n2 = 1;
+  while (n2 < nb) n2 <<= 1;
+  for (int i = tid; i < n2; i += 1024) {
+    uint64_t kv = ~0ull;  // padding sorts last
+    if (i < nb) {
+      const int32_t* row = block_idx + (bh * nb + i) * (size_t)krow;
+      kv = (uint64_t)i;  // bits [0, 11): the block; three 12-bit fields above
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < krow) kv |= (uint64_t)(row[j] + 1) << (11 + 12 * (2 - j));  // -1 padding -> 0
+    }
+    key[i] = kv;
+  }
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (n2 >> 1); i += 1024) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const uint64_t a = key[lo], b = key[hi];
+        if ((a > b) == ((lo & size) == 0)) {
+          key[lo] = b;
+          key[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < nb; i += 1024) order[bh * nb + i] = (int32_t)(key[i] & 2047u);
+}
+
 // ------------------------------------------------------------- attention ---
 // One workgroup (4 wavefronts, 2 workgroups per CU) per (b, h, query block r):
 // 128 query rows, wavefront w owning queries [32w, 32w + 32).  The keys are
@@ -642,8 +684,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ sum_k,
     const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
     const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ perm, uint16_t* __restrict__ out, int N,
-    int nb, int krow, int nsb, float scale_log2, int total_wg, int chunk, int f0, int f1, int E) {
+    const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ perm, const int32_t* __restrict__ order,
+    uint16_t* __restrict__ out, int N, int nb, int krow, int nsb, float scale_log2, int total_wg, int chunk, int f0,
+    int f1, int E) {
   // LDS buffers as distinct variables, so the compiler can tell the DMA
   // targets from the buffers being read
   __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
@@ -673,7 +716,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     rr = logical % nb;
     bh = (size_t)(logical / nb);
   }
-  const int r = (rr + f0) % nb;
+  // position rr of the head's visiting order (row_order_kernel), or with
+  // sinks rr blocks after the first sink block
+  const int r = order ? order[bh * nb + rr] : (rr + f0) % nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
   const int g = lane >> 5, ln = lane & 31;
@@ -1680,7 +1725,7 @@ struct Geometry {
 };
 
 struct WsLayout {
-  size_t vt, svt, apart, anchor, tsel, total;
+  size_t vt, svt, apart, anchor, tsel, order, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1743,6 +1788,9 @@ WsLayout ws_layout(const Geometry& g) {
     w.tsel = off;
     off = align256(off + bh * g.nb * 4 * SEG_CAP * sizeof(uint64_t));
   }
+  // the attention grid's visiting order of each head's query blocks
+  w.order = off;
+  off = align256(off + bh * g.nb * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -1781,7 +1829,7 @@ int check_forward(const Geometry& g, const void* q, const void* k, const void* s
 }
 
 int launch_attention(const Geometry& g, const void* q, const void* k, const void* sum_k,
-                     const float* sum_bias, const int32_t* block_idx, const char* ws, const void* v,
+                     const float* sum_bias, const int32_t* block_idx, char* ws, const void* v,
                      const int32_t* tok_idx, const int32_t* perm, void* out, hipStream_t stream) {
   const WsLayout w = ws_layout(g);
   // The head-synchronous map (8 chunks of ceil(nb / 8) query blocks per head)
@@ -1793,10 +1841,18 @@ int launch_attention(const Geometry& g, const void* q, const void* k, const void
   const int chunk = (g.f1 < g.f0 && g.nb > 384) ? (int)((g.nb + 7) / 8) : 0;
   const int total = chunk > 0 ? (int)(g.B * g.H * 8 * chunk) : (int)(g.B * g.H * g.nb);
   const float scale_log2 = (float)(g.scale * 1.4426950408889634);
+  // the visiting order by kept blocks (none with sinks: there the dense sink
+  // rows go first)
+  int32_t* order = nullptr;
+  if (g.f1 < g.f0 && g.k > 0 && block_idx) {
+    order = (int32_t*)(ws + w.order);
+    hipLaunchKernelGGL(row_order_kernel, dim3((unsigned)(g.B * g.H)), dim3(1024), 0, stream, block_idx, order,
+                       (int)g.nb, (int)g.k);
+  }
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, stream, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)(ws + w.vt), (const uint16_t*)sum_k,
                      (const uint16_t*)(ws + w.svt), sum_bias, block_idx, (const uint16_t*)v, tok_idx, perm,
-                     (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, chunk,
+                     order, (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, chunk,
                      (int)g.f0, (int)g.f1, tok_idx ? g.E : 0);
   return launch_status();
 }
@@ -1937,7 +1993,7 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
 }
 
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
-                const float* sum_bias, const int32_t* block_idx, const void* workspace,
+                const float* sum_bias, const int32_t* block_idx, void* workspace,
                 size_t workspace_bytes, void* out, void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
@@ -1945,7 +2001,7 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
   if (g.E > 0) return BSA_ERR_INVALID;  // extra tokens go through bsa_forward_tokens
   if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
     return st;
-  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, (const char*)workspace, nullptr, nullptr,
+  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, (char*)workspace, nullptr, nullptr,
                           nullptr, out, (hipStream_t)hip_stream);
 }
 
@@ -1973,7 +2029,7 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
 
 int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
                        const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                       const int32_t* token_idx, const void* workspace, size_t workspace_bytes, void* out,
+                       const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
                        void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
@@ -1981,7 +2037,7 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
   if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
     return st;
   hipStream_t s = (hipStream_t)hip_stream;
-  const char* ws = (const char*)workspace;
+  char* ws = (char*)workspace;
   if (g.E == 0) return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, nullptr, out, s);
   if (!v || !token_idx || !aligned16(v)) return BSA_ERR_INVALID;
   return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, v, token_idx, nullptr, out, s);
@@ -1989,7 +2045,7 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
 
 int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k_r,
                           const void* v, const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                          const int32_t* token_idx, const void* workspace, size_t workspace_bytes, void* out,
+                          const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
                           void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
@@ -2000,7 +2056,7 @@ int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void*
     return st;
   if (out == q || out == k_r) return BSA_ERR_INVALID;
   hipStream_t s = (hipStream_t)hip_stream;
-  const char* ws = (const char*)workspace;
+  char* ws = (char*)workspace;
   if (g.E == 0) return launch_attention(g, q, k_r, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, perm, out, s);
   if (!v || !token_idx || !aligned16(v) || out == v) return BSA_ERR_INVALID;
   return launch_attention(g, q, k_r, sum_k, sum_bias, block_idx, ws, v, token_idx, perm, out, s);

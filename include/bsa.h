@@ -118,9 +118,10 @@ int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff);
  * transposed (feature-major, key order interleaved for the matrix cores, zero
  * past the end of a short block), the summary values transposed in groups of
  * 128 blocks, in reweight mode the anchor and its per-block partial sums,
- * and with extra tokens the candidate keys of bsa_select_tokens (16 KB per
- * query block).  Its contents are private to this library; it must be
- * 256-byte aligned.
+ * with extra tokens the candidate keys of bsa_select_tokens (16 KB per
+ * query block), and the order in which bsa_forward visits each head's query
+ * blocks (written by bsa_forward itself).  Its contents are private to this
+ * library; it must be 256-byte aligned, and it serves one call at a time.
  */
 int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes);
 
@@ -183,7 +184,11 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
  *   block_idx  in   int32 [B, H, nb, k]    distinct, in [0, nb), ascending,
  *                                          then -1 padding; the kernel trusts
  *                                          this (bsa_select's output)
- *   workspace  in   as filled by bsa_pool for the same q, k, v and problem
+ *   workspace  in/out  as filled by bsa_pool for the same q, k, v and
+ *                   problem; bsa_forward writes only its visiting-order
+ *                   region (query blocks sorted by their first kept blocks,
+ *                   so that workgroups running together read the same key
+ *                   blocks; the result does not depend on the order)
  *   out        out  bf16 [B, H, N, 128]
  *
  * For query i of block r: logits scale * q_i . k_j for every row j of every
@@ -196,7 +201,7 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
  * bsa_forward_tokens.
  */
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
-                const float* sum_bias, const int32_t* block_idx, const void* workspace,
+                const float* sum_bias, const int32_t* block_idx, void* workspace,
                 size_t workspace_bytes, void* out, void* hip_stream);
 
 /*
@@ -237,7 +242,7 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
  *                   E == 0): tokens in [0, N), distinct, none in a block of
  *                   block_idx[r], valid entries first, then -1 padding; the
  *                   kernels trust this (bsa_select_tokens' output)
- *   workspace  in   as filled by bsa_pool for the same q, k, v and problem
+ *   workspace  in/out  as for bsa_forward
  *   out        out  bf16 [B, H, N, 128]
  *
  * The attention kernel takes each query block's extra tokens first (their K
@@ -247,7 +252,7 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
  */
 int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
                        const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                       const int32_t* token_idx, const void* workspace, size_t workspace_bytes,
+                       const int32_t* token_idx, void* workspace, size_t workspace_bytes,
                        void* out, void* hip_stream);
 
 /*
@@ -330,7 +335,7 @@ int bsa_pool_reordered(const bsa_problem* p, const int32_t* perm, const void* q,
                        void* hip_stream);
 int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k_r,
                           const void* v, const void* sum_k, const float* sum_bias,
-                          const int32_t* block_idx, const int32_t* token_idx, const void* workspace,
+                          const int32_t* block_idx, const int32_t* token_idx, void* workspace,
                           size_t workspace_bytes, void* out, void* hip_stream);
 
 /*
