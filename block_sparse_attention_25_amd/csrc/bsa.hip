@@ -584,10 +584,13 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
 // their first three kept blocks, then by block (a bitonic sort of 64-bit keys
 // in LDS, one workgroup per head).  Every query block walks its kept blocks
 // in ascending order, so workgroups that run at the same time on an XCD then
-// start on the same key blocks and meet in its L2 (measured at 295 blocks:
-// attention 2% faster than in sequence order).
+// start on the same key blocks and meet in its L2 (measured inside whole
+// steps: attention 2.7% faster at 295 blocks, 1.6% at 1,045).  Conditioning
+// sink query blocks [f0, f1] (dense rows, the longest) come first.  The
+// attention calls on a reblocked row order keep that order instead.
 __global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restrict__ block_idx,
-                                                         int32_t* __restrict__ order, int nb, int krow) {
+                                                         int32_t* __restrict__ order, int nb, int krow, int f0,
+                                                         int f1) {
   __shared__ uint64_t key[BSA_MAX_BLOCKS];
   const size_t bh = blockIdx.x;
   const int tid = threadIdx.x;
@@ -598,9 +601,13 @@ __global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restri
     if (i < nb) {
       const int32_t* row = block_idx + (bh * nb + i) * (size_t)krow;
       kv = (uint64_t)i;  // bits [0, 11): the block; three 12-bit fields above
+      if (i < f0 || i > f1) {
+        // a kept block c enters as c + 1 >= 1, so these sort after the sink rows
+        kv |= (uint64_t)1 << 47;
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < krow) kv |= (uint64_t)(row[j] + 1) << (11 + 12 * (2 - j));  // -1 padding -> 0
+        for (int j = 0; j < 3; ++j)
+          if (j < krow) kv |= (uint64_t)(row[j] + 1) << (11 + 12 * (2 - j));  // -1 padding -> 0
+      }
     }
     key[i] = kv;
   }
@@ -695,11 +702,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ uint32_t selmask[BSA_MAX_BLOCKS / 32];
   __shared__ int32_t sidx[BSA_MAX_BLOCKS];  // this query block's selected blocks
 
-  // Workgroup -> (b, h, query block).  Workgroups are dealt to the 8 XCDs
-  // round-robin.  With chunk = 0 each XCD takes a contiguous range of (head,
-  // query block), each head's query blocks in sequence order starting at the
-  // first sink block (so the longer dense sink rows are dispatched first).
-  // With chunk > 0 XCD x takes query blocks [x chunk, x chunk + chunk) of
+  // Workgroup -> (b, h, position in the head's visiting order).  Workgroups
+  // are dealt to the 8 XCDs round-robin.  With chunk = 0 each XCD takes a
+  // contiguous range of (head, position), so the longer dense sink rows,
+  // first in each head's order, spread over the XCDs and start first.
+  // With chunk > 0 XCD x takes positions [x chunk, x chunk + chunk) of
   // every head in turn, so the XCDs all work on the same one or two heads at
   // a time and their L2 misses meet in the memory-side cache, while each L2
   // still sees neighbouring query blocks; padding workgroups past nb leave at
@@ -716,8 +723,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     rr = logical % nb;
     bh = (size_t)(logical / nb);
   }
-  // position rr of the head's visiting order (row_order_kernel), or with
-  // sinks rr blocks after the first sink block
+  // position rr of the head's visiting order (row_order_kernel), else (no
+  // selection) rr blocks after the first sink block
   const int r = order ? order[bh * nb + rr] : (rr + f0) % nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep in SGPRs
@@ -1841,13 +1848,14 @@ int launch_attention(const Geometry& g, const void* q, const void* k, const void
   const int chunk = (g.f1 < g.f0 && g.nb > 384) ? (int)((g.nb + 7) / 8) : 0;
   const int total = chunk > 0 ? (int)(g.B * g.H * 8 * chunk) : (int)(g.B * g.H * g.nb);
   const float scale_log2 = (float)(g.scale * 1.4426950408889634);
-  // the visiting order by kept blocks (none with sinks: there the dense sink
-  // rows go first)
+  // the visiting order by kept blocks, sink query blocks first; not on a
+  // reblocked row order, whose neighbouring query blocks already share their
+  // key blocks (there the sort measured 1.7% slower, elsewhere 1.1-2.7% faster)
   int32_t* order = nullptr;
-  if (g.f1 < g.f0 && g.k > 0 && block_idx) {
+  if (g.k > 0 && block_idx && !perm) {
     order = (int32_t*)(ws + w.order);
     hipLaunchKernelGGL(row_order_kernel, dim3((unsigned)(g.B * g.H)), dim3(1024), 0, stream, block_idx, order,
-                       (int)g.nb, (int)g.k);
+                       (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1);
   }
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, stream, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)(ws + w.vt), (const uint16_t*)sum_k,

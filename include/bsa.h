@@ -187,8 +187,9 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
  *   workspace  in/out  as filled by bsa_pool for the same q, k, v and
  *                   problem; bsa_forward writes only its visiting-order
  *                   region (query blocks sorted by their first kept blocks,
- *                   so that workgroups running together read the same key
- *                   blocks; the result does not depend on the order)
+ *                   sink query blocks first, so that workgroups running
+ *                   together read the same key blocks; the result does not
+ *                   depend on the order)
  *   out        out  bf16 [B, H, N, 128]
  *
  * For query i of block r: logits scale * q_i . k_j for every row j of every
