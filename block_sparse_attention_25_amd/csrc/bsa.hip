@@ -984,7 +984,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // Returns the O rescale factor (1 unless the reference max moved).
   auto region_a = [&](const uint16_t* kn, f32x16* sn, f32x16* sc, bool need_add,
                       const float* addvc, bf16x8* pb, const TileSrc& dk, uint16_t* kd,
-                      const TileSrc& dv, uint16_t* vd) -> float {
+                      const TileSrc& dv, uint16_t* vd, const uint16_t* vc, bf16x8* vpre) -> float {
     bf16x8 kop0 = k_operand(kn, 0), kop1 = k_operand(kn, 1), kop2;
     float mx = -INFINITY, m_use = 0.f, alpha = 1.f, psum = 0.f;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -1051,6 +1051,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       }
       kop0 = kop1;
       kop1 = kop2;
+      // the first two V^T operands of region B, read in the last two slots
+      // (V^T(t) has been in LDS since the step began; 0.3-0.5% faster)
+      if (i >= 14) vpre[i - 14] = v_operand(vc, i - 14);
       // no scheduling fence here: the compiler's own interleaving of the
       // slots measures about 1.5% faster than a fixed slot order
     }
@@ -1059,10 +1062,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   };
 
   // Region B: O^T += V^T(t) P(t)^T, 16 MFMAs (db fastest: 4 independent chains)
-  auto region_b = [&](const uint16_t* vc, const bf16x8* pb, auto&& bookkeeping) {
+  auto region_b = [&](const uint16_t* vc, const bf16x8* pb, const bf16x8* vpre, auto&& bookkeeping) {
     // operands read three slots ahead (region B has no VALU work to hide
-    // the LDS latency behind)
-    bf16x8 vop0 = v_operand(vc, 0), vop1 = v_operand(vc, 1), vop2 = v_operand(vc, 2), vop3;
+    // the LDS latency behind); the first two come from region A
+    bf16x8 vop0 = vpre[0], vop1 = vpre[1], vop2 = v_operand(vc, 2), vop3;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 3 < 16) vop3 = v_operand(vc, i + 3);
@@ -1096,21 +1099,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     // early: the block index of half tile t+3 and the mask of half tile t+1
     const int c3 = tile_block(t + 3);
     const float mask1 = mask_value(d1);
-    bf16x8 pb[4];
+    bf16x8 pb[4], vpre[2];
     float alpha;
     // the softmax-heavy region issues at raised priority so its VALU work
     // is not starved by the other wavefront's MFMA-only region on this SIMD
     __builtin_amdgcn_s_setprio(3);
     if (need_add)
-      alpha = region_a(kn, sn, sc, true, addvc, pb, d2, kd, d1, vd);
+      alpha = region_a(kn, sn, sc, true, addvc, pb, d2, kd, d1, vd, vc, vpre);
     else
-      alpha = region_a(kn, sn, sc, false, addvc, pb, d2, kd, d1, vd);
+      alpha = region_a(kn, sn, sc, false, addvc, pb, d2, kd, d1, vd, vc, vpre);
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
     __builtin_amdgcn_s_setprio(0);
-    region_b(vc, pb, [&]() {
+    region_b(vc, pb, vpre, [&]() {
       store_mask(d1, mask1, addvn);
       d0 = d1;
       d1 = d2;
