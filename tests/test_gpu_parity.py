@@ -271,8 +271,8 @@ def test_forward_with_given_indices(torch_cuda):
         assert mx <= MAX_ABS and mean <= MEAN_ABS
 
 
-@pytest.mark.parametrize("heads,extra", [(3, 0), (1, 64)])
-def test_head_synchronous_map_every_block(torch_cuda, heads, extra):
+@pytest.mark.parametrize("batch,heads,extra", [(1, 3, 0), (2, 1, 0), (1, 1, 64)])
+def test_head_synchronous_map_every_block(torch_cuda, batch, heads, extra):
     """Past 384 blocks the attention grid deals each head to the 8 XCDs in
     chunks of ceil(nb / 8) query blocks with padding workgroups at the end
     (391 blocks: chunks of 49, one padding workgroup per head); every query
@@ -280,13 +280,15 @@ def test_head_synchronous_map_every_block(torch_cuda, heads, extra):
     is slow, the query blocks on both sides of each chunk boundary and the
     last two)."""
     N = 50000
-    _log("case head-synchronous map heads=%d extra=%d" % (heads, extra))
-    w = custom(N, heads=heads, seed=43 + extra)
+    _log("case head-synchronous map batch=%d heads=%d extra=%d" % (batch, heads, extra))
+    w = custom(N, heads=heads, batch=batch, seed=43 + extra + batch)
     qb, kb, vb = generate(w, threads=16)
     host = _run_gpu(torch_cuda, qb, kb, vb, top_k=4, extra_tokens=extra)
     rows = None if not extra else sorted({0, 389, 390} | {49 * x + d for x in range(1, 8) for d in (-1, 0)})
-    for h in range(heads):
-        _check_head(host, qb, kb, vb, 0, h, 4, label="nb391-h%d" % h, extra=extra, query_blocks=rows)
+    for b in range(batch):
+        for h in range(heads):
+            _check_head(host, qb, kb, vb, b, h, 4, label="nb391-b%d-h%d" % (b, h), extra=extra,
+                        query_blocks=rows)
 
 
 @pytest.mark.parametrize("N", [262144, 262100])
