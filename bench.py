@@ -26,7 +26,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PAGES_MS = {"768p_5s": 30.7, "768p_10s": 61.8, "2k_5s": 121.8}  # RTX PRO 6000, context only
 
@@ -103,6 +103,23 @@ def counted_flops(torch, idx, N, nb, H, B, dense=(), tok=None):
     exact = int((per_row * n).sum().item())
     summary = int((n * n_skip).sum().item())
     return 4 * 128 * exact, 4 * 128 * summary
+
+
+def tie_zone_rows(torch, q_pool, k_pool, k, plain_topk):
+    """Rows whose k-th and (k+1)-th block scores (float64 dot products of the
+    pooled vectors) differ by less than 1e-4 relative: the rows where the
+    selection may legitimately differ from an exact ranking.  Plain top-k
+    only (None otherwise)."""
+    if not plain_topk or k == 0 or k >= q_pool.shape[2]:
+        return None if not plain_topk else 0
+    n = 0
+    for b in range(q_pool.shape[0]):
+        for h in range(q_pool.shape[1]):
+            s = q_pool[b, h].double() @ k_pool[b, h].double().T
+            top = torch.topk(s, k + 1, dim=-1).values
+            a, c = top[:, k - 1], top[:, k]
+            n += int(((a - c).abs() < 1e-4 * torch.maximum(a.abs(), c.abs())).sum().item())
+    return n
 
 
 def cpu_baseline(w, qb, kb, vb, budget_s):
@@ -209,9 +226,9 @@ def main():
     if w.reblock:
         perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
         rws = torch.empty(bsa.bsa_reblock_workspace_bytes(p), dtype=torch.uint8, device=dev)
-        kr = torch.empty_like(k)   # the keys in the new order
+        kr, vr = torch.empty_like(k), torch.empty_like(v)   # keys and values in the new order
     else:
-        kr = k
+        kr, vr = k, v
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
 
@@ -221,7 +238,7 @@ def main():
             bsa.bsa_reblock(p, q, k, perm, rws)
         if e: e[1].record()
         if w.reblock:
-            bsa.bsa_pool_reordered(p, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, kr, ws)
+            bsa.bsa_pool_reordered(p, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, kr, vr, ws)
         else:
             bsa.bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws)
         if e: e[2].record()
@@ -231,12 +248,11 @@ def main():
             bsa.bsa_select_tokens(p, q_pool, kr, idx, tok, ws)
         if e: e[4].record()
         if w.reblock:
-            bsa.bsa_forward_reordered(p, perm, q, kr, v if tok is not None else None, sum_k, sum_bias, idx,
-                                      tok, ws, out)
+            bsa.bsa_forward_reordered(p, perm, q, kr, vr, sum_k, sum_v, sum_bias, idx, tok, out, ws)
         elif tok is not None:
-            bsa.bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx, tok, ws, out)
+            bsa.bsa_forward_tokens(p, q, k, v, sum_k, sum_v, sum_bias, idx, tok, out, ws)
         else:
-            bsa.bsa_forward(p, q, k, sum_k, sum_bias, idx, ws, out)
+            bsa.bsa_forward(p, q, k, v, sum_k, sum_v, sum_bias, idx, out, ws)
         if e: e[5].record()
 
     for _ in range(args.warmup):
@@ -255,12 +271,14 @@ def main():
     flops, summary_flops = counted_flops(torch, idx, N, nb, H, B, dense, tok)
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
-    # pool: read Q, K, V once; write q_pool, k_pool (fp32), sum_k, sum_v (bf16),
-    # the bias, V^T of every block (32 KiB) and one summary-V^T column (256 B)
-    pool_bytes = 3 * B * H * N * 128 * 2 + B * H * nb * (2 * 512 + 2 * 256 + 4 + 32768 + 256)
-    if w.reblock:  # plus the keys in the new order, and each row's perm entry read twice
-        pool_bytes += B * H * N * (128 * 2 + 2 * 4)
+    # pool, algorithmic bytes: read Q, K, V once; write q_pool, k_pool (fp32),
+    # sum_k, sum_v (bf16) and the bias: 1,540 B per block
+    pool_bytes = 3 * B * H * N * 128 * 2 + B * H * nb * (2 * 512 + 2 * 256 + 4)
+    # on a reblocked order the pool also writes K and V in the new order and
+    # reads each row's perm entry twice (listed apart, not in pool_frac)
+    pool_copy_bytes = B * H * N * (2 * 128 * 2 + 2 * 4) if w.reblock else 0
     sel_bytes = 2 * B * H * nb * 128 * 4 + B * H * nb * kk * 4
+    tie_rows = tie_zone_rows(torch, q_pool, k_pool, kk, w.tau is None and w.sink_rows == 0)
 
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -298,7 +316,13 @@ def main():
         "counted_tflop_per_step": round(flops / 1e12, 4),
         "summary_tflop_per_step": round(summary_flops / 1e12, 4),
         "pool_gbs": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+        "pool_frac": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "pool_bytes": pool_bytes,
+        **({"pool_reorder_copy_bytes": pool_copy_bytes,
+            "pool_gbs_with_copies": round((pool_bytes + pool_copy_bytes) / (pool_ms * 1e-3) / 1e9, 1)}
+           if w.reblock else {}),
         "select_gbs": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+        "tie_zone_rows": tie_rows,
         "roofline": {"bound": "mfma",
                      "kernel": "attn_fwd_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,

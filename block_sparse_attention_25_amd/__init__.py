@@ -73,17 +73,17 @@ def lib() -> ctypes.CDLL:
         L.bsa_status_str.restype = ctypes.c_char_p
         L.bsa_problem_blocks.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         L.bsa_problem_blocks.restype = ctypes.c_int
-        L.bsa_workspace_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
-        L.bsa_workspace_bytes.restype = ctypes.c_int
+        L.bsa_workspace_bytes.argtypes = [_P]
+        L.bsa_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_pool.argtypes = [_P] + [_vp] * 9 + [ctypes.c_size_t, _vp]
         L.bsa_pool.restype = ctypes.c_int
         L.bsa_select.argtypes = [_P, _vp, _vp, _vp, _vp]
         L.bsa_select.restype = ctypes.c_int
-        L.bsa_forward.argtypes = [_P] + [_vp] * 6 + [ctypes.c_size_t, _vp, _vp]
+        L.bsa_forward.argtypes = [_P] + [_vp] * 9 + [ctypes.c_size_t, _vp]
         L.bsa_forward.restype = ctypes.c_int
         L.bsa_select_tokens.argtypes = [_P] + [_vp] * 5 + [ctypes.c_size_t, _vp]
         L.bsa_select_tokens.restype = ctypes.c_int
-        L.bsa_forward_tokens.argtypes = [_P] + [_vp] * 8 + [ctypes.c_size_t, _vp, _vp]
+        L.bsa_forward_tokens.argtypes = [_P] + [_vp] * 10 + [ctypes.c_size_t, _vp]
         L.bsa_forward_tokens.restype = ctypes.c_int
         L.bsa_reblock_workspace_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
         L.bsa_reblock_workspace_bytes.restype = ctypes.c_int
@@ -93,9 +93,9 @@ def lib() -> ctypes.CDLL:
         L.bsa_permute_rows.restype = ctypes.c_int
         L.bsa_unpermute_rows.argtypes = [_P] + [_vp] * 4
         L.bsa_unpermute_rows.restype = ctypes.c_int
-        L.bsa_pool_reordered.argtypes = [_P] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+        L.bsa_pool_reordered.argtypes = [_P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
         L.bsa_pool_reordered.restype = ctypes.c_int
-        L.bsa_forward_reordered.argtypes = [_P] + [_vp] * 9 + [ctypes.c_size_t, _vp, _vp]
+        L.bsa_forward_reordered.argtypes = [_P] + [_vp] * 11 + [ctypes.c_size_t, _vp]
         L.bsa_forward_reordered.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -124,13 +124,18 @@ def bsa_problem_blocks(p: Problem):
 
 
 def bsa_workspace_bytes(p: Problem) -> int:
-    n = ctypes.c_size_t()
-    _raise(lib().bsa_workspace_bytes(ctypes.byref(p), ctypes.byref(n)), "bsa_workspace_bytes")
-    return n.value
+    """Scratch bytes covering every entry point for problem p (0 for a
+    rejected problem: the problem is validated first, so that raises)."""
+    bsa_problem_blocks(p)
+    return int(lib().bsa_workspace_bytes(ctypes.byref(p)))
 
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream):
@@ -139,10 +144,9 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def bsa_pool(p: Problem, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, stream=None):
+def bsa_pool(p: Problem, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace=None, stream=None):
     _raise(lib().bsa_pool(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(q_pool), _ptr(k_pool),
-                          _ptr(sum_k), _ptr(sum_v), _ptr(sum_bias), _ptr(workspace),
-                          0 if workspace is None else workspace.numel() * workspace.element_size(),
+                          _ptr(sum_k), _ptr(sum_v), _ptr(sum_bias), _ptr(workspace), _nbytes(workspace),
                           _stream(stream)), "bsa_pool")
 
 
@@ -151,27 +155,25 @@ def bsa_select(p: Problem, q_pool, k_pool, block_idx, stream=None):
                             _stream(stream)), "bsa_select")
 
 
-def bsa_forward(p: Problem, q, k, sum_k, sum_bias, block_idx, workspace, out, stream=None):
-    _raise(lib().bsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(sum_k), _ptr(sum_bias),
-                             _ptr(block_idx), _ptr(workspace),
-                             0 if workspace is None else workspace.numel() * workspace.element_size(),
-                             _ptr(out), _stream(stream)), "bsa_forward")
+def bsa_forward(p: Problem, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, workspace=None,
+                stream=None):
+    _raise(lib().bsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sum_k), _ptr(sum_v),
+                             _ptr(sum_bias), _ptr(block_idx), _ptr(out), _ptr(workspace),
+                             _nbytes(workspace), _stream(stream)), "bsa_forward")
 
 
 def bsa_select_tokens(p: Problem, q_pool, k, block_idx, token_idx, workspace, stream=None):
     _raise(lib().bsa_select_tokens(ctypes.byref(p), _ptr(q_pool), _ptr(k), _ptr(block_idx),
-                                   _ptr(token_idx), _ptr(workspace),
-                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                   _ptr(token_idx), _ptr(workspace), _nbytes(workspace),
                                    _stream(stream)), "bsa_select_tokens")
 
 
-def bsa_forward_tokens(p: Problem, q, k, v, sum_k, sum_bias, block_idx, token_idx, workspace, out,
-                       stream=None):
+def bsa_forward_tokens(p: Problem, q, k, v, sum_k, sum_v, sum_bias, block_idx, token_idx, out,
+                       workspace=None, stream=None):
     _raise(lib().bsa_forward_tokens(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sum_k),
-                                    _ptr(sum_bias), _ptr(block_idx), _ptr(token_idx),
-                                    _ptr(workspace),
-                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                    _ptr(out), _stream(stream)), "bsa_forward_tokens")
+                                    _ptr(sum_v), _ptr(sum_bias), _ptr(block_idx), _ptr(token_idx),
+                                    _ptr(out), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "bsa_forward_tokens")
 
 
 def bsa_reblock_workspace_bytes(p: Problem) -> int:
@@ -183,8 +185,7 @@ def bsa_reblock_workspace_bytes(p: Problem) -> int:
 
 def bsa_reblock(p: Problem, q, k, perm, workspace, stream=None):
     _raise(lib().bsa_reblock(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(perm), _ptr(workspace),
-                             0 if workspace is None else workspace.numel() * workspace.element_size(),
-                             _stream(stream)), "bsa_reblock")
+                             _nbytes(workspace), _stream(stream)), "bsa_reblock")
 
 
 def bsa_permute_rows(p: Problem, perm, q, k, v, q_out, k_out, v_out, stream=None):
@@ -198,22 +199,20 @@ def bsa_unpermute_rows(p: Problem, perm, x, out, stream=None):
                                     _stream(stream)), "bsa_unpermute_rows")
 
 
-def bsa_pool_reordered(p: Problem, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out,
-                       workspace, stream=None):
+def bsa_pool_reordered(p: Problem, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out,
+                       workspace=None, stream=None):
     _raise(lib().bsa_pool_reordered(ctypes.byref(p), _ptr(perm), _ptr(q), _ptr(k), _ptr(v),
                                     _ptr(q_pool), _ptr(k_pool), _ptr(sum_k), _ptr(sum_v),
-                                    _ptr(sum_bias), _ptr(k_out), _ptr(workspace),
-                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                    _stream(stream)), "bsa_pool_reordered")
+                                    _ptr(sum_bias), _ptr(k_out), _ptr(v_out), _ptr(workspace),
+                                    _nbytes(workspace), _stream(stream)), "bsa_pool_reordered")
 
 
-def bsa_forward_reordered(p: Problem, perm, q, k_r, v, sum_k, sum_bias, block_idx, token_idx, workspace,
-                          out, stream=None):
-    _raise(lib().bsa_forward_reordered(ctypes.byref(p), _ptr(perm), _ptr(q), _ptr(k_r), _ptr(v),
-                                       _ptr(sum_k), _ptr(sum_bias), _ptr(block_idx), _ptr(token_idx),
-                                       _ptr(workspace),
-                                       0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                       _ptr(out), _stream(stream)), "bsa_forward_reordered")
+def bsa_forward_reordered(p: Problem, perm, q, k_r, v_r, sum_k, sum_v, sum_bias, block_idx, token_idx,
+                          out, workspace=None, stream=None):
+    _raise(lib().bsa_forward_reordered(ctypes.byref(p), _ptr(perm), _ptr(q), _ptr(k_r), _ptr(v_r),
+                                       _ptr(sum_k), _ptr(sum_v), _ptr(sum_bias), _ptr(block_idx),
+                                       _ptr(token_idx), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                       _stream(stream)), "bsa_forward_reordered")
 
 
 # ---------------------------------------------------------------- helpers ---
@@ -267,7 +266,7 @@ def _check_qkv(q, k, v):
 
 def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows=0, scale=None,
               sink_rows=0, sink_start=None, tau=None, extra_tokens=0, reblock=False,
-              return_aux=False, stream=None):
+              return_aux=False, stream=None, out=None):
     """Block-sparse attention of bf16 q, k, v [B, H, N, 128] on the GPU.
 
     top_k counts 128-token key blocks (or give top_k_ratio, e.g. "0.1");
@@ -282,11 +281,12 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     skipped, those scoring highest against its pooled query (token_idx in the
     aux dict).  reblock=True runs the path on Spark-Reblock's row order (the
     q_reuse_k layout: Q, K and V permuted alike, the output put back in
-    place; perm and k_r, the keys in the new order, in the aux dict, the
-    other aux tensors in the new order); it rejects sink rows and an anchor
-    over part of the rows.  Returns out
-    [B, H, N, 128] bf16, plus a dict of intermediate tensors when return_aux
-    is set."""
+    place; perm and k_r, v_r, the keys and values in the new order, in the
+    aux dict, the other aux tensors in the new order); it rejects sink rows
+    and an anchor over part of the rows.  Returns out
+    [B, H, N, 128] bf16 (written into `out` when given: a contiguous bf16
+    tensor of q's shape on its device, not overlapping q, k or v), plus a
+    dict of intermediate tensors when return_aux is set."""
     import torch
     _check_qkv(q, k, v)
     B, H, N, _ = q.shape
@@ -310,12 +310,17 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     sum_bias = torch.empty((B, H, nb), dtype=f32, device=dev)
     idx = torch.empty((B, H, nb, kk), dtype=torch.int32, device=dev)
     ws = torch.empty(bsa_workspace_bytes(p), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(q)
-    k_r = None
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.dtype != torch.bfloat16 or out.shape != q.shape or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped and placed like q")
+    k_r = v_r = None
     if perm is not None:
-        # q and v are read through perm; K gets one copy in the new order
-        k_r = torch.empty_like(k)
-        bsa_pool_reordered(p, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_r, ws, stream)
+        # q is read through perm; K and V get one copy each in the new order
+        k_r, v_r = torch.empty_like(k), torch.empty_like(v)
+        bsa_pool_reordered(p, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_r, v_r, ws,
+                           stream)
     else:
         bsa_pool(p, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, ws, stream)
     bsa_select(p, q_pool, k_pool, idx if kk > 0 else None, stream)
@@ -324,15 +329,15 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
         tok = torch.empty((B, H, nb, p.extra_tokens), dtype=torch.int32, device=dev)
         bsa_select_tokens(p, q_pool, k if k_r is None else k_r, idx if kk > 0 else None, tok, ws, stream)
     if perm is not None:
-        bsa_forward_reordered(p, perm, q, k_r, v if tok is not None else None, sum_k, sum_bias,
-                              idx if kk > 0 else None, tok, ws, out, stream)
+        bsa_forward_reordered(p, perm, q, k_r, v_r, sum_k, sum_v, sum_bias, idx if kk > 0 else None,
+                              tok, out, ws, stream)
     elif tok is not None:
-        bsa_forward_tokens(p, q, k, v, sum_k, sum_bias, idx if kk > 0 else None, tok, ws, out,
+        bsa_forward_tokens(p, q, k, v, sum_k, sum_v, sum_bias, idx if kk > 0 else None, tok, out, ws,
                            stream)
     else:
-        bsa_forward(p, q, k, sum_k, sum_bias, idx if kk > 0 else None, ws, out, stream)
+        bsa_forward(p, q, k, v, sum_k, sum_v, sum_bias, idx if kk > 0 else None, out, ws, stream)
     if return_aux:
         return out, dict(q_pool=q_pool, k_pool=k_pool, sum_k=sum_k, sum_v=sum_v,
                          sum_bias=sum_bias, block_idx=idx, token_idx=tok, workspace=ws, problem=p,
-                         perm=perm, k_r=k_r)
+                         perm=perm, k_r=k_r, v_r=v_r)
     return out

@@ -48,15 +48,6 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Column order of V^T inside each 16-key group.  The P operand of the PV
-// product comes straight from the S^T accumulator, whose lane holds keys
-// {8a + 4g + e : a in 0..1, e in 0..3} of every 16-key slice (g = lane / 32).
-// Storing key j at position swap(bits 2, 3 of j) makes those 8 keys contiguous,
-// so the V^T operand is one 16-byte LDS read.  The map is its own inverse.
-__host__ __device__ __forceinline__ int vt_pos(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-}
-
 __device__ __forceinline__ uint4 zero_unless(uint4 u, bool keep) {
   u.x = keep ? u.x : 0u;
   u.y = keep ? u.y : 0u;
@@ -161,16 +152,15 @@ __global__ __launch_bounds__(1024) void anchor_kernel(const double* __restrict__
   }
 }
 
-// GATHER also writes the block's K rows in the order's positions to k_out.
+// GATHER also writes the block's K and V rows in the order's positions to
+// k_out and v_out (the tiles the attention kernel loads).
 template <bool REWEIGHT, bool GATHER>
 __global__ __launch_bounds__(256) void pool_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
-    uint16_t* __restrict__ k_out, const double* __restrict__ anchor,
+    uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out, const double* __restrict__ anchor,
     float* __restrict__ k_pool, uint16_t* __restrict__ sum_k, uint16_t* __restrict__ sum_v,
-    float* __restrict__ sum_bias, uint16_t* __restrict__ vt, uint16_t* __restrict__ svt, int N,
-    int nb, int nsb, double scale) {
+    float* __restrict__ sum_bias, int N, int nb, double scale) {
   __shared__ double red[16][HD];
-  __shared__ uint16_t vl[BLK][HD + 2];  // V block, rows padded against bank conflicts
   __shared__ double rowred[16][3];
   __shared__ double lrow[BLK];  // reweight: anchor logit, then weight, of each row
   const int c = blockIdx.x, tid = threadIdx.x;
@@ -193,15 +183,15 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
     // load a valid row (clamped) and zero it afterwards: no pointer select
     kr[i] = zero_unless(*(const uint4*)(kb + (size_t)src[i] * HD + cc * 8), row < n);
     vr[i] = zero_unless(*(const uint4*)(vb + (size_t)src[i] * HD + cc * 8), row < n);
-    // stage V (zeros past the end of a short block) for the transpose below
-    uint32_t* dst = (uint32_t*)&vl[row][cc * 8];
-    dst[0] = vr[i].x; dst[1] = vr[i].y; dst[2] = vr[i].z; dst[3] = vr[i].w;
   }
   if (GATHER) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = rp + 16 * i;
-      if (row < n) *(uint4*)(k_out + (bh * N + s + row) * HD + cc * 8) = kr[i];
+      if (row < n) {
+        *(uint4*)(k_out + (bh * N + s + row) * HD + cc * 8) = kr[i];
+        *(uint4*)(v_out + (bh * N + s + row) * HD + cc * 8) = vr[i];
+      }
     }
   }
 
@@ -301,32 +291,9 @@ __global__ __launch_bounds__(256) void pool_kv_kernel(
   }
   if (tid < HD) {
     sum_k[(bh * nb + c) * HD + tid] = f2bf((float)sk_out);
-    const uint16_t svb = f2bf((float)sv_out);
-    sum_v[(bh * nb + c) * HD + tid] = svb;
-    // summary values transposed, groups of 128 blocks: svt[bh][c/128][d][pos]
-    uint16_t* sg = svt + ((bh * nsb + c / BLK) * HD + tid) * BLK;
-    sg[vt_pos(c % BLK)] = svb;
-    if (c == nb - 1)
-      for (int cp = nb; cp < nsb * BLK; ++cp) sg[vt_pos(cp % BLK) + 0] = 0;
+    sum_v[(bh * nb + c) * HD + tid] = f2bf((float)sv_out);
   }
   if (tid == 0) sum_bias[bh * nb + c] = (float)bias_out;
-  __syncthreads();
-
-  // V^T of this block: vt[bh][c][d][vt_pos(j)] = V[s + j][d]; 16-byte stores,
-  // 16 threads per 256-byte output row.
-  uint16_t* vto = vt + (bh * nb + c) * (size_t)(BLK * HD);
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int id = it * 256 + tid;
-    const int d = id >> 4, pc = id & 15;
-    uint32_t wv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j0 = vt_pos(pc * 8 + 2 * e), j1 = vt_pos(pc * 8 + 2 * e + 1);
-      wv[e] = (uint32_t)vl[j0][d] | ((uint32_t)vl[j1][d] << 16);
-    }
-    *(uint4*)(vto + d * BLK + pc * 8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
 }
 
 // ---------------------------------------------------------------- select ---
@@ -635,13 +602,14 @@ __global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restri
 // the summary rows in groups of 64.
 //
 // Software pipeline, per half tile t (one barrier each):
-//   - direct global->LDS loads of K(t+2) and V^T(t+1) are issued first;
+//   - direct global->LDS loads of K(t+2) and V(t+1) are issued first;
 //   - the MFMAs of S(t+1) = K(t+1) Q^T run interleaved with the softmax of
 //     S(t) (computed one step earlier), so the matrix cores and the vector
 //     ALUs of one wavefront work at the same time;
 //   - then O^T += V^T(t) P(t)^T, with P(t) taken straight from the S^T
-//     accumulator layout.
-// K is therefore staged two half tiles ahead and V^T one ahead, in two LDS
+//     accumulator layout and the V^T operand read from the row-major V tile
+//     by transposing LDS reads.
+// K is therefore staged two half tiles ahead and V one ahead, in two LDS
 // buffers each (64 KB per workgroup).  Lane l holds query 32w + l%32; lanes l
 // and l^32 hold the two halves of its 64 keys.
 //
@@ -652,16 +620,35 @@ __global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restri
 constexpr int HT = 64;            // keys per half tile
 constexpr float LAZY_MAX = 8.0f;
 
-// K half tile: 64 rows x 256 B, 16-byte chunks XOR-swizzled by row
+// K half tile: 64 rows x 256 B of 16-byte chunks; chunk c of row `row` at
+// position c ^ (row & 15), so the K operand reads (16 lanes x 16 B from 16
+// consecutive rows) touch all 64 banks.
 __device__ __forceinline__ int swz_k(int row, int chunk) { return row * HD + ((chunk ^ (row & 15)) << 3); }
-// V^T half tile: 128 rows x 128 B; rows 2i, 2i+1 share a swizzle and sit in
-// opposite halves of the 256-byte bank window
-__device__ __forceinline__ int swz_v(int row, int chunk) {
-  return row * HT + ((chunk ^ ((row >> 1) & 7)) << 3);
+// V half tile, laid out for transposing reads (ds_read_b64_tr_b16 takes, in
+// each group of 16 lanes, 4 rows x 16 columns: lane 4e + c supplies row e's
+// columns 4c..4c+3, lane i receives column i): 128-byte blocks of 4 keys x
+// 16 features (row-major), four blocks (key quads 4g, feature halves h1) per
+// 512-byte unit, one unit per (key slice kk of 16, half of it, feature block
+// db of 32).  Key 16 kk + 8 half + 4 g + e, feature chunk 4 db + 2 h1 + c2
+// (8 features) sits at 16-byte slot 32 (8 kk + 4 half + db) + 8 (2 g + h1) +
+// 2 e + c2, so every transposing read covers one unit: 512 contiguous bytes
+// (measured about 20% faster per read than a bank-spread row-major pattern).
+__device__ __forceinline__ int vslot(int key, int ch) {
+  const int u = 8 * (key >> 4) + 4 * ((key >> 3) & 1) + (ch >> 2);
+  return 32 * u + 8 * (2 * ((key >> 2) & 1) + ((ch >> 1) & 1)) + 2 * (key & 3) + (ch & 1);
 }
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) { return *(const bf16x8*)p; }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4e + c supplies the address of columns [4c, 4c + 4) of row e, and
+// lane i receives column i of rows 0..3 (element e from row e).
+__device__ __forceinline__ bf16x4 ld_tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(p));
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -679,21 +666,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 struct TileSrc {
-  uint32_t koff;   // byte offset of the half tile's first key row (K or sum_k)
-  uint32_t voff;   // byte offset of the half tile in V^T (per-block or summary)
+  uint32_t off;    // byte offset of the half tile's first row (K and V, or sum_k and sum_v)
   int nvalid;      // rows of the half tile that exist (may be <= 0)
   int c0;          // summary tiles: first summary block
   bool summary;
 };
 
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ vt, const uint16_t* __restrict__ sum_k,
-    const uint16_t* __restrict__ svt, const float* __restrict__ sum_bias,
-    const int32_t* __restrict__ block_idx, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ perm, const int32_t* __restrict__ order,
-    uint16_t* __restrict__ out, int N, int nb, int krow, int nsb, float scale_log2, int total_wg, int chunk, int f0,
-    int f1, int E) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ sum_k, const uint16_t* __restrict__ sum_v, const float* __restrict__ sum_bias,
+    const int32_t* __restrict__ block_idx, const int32_t* __restrict__ tok_idx, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ order, uint16_t* __restrict__ out, int N, int nb, int krow, float scale_log2,
+    int total_wg, int chunk, int f0, int f1, int E) {
   // LDS buffers as distinct variables, so the compiler can tell the DMA
   // targets from the buffers being read
   __shared__ __attribute__((aligned(16))) uint16_t ks0[HT * HD], ks1[HT * HD];
@@ -735,16 +719,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // a conditioning sink query block attends to every key block exactly
   const bool dense_row = r >= f0 && r <= f1;
   const int kslots = dense_row ? nb : krow;
-  // per-head buffer descriptors: K, V^T, summary K, summary V^T
+  // per-head buffer descriptors: K, V, summary K, summary V (rows past the
+  // end of a buffer read as zeros)
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + bh * (size_t)N * HD, (uint32_t)N * HD * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + bh * (size_t)nb * BLK * HD, (uint32_t)nb * BLK * HD * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + bh * (size_t)N * HD, (uint32_t)N * HD * 2);
   const __amdgpu_buffer_rsrc_t rsk =
       make_rsrc(sum_k ? sum_k + bh * (size_t)nb * HD : k, sum_k ? (uint32_t)nb * HD * 2 : 0u);
-  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(svt + bh * (size_t)nsb * BLK * HD, (uint32_t)nsb * BLK * HD * 2);
+  const __amdgpu_buffer_rsrc_t rsv =
+      make_rsrc(sum_v ? sum_v + bh * (size_t)nb * HD : v, sum_v ? (uint32_t)nb * HD * 2 : 0u);
 
   // Q fragments (B operand of S^T = K Q^T): query qi, features 16kk + 8g + [0, 8).
   // With a row order perm, query qi (a position) is row perm[qi] of q and
-  // of out, and token t of the extra tokens is row perm[t] of v.
+  // of out; k and v already hold their rows in the new order.
   const int qi = r * BLK + 32 * wave + ln;
   bf16x8 qf[8];
   {
@@ -793,16 +779,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     const int h = t & 1;
     if (t < n_exact) {
       const int row0 = c * BLK + h * HT;
-      d.koff = (uint32_t)row0 * (HD * 2);
-      d.voff = (uint32_t)c * (BLK * HD * 2) + h * (HT * 2);
+      d.off = (uint32_t)row0 * (HD * 2);
       d.nvalid = min(HT, N - row0);
       d.c0 = 0;
       d.summary = false;
     } else {
       const int st = (t - n_exact) >> 1;
       const int row0 = st * BLK + h * HT;
-      d.koff = (uint32_t)row0 * (HD * 2);
-      d.voff = (uint32_t)st * (BLK * HD * 2) + h * (HT * 2);
+      d.off = (uint32_t)row0 * (HD * 2);
       d.nvalid = min(HT, nb - row0);
       d.c0 = row0;
       d.summary = true;
@@ -811,45 +795,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   };
 
   // Direct global -> LDS loads.  Instruction j of wavefront w fills the 64
-  // consecutive 16-byte LDS chunks P = (4w + j) * 64 + lane; each lane fetches
-  // the global chunk that the XOR swizzle places at P.  Rows past the end of
-  // the buffer (ragged tails) arrive as zeros.
-  // The swizzled offsets have XOR structure: for K instruction j the offset is
-  // kbase + 1024 j + (kx ^ 64 j); for V^T it is vvo[j & 1] + 4096 (j >> 1).  Keeping
-  // four registers instead of eight matters: the kernel sits at the VGPR limit.
-  const int P0 = 4 * wave * 64 + lane;
-  const uint32_t kbase = (uint32_t)((P0 >> 4) * (HD * 2));
-  const uint32_t kx = (uint32_t)((((P0 & 15) ^ ((P0 >> 4) & 15))) * 16);
-  uint32_t vvo[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int P = P0 + j * 64;
-    const int vrow = P >> 3, vch = (P & 7) ^ ((vrow >> 1) & 7);
-    vvo[j] = (uint32_t)(vrow * (BLK * 2) + vch * 16);
-  }
+  // consecutive 16-byte LDS slots P = (4w + j) * 64 + lane; each lane
+  // fetches the global chunk that the tile's layout places there.  K: row
+  // 16w + 4j + lane/16 at position lane % 16, offset kbase + 1024 j +
+  // (kx ^ 64 j).  V (slot -> key, chunk: the inverse of vslot): key
+  // 16 w + 8 (j / 2) + 4 ((lane / 16) & 1) + (lane / 2) % 4, chunk
+  // 4 (2 (j & 1) + lane / 32) + 2 ((lane / 8) & 1) + lane % 2, offset vbase +
+  // 2048 (j / 2) + 128 (j & 1).  Rows past the end of the buffer (ragged
+  // tails) arrive as zeros.
+  const uint32_t kbase = (uint32_t)((16 * wave + (lane >> 4)) * (HD * 2));
+  const uint32_t kx = (uint32_t)(((lane & 15) ^ (lane >> 4)) * 16);
+  const uint32_t vbase = (uint32_t)((16 * wave + 4 * ((lane >> 4) & 1) + ((lane >> 1) & 3)) * (HD * 2) +
+                                    (4 * (lane >> 5) + 2 * ((lane >> 3) & 1) + (lane & 1)) * 16);
   auto kvo = [&](int j) { return kbase + 1024u * j + (kx ^ (64u * j)); };
-  auto vvo_of = [&](int j) { return vvo[j & 1] + 4096u * (j >> 1); };
   auto load_k1 = [&](const TileSrc& d, uint16_t* ksd, int j) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.summary ? rsk : rk, (lds_ptr_t)(ksd + (4 * wave + j) * 512),
-                                             16, (int)(d.koff + kvo(j)), 0, 0, 0);
+                                             16, (int)(d.off + kvo(j)), 0, 0, 0);
   };
   auto load_v1 = [&](const TileSrc& d, uint16_t* vsd, int j) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.summary ? rsv : rv, (lds_ptr_t)(vsd + (4 * wave + j) * 512),
-                                             16, (int)(d.voff + vvo_of(j)), 0, 0, 0);
+                                             16, (int)(d.off + vbase + 2048u * (j >> 1) + 128u * (j & 1)), 0, 0, 0);
   };
   auto load_k = [&](const TileSrc& d, uint16_t* ksd) {
-    const __amdgpu_buffer_rsrc_t rK = d.summary ? rsk : rk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_ptr_t)(ksd + (4 * wave + j) * 512), 16,
-                                               (int)(d.koff + kvo(j)), 0, 0, 0);
+    for (int j = 0; j < 4; ++j) load_k1(d, ksd, j);
   };
   auto load_v = [&](const TileSrc& d, uint16_t* vsd) {
-    const __amdgpu_buffer_rsrc_t rV = d.summary ? rsv : rv;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_ptr_t)(vsd + (4 * wave + j) * 512), 16,
-                                               (int)(d.voff + vvo_of(j)), 0, 0, 0);
+    for (int j = 0; j < 4; ++j) load_v1(d, vsd, j);
   };
   // additive logit term of each key of a half tile (base-2 units)
   // Only summary tiles and the short halves of the last block need it; full
@@ -868,7 +841,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     return a;
   };
   auto store_mask = [&](const TileSrc& d, float a, float* addvd) {
-    if (tid < HT && (d.summary || d.nvalid < HT)) addvd[tid] = a;
+    if (tid < HT && (d.summary || d.nvalid < HT)) {
+      // the lane index recomputed here (wavefront 0: lane == tid) instead of
+      // an address kept across the loop, which the register allocator would
+      // spill: its reload waits for every direct-to-LDS load in flight
+      int l;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+      addvd[l] = a;
+    }
+  };
+
+  // V^T operand of O^T += V^T P^T for feature block db (32 features) and
+  // key slice kk (16 keys), from the V tile by two transposing reads, of the
+  // units (kk, half 0, db) and (kk, half 1, db): lane l = 32 g + 16 h1 + i
+  // addresses element 4 l of the unit, i.e. key 16 kk + 8 half + 4 g + i / 4,
+  // features 32 db + 16 h1 + 4 (i % 4) .. +3, and receives feature
+  // 32 db + 16 h1 + i = 32 db + ln of keys 16 kk + 4 g + {0..3} and
+  // 16 kk + 8 + 4 g + {0..3}: exactly the eight keys, in the same order, that
+  // its P operand (the S^T accumulator of query ln) holds.  The address is
+  // the lane's 4 l plus compile-time offsets.
+  auto v_operand_db = [&](const uint16_t* vsc, int db, int kk) {
+    const uint16_t* p = vsc + 4 * lane + 256 * (8 * kk + db);
+    const bf16x4 a = ld_tr4(p), b = ld_tr4(p + 1024);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   };
 
   f32x16 o[4];
@@ -877,12 +872,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 sA[2], sB[2];
   if (E > 0 && !dense_row) {
-    // Extra tokens first, 64 at a time: their K rows gathered into ks0 (this
-    // kernel's K layout) and their V rows transposed into vs0 (its V^T
-    // layout), then S^T = K Q^T, a softmax update with the exact max and
-    // O^T += V^T P^T.  The state (o, m_run, l_run) carries into the online
-    // softmax of the main loop.  ks1 holds the row's token list until the
-    // main loop's first loads.
+    // Extra tokens first, 64 at a time: their K and V rows gathered into ks0
+    // and vs0 (the tile layout), then S^T = K Q^T, a softmax update with the
+    // exact max and O^T += V^T P^T.  The state (o, m_run, l_run) carries into
+    // the online softmax of the main loop.  ks1 holds the row's token list
+    // until the main loop's first loads.
     int* tok = (int*)ks1;
     const int t_in = tid < E ? tok_idx[(bh * nb + r) * (size_t)E + tid] : -1;
     tok[tid] = t_in;
@@ -898,14 +892,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
         uint4 kd = make_uint4(0u, 0u, 0u, 0u), vd = kd;
         if (t >= 0) {
           kd = *(const uint4*)(kb + (size_t)t * HD + 8 * ch);
-          vd = *(const uint4*)(vb + (size_t)(perm ? perm[bh * N + t] : t) * HD + 8 * ch);
+          vd = *(const uint4*)(vb + (size_t)t * HD + 8 * ch);
         }
         *(uint4*)(ks0 + swz_k(row, ch)) = kd;
-        const int pos = vt_pos(row);
-        const uint32_t w[4] = {vd.x, vd.y, vd.z, vd.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vs0[swz_v(8 * ch + e, pos >> 3) + (pos & 7)] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        *(uint4*)(vs0 + 8 * vslot(row, ch)) = vd;
       }
       __syncthreads();
       // S^T: sA[mb] element ii is key base + 32 mb + 8 (ii / 4) + 4 g + ii % 4
@@ -929,7 +919,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       const float m_new = fmaxf(m_run, mx);  // finite: the group holds a token
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
-      // P slice kk (keys 16 kk .. 16 kk + 15) in the V^T key order
+      // P slice kk: keys 16 kk + 8 (e / 4) + 4 g + e % 4, e = 0..7
       bf16x8 pb[4];
       float psum = 0.f;
 #pragma unroll
@@ -949,8 +939,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ld_bf16x8(vs0 + swz_v(32 * (i & 3) + ln, 2 * (i >> 2) + g)), pb[i >> 2], o[i & 3], 0, 0, 0);
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_db(vs0, i & 3, i >> 2), pb[i >> 2], o[i & 3],
+                                                           0, 0, 0);
       __syncthreads();
     }
   }
@@ -963,7 +953,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
     return ld_bf16x8(ksc + swz_k(32 * (i & 1) + ln, 2 * (i >> 1) + g));
   };
   auto v_operand = [&](const uint16_t* vsc, int i) {  // i = 4 kk + db
-    return ld_bf16x8(vsc + swz_v(32 * (i & 3) + ln, 2 * (i >> 2) + g));
+    return v_operand_db(vsc, i & 3, i >> 2);
   };
 
   // prologue S(0), plain order
@@ -1726,7 +1716,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
 
 // ------------------------------------------------------------------ host ---
 struct Geometry {
-  int64_t B, H, N, nb, nsb, k;
+  int64_t B, H, N, nb, k;
   int64_t f0, f1;  // conditioning sink blocks [f0, f1]; f1 < f0 when there are none
   bool threshold;
   double tau;
@@ -1736,11 +1726,23 @@ struct Geometry {
   int E;  // extra tokens per query block
 };
 
-struct WsLayout {
-  size_t vt, svt, apart, anchor, tsel, order, total;
-};
-
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Scratch of each call, always from the start of the workspace: no call
+// reads anything that another call left there.
+//   pool (reweight only): float64 anchor partial sums [B, H, nb, 128], then
+//     the anchor [B, H, 128] at pool_anchor_off();
+//   forward: the visiting order of each head's query blocks, int32 [B, H, nb];
+//   select_tokens: key segments, u64 [B, H, nb, 4, SEG_CAP].
+size_t pool_anchor_off(const Geometry& g) { return align256((size_t)(g.B * g.H * g.nb) * HD * sizeof(double)); }
+size_t pool_ws(const Geometry& g) {
+  return g.reweight ? pool_anchor_off(g) + align256((size_t)(g.B * g.H) * HD * sizeof(double)) : 0;
+}
+size_t forward_ws(const Geometry& g) { return align256((size_t)(g.B * g.H * g.nb) * sizeof(int32_t)); }
+size_t tokens_ws(const Geometry& g) {
+  return g.E > 0 ? align256((size_t)(g.B * g.H * g.nb) * 4 * SEG_CAP * sizeof(uint64_t)) : 0;
+}
+size_t ws_total(const Geometry& g) { return std::max(pool_ws(g), std::max(forward_ws(g), tokens_ws(g))); }
 
 int make_geometry(const bsa_problem* p, Geometry* g) {
   if (!p) return BSA_ERR_INVALID;
@@ -1763,7 +1765,6 @@ int make_geometry(const bsa_problem* p, Geometry* g) {
   g->N = p->seq_len;
   g->nb = (g->N + BLK - 1) / BLK;
   if (g->nb > BSA_MAX_BLOCKS) return BSA_ERR_UNSUPPORTED;
-  g->nsb = (g->nb + BLK - 1) / BLK;
   if (p->sink_rows > 0) {
     g->f0 = p->sink_start / BLK;
     g->f1 = ((int64_t)p->sink_start + p->sink_rows - 1) / BLK;
@@ -1779,32 +1780,9 @@ int make_geometry(const bsa_problem* p, Geometry* g) {
   // the attention launch is a 1-D grid of 256-thread workgroups (at most
   // 8 ceil(nb / 8) per head), and a grid dimension counts work-items in 32 bits
   if (g->B * g->H * (8 * ((g->nb + 7) / 8)) * 256 >= (1ll << 32)) return BSA_ERR_UNSUPPORTED;
+  // every per-head tensor of the attention kernel is addressed with 32-bit
+  // byte offsets (buffer descriptors): N rows of 256 bytes fit for N <= 2^24
   return BSA_OK;
-}
-
-WsLayout ws_layout(const Geometry& g) {
-  WsLayout w{};
-  const size_t bh = (size_t)(g.B * g.H);
-  w.vt = 0;
-  size_t off = align256(bh * g.nb * BLK * HD * 2);
-  w.svt = off;
-  off = align256(off + bh * g.nsb * BLK * HD * 2);
-  if (g.reweight) {
-    w.apart = off;
-    off = align256(off + bh * g.nb * HD * sizeof(double));
-    w.anchor = off;
-    off = align256(off + bh * HD * sizeof(double));
-  }
-  if (g.E > 0) {
-    // extra-token selection: a key segment per (query block, token quarter)
-    w.tsel = off;
-    off = align256(off + bh * g.nb * 4 * SEG_CAP * sizeof(uint64_t));
-  }
-  // the attention grid's visiting order of each head's query blocks
-  w.order = off;
-  off = align256(off + bh * g.nb * sizeof(int32_t));
-  w.total = off;
-  return w;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -1827,25 +1805,29 @@ int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, i
   return launch_status();
 }
 
-int check_forward(const Geometry& g, const void* q, const void* k, const void* sum_k,
-                  const float* sum_bias, const int32_t* block_idx, const void* workspace,
-                  size_t workspace_bytes, const void* out) {
-  if (!q || !k || !out) return BSA_ERR_INVALID;
+// Whether a row can skip a block, i.e. the summary rows take part: top-k
+// with k < nb, or threshold selection (rows keep at most k blocks).
+bool uses_summaries(const Geometry& g) { return g.k < g.nb || g.threshold; }
+
+int check_forward(const Geometry& g, const void* q, const void* k, const void* v, const void* sum_k,
+                  const void* sum_v, const float* sum_bias, const int32_t* block_idx, const void* out,
+                  const void* workspace, size_t workspace_bytes) {
+  if (!q || !k || !v || !out) return BSA_ERR_INVALID;
   if (g.k > 0 && !block_idx) return BSA_ERR_INVALID;
-  if (g.k < g.nb && (!sum_k || !sum_bias)) return BSA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(out) || (sum_k && !aligned16(sum_k)))
+  if (uses_summaries(g) && (!sum_k || !sum_v || !sum_bias)) return BSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (sum_k && !aligned16(sum_k)) ||
+      (sum_v && !aligned16(sum_v)) || ((uintptr_t)sum_bias & 3u) || ((uintptr_t)block_idx & 3u))
     return BSA_ERR_INVALID;
-  if (!workspace || workspace_bytes < ws_layout(g).total || ((uintptr_t)workspace & 255u))
-    return BSA_ERR_WORKSPACE;
+  // the workspace is optional here (it only holds the visiting order)
+  if (workspace && (workspace_bytes < forward_ws(g) || ((uintptr_t)workspace & 255u))) return BSA_ERR_WORKSPACE;
   return BSA_OK;
 }
 
-int launch_attention(const Geometry& g, const void* q, const void* k, const void* sum_k,
-                     const float* sum_bias, const int32_t* block_idx, char* ws, const void* v,
-                     const int32_t* tok_idx, const int32_t* perm, void* out, hipStream_t stream) {
-  const WsLayout w = ws_layout(g);
+int launch_attention(const Geometry& g, const void* q, const void* k, const void* v, const void* sum_k,
+                     const void* sum_v, const float* sum_bias, const int32_t* block_idx, const int32_t* tok_idx,
+                     const int32_t* perm, void* out, int32_t* order_buf, hipStream_t stream) {
   // The head-synchronous map (8 chunks of ceil(nb / 8) query blocks per head)
-  // once the K and V^T of eight heads, one per XCD, would pass 192 MiB
+  // once the K and V of eight heads, one per XCD, would pass 192 MiB
   // (nb > 384); below that, and with sinks, one contiguous range per XCD.
   // Measured inside whole steps: 4.9% faster at 1,045 blocks, 0.7% at 574,
   // 0.7% slower at 295 (there the XCDs' own heads still share the
@@ -1857,16 +1839,17 @@ int launch_attention(const Geometry& g, const void* q, const void* k, const void
   // reblocked row order, whose neighbouring query blocks already share their
   // key blocks (there the sort measured 1.7% slower, elsewhere 1.1-2.7% faster)
   int32_t* order = nullptr;
-  if (g.k > 0 && block_idx && !perm) {
-    order = (int32_t*)(ws + w.order);
+  if (g.k > 0 && block_idx && !perm && order_buf) {
+    order = order_buf;
     hipLaunchKernelGGL(row_order_kernel, dim3((unsigned)(g.B * g.H)), dim3(1024), 0, stream, block_idx, order,
                        (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1);
   }
+  const bool summ = uses_summaries(g);
   hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)total), dim3(256), 0, stream, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)(ws + w.vt), (const uint16_t*)sum_k,
-                     (const uint16_t*)(ws + w.svt), sum_bias, block_idx, (const uint16_t*)v, tok_idx, perm,
-                     order, (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, (int)g.nsb, scale_log2, total, chunk,
-                     (int)g.f0, (int)g.f1, tok_idx ? g.E : 0);
+                     (const uint16_t*)k, (const uint16_t*)v, summ ? (const uint16_t*)sum_k : nullptr,
+                     summ ? (const uint16_t*)sum_v : nullptr, summ ? sum_bias : nullptr, block_idx, tok_idx, perm,
+                     order, (uint16_t*)out, (int)g.N, (int)g.nb, (int)g.k, scale_log2, total, chunk, (int)g.f0,
+                     (int)g.f1, tok_idx ? g.E : 0);
   return launch_status();
 }
 
@@ -1875,9 +1858,9 @@ int check_pool(const Geometry& g, const void* q, const void* k, const void* v, c
                const void* workspace, size_t workspace_bytes) {
   if (!q || !k || !v || !q_pool || !k_pool || !sum_k || !sum_v || !sum_bias) return BSA_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_pool) || !aligned16(k_pool) ||
-      !aligned16(sum_k) || !aligned16(sum_v))
+      !aligned16(sum_k) || !aligned16(sum_v) || ((uintptr_t)sum_bias & 3u))
     return BSA_ERR_INVALID;
-  if (!workspace || workspace_bytes < ws_layout(g).total || ((uintptr_t)workspace & 255u))
+  if (g.reweight && (!workspace || workspace_bytes < pool_ws(g) || ((uintptr_t)workspace & 255u)))
     return BSA_ERR_WORKSPACE;
   return BSA_OK;
 }
@@ -1893,36 +1876,34 @@ int check_reorder(const bsa_problem* p) {
 
 template <bool REWEIGHT, bool GATHER>
 void launch_pool_t(const Geometry& g, const int32_t* perm, const void* q, const void* k, const void* v,
-                   float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out, char* ws,
-                   hipStream_t s) {
-  const WsLayout w = ws_layout(g);
+                   float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out, void* v_out,
+                   char* ws, hipStream_t s) {
   const dim3 grid((unsigned)g.nb, (unsigned)g.H, (unsigned)g.B);
-  double* apart = REWEIGHT ? (double*)(ws + w.apart) : nullptr;
-  double* anc = REWEIGHT ? (double*)(ws + w.anchor) : nullptr;
+  double* apart = REWEIGHT ? (double*)ws : nullptr;
+  double* anc = REWEIGHT ? (double*)(ws + pool_anchor_off(g)) : nullptr;
   hipLaunchKernelGGL((pool_q_kernel<REWEIGHT, GATHER>), grid, dim3(256), 0, s, (const uint16_t*)q, perm, q_pool,
                      apart, (int)g.N, (int)g.nb, REWEIGHT ? g.anchor_rows : 0);
   if (REWEIGHT)
     hipLaunchKernelGGL(anchor_kernel, dim3((unsigned)g.H, (unsigned)g.B), dim3(8 * HD), 0, s,
                        (const double*)apart, anc, (int)g.nb, g.anchor_rows);
   hipLaunchKernelGGL((pool_kv_kernel<REWEIGHT, GATHER>), grid, dim3(256), 0, s, (const uint16_t*)k,
-                     (const uint16_t*)v, perm, (uint16_t*)k_out, (const double*)anc, k_pool, (uint16_t*)sum_k,
-                     (uint16_t*)sum_v, sum_bias, (uint16_t*)(ws + w.vt), (uint16_t*)(ws + w.svt), (int)g.N,
-                     (int)g.nb, (int)g.nsb, g.scale);
+                     (const uint16_t*)v, perm, (uint16_t*)k_out, (uint16_t*)v_out, (const double*)anc, k_pool,
+                     (uint16_t*)sum_k, (uint16_t*)sum_v, sum_bias, (int)g.N, (int)g.nb, g.scale);
 }
 
 int launch_pool(const Geometry& g, const int32_t* perm, const void* q, const void* k, const void* v,
-                float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out, char* ws,
-                hipStream_t s) {
+                float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out, void* v_out,
+                char* ws, hipStream_t s) {
   if (g.reweight) {
     if (perm)
-      launch_pool_t<true, true>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+      launch_pool_t<true, true>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out, ws, s);
     else
-      launch_pool_t<true, false>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+      launch_pool_t<true, false>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out, ws, s);
   } else {
     if (perm)
-      launch_pool_t<false, true>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+      launch_pool_t<false, true>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out, ws, s);
     else
-      launch_pool_t<false, false>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, ws, s);
+      launch_pool_t<false, false>(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out, ws, s);
   }
   return launch_status();
 }
@@ -1951,13 +1932,10 @@ int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff) 
   return BSA_OK;
 }
 
-int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes) {
+size_t bsa_workspace_bytes(const bsa_problem* p) {
   Geometry g;
-  const int st = make_geometry(p, &g);
-  if (st != BSA_OK) return st;
-  if (!bytes) return BSA_ERR_INVALID;
-  *bytes = ws_layout(g).total;
-  return BSA_OK;
+  if (make_geometry(p, &g) != BSA_OK) return 0;
+  return ws_total(g);
 }
 
 int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v, float* q_pool,
@@ -1968,21 +1946,24 @@ int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v, 
   if (st != BSA_OK) return st;
   if ((st = check_pool(g, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, workspace_bytes)) != BSA_OK)
     return st;
-  return launch_pool(g, nullptr, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, nullptr, (char*)workspace,
-                     (hipStream_t)hip_stream);
+  return launch_pool(g, nullptr, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, nullptr, nullptr,
+                     (char*)workspace, (hipStream_t)hip_stream);
 }
 
 int bsa_pool_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k, const void* v,
                        float* q_pool, float* k_pool, void* sum_k, void* sum_v, float* sum_bias, void* k_out,
-                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+                       void* v_out, void* workspace, size_t workspace_bytes, void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
   if (st != BSA_OK) return st;
   if ((st = check_reorder(p)) != BSA_OK) return st;
-  if (!perm || ((uintptr_t)perm & 3u) || !k_out || !aligned16(k_out) || k_out == k) return BSA_ERR_INVALID;
+  if (!perm || ((uintptr_t)perm & 3u) || !k_out || !v_out || !aligned16(k_out) || !aligned16(v_out))
+    return BSA_ERR_INVALID;
+  if (k_out == v_out || k_out == q || k_out == k || k_out == v || v_out == q || v_out == k || v_out == v)
+    return BSA_ERR_INVALID;
   if ((st = check_pool(g, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, workspace_bytes)) != BSA_OK)
     return st;
-  return launch_pool(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, (char*)workspace,
+  return launch_pool(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out, (char*)workspace,
                      (hipStream_t)hip_stream);
 }
 
@@ -1993,7 +1974,7 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   if (st != BSA_OK) return st;
   if (g.k == 0) return BSA_OK;
   if (!q_pool || !k_pool || !block_idx) return BSA_ERR_INVALID;
-  if (!aligned16(q_pool) || !aligned16(k_pool)) return BSA_ERR_INVALID;
+  if (!aligned16(q_pool) || !aligned16(k_pool) || ((uintptr_t)block_idx & 3u)) return BSA_ERR_INVALID;
   hipStream_t s = (hipStream_t)hip_stream;
   // key blocks per lane (top-k phase) sized to nb.  The row-split score
   // phase (four query rows in registers, whole-line key loads) is fastest
@@ -2005,17 +1986,18 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   return launch_select<8, 4, true>(g, q_pool, k_pool, block_idx, s);
 }
 
-int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
-                const float* sum_bias, const int32_t* block_idx, void* workspace,
-                size_t workspace_bytes, void* out, void* hip_stream) {
+int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v, const void* sum_k,
+                const void* sum_v, const float* sum_bias, const int32_t* block_idx, void* out, void* workspace,
+                size_t workspace_bytes, void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
   if (st != BSA_OK) return st;
   if (g.E > 0) return BSA_ERR_INVALID;  // extra tokens go through bsa_forward_tokens
-  if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
+  if ((st = check_forward(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, workspace, workspace_bytes)) !=
+      BSA_OK)
     return st;
-  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, (char*)workspace, nullptr, nullptr,
-                          nullptr, out, (hipStream_t)hip_stream);
+  return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, nullptr, nullptr, out,
+                          (int32_t*)workspace, (hipStream_t)hip_stream);
 }
 
 int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
@@ -2026,54 +2008,51 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
   if (st != BSA_OK) return st;
   if (g.E == 0) return BSA_OK;
   if (!q_pool || !k || !token_idx || (g.k > 0 && !block_idx)) return BSA_ERR_INVALID;
-  if (!aligned16(q_pool) || !aligned16(k)) return BSA_ERR_INVALID;
-  const WsLayout w = ws_layout(g);
-  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return BSA_ERR_WORKSPACE;
+  if (!aligned16(q_pool) || !aligned16(k) || ((uintptr_t)token_idx & 3u) || ((uintptr_t)block_idx & 3u))
+    return BSA_ERR_INVALID;
+  if (!workspace || workspace_bytes < tokens_ws(g) || ((uintptr_t)workspace & 255u)) return BSA_ERR_WORKSPACE;
   // sample size of the first phase: T_m lands near the 2E- to 3E-th score,
   // with a margin for samples that are not random (small E: no sample)
   const double S = TS_STRIDE;
   const int m = g.E >= 64 ? std::min(g.E, (int)ceil(g.E / S + 8.0 * sqrt(g.E / S))) : 0;
   const int total = (int)(((g.nb + TS_ROWS - 1) / TS_ROWS) * g.H * g.B);
   hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)total), dim3(TS_THREADS), 0, (hipStream_t)hip_stream,
-                     q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx,
-                     (uint64_t*)((char*)workspace + w.tsel), (int)g.N, (int)g.nb, (int)g.k, g.E, m,
-                     (int)g.f0, (int)g.f1, total);
+                     q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx, (uint64_t*)workspace,
+                     (int)g.N, (int)g.nb, (int)g.k, g.E, m, (int)g.f0, (int)g.f1, total);
   return launch_status();
 }
 
-int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
-                       const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                       const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
+int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v, const void* sum_k,
+                       const void* sum_v, const float* sum_bias, const int32_t* block_idx,
+                       const int32_t* token_idx, void* out, void* workspace, size_t workspace_bytes,
                        void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
   if (st != BSA_OK) return st;
-  if ((st = check_forward(g, q, k, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
+  if ((st = check_forward(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, workspace, workspace_bytes)) !=
+      BSA_OK)
     return st;
-  hipStream_t s = (hipStream_t)hip_stream;
-  char* ws = (char*)workspace;
-  if (g.E == 0) return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, nullptr, out, s);
-  if (!v || !token_idx || !aligned16(v)) return BSA_ERR_INVALID;
-  return launch_attention(g, q, k, sum_k, sum_bias, block_idx, ws, v, token_idx, nullptr, out, s);
+  if (g.E > 0 && (!token_idx || ((uintptr_t)token_idx & 3u))) return BSA_ERR_INVALID;
+  return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, g.E > 0 ? token_idx : nullptr, nullptr,
+                          out, (int32_t*)workspace, (hipStream_t)hip_stream);
 }
 
 int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k_r,
-                          const void* v, const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                          const int32_t* token_idx, void* workspace, size_t workspace_bytes, void* out,
-                          void* hip_stream) {
+                          const void* v_r, const void* sum_k, const void* sum_v, const float* sum_bias,
+                          const int32_t* block_idx, const int32_t* token_idx, void* out, void* workspace,
+                          size_t workspace_bytes, void* hip_stream) {
   Geometry g;
   int st = make_geometry(p, &g);
   if (st != BSA_OK) return st;
   if ((st = check_reorder(p)) != BSA_OK) return st;
   if (!perm || ((uintptr_t)perm & 3u)) return BSA_ERR_INVALID;
-  if ((st = check_forward(g, q, k_r, sum_k, sum_bias, block_idx, workspace, workspace_bytes, out)) != BSA_OK)
+  if ((st = check_forward(g, q, k_r, v_r, sum_k, sum_v, sum_bias, block_idx, out, workspace, workspace_bytes)) !=
+      BSA_OK)
     return st;
-  if (out == q || out == k_r) return BSA_ERR_INVALID;
-  hipStream_t s = (hipStream_t)hip_stream;
-  char* ws = (char*)workspace;
-  if (g.E == 0) return launch_attention(g, q, k_r, sum_k, sum_bias, block_idx, ws, nullptr, nullptr, perm, out, s);
-  if (!v || !token_idx || !aligned16(v) || out == v) return BSA_ERR_INVALID;
-  return launch_attention(g, q, k_r, sum_k, sum_bias, block_idx, ws, v, token_idx, perm, out, s);
+  if (out == q || out == k_r || out == v_r) return BSA_ERR_INVALID;
+  if (g.E > 0 && (!token_idx || ((uintptr_t)token_idx & 3u))) return BSA_ERR_INVALID;
+  return launch_attention(g, q, k_r, v_r, sum_k, sum_v, sum_bias, block_idx, g.E > 0 ? token_idx : nullptr, perm,
+                          out, nullptr, (hipStream_t)hip_stream);
 }
 
 }  // extern "C"

@@ -113,17 +113,18 @@ const char* bsa_status_str(int status);
 int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff);
 
 /*
- * Bytes of device workspace that bsa_pool fills and bsa_forward reads, written
- * to *bytes.  The workspace holds, for every (b, h): V of each key block
- * transposed (feature-major, key order interleaved for the matrix cores, zero
- * past the end of a short block), the summary values transposed in groups of
- * 128 blocks, in reweight mode the anchor and its per-block partial sums,
- * with extra tokens the candidate keys of bsa_select_tokens (16 KB per
- * query block), and the order in which bsa_forward visits each head's query
- * blocks (written by bsa_forward itself).  Its contents are private to this
- * library; it must be 256-byte aligned, and it serves one call at a time.
+ * Bytes of device scratch memory ("workspace") that covers every entry point
+ * below for problem p; 0 when the problem is rejected (bsa_problem_blocks
+ * tells why).  The calls share no state through it: each call writes before
+ * it reads, so one workspace can serve a sequence of calls on one stream,
+ * while calls that may run at the same time need workspaces of their own.
+ * What uses it: bsa_pool in reweight mode (the anchor and its per-block
+ * partial sums, B*H*(nb+1)*128 float64); bsa_forward and its variants (the
+ * order in which query blocks are visited, B*H*nb int32; optional);
+ * bsa_select_tokens (16 KB of candidate keys per query block).  Must be
+ * 256-byte aligned.
  */
-int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes);
+size_t bsa_workspace_bytes(const bsa_problem* p);
 
 /*
  * Stage 1 (and the Spark-Reweight summaries): block pooling.
@@ -138,7 +139,8 @@ int bsa_workspace_bytes(const bsa_problem* p, size_t* bytes);
  *   sum_k      out  bf16 [B, H, nb, 128]  summary key of each block
  *   sum_v      out  bf16 [B, H, nb, 128]  summary value of each block
  *   sum_bias   out  fp32 [B, H, nb]       additive summary logit bias
- *   workspace  out  bsa_workspace_bytes() bytes, read later by bsa_forward
+ *   workspace  scratch, bsa_workspace_bytes() bytes; used in reweight mode
+ *              only (NULL allowed in mean mode)
  *
  * Mean mode: sum_k / sum_v are the block means of K / V and sum_bias is 0.
  * Reweight mode: with a = mean of the query rows [0, anchor_rows) and, for
@@ -178,32 +180,33 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
  * blocks folded back in as one summary row each); Spark-H3 page, "What
  * Spark-Attn changes" (exact and compressed branches of one attention pass).
  *
- *   q, k       in   bf16 [B, H, N, 128]
- *   sum_k      in   bf16 [B, H, nb, 128]   (may be NULL iff k == nb)
- *   sum_bias   in   fp32 [B, H, nb]        (may be NULL iff k == nb)
+ *   q, k, v    in   bf16 [B, H, N, 128]
+ *   sum_k      in   bf16 [B, H, nb, 128]   summary keys   } any values (bsa_pool's or
+ *   sum_v      in   bf16 [B, H, nb, 128]   summary values } the caller's); all three
+ *   sum_bias   in   fp32 [B, H, nb]        summary biases } may be NULL only when no
+ *                                          row can skip a block (k == nb, top-k mode)
  *   block_idx  in   int32 [B, H, nb, k]    distinct, in [0, nb), ascending,
  *                                          then -1 padding; the kernel trusts
- *                                          this (bsa_select's output)
- *   workspace  in/out  as filled by bsa_pool for the same q, k, v and
- *                   problem; bsa_forward writes only its visiting-order
- *                   region (query blocks sorted by their first kept blocks,
- *                   sink query blocks first, so that workgroups running
- *                   together read the same key blocks; the result does not
- *                   depend on the order)
- *   out        out  bf16 [B, H, N, 128]
+ *                                          this (bsa_select's output); may be
+ *                                          NULL iff k == 0
+ *   out        out  bf16 [B, H, N, 128]; must not overlap the inputs
+ *   workspace  scratch or NULL: with at least bsa_workspace_bytes() bytes
+ *              the query blocks of each head are visited sorted by their
+ *              first kept blocks (sink query blocks first), so workgroups
+ *              running together read the same key blocks; with NULL they
+ *              are visited in block order.  The result is the same bits.
  *
  * For query i of block r: logits scale * q_i . k_j for every row j of every
  * block in block_idx[r], and scale * q_i . sum_k[c] + sum_bias[c] for every
  * other block c; out_i = softmax(logits) . [v_j ... ; sum_v[c] ...], with
- * float32 accumulation and one final bf16 rounding.  V and the summary values
- * are read from the workspace.  A query block that is a conditioning sink
- * block attends to every key block exactly and ignores its block_idx row.
- * A problem with extra tokens is rejected (BSA_ERR_INVALID): use
- * bsa_forward_tokens.
+ * float32 accumulation and one final bf16 rounding.  A query block that is a
+ * conditioning sink block attends to every key block exactly and ignores its
+ * block_idx row.  A problem with extra tokens is rejected (BSA_ERR_INVALID):
+ * use bsa_forward_tokens.
  */
-int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* sum_k,
-                const float* sum_bias, const int32_t* block_idx, void* workspace,
-                size_t workspace_bytes, void* out, void* hip_stream);
+int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v, const void* sum_k,
+                const void* sum_v, const float* sum_bias, const int32_t* block_idx, void* out,
+                void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * Extra tokens, selection.
@@ -215,8 +218,7 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
  *   k          in   bf16 [B, H, N, 128]
  *   block_idx  in   int32 [B, H, nb, k] (from bsa_select; may be NULL iff k == 0)
  *   token_idx  out  int32 [B, H, nb, E], E = p->extra_tokens
- *   workspace  in/out  bsa_workspace_bytes() bytes (the region bsa_pool and
- *                   bsa_forward use is left as it is)
+ *   workspace  scratch, bsa_workspace_bytes() bytes
  *
  * Candidates of query block r: every token j of the blocks not in
  * block_idx[r].  Score: q_pool[r] . k_j, with q_pool[r] split exactly into
@@ -237,24 +239,22 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
  * token_idx[r] (value v_j), all in one softmax.
  * Sources: as for bsa_forward and bsa_select_tokens.
  *
- *   q, k, v    in   bf16 [B, H, N, 128]
- *   sum_k, sum_bias, block_idx   in   as for bsa_forward
+ *   q, k, v, sum_k, sum_v, sum_bias, block_idx, out, workspace
+ *              as for bsa_forward
  *   token_idx  in   int32 [B, H, nb, E], E = p->extra_tokens (may be NULL iff
  *                   E == 0): tokens in [0, N), distinct, none in a block of
  *                   block_idx[r], valid entries first, then -1 padding; the
  *                   kernels trust this (bsa_select_tokens' output)
- *   workspace  in/out  as for bsa_forward
- *   out        out  bf16 [B, H, N, 128]
  *
  * The attention kernel takes each query block's extra tokens first (their K
  * and V rows gathered on chip) and continues the same online softmax over
- * its blocks and summary rows.  With E == 0 this is bsa_forward (v and
- * token_idx unused).
+ * its blocks and summary rows.  With E == 0 this is bsa_forward (token_idx
+ * unused).
  */
 int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const void* v,
-                       const void* sum_k, const float* sum_bias, const int32_t* block_idx,
-                       const int32_t* token_idx, void* workspace, size_t workspace_bytes,
-                       void* out, void* hip_stream);
+                       const void* sum_k, const void* sum_v, const float* sum_bias,
+                       const int32_t* block_idx, const int32_t* token_idx, void* out, void* workspace,
+                       size_t workspace_bytes, void* hip_stream);
 
 /*
  * Spark-Reblock (the q_reuse_k layout): an adaptive order of the N rows of
@@ -267,9 +267,9 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
  * q_reuse_k: keys and values take the query layout).
  *
  * Use: bsa_reblock -> perm, then either
- *  - bsa_pool_reordered (-> k', the keys in the new order), bsa_select,
- *    [bsa_select_tokens on k'], bsa_forward_reordered -> out, which read
- *    q and v through perm and write out in the original row order, or
+ *  - bsa_pool_reordered (-> k', v', the keys and values in the new order),
+ *    bsa_select, [bsa_select_tokens on k'], bsa_forward_reordered -> out,
+ *    which read q through perm and write out in the original row order, or
  *  - bsa_permute_rows(q, k, v) -> q', k', v'; the block-sparse path
  *    (bsa_pool ... bsa_forward or bsa_forward_tokens) on q', k', v' with the
  *    same problem -> out'; bsa_unpermute_rows(out') -> out.
@@ -305,26 +305,28 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * The block-sparse path on a row order without permuted copies of Q, V and
- * the output.  Sources: as for bsa_pool, bsa_forward and bsa_reblock.
+ * The block-sparse path on a row order without permuted copies of Q and the
+ * output.  Sources: as for bsa_pool, bsa_forward and bsa_reblock.
  *
  * bsa_pool_reordered: bsa_pool of q', k', v' where x'[b, h, p, :] =
  * x[b, h, perm[b, h, p], :], every row read through perm, plus
- *   k_out  out  bf16 [B, H, N, 128]: k', the keys in the new order, which
- *               bsa_forward_reordered (and bsa_select_tokens) read as
- *               contiguous tiles; not overlapping q, k or v
+ *   k_out, v_out  out  bf16 [B, H, N, 128]: k' and v', the keys and values
+ *               in the new order, which bsa_forward_reordered (and
+ *               bsa_select_tokens) read as contiguous tiles; neither may
+ *               overlap q, k, v or the other
  * The pooled vectors, summaries and block indices that follow are those of
  * the new order (block c = positions [128 c, 128 c + 128)).
  *
  * bsa_forward_reordered: bsa_forward_tokens of q', k', v' (bsa_forward when
- * p->extra_tokens == 0; v and token_idx may then be NULL), with its output
- * row p written to out[b, h, perm[b, h, p], :]:
- *   q, v       in   bf16 [B, H, N, 128], the original row order
- *   k_r        in   bf16 [B, H, N, 128], k_out of bsa_pool_reordered
- *   sum_k, sum_bias, block_idx, token_idx, workspace   in   as for
+ * p->extra_tokens == 0; token_idx may then be NULL), with its output row p
+ * written to out[b, h, perm[b, h, p], :]:
+ *   q          in   bf16 [B, H, N, 128], the original row order
+ *   k_r, v_r   in   bf16 [B, H, N, 128], k_out and v_out of bsa_pool_reordered
+ *   sum_k, sum_v, sum_bias, block_idx, token_idx   in   as for
  *              bsa_forward_tokens, from the calls on the new order
  *   out        out  bf16 [B, H, N, 128], the original row order; not
  *              overlapping any input
+ *   workspace  unused (may be NULL): the reblocked order is visited as it is
  *
  *   perm  in  int32 [B, H, N], a permutation of 0..N-1 per (b, h) (as
  *             bsa_reblock writes it; other values are not checked and read
@@ -332,12 +334,12 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
  */
 int bsa_pool_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k,
                        const void* v, float* q_pool, float* k_pool, void* sum_k, void* sum_v,
-                       float* sum_bias, void* k_out, void* workspace, size_t workspace_bytes,
-                       void* hip_stream);
+                       float* sum_bias, void* k_out, void* v_out, void* workspace,
+                       size_t workspace_bytes, void* hip_stream);
 int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void* q, const void* k_r,
-                          const void* v, const void* sum_k, const float* sum_bias,
-                          const int32_t* block_idx, const int32_t* token_idx, void* workspace,
-                          size_t workspace_bytes, void* out, void* hip_stream);
+                          const void* v_r, const void* sum_k, const void* sum_v, const float* sum_bias,
+                          const int32_t* block_idx, const int32_t* token_idx, void* out, void* workspace,
+                          size_t workspace_bytes, void* hip_stream);
 
 /*
  * Rows of Q, K and V in the new order (the q_reuse_k layout):

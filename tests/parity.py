@@ -50,6 +50,32 @@ def check_idx_row(gpu_row, scores_row, k):
     return ok, True
 
 
+def check_idx_rows(gidx, scores, k):
+    """check_idx_row over every row of one (b, h): the oracle's top-k of each
+    row (descending score, ties to the lower index) taken for all rows at
+    once; rows whose set differs are judged by check_idx_row (tie zone).
+    Returns (bad_rows, tie_rows)."""
+    gidx = np.asarray(gidx)
+    s = np.asarray(scores, dtype=np.float64)
+    nq, nb = s.shape
+    if gidx.shape != (nq, k):
+        return list(range(nq)), 0
+    if k == 0:
+        return [], 0
+    cols = np.broadcast_to(np.arange(nb), (nq, nb))
+    order = np.lexsort((cols, -s), axis=-1)[:, :k]
+    want = np.sort(order, axis=-1)
+    bad, ties = [], 0
+    for r in np.nonzero(np.any(gidx != want, axis=-1))[0]:
+        ok, tie = check_idx_row(gidx[r], s[r], k)
+        if not ok:
+            bad.append(int(r))
+        ties += tie
+    # rows equal to the oracle's must still be strictly ascending (they are,
+    # being sorted), so only the differing rows needed the full check
+    return bad, ties
+
+
 def check_idx_row_forced(gpu_row, scores_row, k, forced):
     """check_idx_row with conditioning sinks: the row holds every forced block,
     and its other entries are the top-(k - len(forced)) of the remaining

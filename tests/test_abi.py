@@ -47,12 +47,21 @@ def test_blocks_and_workspace():
     assert bsa.bsa_problem_blocks(p) == (1045, 64)
     p = _prob(seq_len=100, top_k=5)
     assert bsa.bsa_problem_blocks(p) == (1, 1)
-    # workspace: V^T of every block + summary V^T groups (+ reweight anchor data)
+    # scratch only, the largest need of any one call: the forward calls'
+    # visiting order (int32 per query block), the reweight anchor and its
+    # float64 per-block partial sums, the token selection's key segments
+    def a256(x):
+        return (x + 255) // 256 * 256
     p = _prob(seq_len=37740, heads=56, top_k=64)
-    ws = bsa.bsa_workspace_bytes(p)
-    assert ws >= 56 * 295 * 128 * 128 * 2 + 56 * 3 * 128 * 128 * 2
+    assert bsa.bsa_workspace_bytes(p) == a256(56 * 295 * 4)
     pr = _prob(seq_len=37740, heads=56, top_k=64, summary="reweight")
-    assert bsa.bsa_workspace_bytes(pr) >= ws + 56 * 295 * 128 * 8
+    assert bsa.bsa_workspace_bytes(pr) == a256(56 * 295 * 128 * 8) + a256(56 * 128 * 8)
+    pe = _prob(extra_tokens=256)
+    assert bsa.bsa_workspace_bytes(pe) == 2 * 32 * 4 * 512 * 8
+    # the raw call returns 0 for a rejected problem
+    bad = _prob()
+    bad.head_dim = 64
+    assert bsa.lib().bsa_workspace_bytes(ctypes.byref(bad)) == 0
 
 
 def test_struct_layout_matches_header():
@@ -111,7 +120,7 @@ def test_invalid_problems_rejected_before_launch(field, value, err):
     L = bsa.lib()
     st = L.bsa_pool(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0, None)
     assert st in (bsa.BSA_ERR_INVALID, bsa.BSA_ERR_UNSUPPORTED)
-    st = L.bsa_forward(ctypes.byref(p), None, None, None, None, None, None, 0, None, None)
+    st = L.bsa_forward(ctypes.byref(p), None, None, None, None, None, None, None, None, None, 0, None)
     assert st in (bsa.BSA_ERR_INVALID, bsa.BSA_ERR_UNSUPPORTED)
 
 
@@ -121,20 +130,39 @@ def test_null_pointers_and_small_workspace_rejected():
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
     assert L.bsa_pool(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake, fake, fake,
                       1 << 30, None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_pool(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+    # reweight mode needs the workspace (the anchor); mean mode does not
+    pr = _prob(summary="reweight")
+    assert L.bsa_pool(ctypes.byref(pr), fake, fake, fake, fake, fake, fake, fake, fake, fake,
                       16, None) == bsa.BSA_ERR_WORKSPACE
-    assert L.bsa_pool(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, None,
+    assert L.bsa_pool(ctypes.byref(pr), fake, fake, fake, fake, fake, fake, fake, fake, None,
                       1 << 30, None) == bsa.BSA_ERR_WORKSPACE
     assert L.bsa_select(ctypes.byref(p), fake, fake, None, None) == bsa.BSA_ERR_INVALID
     # misaligned tensors
     odd = ctypes.c_void_p((1 << 20) + 2)
     assert L.bsa_pool(ctypes.byref(p), odd, fake, fake, fake, fake, fake, fake, fake, fake,
                       1 << 30, None) == bsa.BSA_ERR_INVALID
-    # sum_k may be NULL only when every block is selected
-    assert L.bsa_forward(ctypes.byref(p), fake, fake, None, None, fake, fake, 1 << 30, fake,
-                         None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_forward(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 16, fake,
-                         None) == bsa.BSA_ERR_WORKSPACE
+    big = 1 << 30
+    # bsa_forward(p, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, ws, ws_bytes, stream):
+    # every summary tensor is needed while a row can skip a block
+    for i in (3, 4, 5, 0, 1, 2, 7):   # sum_k, sum_v, sum_bias, then q, k, v, out
+        args = [fake] * 8
+        args[i] = None
+        assert L.bsa_forward(ctypes.byref(p), *args, fake, big, None) == bsa.BSA_ERR_INVALID, i
+    assert L.bsa_forward(ctypes.byref(p), fake, fake, fake, odd, fake, fake, fake, fake, fake, big,
+                         None) == bsa.BSA_ERR_INVALID                      # misaligned sum_k
+    assert L.bsa_forward(ctypes.byref(p), fake, fake, fake, fake, odd, fake, fake, fake, fake, big,
+                         None) == bsa.BSA_ERR_INVALID                      # misaligned sum_v
+    # the optional workspace, when given, must hold the visiting order
+    assert L.bsa_forward(ctypes.byref(p), *([fake] * 8), fake, 16, None) == bsa.BSA_ERR_WORKSPACE
+    assert L.bsa_forward(ctypes.byref(p), *([fake] * 8), odd, big, None) == bsa.BSA_ERR_WORKSPACE
+    # threshold selection with the cap at every block: k == nb, yet rows keep
+    # fewer blocks, so the summary rows are still read and must be given
+    pt = _prob(top_k=32, tau=0.5)
+    assert bsa.bsa_problem_blocks(pt) == (32, 32)
+    for i in (3, 4, 5):
+        args = [fake] * 8
+        args[i] = None
+        assert L.bsa_forward(ctypes.byref(pt), *args, None, 0, None) == bsa.BSA_ERR_INVALID, i
     # top_k = 0: select has nothing to do and needs no pointers
     p0 = _prob(top_k=0)
     assert L.bsa_select(ctypes.byref(p0), None, None, None, None) == bsa.BSA_OK
@@ -157,17 +185,16 @@ def test_extra_token_entry_points_validate():
     # and the workspace, which holds a key segment per (query block, token quarter)
     assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, fake, fake, None, big, None) == bsa.BSA_ERR_WORKSPACE
     assert L.bsa_select_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, 16, None) == bsa.BSA_ERR_WORKSPACE
-    n = bsa.bsa_workspace_bytes(pe) - bsa.bsa_workspace_bytes(p)
-    assert 2 * 32 * 4 * 512 * 8 <= n <= 2 * 32 * 4 * 512 * 8 + 256
-    # bsa_forward refuses a problem with extra tokens; bsa_forward_tokens needs v and token_idx
-    assert L.bsa_forward(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, big, fake,
-                         None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, None, fake, fake, fake, fake, fake, big,
-                                fake, None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, None, fake, big,
-                                fake, None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, fake, fake,
-                                16, fake, None) == bsa.BSA_ERR_WORKSPACE
+    assert bsa.bsa_workspace_bytes(pe) == 2 * 32 * 4 * 512 * 8
+    # bsa_forward refuses a problem with extra tokens; bsa_forward_tokens
+    # (p, q, k, v, sum_k, sum_v, sum_bias, block_idx, token_idx, out, ws, ws_bytes, stream)
+    # needs v and token_idx
+    assert L.bsa_forward(ctypes.byref(pe), *([fake] * 8), fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, None, fake, fake, fake, fake, fake, fake,
+                                fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_forward_tokens(ctypes.byref(pe), fake, fake, fake, fake, fake, fake, fake, None, fake,
+                                fake, big, None) == bsa.BSA_ERR_INVALID
+    assert L.bsa_forward_tokens(ctypes.byref(pe), *([fake] * 9), fake, 16, None) == bsa.BSA_ERR_WORKSPACE
 
 
 def test_reblock_entry_points_validate():
@@ -194,18 +221,31 @@ def test_reblock_entry_points_validate():
                               None) == bsa.BSA_ERR_INVALID
     assert L.bsa_unpermute_rows(ctypes.byref(p), fake, None, fake, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_unpermute_rows(ctypes.byref(p), fake, fake, odd, None) == bsa.BSA_ERR_INVALID
-    # the reordered calls: a missing or misaligned perm, k_out on k, out on q
+    # the reordered calls: a missing or misaligned perm, k_out / v_out on an
+    # input or on each other, out on an input.
+    # bsa_pool_reordered(p, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out,
+    #                    ws, ws_bytes, stream)
     f = fake
-    assert L.bsa_pool_reordered(ctypes.byref(p), None, f, f, f, f, f, f, f, f, odd, f, big,
+    g = ctypes.c_void_p((1 << 20) + 4096)
+    h = ctypes.c_void_p((1 << 20) + 8192)
+    assert L.bsa_pool_reordered(ctypes.byref(p), None, f, f, f, f, f, f, f, f, g, h, f, big,
                                 None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_pool_reordered(ctypes.byref(p), odd, f, f, f, f, f, f, f, f, f, f, big,
+    assert L.bsa_pool_reordered(ctypes.byref(p), odd, f, f, f, f, f, f, f, f, g, h, f, big,
                                 None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_pool_reordered(ctypes.byref(p), f, f, f, f, f, f, f, f, f, f, f, big,
+    assert L.bsa_pool_reordered(ctypes.byref(p), g, h, f, h, f, f, f, f, f, f, g, f, big,
                                 None) == bsa.BSA_ERR_INVALID       # k_out == k
-    assert L.bsa_forward_reordered(ctypes.byref(p), None, f, f, f, f, f, f, None, f, big, odd,
+    assert L.bsa_pool_reordered(ctypes.byref(p), g, h, h, f, f, f, f, f, f, g, g, f, big,
+                                None) == bsa.BSA_ERR_INVALID       # k_out == v_out
+    assert L.bsa_pool_reordered(ctypes.byref(p), g, h, h, f, f, f, f, f, f, g, odd, f, big,
+                                None) == bsa.BSA_ERR_INVALID       # misaligned v_out
+    # bsa_forward_reordered(p, perm, q, k_r, v_r, sum_k, sum_v, sum_bias, block_idx, token_idx,
+    #                       out, ws, ws_bytes, stream)
+    assert L.bsa_forward_reordered(ctypes.byref(p), None, f, g, h, f, f, f, f, None, odd, None, 0,
                                    None) == bsa.BSA_ERR_INVALID
-    assert L.bsa_forward_reordered(ctypes.byref(p), f, f, f, f, f, f, f, None, f, big, f,
+    assert L.bsa_forward_reordered(ctypes.byref(p), f, f, g, h, f, f, f, f, None, f, None, 0,
                                    None) == bsa.BSA_ERR_INVALID    # out == q
+    assert L.bsa_forward_reordered(ctypes.byref(p), f, g, f, h, f, f, f, f, None, h, None, 0,
+                                   None) == bsa.BSA_ERR_INVALID    # out == v_r
     # options that name rows by position are refused by all the reblock calls
     size = ctypes.c_size_t()
     for q in (bsa.make_problem(1, 2, 4096, top_k=8, sink_rows=100),
@@ -215,9 +255,9 @@ def test_reblock_entry_points_validate():
         assert L.bsa_permute_rows(ctypes.byref(q), fake, fake, fake, fake, fake, fake, fake,
                                   None) == bsa.BSA_ERR_UNSUPPORTED
         assert L.bsa_unpermute_rows(ctypes.byref(q), fake, fake, fake, None) == bsa.BSA_ERR_UNSUPPORTED
-        assert L.bsa_pool_reordered(ctypes.byref(q), f, f, f, f, f, f, f, f, f, odd, f, big,
+        assert L.bsa_pool_reordered(ctypes.byref(q), f, f, f, f, f, f, f, f, f, odd, odd, f, big,
                                     None) == bsa.BSA_ERR_UNSUPPORTED
-        assert L.bsa_forward_reordered(ctypes.byref(q), f, f, f, f, f, f, f, None, f, big, odd,
+        assert L.bsa_forward_reordered(ctypes.byref(q), f, f, f, f, f, f, f, f, None, odd, None, 0,
                                        None) == bsa.BSA_ERR_UNSUPPORTED
     # an anchor over every row does not depend on the order
     for rows in (0, 4096):

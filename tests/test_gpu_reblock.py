@@ -153,7 +153,7 @@ def test_reordered_calls_equal_permuted_copies(torch_cuda, N, top_k, summary, ta
     """bsa_pool_reordered / bsa_forward_reordered (rows read through perm, the
     output written back through it) against the permuted-copy path
     (bsa_permute_rows, the plain calls, bsa_unpermute_rows): the same bits in
-    every output, and k_r equal to the permuted K."""
+    every output, and k_r, v_r equal to the permuted K and V."""
     torch = torch_cuda
     _log("case reordered calls N=%d k=%d %s tau=%s extra=%d" % (N, top_k, summary, tau, extra))
     qb, kb, vb = generate(custom(N, heads=2, seed=71), threads=2)
@@ -169,19 +169,23 @@ def test_reordered_calls_equal_permuted_copies(torch_cuda, N, top_k, summary, ta
     bsa.bsa_unpermute_rows(p, perm, out_r, out_b)
     torch.cuda.synchronize()
     assert torch.equal(aux_a["k_r"], kr)
+    assert torch.equal(aux_a["v_r"], vr)
     for name in ("q_pool", "k_pool", "sum_k", "sum_v", "sum_bias", "block_idx", "token_idx"):
         if aux_a[name] is not None:
             assert torch.equal(aux_a[name], aux_b[name]), name
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
-    # k_out is written row by row: every element of it, nothing past it
+    # k_out and v_out are written row by row: every element of them, nothing past them
     G = 4096
     n_el = 2 * N * 128
-    k_out = torch.full((n_el + G,), float("nan"), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    k_out, v_out = (torch.full((n_el + G,), float("nan"), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+                    for _ in range(2))
     bsa.bsa_pool_reordered(p, perm, q, k, v, aux_a["q_pool"], aux_a["k_pool"], aux_a["sum_k"],
-                           aux_a["sum_v"], aux_a["sum_bias"], k_out, aux_a["workspace"])
+                           aux_a["sum_v"], aux_a["sum_bias"], k_out, v_out, aux_a["workspace"])
     torch.cuda.synchronize()
     assert torch.equal(k_out[:n_el].view(1, 2, N, 128), kr)
+    assert torch.equal(v_out[:n_el].view(1, 2, N, 128), vr)
     assert bool(torch.isnan(k_out[n_el:].float()).all())
+    assert bool(torch.isnan(v_out[n_el:].float()).all())
 
 
 def test_reblock_rejects_position_options(torch_cuda):
