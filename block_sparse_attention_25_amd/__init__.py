@@ -23,11 +23,11 @@ __all__ = [
     "BSA_OK", "BSA_ERR_INVALID", "BSA_ERR_UNSUPPORTED", "BSA_ERR_WORKSPACE", "BSA_ERR_HIP",
     "SUMMARY_MEAN", "SUMMARY_REWEIGHT", "BsaError", "Problem", "lib", "library_path",
     "bsa_status_str", "bsa_problem_blocks", "bsa_workspace_bytes", "bsa_pool", "bsa_select",
-    "bsa_forward", "bsa_select_tokens", "bsa_forward_tokens", "k_from_ratio", "make_problem",
+    "bsa_forward", "bsa_forward_noalloc", "bsa_select_tokens", "bsa_forward_tokens", "k_from_ratio", "make_problem",
     "attention", "MAX_EXTRA",
 ]
 
-BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP = 0, 1, 2, 3, 4
+BSA_OK, BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE, BSA_ERR_HIP, BSA_ERR_SCRATCH = 0, 1, 2, 3, 4, 5
 SUMMARY_MEAN, SUMMARY_REWEIGHT = 0, 1
 SELECT_TOPK, SELECT_THRESHOLD = 0, 1
 BLOCK = 128
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.bsa_select.restype = ctypes.c_int
         L.bsa_forward.argtypes = [_P] + [_vp] * 9 + [ctypes.c_size_t, _vp]
         L.bsa_forward.restype = ctypes.c_int
+        L.bsa_forward_noalloc.argtypes = [_P] + [_vp] * 9
+        L.bsa_forward_noalloc.restype = ctypes.c_int
         L.bsa_select_tokens.argtypes = [_P] + [_vp] * 5 + [ctypes.c_size_t, _vp]
         L.bsa_select_tokens.restype = ctypes.c_int
         L.bsa_forward_tokens.argtypes = [_P] + [_vp] * 10 + [ctypes.c_size_t, _vp]
@@ -106,7 +108,7 @@ def _raise(status: int, where: str):
         return
     if status == BSA_ERR_UNSUPPORTED:
         raise NotImplementedError("%s: %s" % (where, bsa_status_str(status)))
-    if status in (BSA_ERR_INVALID, BSA_ERR_WORKSPACE):
+    if status in (BSA_ERR_INVALID, BSA_ERR_WORKSPACE, BSA_ERR_SCRATCH):
         raise ValueError("%s: %s" % (where, bsa_status_str(status)))
     raise BsaError(status, where)
 
@@ -160,6 +162,12 @@ def bsa_forward(p: Problem, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, wor
     _raise(lib().bsa_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sum_k), _ptr(sum_v),
                              _ptr(sum_bias), _ptr(block_idx), _ptr(out), _ptr(workspace),
                              _nbytes(workspace), _stream(stream)), "bsa_forward")
+
+
+def bsa_forward_noalloc(p: Problem, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, stream=None):
+    _raise(lib().bsa_forward_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sum_k),
+                                     _ptr(sum_v), _ptr(sum_bias), _ptr(block_idx), _ptr(out),
+                                     _stream(stream)), "bsa_forward_noalloc")
 
 
 def bsa_select_tokens(p: Problem, q_pool, k, block_idx, token_idx, workspace, stream=None):

@@ -25,6 +25,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include "bsa.h"
@@ -1908,6 +1909,31 @@ int launch_pool(const Geometry& g, const int32_t* perm, const void* q, const voi
   return launch_status();
 }
 
+// Scratch of bsa_forward_noalloc: the visiting order (int32 per (b, h, query
+// block)) in a file-scope device array instead of a workspace argument.  In
+// host code `scratch` only names the symbol; its device address, one per GPU,
+// comes from hipGetSymbolAddress on the first call on that device.
+constexpr size_t NOALLOC_ORDER_MAX = (size_t)1 << 20;  // entries: 4 MiB
+__device__ __align__(256) int32_t scratch[NOALLOC_ORDER_MAX];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+int32_t* scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// Device address of this GPU's scratch array (looked up once per device, with
+// that device current), or nullptr on failure.
+int32_t* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = (int32_t*)ptr;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -1919,6 +1945,8 @@ const char* bsa_status_str(int status) {
     case BSA_ERR_UNSUPPORTED: return "unsupported problem (head_dim/block must be 128, nb <= 2048)";
     case BSA_ERR_WORKSPACE: return "workspace missing or too small";
     case BSA_ERR_HIP: return "HIP launch failed";
+    case BSA_ERR_SCRATCH:
+      return "problem too large for the static scratch of bsa_forward_noalloc (B*H*nb > 1048576)";
     default: return "unknown status";
   }
 }
@@ -1998,6 +2026,21 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
     return st;
   return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, nullptr, nullptr, out,
                           (int32_t*)workspace, (hipStream_t)hip_stream);
+}
+
+int bsa_forward_noalloc(const bsa_problem* p, const void* q, const void* k, const void* v, const void* sum_k,
+                        const void* sum_v, const float* sum_bias, const int32_t* block_idx, void* out,
+                        void* hip_stream) {
+  Geometry g;
+  int st = make_geometry(p, &g);
+  if (st != BSA_OK) return st;
+  if (g.E > 0) return BSA_ERR_INVALID;
+  if ((st = check_forward(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, nullptr, 0)) != BSA_OK) return st;
+  if ((size_t)(g.B * g.H * g.nb) > NOALLOC_ORDER_MAX) return BSA_ERR_SCRATCH;
+  int32_t* order = device_scratch();
+  if (!order) return BSA_ERR_HIP;
+  return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, nullptr, nullptr, out, order,
+                          (hipStream_t)hip_stream);
 }
 
 int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,

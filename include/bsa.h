@@ -52,7 +52,8 @@ enum {
   BSA_ERR_INVALID = 1,      /* bad pointer, size, range or mode */
   BSA_ERR_UNSUPPORTED = 2,  /* head_dim or block size other than 128, or N too large */
   BSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than bsa_workspace_bytes */
-  BSA_ERR_HIP = 4           /* a HIP launch failed */
+  BSA_ERR_HIP = 4,          /* a HIP launch failed */
+  BSA_ERR_SCRATCH = 5       /* bsa_forward_noalloc: problem larger than its static scratch */
 };
 
 enum { BSA_SUMMARY_MEAN = 0, BSA_SUMMARY_REWEIGHT = 1 };
@@ -207,6 +208,23 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool,
 int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* v, const void* sum_k,
                 const void* sum_v, const float* sum_bias, const int32_t* block_idx, void* out,
                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * bsa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and bits as bsa_forward with a workspace, with no
+ * workspace argument.  Its scratch (the visiting order, B*H*nb int32) lives
+ * in a static device array of the library, 4 MiB on each GPU it runs on
+ * (held until the process ends): problems with B*H*nb > 1048576 are rejected
+ * with BSA_ERR_SCRATCH.  It allocates and frees nothing.  Every call on one
+ * GPU shares that array, so calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller; each call
+ * writes the entries it reads before reading them.  Arguments and errors
+ * otherwise as for bsa_forward (extra tokens are rejected).
+ */
+int bsa_forward_noalloc(const bsa_problem* p, const void* q, const void* k, const void* v,
+                        const void* sum_k, const void* sum_v, const float* sum_bias,
+                        const int32_t* block_idx, void* out, void* hip_stream);
 
 /*
  * Extra tokens, selection.

@@ -29,8 +29,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(5):
-        assert bsa.bsa_status_str(st)
+    for st in range(6):
+        assert bsa.bsa_status_str(st) != "unknown status"
     assert bsa.bsa_status_str(99) == "unknown status"
 
 
@@ -266,3 +266,22 @@ def test_reblock_entry_points_validate():
     bad = bsa.make_problem(1, 2, 4096, top_k=8)
     bad.head_dim = 64
     assert L.bsa_reblock_workspace_bytes(ctypes.byref(bad), ctypes.byref(size)) == bsa.BSA_ERR_UNSUPPORTED
+
+
+def test_noalloc_entry_point_validates():
+    """bsa_forward_noalloc(p, q, k, v, sum_k, sum_v, sum_bias, block_idx, out,
+    stream): bsa_forward's checks, then the size of its static scratch (the
+    visiting order, 2^20 int32 entries), all before any HIP call."""
+    L = bsa.lib()
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    p = _prob()
+    for i in range(8):
+        args = [fake] * 8
+        args[i] = None
+        if i == 6:   # block_idx
+            continue
+        assert L.bsa_forward_noalloc(ctypes.byref(p), *args, None) == bsa.BSA_ERR_INVALID, i
+    assert L.bsa_forward_noalloc(ctypes.byref(_prob(extra_tokens=64)), *([fake] * 8), None) == \
+        bsa.BSA_ERR_INVALID
+    big = bsa.make_problem(1, 513, 262144, top_k=64)   # 513 x 2048 blocks > 2^20
+    assert L.bsa_forward_noalloc(ctypes.byref(big), *([fake] * 8), None) == bsa.BSA_ERR_SCRATCH
