@@ -1143,8 +1143,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 // the blocks it skipped with the largest q_pool[r] . k_j, equal scores going
 // to the lower token; every skipped block keeps its summary row.
 // Source: "H3 Sparse Attention" (WAS Node Suite node page), section "The
-// inputs that matter" (extra_tokens: the top-scoring tokens each query block
-// reads beyond its chosen blocks, 256 by default).
+// inputs that matter" (extra_tokens: per query block, individually
+// highest-scoring tokens on top of its selected blocks; 256 by default).
 //
 // token_select_kernel: one workgroup of 8 wavefronts (two per SIMD) per 32
 // query blocks of one (b, h), on a 1-D grid remapped like the select kernel.

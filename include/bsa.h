@@ -76,8 +76,9 @@ typedef struct bsa_problem {
    * that is a sink block attends to every key block exactly.  sink_rows = 0
    * (with sink_start 0) means no sinks: pure top-k.  The range must lie in
    * [0, N].  Sources: "H3 Sparse Attention" (WAS Node Suite node page),
-   * section "The inputs that matter" (sink_conditioning reads the prompt,
-   * reference and audio rows exactly and runs those rows dense); "H3 Sparse
+   * section "The inputs that matter" (with sink_conditioning on, the
+   * prompt, reference and audio rows are attended exactly and their own
+   * queries attend densely); "H3 Sparse
    * Attention" (node page on video budgets), opening section (conditioning
    * and non-video queries, and the tiles on the boundary between contexts,
    * stay dense). */
@@ -89,8 +90,9 @@ typedef struct bsa_problem {
    * statistics, float64), at most top_k of them (largest first), so rows keep
    * different numbers of blocks and are padded with -1.  Source: "H3 Sparse
    * Attention" (WAS Node Suite node page), section "The inputs that matter"
-   * (tau 1.0 keeps roughly 16% of key blocks, 1.5 about 7%, 2.0 about 3%:
-   * the normal tail beyond tau standard deviations). */
+   * (the share of key blocks kept exact is given as about 16% at tau 1.0,
+   * 7% at 1.5 and 3% at 2.0: the normal tail beyond tau standard
+   * deviations). */
   int32_t select_mode;
   float select_tau;    /* threshold mode only; finite */
   /* Extra tokens, in [0, BSA_MAX_EXTRA]: besides its kept blocks, each query
@@ -99,9 +101,9 @@ typedef struct bsa_problem {
    * those blocks keep their summary rows.  0 turns the option off.  Used by
    * bsa_select_tokens and bsa_forward_tokens; bsa_forward rejects a problem
    * with extra tokens.  Source: "H3 Sparse Attention" (WAS Node Suite node
-   * page), section "The inputs that matter" (extra_tokens, the top-scoring
-   * tokens each query block reads beyond its chosen blocks; 256 by default,
-   * 0 fastest). */
+   * page), section "The inputs that matter" (extra_tokens: per query block,
+   * that many individually highest-scoring tokens on top of its selected
+   * blocks; 256 by default, 0 the fastest setting). */
   int32_t extra_tokens;
 } bsa_problem;
 
@@ -229,8 +231,8 @@ int bsa_forward_noalloc(const bsa_problem* p, const void* q, const void* k, cons
 /*
  * Extra tokens, selection.
  * Source: "H3 Sparse Attention" (WAS Node Suite node page), section "The
- * inputs that matter" (extra_tokens: the top-scoring tokens each query block
- * reads beyond its chosen blocks).
+ * inputs that matter" (extra_tokens: per query block, individually
+ * highest-scoring tokens on top of its selected blocks).
  *
  *   q_pool     in   fp32 [B, H, nb, 128] (from bsa_pool)
  *   k          in   bf16 [B, H, N, 128]

@@ -50,21 +50,22 @@ Readings taken where the pages are silent (each is exercised by a test):
      other blocks (so a row holds min(top_k, nb - n_sink) + n_sink blocks),
      and a query block that is itself a sink block attends to every key block
      exactly (no summary rows).  Sources: "H3 Sparse Attention" (WAS Node
-     Suite node page), section "The inputs that matter" (sink_conditioning
-     reads the prompt, reference and audio rows exactly and runs those rows
-     dense); "H3 Sparse Attention" (the node page on video budgets), opening
-     section (conditioning, non-video queries and the tiles on the boundary
-     between contexts stay fully dense; only video-to-video attention is
-     cut).  The block straddling the boundary counts as a sink block.
+     Suite node page), section "The inputs that matter" (with
+     sink_conditioning on, the prompt, reference and audio rows are attended
+     exactly and their own queries attend densely); "H3 Sparse Attention"
+     (the node page on video budgets), opening section (only attention among
+     video tokens is made sparse: conditioning and non-video queries, and
+     the tiles where two contexts meet, keep dense attention).  The block straddling the boundary counts as a sink block.
   R14 threshold (variable-k) selection with parameter tau: a key block is
      kept when its score exceeds the mean of its row's block scores by more
      than tau population standard deviations, s > mean + tau * std (both over
      all nb blocks of the row, in float64); at most top_k blocks are kept
      (the highest, ties to the lower index), sink blocks always.  Rows are
      padded with -1 after their kept blocks.  Source: "H3 Sparse Attention"
-     (WAS Node Suite node page), section "The inputs that matter" (tau 1.0
-     keeps roughly 16% of key blocks exact, 1.5 about 7%, 2.0 about 3%): the
-     normal tail beyond tau standard deviations is 15.9%, 6.7% and 2.3%.
+     (WAS Node Suite node page), section "The inputs that matter" (the
+     share of key blocks kept exact is given as about 16% at tau 1.0, 7% at
+     1.5 and 3% at 2.0): the normal tail beyond tau standard deviations is
+     15.9%, 6.7% and 2.3%.
   R15 extra tokens: besides its kept blocks, each query block r reads exactly
      the E tokens j of the blocks it skipped with the largest q_pool[r] . k_j
      (the same pooled-query score as block selection, float64), ties to the
@@ -72,8 +73,8 @@ Readings taken where the pages are silent (each is exercised by a test):
      a summary row as one key, so nothing is counted twice).  Sink query
      blocks skip nothing and read no extra tokens.  Source: "H3 Sparse
      Attention" (WAS Node Suite node page), section "The inputs that matter"
-     (extra_tokens, the top-scoring tokens each query block reads beyond its
-     chosen blocks).
+     (extra_tokens: per query block, individually highest-scoring tokens on
+     top of its selected blocks).
 
   R17 Spark-Reblock (the "q_reuse_k" layout).  Sources: "Spark-H3: Block
      Sparse Attention Speeds Up MiniMax-H3 in ComfyUI", section "What
