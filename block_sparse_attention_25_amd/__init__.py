@@ -35,7 +35,9 @@ HEAD_DIM = 128
 MAX_EXTRA = 256
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libbsa.so")
+# BSA_LIBRARY may name another build of the same library (e.g. the host-side
+# sanitizer build that the CPU tests exercise)
+library_path = os.environ.get("BSA_LIBRARY") or os.path.join(_HERE, "libbsa.so")
 
 
 class Problem(ctypes.Structure):

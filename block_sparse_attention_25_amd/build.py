@@ -29,5 +29,33 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     return LIB
 
 
+# Host-side sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer on
+# the host code only: argument checks, geometry, workspace layout, launch
+# set-up).  Each -fsanitize flag applies to the host pass alone, so the GPU
+# code is built as usual.  Load it with the sanitizer runtime preloaded (see
+# asan_runtime()) and BSA_LIBRARY pointing at it.
+SANITIZE_FLAGS = [
+    "-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan",
+]
+
+
+def asan_runtime():
+    """Path of the compiler's shared AddressSanitizer runtime, or None."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_sanitized(out_path: str) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + SANITIZE_FLAGS
+    cmd = [hipcc, *flags, "-I", INCLUDE, *SRCS, "-o", out_path]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed (exit %d): %s\n%s" % (res.returncode, " ".join(cmd), res.stderr))
+    return out_path
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

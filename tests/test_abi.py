@@ -28,6 +28,16 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_loaded_library_is_the_one_named():
+    """BSA_LIBRARY selects another build (the sanitizer build in
+    test_sanitized_host.py): the process must have mapped exactly that file."""
+    L = bsa.lib()
+    want = os.path.realpath(bsa.library_path)
+    assert os.path.realpath(L._name) == want
+    maps = open("/proc/self/maps").read()
+    assert want in maps
+
+
 def test_status_strings():
     for st in range(6):
         assert bsa.bsa_status_str(st) != "unknown status"
