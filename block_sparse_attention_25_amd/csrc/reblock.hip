@@ -13,11 +13,13 @@
 //   M = (1/N) sum_j k_j k_j^T, L L^T = M + 1e-6 (trace(M) / 128) I + 1e-30 I,
 //   z_i = L^T q_i / |L^T q_i|, so that z_i . z_j is the cosine of q_i and q_j
 //   in the metric M.  A group of n rows (m = ceil(n / 128) blocks, m >= 2)
-//   splits on the coordinate of z with the largest variance over the group
-//   (lowest coordinate on ties): its 128 ceil(m / 2) rows with the smallest
-//   value of that coordinate (ties to the lower row) go left, the rest right,
-//   each in ascending row order.  The leaves, left to right, are the new
-//   order: perm[p] is the row placed at position p.
+//   splits by two pivots: a, its row farthest from the centroid of its z
+//   rows, and b, its row farthest from a (lowest row on ties); its 128
+//   ceil(m / 2) rows with the smallest z_i . (z_b - z_a) (ties to the lower
+//   row) go left, the rest right, each in ascending row order.  The leaves,
+//   left to right, are the new order: perm[p] is the row placed at position
+//   p.  Only distances between z rows enter, so the order depends on the
+//   metric cosines alone, not on the basis of the head features.
 //
 // Kernels:
 //   rb_moment_kernel    K^T K over 2048-row chunks on the matrix cores (bf16
@@ -28,15 +30,19 @@
 //                       each entry
 //   rb_embed_kernel     z = Q L on the matrix cores (three terms), each row
 //                       normalised (float32); the identity order
-//   rb_stats_kernel     one level of the bisection, first half: float64 sums of
-//                       z and z^2 per coordinate over 128-position slices of
-//                       the root and of left children (a right child's sums
-//                       are its parent's less its left sibling's)
-//   rb_split_*_kernel   second half, per group: the coordinate of largest
-//                       variance, the split value (a radix select, or a
-//                       bitwise search for small groups), a stable partition
-//                       of the group's rows (one wavefront per group up to
-//                       1024 rows, else one workgroup)
+//   per level of the bisection:
+//   rb_stats_kernel     float64 sums of z per coordinate over 128-position
+//                       slices of the root and of left children (a right
+//                       child's sums are its parent's less its left sibling's)
+//   rb_center_kernel    per group: its totals and centroid
+//   rb_far_kernel       per slice: the row farthest from the group's centroid
+//                       (then from its first pivot), float64 distances
+//   rb_pivot_kernel     per group: the farthest of its slices' rows
+//   rb_keys_kernel      per slice: each row's split key z_i . (z_b - z_a)
+//   rb_split_*_kernel   per group: the split value of the keys (a radix
+//                       select, or a bitwise search for small groups), a
+//                       stable partition of the group's rows (one wavefront
+//                       per group up to 1024 rows, else one workgroup)
 //   rb_permute_kernel   rows of Q, K, V gathered into the new order
 //   rb_unpermute_kernel output rows put back in their original places
 #include <hip/hip_runtime.h>
@@ -349,25 +355,25 @@ __device__ __forceinline__ void rb_group_of(int N, int level, int pos, int& s, i
 
 // One workgroup of 4 wavefronts per (slice, batch x head); wavefront w sums
 // rows w + 4 i of the slice, lane l coordinates 2 l and 2 l + 1, with eight
-// row loads in flight.  stats[bh][slice][0 | 1][d]: sums of z_d and z_d^2.
+// row loads in flight.  stats[bh][slice][d]: sum of z_d.
 __global__ __launch_bounds__(256) void rb_stats_kernel(const float* __restrict__ zh,
                                                        const int32_t* __restrict__ pin,
                                                        double* __restrict__ stats, int N, int nb, int level) {
-  __shared__ double red[2][4][RB_HD];
+  __shared__ double red[4][RB_HD];
   const int c = blockIdx.x % nb;
   const size_t bh = blockIdx.x / nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int s, n;
   bool right;
   rb_group_of(N, level, c * RB_BLK, s, n, right);
-  if (n <= RB_BLK || right) return;  // a leaf, or sums the split kernel derives
+  if (n <= RB_BLK || right) return;  // a leaf, or sums the centre kernel derives
   const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
   const float* zb = zh + bh * (size_t)N * RB_HD;
   // lane i < 32 holds the row of slice position wave + 4 i; positions past
   // the end of a short last slice read its last row and are weighted out, so
   // every load is unconditional and all eight are in flight together
   const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
-  double s1x = 0.0, s1y = 0.0, s2x = 0.0, s2y = 0.0;
+  double s1x = 0.0, s1y = 0.0;
 #pragma unroll
   for (int i0 = 0; i0 < 32; i0 += 8) {
     float2 v[8];
@@ -379,22 +385,14 @@ __global__ __launch_bounds__(256) void rb_stats_kernel(const float* __restrict__
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const double w = wave + 4 * (i0 + u) < cnt ? 1.0 : 0.0;
-      const double x = (double)v[u].x, y = (double)v[u].y;
-      s1x += w * x;
-      s1y += w * y;
-      s2x += w * x * x;
-      s2y += w * y * y;
+      s1x += w * (double)v[u].x;
+      s1y += w * (double)v[u].y;
     }
   }
-  red[0][wave][2 * lane] = s1x;
-  red[0][wave][2 * lane + 1] = s1y;
-  red[1][wave][2 * lane] = s2x;
-  red[1][wave][2 * lane + 1] = s2y;
+  red[wave][2 * lane] = s1x;
+  red[wave][2 * lane + 1] = s1y;
   __syncthreads();
-  if (tid < 2 * RB_HD) {
-    const int a = tid >> 7, d = tid & (RB_HD - 1);
-    stats[((bh * nb + c) * 2 + a) * RB_HD + d] = red[a][0][d] + red[a][1][d] + red[a][2][d] + red[a][3][d];
-  }
+  if (tid < RB_HD) stats[(bh * nb + c) * RB_HD + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
 }
 
 // exclusive prefix over the workgroup of two counters (x, y) per thread
@@ -451,126 +449,202 @@ __device__ __forceinline__ bool rb_locate(int N, int level, int gi, int& s, int&
   return true;
 }
 
-// the split coordinate of a wavefront that holds the variances of
-// coordinates lane and lane + 64: the largest variance, the lowest
-// coordinate on ties (the same in every lane)
-__device__ __forceinline__ int rb_argmax_wave(double v0, double v1, int lane) {
-  double best = v0;
-  int bd = lane;
-  if (v1 > best) {
-    best = v1;
-    bd = lane + 64;
+// sum of z_d over the slices [c0, c0 + cnt), added in slice order with eight
+// loads in flight
+__device__ __forceinline__ double rb_slice_sum(const double* stats_bh, int c0, int cnt, int d) {
+  const double* sp = stats_bh + (size_t)c0 * RB_HD + d;
+  double a = 0.0;
+  for (int base = 0; base < cnt; base += 8) {
+    double va[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) va[c] = sp[(size_t)min(base + c, cnt - 1) * RB_HD];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a += base + c < cnt ? va[c] : 0.0;
+  }
+  return a;
+}
+
+// One workgroup of 128 threads (one per coordinate) per group slot of the
+// level: the group's totals (its slices' sums, or for a right child its
+// parent's totals less its left sibling's slices), kept in tcur for its
+// children, and its centroid.  Per-group arrays are indexed by the group's
+// first slice.
+__global__ __launch_bounds__(RB_HD) void rb_center_kernel(const double* __restrict__ stats,
+                                                          const double* __restrict__ tprev,
+                                                          double* __restrict__ tcur, double* __restrict__ cen,
+                                                          int N, int nb, int level) {
+  const int ng = 1 << level;
+  const int gi = blockIdx.x % ng;
+  const size_t bh = blockIdx.x / ng;
+  const int d = threadIdx.x;
+  int s, n, sp;
+  if (!rb_locate(N, level, gi, s, n, sp)) return;
+  if (n <= RB_BLK) return;
+  const double* st = stats + bh * (size_t)nb * RB_HD;
+  double tot;
+  if (sp == s) {
+    tot = rb_slice_sum(st, s / RB_BLK, (n + RB_BLK - 1) / RB_BLK, d);
+  } else {
+    tot = tprev[(bh * nb + sp / RB_BLK) * RB_HD + d] - rb_slice_sum(st, sp / RB_BLK, (s - sp) / RB_BLK, d);
+  }
+  tcur[(bh * nb + s / RB_BLK) * RB_HD + d] = tot;
+  cen[(bh * nb + s / RB_BLK) * RB_HD + d] = tot / (double)n;
+}
+
+// (t, row) pairs: the larger distance wins, the lower row on ties
+__device__ __forceinline__ bool rb_better(double t, int r, double bt, int br) {
+  return t > bt || (t == bt && r < br);
+}
+
+__device__ __forceinline__ double rb_wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// One workgroup of 4 wavefronts per (slice, batch x head): the squared
+// distance, in float64, of each row of the slice from the group's centroid
+// (FROM_PIVOT false) or from its first pivot's z row (FROM_PIVOT true), and
+// the farthest row of the slice (lowest row on ties).  Wavefront w takes
+// positions w + 4 i, lane l coordinates 2 l and 2 l + 1.
+template <bool FROM_PIVOT>
+__global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ zh, const int32_t* __restrict__ pin,
+                                                     const double* __restrict__ cen,
+                                                     const int32_t* __restrict__ piv,
+                                                     double* __restrict__ best_t, int32_t* __restrict__ best_r,
+                                                     int N, int nb, int level) {
+  __shared__ double wt[4];
+  __shared__ int wr[4];
+  const int c = blockIdx.x % nb;
+  const size_t bh = blockIdx.x / nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int s, n;
+  bool right;
+  rb_group_of(N, level, c * RB_BLK, s, n, right);
+  if (n <= RB_BLK) return;  // a leaf
+  const size_t g0 = bh * nb + s / RB_BLK;
+  const float* zb = zh + bh * (size_t)N * RB_HD;
+  double v0, v1;
+  if (FROM_PIVOT) {
+    const float2 pz = *(const float2*)(zb + (size_t)piv[2 * g0] * RB_HD + 2 * lane);
+    v0 = pz.x;
+    v1 = pz.y;
+  } else {
+    v0 = cen[g0 * RB_HD + 2 * lane];
+    v1 = cen[g0 * RB_HD + 2 * lane + 1];
+  }
+  const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
+  const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
+  double bt = -1.0;
+  int br = 0x7fffffff;
+#pragma unroll
+  for (int i0 = 0; i0 < 32; i0 += 8) {
+    float2 v[8];
+    int r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      r[u] = __builtin_amdgcn_readlane(myrow, i0 + u);
+      v[u] = *(const float2*)(zb + (size_t)r[u] * RB_HD + 2 * lane);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double dx = (double)v[u].x - v0, dy = (double)v[u].y - v1;
+      const double t = rb_wave_sum(dx * dx + dy * dy);
+      if (wave + 4 * (i0 + u) < cnt && rb_better(t, r[u], bt, br)) {
+        bt = t;
+        br = r[u];
+      }
+    }
+  }
+  if (lane == 0) {
+    wt[wave] = bt;
+    wr[wave] = br;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (rb_better(wt[w], wr[w], bt, br)) {
+        bt = wt[w];
+        br = wr[w];
+      }
+    best_t[bh * nb + c] = bt;
+    best_r[bh * nb + c] = br;
+  }
+}
+
+// One wavefront per group slot: the farthest row over the group's slices
+// (lowest row on ties), written as pivot WHICH (0: a, 1: b) of the group.
+template <int WHICH>
+__global__ __launch_bounds__(64) void rb_pivot_kernel(const double* __restrict__ best_t,
+                                                      const int32_t* __restrict__ best_r,
+                                                      int32_t* __restrict__ piv, int N, int nb, int level) {
+  const int ng = 1 << level;
+  const int gi = blockIdx.x % ng;
+  const size_t bh = blockIdx.x / ng;
+  const int lane = threadIdx.x;
+  int s, n, sp;
+  if (!rb_locate(N, level, gi, s, n, sp)) return;
+  if (n <= RB_BLK) return;
+  const int c0 = s / RB_BLK, m = (n + RB_BLK - 1) / RB_BLK;
+  double bt = -1.0;
+  int br = 0x7fffffff;
+  for (int j = lane; j < m; j += 64) {
+    const double t = best_t[bh * nb + c0 + j];
+    const int r = best_r[bh * nb + c0 + j];
+    if (rb_better(t, r, bt, br)) {
+      bt = t;
+      br = r;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const double ob = __shfl_xor(best, off, 64);
-    const int od = __shfl_xor(bd, off, 64);
-    if (ob > best || (ob == best && od < bd)) {
-      best = ob;
-      bd = od;
+    const double ot = __shfl_xor(bt, off, 64);
+    const int orr = __shfl_xor(br, off, 64);
+    if (rb_better(ot, orr, bt, br)) {
+      bt = ot;
+      br = orr;
     }
   }
-  return bd;
+  // a row of the head even if no distance compared as a number (non-finite
+  // inputs), so that later reads stay inside z
+  if (lane == 0) piv[2 * (bh * nb + c0) + WHICH] = min(max(br, 0), N - 1);
 }
 
-// sums of z_d and z_d^2 over the slices [c0, c0 + cnt) (cnt >= 1), added in
-// slice order with eight loads in flight
-__device__ __forceinline__ void rb_slice_sums(const double* stats_bh, int c0, int cnt, int d, double& a,
-                                              double& b) {
-  const double* sp = stats_bh + (size_t)c0 * 2 * RB_HD + d;
-  a = 0.0;
-  b = 0.0;
-  for (int base = 0; base < cnt; base += 8) {
-    double va[8], vb[8];
+// One workgroup of 4 wavefronts per (slice, batch x head): the split key of
+// each row of the slice, z_i . (z_b - z_a) in float64 rounded to float32,
+// as an order-preserving 32-bit key at the row's position.
+__global__ __launch_bounds__(256) void rb_keys_kernel(const float* __restrict__ zh, const int32_t* __restrict__ pin,
+                                                      const int32_t* __restrict__ piv, uint32_t* __restrict__ keys,
+                                                      int N, int nb, int level) {
+  const int c = blockIdx.x % nb;
+  const size_t bh = blockIdx.x / nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int s, n;
+  bool right;
+  rb_group_of(N, level, c * RB_BLK, s, n, right);
+  if (n <= RB_BLK) return;
+  const size_t g0 = bh * nb + s / RB_BLK;
+  const float* zb = zh + bh * (size_t)N * RB_HD;
+  const float2 za = *(const float2*)(zb + (size_t)piv[2 * g0] * RB_HD + 2 * lane);
+  const float2 zbb = *(const float2*)(zb + (size_t)piv[2 * g0 + 1] * RB_HD + 2 * lane);
+  const double w0 = (double)zbb.x - (double)za.x, w1 = (double)zbb.y - (double)za.y;
+  const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
+  const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      va[c] = sp[(size_t)min(base + c, cnt - 1) * 2 * RB_HD];
-      vb[c] = sp[(size_t)min(base + c, cnt - 1) * 2 * RB_HD + RB_HD];
+  for (int i0 = 0; i0 < 32; i0 += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = __builtin_amdgcn_readlane(myrow, i0 + u);
+      v[u] = *(const float2*)(zb + (size_t)r * RB_HD + 2 * lane);
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      a += base + c < cnt ? va[c] : 0.0;
-      b += base + c < cnt ? vb[c] : 0.0;
-    }
-  }
-}
-
-// variance of coordinate d over the group [s, s + n): its slices' sums, or
-// for a right child (sp < s) its parent's totals less its left sibling's
-// slices [sp, s); the group's totals go to tcur for its children
-__device__ __forceinline__ double rb_group_var(const double* stats_bh, const double* tprev_bh, double* tcur_bh,
-                                               int s, int n, int sp, int d) {
-  double a, b;
-  if (sp == s) {
-    rb_slice_sums(stats_bh, s / RB_BLK, (n + RB_BLK - 1) / RB_BLK, d, a, b);
-  } else {
-    double la, lb;
-    rb_slice_sums(stats_bh, sp / RB_BLK, (s - sp) / RB_BLK, d, la, lb);
-    a = tprev_bh[(size_t)(sp / RB_BLK) * 2 * RB_HD + d] - la;
-    b = tprev_bh[(size_t)(sp / RB_BLK) * 2 * RB_HD + RB_HD + d] - lb;
-  }
-  tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + d] = a;
-  tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + RB_HD + d] = b;
-  const double mu = a / n;
-  return b / n - mu * mu;
-}
-
-// Split coordinate of a group of any size, all 1024 threads of the
-// workgroup: thread t adds the slices c = t / 128 (mod 8) of coordinate
-// t mod 128 in slice order (a right child, sp < s: the slices of its left
-// sibling [sp, s), subtracted from the parent's totals), the eight partial
-// sums are added in order, the group's totals go to tcur, and wavefront 0
-// takes the largest variance (the lowest coordinate on ties).
-__device__ __forceinline__ int rb_split_coord_block(const double* stats_bh, const double* tprev_bh,
-                                                    double* tcur_bh, int s, int n, int sp_, double (*part)[2][RB_HD],
-                                                    int* sh_d, int tid) {
-  const int d = tid & (RB_HD - 1), p = tid >> 7;
-  const bool right = sp_ != s;
-  const int m = right ? (s - sp_) / RB_BLK : (n + RB_BLK - 1) / RB_BLK;
-  const double* sp = stats_bh + ((right ? sp_ : s) / RB_BLK) * 2 * RB_HD + d;
-  double a = 0.0, b = 0.0;
-  for (int c0 = p; c0 < m; c0 += 32) {
-    double va[4], vb[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = min(c0 + 8 * u, m - 1);
-      va[u] = sp[(size_t)c * 2 * RB_HD];
-      vb[u] = sp[(size_t)c * 2 * RB_HD + RB_HD];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a += c0 + 8 * u < m ? va[u] : 0.0;
-      b += c0 + 8 * u < m ? vb[u] : 0.0;
+    for (int u = 0; u < 8; ++u) {
+      const double key = rb_wave_sum((double)v[u].x * w0 + (double)v[u].y * w1);
+      const int pos = wave + 4 * (i0 + u);
+      if (lane == 0 && pos < cnt) keys[bh * N + p0 + pos] = rb_key((float)key);
     }
   }
-  part[p][0][d] = a;
-  part[p][1][d] = b;
-  __syncthreads();
-  if (tid < 64) {
-    double v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int dd = tid + 64 * h;
-      double sa = 0.0, sb = 0.0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        sa += part[q][0][dd];
-        sb += part[q][1][dd];
-      }
-      if (right) {
-        sa = tprev_bh[(size_t)(sp_ / RB_BLK) * 2 * RB_HD + dd] - sa;
-        sb = tprev_bh[(size_t)(sp_ / RB_BLK) * 2 * RB_HD + RB_HD + dd] - sb;
-      }
-      tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + dd] = sa;
-      tcur_bh[(size_t)(s / RB_BLK) * 2 * RB_HD + RB_HD + dd] = sb;
-      const double mu = sa / n;
-      v[h] = sb / n - mu * mu;
-    }
-    const int bd = rb_argmax_wave(v[0], v[1], tid);
-    if (tid == 0) *sh_d = bd;
-  }
-  __syncthreads();
-  return *sh_d;
 }
 
 // Groups of at most 1024 rows: one wavefront per group, four per workgroup,
@@ -579,12 +653,9 @@ __device__ __forceinline__ int rb_split_coord_block(const double* stats_bh, cons
 // (the smallest key with at least n_left keys at or below it).
 constexpr int WS_KPT = 16;
 
-__global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restrict__ zh,
-                                                            const double* __restrict__ stats,
-                                                            const double* __restrict__ tprev,
-                                                            double* __restrict__ tcur,
+__global__ __launch_bounds__(256) void rb_split_wave_kernel(const uint32_t* __restrict__ keys,
                                                             const int32_t* __restrict__ pin,
-                                                            int32_t* __restrict__ pout, int N, int nb, int level,
+                                                            int32_t* __restrict__ pout, int N, int level,
                                                             int total) {
   const int lane = threadIdx.x & 63;
   const int G = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -601,21 +672,15 @@ __global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restr
     return;
   }
   const int nl = RB_BLK * ((m + 1) / 2);
-  const size_t so = bh * nb * 2 * RB_HD;
-  const int dstar = rb_argmax_wave(rb_group_var(stats + so, tprev + so, tcur + so, s, n, sp, lane),
-                                   rb_group_var(stats + so, tprev + so, tcur + so, s, n, sp, lane + 64), lane);
-  const float* zb = zh + bh * (size_t)N * RB_HD;
+  const uint32_t* kb = keys + bh * N + s;
   const int C = (n + 63) / 64;
   const int j0 = lane * C;
   int32_t pr[WS_KPT];
   uint32_t kr[WS_KPT];
 #pragma unroll
   for (int u = 0; u < WS_KPT; ++u) pr[u] = pi[min(j0 + u, n - 1)];
-  float x[WS_KPT];
 #pragma unroll
-  for (int u = 0; u < WS_KPT; ++u) x[u] = zb[(size_t)pr[u] * RB_HD + dstar];
-#pragma unroll
-  for (int u = 0; u < WS_KPT; ++u) kr[u] = rb_key(x[u]);
+  for (int u = 0; u < WS_KPT; ++u) kr[u] = kb[min(j0 + u, n - 1)];
   auto valid = [&](int u) { return u < C && j0 + u < n; };
   // counts by ballot: no cross-lane data movement
   auto count_le = [&](uint32_t cand) {
@@ -662,17 +727,13 @@ __global__ __launch_bounds__(256) void rb_split_wave_kernel(const float* __restr
 // positions [t C, t C + C), C <= KPT, keys and rows in registers; the split
 // value by an MSB-first radix select, 8 bits a pass.
 template <int KPT>
-__global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restrict__ zh,
-                                                            const double* __restrict__ stats,
-                                                            const double* __restrict__ tprev,
-                                                            double* __restrict__ tcur,
+__global__ __launch_bounds__(1024) void rb_split_reg_kernel(const uint32_t* __restrict__ keys,
                                                             const int32_t* __restrict__ pin,
-                                                            int32_t* __restrict__ pout, int N, int nb, int level) {
+                                                            int32_t* __restrict__ pout, int N, int level) {
   constexpr int T = 1024, W = T / 64;
   __shared__ uint32_t hist[256];
   __shared__ int wt[W][2];
-  __shared__ double part[8][2][RB_HD];
-  __shared__ int sh_d, sh_digit, sh_want;
+  __shared__ int sh_digit, sh_want;
   const int ng = 1 << level;
   const int gi = blockIdx.x % ng;
   const size_t bh = blockIdx.x / ng;
@@ -687,19 +748,12 @@ __global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restr
     return;
   }
   const int nl = RB_BLK * ((m + 1) / 2);
-  const size_t so = bh * nb * 2 * RB_HD;
-  const int dstar = rb_split_coord_block(stats + so, tprev + so, tcur + so, s, n, sp, part, &sh_d, tid);
-  const float* zb = zh + bh * (size_t)N * RB_HD;
+  const uint32_t* kbg = keys + bh * N + s;
   const int C = (n + T - 1) / T;
   const int j0 = min(n, tid * C);
   uint32_t kr[KPT];
-  {
-    int32_t pr[KPT];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) pr[u] = pi[(uint32_t)min(j0 + u, n - 1)];
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) kr[u] = rb_key(zb[(uint32_t)(pr[u] * RB_HD + dstar)]);
-  }
+  for (int u = 0; u < KPT; ++u) kr[u] = kbg[(uint32_t)min(j0 + u, n - 1)];
   auto valid = [&](int u) { return u < C && j0 + u < n; };
 
   uint32_t prefix = 0u, pmask = 0u;
@@ -771,18 +825,13 @@ __global__ __launch_bounds__(1024) void rb_split_reg_kernel(const float* __restr
 // The largest groups (more than 20 rows per thread of 1024): one workgroup
 // per group, keys in the global key buffer (read from L2 in every pass, eight
 // loads in flight), the split value by an MSB-first radix select.
-__global__ __launch_bounds__(1024) void rb_split_big_kernel(const float* __restrict__ zh,
-                                                            const double* __restrict__ stats,
-                                                            const double* __restrict__ tprev,
-                                                            double* __restrict__ tcur,
+__global__ __launch_bounds__(1024) void rb_split_big_kernel(const uint32_t* __restrict__ keys,
                                                             const int32_t* __restrict__ pin,
-                                                            int32_t* __restrict__ pout,
-                                                            uint32_t* __restrict__ keys, int N, int nb, int level) {
+                                                            int32_t* __restrict__ pout, int N, int level) {
   constexpr int T = 1024, W = T / 64, U = 8;
   __shared__ uint32_t hist[256];
   __shared__ int wt[W][2];
-  __shared__ double part[8][2][RB_HD];
-  __shared__ int sh_d, sh_digit, sh_want;
+  __shared__ int sh_digit, sh_want;
   const int ng = 1 << level;
   const int gi = blockIdx.x % ng;
   const size_t bh = blockIdx.x / ng;
@@ -797,25 +846,7 @@ __global__ __launch_bounds__(1024) void rb_split_big_kernel(const float* __restr
     return;
   }
   const int nl = RB_BLK * ((m + 1) / 2);
-  const size_t so = bh * nb * 2 * RB_HD;
-  const int dstar = rb_split_coord_block(stats + so, tprev + so, tcur + so, s, n, sp, part, &sh_d, tid);
-  const float* zb = zh + bh * (size_t)N * RB_HD;
-  uint32_t* kb = keys + bh * N + s;
-
-  // keys of the split coordinate, in group order; positions past the end
-  // read the last row and store nothing
-  for (int j0 = tid; j0 < n; j0 += U * T) {
-    int r[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) r[u] = pi[(uint32_t)min(j0 + u * T, n - 1)];
-    float x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = zb[(uint32_t)(r[u] * RB_HD + dstar)];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (j0 + u * T < n) kb[j0 + u * T] = rb_key(x[u]);
-  }
-  __syncthreads();
+  const uint32_t* kb = keys + bh * N + s;
 
   uint32_t prefix = 0u, pmask = 0u;
   int want = nl - 1;
@@ -944,7 +975,7 @@ struct RbGeom {
 };
 
 struct RbLayout {
-  size_t part, msum, ltw, zh, keys, perm, stats, tot, total;
+  size_t part, msum, ltw, zh, keys, perm, stats, tot, cen, best_t, best_r, piv, total;
 };
 
 size_t rb_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -988,10 +1019,18 @@ RbLayout rb_layout(const RbGeom& g) {
   off = rb_align(off + (size_t)g.BH * g.N * sizeof(uint32_t));
   w.perm = off;
   off = rb_align(off + (size_t)g.BH * g.N * sizeof(int32_t));
-  w.stats = off;
-  off = rb_align(off + (size_t)g.BH * g.nb * 2 * RB_HD * sizeof(double));
+  w.stats = off;  // slice sums of z
+  off = rb_align(off + (size_t)g.BH * g.nb * RB_HD * sizeof(double));
   w.tot = off;  // group totals, two levels (by level parity)
-  off = rb_align(off + 2 * (size_t)g.BH * g.nb * 2 * RB_HD * sizeof(double));
+  off = rb_align(off + 2 * (size_t)g.BH * g.nb * RB_HD * sizeof(double));
+  w.cen = off;  // group centroids
+  off = rb_align(off + (size_t)g.BH * g.nb * RB_HD * sizeof(double));
+  w.best_t = off;  // each slice's farthest row: distance and row
+  off = rb_align(off + (size_t)g.BH * g.nb * sizeof(double));
+  w.best_r = off;
+  off = rb_align(off + (size_t)g.BH * g.nb * sizeof(int32_t));
+  w.piv = off;  // each group's two pivot rows
+  off = rb_align(off + (size_t)g.BH * g.nb * 2 * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -1045,33 +1084,46 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
   double* stats = (double*)(ws + w.stats);
   // level l writes its groups' totals to tot[l % 2] and reads its parents'
   // from tot[(l + 1) % 2]
-  double* tot[2] = {(double*)(ws + w.tot), (double*)(ws + w.tot) + (size_t)g.BH * g.nb * 2 * RB_HD};
+  double* tot[2] = {(double*)(ws + w.tot), (double*)(ws + w.tot) + (size_t)g.BH * g.nb * RB_HD};
+  double* cen = (double*)(ws + w.cen);
+  double* best_t = (double*)(ws + w.best_t);
+  int32_t* best_r = (int32_t*)(ws + w.best_r);
+  int32_t* piv = (int32_t*)(ws + w.piv);
   const int nb = (int)g.nb;
+  const dim3 slices((unsigned)(g.BH * nb));
   for (int l = 0; l < g.levels; ++l) {
-    hipLaunchKernelGGL(rb_stats_kernel, dim3((unsigned)(g.BH * nb)), dim3(256), 0, s, (const float*)zh,
-                       (const int32_t*)buf[l & 1], stats, N, nb, l);
+    const int32_t* pin = buf[l & 1];
+    int32_t* pout = buf[(l + 1) & 1];
+    const dim3 groups((unsigned)(g.BH << l));
+    hipLaunchKernelGGL(rb_stats_kernel, slices, dim3(256), 0, s, (const float*)zh, pin, stats, N, nb, l);
+    hipLaunchKernelGGL(rb_center_kernel, groups, dim3(RB_HD), 0, s, (const double*)stats,
+                       (const double*)tot[(l + 1) & 1], tot[l & 1], cen, N, nb, l);
+    hipLaunchKernelGGL(rb_far_kernel<false>, slices, dim3(256), 0, s, (const float*)zh, pin, (const double*)cen,
+                       (const int32_t*)piv, best_t, best_r, N, nb, l);
+    hipLaunchKernelGGL(rb_pivot_kernel<0>, groups, dim3(64), 0, s, (const double*)best_t, (const int32_t*)best_r,
+                       piv, N, nb, l);
+    hipLaunchKernelGGL(rb_far_kernel<true>, slices, dim3(256), 0, s, (const float*)zh, pin, (const double*)cen,
+                       (const int32_t*)piv, best_t, best_r, N, nb, l);
+    hipLaunchKernelGGL(rb_pivot_kernel<1>, groups, dim3(64), 0, s, (const double*)best_t, (const int32_t*)best_r,
+                       piv, N, nb, l);
+    hipLaunchKernelGGL(rb_keys_kernel, slices, dim3(256), 0, s, (const float*)zh, pin, (const int32_t*)piv, keys, N,
+                       nb, l);
     // largest group at this level: 128 ceil(nb / 2^l) rows
     const int64_t largest = (int64_t)RB_BLK * ((g.nb + (int64_t(1) << l) - 1) >> l);
     const int64_t per = (largest + 1023) / 1024;  // rows per thread of a 1024-thread workgroup
-    const dim3 grid((unsigned)(g.BH << l));
-    const float* zc = zh;
-    const double* sc = stats;
-    const double* tp = tot[(l + 1) & 1];
-    double* tc = tot[l & 1];
-    const int32_t* pin = buf[l & 1];
-    int32_t* pout = buf[(l + 1) & 1];
+    const uint32_t* kc = keys;
     if (largest <= 64 * WS_KPT) {
       const int total = (int)(g.BH << l);
-      hipLaunchKernelGGL(rb_split_wave_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, zc, sc, tp, tc,
-                         pin, pout, N, nb, l, total);
+      hipLaunchKernelGGL(rb_split_wave_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, kc, pin, pout, N,
+                         l, total);
     } else if (per <= 4) {
-      hipLaunchKernelGGL((rb_split_reg_kernel<4>), grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, N, nb, l);
+      hipLaunchKernelGGL((rb_split_reg_kernel<4>), groups, dim3(1024), 0, s, kc, pin, pout, N, l);
     } else if (per <= 12) {
-      hipLaunchKernelGGL((rb_split_reg_kernel<12>), grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, N, nb, l);
+      hipLaunchKernelGGL((rb_split_reg_kernel<12>), groups, dim3(1024), 0, s, kc, pin, pout, N, l);
     } else if (per <= 20) {
-      hipLaunchKernelGGL((rb_split_reg_kernel<20>), grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, N, nb, l);
+      hipLaunchKernelGGL((rb_split_reg_kernel<20>), groups, dim3(1024), 0, s, kc, pin, pout, N, l);
     } else {
-      hipLaunchKernelGGL(rb_split_big_kernel, grid, dim3(1024), 0, s, zc, sc, tp, tc, pin, pout, keys, N, nb, l);
+      hipLaunchKernelGGL(rb_split_big_kernel, groups, dim3(1024), 0, s, kc, pin, pout, N, l);
     }
   }
   return rb_status();

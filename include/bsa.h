@@ -302,22 +302,25 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
  * What bsa_reblock computes, per (b, h):
  *   M = (1/N) sum_j k_j k_j^T;  L L^T = M + (1e-6 trace(M) / 128 + 1e-30) I;
  *   z_i = L^T q_i / |L^T q_i| (zero rows stay zero).
- *   A group of n rows, m = ceil(n / 128) >= 2 blocks, splits on the
- *   coordinate c of z with the largest variance over the group (the lowest c
- *   on ties): its 128 ceil(m / 2) rows with the smallest z_i[c] (ties to the
- *   lower row) form the left group, the others the right group, both in
- *   ascending row order; groups of one block are leaves.  perm lists the
- *   leaves left to right, so every 128-row block of the new order but the
- *   last is full, and its rows ascend.
+ *   A group of n rows, m = ceil(n / 128) >= 2 blocks, splits by two pivot
+ *   rows: a, the row farthest from the centroid of the group's z rows, and
+ *   b, the row farthest from a (squared Euclidean distances; the lowest row
+ *   on ties).  Its 128 ceil(m / 2) rows with the smallest z_i . (z_b - z_a)
+ *   (ties to the lower row) form the left group, the others the right group,
+ *   both in ascending row order; groups of one block are leaves.  perm lists
+ *   the leaves left to right, so every 128-row block of the new order but
+ *   the last is full, and its rows ascend.  Only distances between z rows
+ *   enter, so the order is a function of the metric cosines z_i . z_j alone.
  * Precision: M as float32 sums of exact products over 2048-row chunks, the
- * chunks and the factorisation in float64, z in float32.  Where two split
- * values (or two coordinate variances) are within float32 rounding of each
- * other, the order may differ from an exact evaluation's.
+ * chunks and the factorisation in float64, z in float32, distances and keys
+ * in float64 from that z (keys then rounded to float32).  Where two
+ * distances or two keys are within that rounding of each other, the order
+ * may differ from an exact evaluation's.
  *
  *   q, k       in   bf16 [B, H, N, 128]
  *   perm       out  int32 [B, H, N]: perm[p] = the row placed at position p
  *   workspace  in/out  bsa_reblock_workspace_bytes() bytes, 256-byte aligned
- *                   (about N * 568 bytes per (b, h)); its contents are
+ *                   (about N * 552 bytes per (b, h)); its contents are
  *                   scratch and need no initialisation
  */
 int bsa_reblock_workspace_bytes(const bsa_problem* p, size_t* bytes);

@@ -88,17 +88,23 @@ Readings taken where the pages are silent (each is exercised by a test):
      eps = 1e-6 (the small ridge keeps L defined for rank-deficient keys);
      each query row becomes the unit vector z_i = L^T q_i / |L^T q_i| (zero
      stays zero), so z_i . z_j is the cosine of q_i and q_j in the metric M.
-     A group of n rows (m = ceil(n / 128) blocks, m >= 2) splits on the
-     coordinate of z with the largest population variance over the group
-     (the lowest coordinate on ties): the 128 * ceil(m / 2) rows with the
-     smallest value of that coordinate (ties to the lower row index) form the
-     left group, the rest the right one, each in ascending row order.  The
-     leaves, left to right, give the permutation; Q, K and V are all permuted
-     by it, the block-sparse path runs on the permuted rows, and the output
-     rows are put back in their original places.  The pages name neither the
-     split rule nor its direction: a split on one coordinate of the whitened
-     unit vectors is the simplest hierarchical partitioner of that metric that
-     runs in O(N log N) with no iteration.
+     A group of n rows (m = ceil(n / 128) blocks, m >= 2) splits by two
+     pivot rows: a, the row farthest from the group's centroid (mean of its
+     z rows), and b, the row farthest from a (Euclidean distances between
+     the z rows, i.e. the chordal form of the metric cosine distance; the
+     lowest row index on ties); the 128 * ceil(m / 2) rows with the smallest
+     z_i . (z_b - z_a), i.e. nearest to a relative to b (ties to the lower
+     row index), form the left group, the rest the right one, each in
+     ascending row order.  The leaves, left to right, give the permutation;
+     Q, K and V are all permuted by it, the block-sparse path runs on the
+     permuted rows, and the output rows are put back in their original
+     places.  The pages name neither the split rule nor its direction; this
+     two-pivot (farthest-point) bisection uses nothing but the distances
+     between the whitened rows, so the partition is a function of the metric
+     cosines alone (any orthogonal map of the head features applied to Q and
+     K leaves it unchanged, and so does any map q -> A q, k -> A^-T k that
+     keeps every score, up to the small ridge), and each level costs O(n d),
+     O(N d log N) in all.
 
 Precision: pooled vectors are summed in float64 and stored as float32 (the
 precision in which a block ranking is decided); block scores are float64 dot
@@ -432,11 +438,23 @@ def reblock_left_rows(n: int, block: int = BLOCK) -> int:
     return block * (-(-m // 2))
 
 
-def split_coordinate(zg: np.ndarray) -> int:
-    """The coordinate with the largest population variance over the group's
-    rows, the lowest one on ties (R17)."""
-    var = zg.var(axis=0)
-    return int(np.argmax(var))
+def split_pivots(zg: np.ndarray):
+    """The two pivots of a group (R17), as positions among its rows (which
+    are in ascending row order): a = the row farthest from the centroid of
+    the group's z rows, b = the row farthest from a; squared Euclidean
+    distances, the first (lowest) row on ties."""
+    zg = np.asarray(zg, dtype=np.float64)
+    c = zg.sum(axis=0) / zg.shape[0]
+    a = int(np.argmax(((zg - c) ** 2).sum(axis=1)))
+    b = int(np.argmax(((zg - zg[a]) ** 2).sum(axis=1)))
+    return a, b
+
+
+def split_keys(zg: np.ndarray, a: int, b: int) -> np.ndarray:
+    """Split key of every row of a group: z_i . (z_b - z_a), which orders the
+    rows as |z_i - z_a|^2 - |z_i - z_b|^2 does (smallest: nearest to a)."""
+    zg = np.asarray(zg, dtype=np.float64)
+    return zg @ (zg[b] - zg[a])
 
 
 def reblock_permutation(q: np.ndarray, k: np.ndarray, block: int = BLOCK) -> np.ndarray:
@@ -451,9 +469,10 @@ def reblock_permutation(q: np.ndarray, k: np.ndarray, block: int = BLOCK) -> np.
         if n_blocks(n, block) <= 1:
             leaves.append(rows)
             return
-        c = split_coordinate(z[rows])
-        # rows ordered by that coordinate, ties to the lower row index
-        order = rows[np.lexsort((rows, z[rows, c]))]
+        a, b = split_pivots(z[rows])
+        key = split_keys(z[rows], a, b)
+        # rows ordered by their key, ties to the lower row index
+        order = rows[np.lexsort((rows, key))]
         nl = reblock_left_rows(n, block)
         split(np.sort(order[:nl]))
         split(np.sort(order[nl:]))

@@ -156,14 +156,17 @@ def check_output(gpu_out, ref_out):
     return float(d.max()), float(d.mean())
 
 
-# Reblock rule: a GPU split is accepted when some coordinate whose variance is
-# within REBLOCK_VAR_REL (relative) of the group's largest separates the left
-# rows from the right ones up to REBLOCK_KEY_ABS.  z has unit rows; the GPU's
-# z differs from the float64 one by the float32 rounding of M, L and z,
-# measured at most 2.1e-7 (768p 5s and 4,173-row heads), a tenth of the key
-# tolerance
-REBLOCK_KEY_ABS = 2e-6
-REBLOCK_VAR_REL = 1e-4
+# Reblock rule: a GPU split is accepted when some pair of pivots (a, b), each
+# within REBLOCK_DIST_ABS of the largest squared distance behind it (from the
+# group's centroid, then from a), orders every left row's key
+# z_i . (z_b - z_a) at or below every right row's, up to REBLOCK_KEY_ABS.  z
+# has unit rows; the GPU's z differs from the float64 one by the float32
+# rounding of M, L and z, measured at most 2.1e-7 per coordinate, so a
+# distance moves by at most about 2 |z_i - c| |dz| <= 2e-5 and a key by about
+# 1e-5 (the GPU forms both in float64 from its float32 z, the key then
+# rounded to float32)
+REBLOCK_KEY_ABS = 2e-5
+REBLOCK_DIST_ABS = 2e-5
 
 
 def reblock_splits(N, left_rows, block=128):
@@ -180,10 +183,23 @@ def reblock_splits(N, left_rows, block=128):
     return out
 
 
+def _pivot_candidates(zg, max_each=8):
+    """Pivot pairs (a, b) within REBLOCK_DIST_ABS of the farthest, as positions
+    in zg (its rows ascending), the lowest first."""
+    c = zg.sum(axis=0) / zg.shape[0]
+    t = ((zg - c) ** 2).sum(axis=1)
+    pairs = []
+    for a in np.nonzero(t >= t.max() - REBLOCK_DIST_ABS)[0][:max_each]:
+        d = ((zg - zg[a]) ** 2).sum(axis=1)
+        for b in np.nonzero(d >= d.max() - REBLOCK_DIST_ABS)[0][:max_each]:
+            pairs.append((int(a), int(b)))
+    return pairs
+
+
 def check_partition(z, perm, left_rows, block=128):
     """Validate a GPU permutation against the float64 embedding z of the same
     head: a permutation; every 128-row block ascending; every split separated
-    on a coordinate of (near-)largest variance.  Returns (ok, message)."""
+    by the keys of an admissible pivot pair.  Returns (ok, message)."""
     N = z.shape[0]
     perm = np.asarray(perm, dtype=np.int64)
     if perm.shape != (N,) or not np.array_equal(np.sort(perm), np.arange(N)):
@@ -192,24 +208,38 @@ def check_partition(z, perm, left_rows, block=128):
         if np.any(np.diff(perm[b0:b0 + block]) <= 0):
             return False, "block at %d not ascending" % b0
     for s, n, nl in reblock_splits(N, left_rows, block):
-        rows, left, right = perm[s:s + n], perm[s:s + nl], perm[s + nl:s + n]
-        var = z[rows].var(axis=0)
-        cands = np.nonzero(var >= var.max() * (1 - REBLOCK_VAR_REL))[0]
-        if not any(z[left, c].max() <= z[right, c].min() + REBLOCK_KEY_ABS for c in cands):
-            return False, "split at %d (n %d) not separated on %s" % (s, n, list(cands))
+        rows = np.sort(perm[s:s + n])
+        zg = z[rows]
+        pos = np.searchsorted(rows, perm[s:s + n])
+        lp, rp = pos[:nl], pos[nl:]
+        ok = False
+        for a, b in _pivot_candidates(zg):
+            key = zg @ (zg[b] - zg[a])
+            if key[lp].max() <= key[rp].min() + REBLOCK_KEY_ABS:
+                ok = True
+                break
+        if not ok:
+            return False, "split at %d (n %d) not separated by any admissible pivot pair" % (s, n)
     return True, ""
 
 
 def reblock_margins(z, perm, left_rows, block=128):
-    """Smallest margins of the oracle's own splits: the relative gap between
-    the largest and second-largest coordinate variance, and the gap between
-    the left group's largest and the right group's smallest split value."""
-    vgap, kgap = np.inf, np.inf
+    """Smallest margins of the oracle's own splits: the gap between the
+    largest and second-largest squared distance behind either pivot, and the
+    gap between the left group's largest and the right group's smallest key."""
+    dgap, kgap = np.inf, np.inf
     for s, n, nl in reblock_splits(z.shape[0], left_rows, block):
-        rows, left, right = perm[s:s + n], perm[s:s + nl], perm[s + nl:s + n]
-        var = z[rows].var(axis=0)
-        order = np.argsort(-var, kind="stable")
-        c = order[0]
-        vgap = min(vgap, (var[c] - var[order[1]]) / var[c] if var[c] > 0 else 0.0)
-        kgap = min(kgap, z[right, c].min() - z[left, c].max())
-    return vgap, kgap
+        rows = np.sort(perm[s:s + n])
+        zg = z[rows]
+        c = zg.sum(axis=0) / n
+        t = ((zg - c) ** 2).sum(axis=1)
+        a = int(np.argmax(t))
+        d = ((zg - zg[a]) ** 2).sum(axis=1)
+        b = int(np.argmax(d))
+        for x in (t, d):
+            top = np.sort(x)[-2:]
+            dgap = min(dgap, top[1] - top[0])
+        key = zg @ (zg[b] - zg[a])
+        pos = np.searchsorted(rows, perm[s:s + n])
+        kgap = min(kgap, key[pos[nl:]].min() - key[pos[:nl]].max())
+    return dgap, kgap

@@ -214,12 +214,13 @@ def test_reblock_entry_points_validate():
     big = 1 << 40
     p = bsa.make_problem(1, 2, 4096, top_k=8)
     # workspace: float32 chunk moments, M (float64), the three terms of L,
-    # z (float32), keys, an order buffer, float64 slice sums and float64
-    # group totals of two levels
+    # z (float32), keys, an order buffer, float64 slice sums, float64 group
+    # totals of two levels and group centroids, each slice's farthest row
+    # (distance, row) and each group's two pivots
     n = bsa.bsa_reblock_workspace_bytes(p)
     expect = (2 * 2 * 128 * 128 * 4 + 2 * 128 * 128 * 8 + 2 * 3 * 128 * 128 * 2 + 2 * 4096 * 128 * 4
-              + 2 * 2 * 4096 * 4 + 3 * 2 * 32 * 2 * 128 * 8)
-    assert expect <= n <= expect + 8 * 256
+              + 2 * 2 * 4096 * 4 + 4 * 2 * 32 * 128 * 8 + 2 * 32 * (8 + 4 + 2 * 4))
+    assert expect <= n <= expect + 12 * 256
     assert L.bsa_reblock(ctypes.byref(p), None, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_reblock(ctypes.byref(p), fake, fake, None, fake, big, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_reblock(ctypes.byref(p), odd, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID

@@ -893,25 +893,34 @@ def _iso_keys(N, scales=None, d=D):
     return k
 
 
-_CENTERS = {0: (1.0, 0.5), 1: (1.0, -0.5), 2: (-1.0, 0.5), 3: (-1.0, -0.5)}
+# cluster c: unit vector at angle _ANGLES[c] in coordinates 0, 1, noise of
+# scale _NOISE[c] in every coordinate
+_ANGLES = {0: 0.0, 1: 30.0, 2: 80.0, 3: 120.0}
+_NOISE = {0: 1e-4, 1: 1e-2, 2: 1e-4, 3: 1e-2}
 
 
 def _cluster_rows(N, seed, d=D):
-    """Row i lies near the unit vector of _CENTERS[i % 4] in coordinates 0, 1,
-    with a positive row scale and 1e-3 noise elsewhere."""
+    """Row i lies near the unit vector of cluster i % 4 (_ANGLES, _NOISE),
+    with a positive row scale."""
     rng = np.random.default_rng(seed)
     c = np.zeros((N, d))
     for i in range(N):
-        a, b = _CENTERS[i % 4]
-        c[i, 0], c[i, 1] = a / math.hypot(a, b), b / math.hypot(a, b)
-    c += 1e-3 * rng.standard_normal((N, d))
+        t = math.radians(_ANGLES[i % 4])
+        c[i, 0], c[i, 1] = math.cos(t), math.sin(t)
+        c[i] += _NOISE[i % 4] * rng.standard_normal(d)
     return c * rng.uniform(0.5, 2.0, size=(N, 1))
 
 
 def _cluster_expected(N):
-    """Hand-derived partition of _cluster_rows: the first split is on
-    coordinate 0 (variance 0.8 against 0.2), negative values left; each half
-    then splits on coordinate 1, negative values left."""
+    """Hand-derived partition of _cluster_rows (A, B, C, D = clusters 0..3 at
+    0, 30, 80, 120 degrees; with isotropic keys z is the normalised row).
+    Root: the centroid is (0.385, 0.588); D is farthest from it (|u - c|^2 =
+    0.86 against 0.72 for A, 0.24 and 0.20 for B and C), so a is in D; A is
+    farthest from D (|A - D|^2 = 3, B 2, C 0.47), so b is in A; the keys
+    z . (A - D) are -1.5 (D), -0.59 (C), 0.87 (B), 1.5 (A): D and C go left.
+    {D, C}: both at 0.117 from their centroid, D's noise puts its rows
+    farther, so a in D, b in C, keys z . (C - D) put D left.  {B, A} likewise:
+    a in the noisier B, B left.  Order: D, C, B, A."""
     return np.concatenate([np.arange(N)[np.arange(N) % 4 == c] for c in (3, 2, 1, 0)])
 
 
@@ -956,7 +965,8 @@ def test_reblock_clusters_hand_partition(N):
 
 def test_reblock_whitening_by_key_moment():
     # M = diag(s): queries c / sqrt(s) embed to the cluster vectors c, so the
-    # hand partition holds; the unwhitened queries would split on coordinate 1
+    # hand partition holds; unwhitened, B, C and D all lie near coordinate 1
+    # and the root split no longer separates {D, C} from {B, A}
     N = 512
     s = np.ones(D)
     s[0], s[1] = 100.0, 0.01
@@ -967,20 +977,40 @@ def test_reblock_whitening_by_key_moment():
 
 
 def test_reblock_exact_ties_go_left_in_row_order():
-    # identical rows: every coordinate has zero variance and every value ties,
-    # so each split keeps the lower rows on the left: the identity
+    # identical rows: every distance is zero, both pivots are the group's
+    # first row and every key ties, so each split keeps the lower rows on the
+    # left: the identity
     N = 700
     q = np.tile(np.random.default_rng(44).standard_normal(D), (N, 1))
     k = np.random.default_rng(45).standard_normal((N, D))
     assert np.array_equal(O.reblock_permutation(q, k), np.arange(N))
 
 
-def test_split_coordinate_rule():
-    zg = np.random.default_rng(46).standard_normal((50, 6)) * 0.1
-    zg[:, 4] = np.linspace(-1, 1, 50)
-    assert O.split_coordinate(zg) == 4
-    zg[:, 2] = zg[:, 4]                # the same variance: the lower coordinate
-    assert O.split_coordinate(zg) == 2
+def _unit(deg, d=6):
+    v = np.zeros(d)
+    v[0], v[1] = math.cos(math.radians(deg)), math.sin(math.radians(deg))
+    return v
+
+
+def test_split_pivot_rule():
+    # rows at 0, 10, 20 and 170 degrees: centroid (0.485, 0.173); squared
+    # distances to it 0.295, 0.250, 0.236, 2.161, so a = 3; from row 3 they
+    # are 3.970, 3.879, 3.702, so b = 0
+    zg = np.array([_unit(0), _unit(10), _unit(20), _unit(170)])
+    assert O.split_pivots(zg) == (3, 0)
+    key = O.split_keys(zg, 3, 0)
+    assert np.abs(key - zg @ (zg[0] - zg[3])).max() == 0.0
+    assert list(np.argsort(key)) == [3, 2, 1, 0]
+    # (1, 0), (-1, 0), (0, 1): rows 0 and 1 tie for the farthest from the
+    # centroid (0, 1/3): a = 0, the lower; then b = 1 (distance 2 > sqrt 2)
+    zg = np.array([_unit(0), _unit(180), _unit(90)])
+    assert O.split_pivots(zg) == (0, 1)
+    # a duplicate of the farthest row: the lower copy is b
+    zg = np.array([_unit(0), _unit(180), _unit(10), _unit(180)])
+    assert O.split_pivots(zg)[1] == 1
+    # a zero row (a zero query) is at distance |c| from the centroid
+    zg = np.array([_unit(0), _unit(5), np.zeros(6), _unit(10)])
+    assert O.split_pivots(zg)[0] == 2
 
 
 @pytest.mark.parametrize("N", [1, 100, 128, 129, 300, 1000, 4097])
@@ -1005,30 +1035,79 @@ def test_reblock_left_rows_closed_form():
 
 
 def test_reblock_root_split_brute_force():
-    # the first split recomputed with plain loops: variances of every
-    # coordinate, then the 256 smallest values, ties to the lower row
+    # the first split recomputed with plain loops: the centroid, the row
+    # farthest from it, the row farthest from that one (first on ties), then
+    # the 256 rows nearest the first pivot relative to the second, by
+    # |z - z_a|^2 - |z - z_b|^2, ties to the lower row
     N = 434
     q, k, _ = _rand_head(N, seed=48)
     z = O.mahalanobis_embedding(q, k)
-    best, bc = -1.0, -1
-    for c in range(D):
-        col = [float(z[i, c]) for i in range(N)]
-        mu = sum(col) / N
-        var = sum((x - mu) ** 2 for x in col) / N
-        if var > best:
-            best, bc = var, c
-    left = sorted(sorted(range(N), key=lambda i: (z[i, bc], i))[:256])
+    rows = [[float(x) for x in z[i]] for i in range(N)]
+    cen = [sum(r[c] for r in rows) / N for c in range(D)]
+
+    def dist2(u, w):
+        return sum((u[c] - w[c]) ** 2 for c in range(D))
+    a = max(range(N), key=lambda i: (dist2(rows[i], cen), -i))
+    b = max(range(N), key=lambda i: (dist2(rows[i], rows[a]), -i))
+    rel = [dist2(rows[i], rows[a]) - dist2(rows[i], rows[b]) for i in range(N)]
+    left = sorted(sorted(range(N), key=lambda i: (rel[i], i))[:256])
     perm = O.reblock_permutation(q, k)
     assert sorted(perm[:256].tolist()) == left
+
+
+def _reblock_pivot_margins(q, k, block=128):
+    """Smallest margins of the oracle's own tree: the relative gap between
+    the largest and second-largest distance behind each pivot, and the gap
+    between the left group's largest and the right group's smallest key."""
+    z = O.mahalanobis_embedding(q, k)
+    perm = O.reblock_permutation(q, k)
+    dgap, kgap = np.inf, np.inf
+    stack = [(0, len(perm))]
+    while stack:
+        s0, n = stack.pop()
+        if O.n_blocks(n, block) <= 1:
+            continue
+        nl = O.reblock_left_rows(n, block)
+        rows = np.sort(perm[s0:s0 + n])
+        zg = z[rows]
+        a, b = O.split_pivots(zg)
+        for dd in (((zg - zg.mean(0)) ** 2).sum(1), ((zg - zg[a]) ** 2).sum(1)):
+            top = np.sort(dd)[-2:]
+            dgap = min(dgap, (top[1] - top[0]) / max(top[1], 1e-300))
+        key = O.split_keys(zg, a, b)
+        pos = {r: i for i, r in enumerate(rows)}
+        kl = key[[pos[r] for r in perm[s0:s0 + nl]]]
+        kr = key[[pos[r] for r in perm[s0 + nl:s0 + n]]]
+        kgap = min(kgap, kr.min() - kl.max())
+        stack += [(s0, nl), (s0 + nl, n - nl)]
+    return dgap, kgap
 
 
 def test_reblock_invariances():
     q, k, _ = _rand_head(700, seed=49)
     perm = O.reblock_permutation(q, k)
+    dgap, kgap = _reblock_pivot_margins(q, k)
+    assert dgap > 1e-9 and kgap > 1e-9      # every decision clear of rounding
     rng = np.random.default_rng(50)
     assert np.array_equal(O.reblock_permutation(q, 3.0 * k), perm)
     assert np.array_equal(O.reblock_permutation(q, k[rng.permutation(700)]), perm)
     assert np.array_equal(O.reblock_permutation(q * rng.uniform(0.1, 5, (700, 1)), k), perm)
+    # the head features permuted and sign-flipped, or rotated, in Q and K
+    # together: every metric cosine is the same, so is the partition
+    P = np.eye(D)[rng.permutation(D)] * rng.choice([-1.0, 1.0], size=D)
+    assert np.array_equal(O.reblock_permutation(q @ P, k @ P), perm)
+    R, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    assert np.array_equal(O.reblock_permutation(q @ R, k @ R), perm)
+
+
+def test_reblock_invariant_under_score_preserving_maps():
+    # q -> A q, k -> A^-T k keeps every score q . k, hence every metric
+    # cosine (up to the ridge, 1e-6 of the mean eigenvalue): the clusters'
+    # partition, whose margins are wide, is unchanged for a random A
+    N = 512
+    q, k = _cluster_rows(N, seed=42), _iso_keys(N)
+    A = np.random.default_rng(53).standard_normal((D, D)) + 4.0 * np.eye(D)
+    assert np.array_equal(O.reblock_permutation(q @ A.T, k @ np.linalg.inv(A)), _cluster_expected(N))
 
 
 @pytest.mark.parametrize("N", [300, 1000])
@@ -1075,7 +1154,7 @@ def _reblock_pins_pass():
         test_reblock_clusters_hand_partition(512)
         test_reblock_whitening_by_key_moment()
         test_reblock_exact_ties_go_left_in_row_order()
-        test_split_coordinate_rule()
+        test_split_pivot_rule()
         test_reblock_structure(1000)
         test_reblock_left_rows_closed_form()
         test_reblock_root_split_brute_force()
@@ -1121,13 +1200,32 @@ def _moment_uncentred_sum(k):
     return k.T @ k          # mistake: no 1/N (the ridge then differs in scale only)
 
 
-def _split_lowest_variance(zg):
-    return int(np.argmin(zg.var(axis=0)))
+def _pivot_nearest_centroid(zg):
+    # mistake: a is the row nearest the centroid
+    c = zg.mean(axis=0)
+    a = int(np.argmin(((zg - c) ** 2).sum(axis=1)))
+    return a, int(np.argmax(((zg - zg[a]) ** 2).sum(axis=1)))
 
 
-def _split_high_index_ties(zg):
-    var = zg.var(axis=0)
-    return int(len(var) - 1 - np.argmax(var[::-1]))
+def _pivot_b_from_centroid(zg):
+    # mistake: b is the second-farthest row from the centroid, not the
+    # farthest from a
+    d = ((zg - zg.mean(axis=0)) ** 2).sum(axis=1)
+    order = np.argsort(-d, kind="stable")
+    return int(order[0]), int(order[1])
+
+
+def _pivot_high_index_ties(zg):
+    c = zg.sum(axis=0) / zg.shape[0]
+    t = ((zg - c) ** 2).sum(axis=1)
+    a = int(len(t) - 1 - np.argmax(t[::-1]))
+    d = ((zg - zg[a]) ** 2).sum(axis=1)
+    return a, int(len(d) - 1 - np.argmax(d[::-1]))
+
+
+def _keys_toward_b(zg, a, b):
+    # mistake: the rows nearest b go left
+    return zg @ (zg[a] - zg[b])
 
 
 def _left_rows_floor(n, block=128):
@@ -1154,8 +1252,10 @@ def _run_reblocked_queries_only(q, k, v, perm, **kw):
     ("mahalanobis_embedding", _embed_untransposed),
     ("mahalanobis_embedding", _embed_unnormalised),
     ("mahalanobis_embedding", _embed_unwhitened),
-    ("split_coordinate", _split_lowest_variance),
-    ("split_coordinate", _split_high_index_ties),
+    ("split_pivots", _pivot_nearest_centroid),
+    ("split_pivots", _pivot_b_from_centroid),
+    ("split_pivots", _pivot_high_index_ties),
+    ("split_keys", _keys_toward_b),
     ("reblock_left_rows", _left_rows_floor),
     ("run_head_reblocked", _run_reblocked_wrong_inverse),
     ("run_head_reblocked", _run_reblocked_queries_only),
@@ -1175,8 +1275,8 @@ def test_planted_reblock_tie_rule_mistake_is_caught(monkeypatch):
             if O.n_blocks(n, block) <= 1:
                 leaves.append(rows)
                 return
-            c = O.split_coordinate(z[rows])
-            order = rows[np.lexsort((-rows, z[rows, c]))]
+            key = O.split_keys(z[rows], *O.split_pivots(z[rows]))
+            order = rows[np.lexsort((-rows, key))]
             nl = O.reblock_left_rows(n, block)
             split(np.sort(order[:nl]))
             split(np.sort(order[nl:]))
@@ -1184,3 +1284,22 @@ def test_planted_reblock_tie_rule_mistake_is_caught(monkeypatch):
         return np.concatenate(leaves)
     monkeypatch.setattr(O, "reblock_permutation", perm_high_ties)
     assert not _reblock_pins_pass()
+
+
+def test_reblock_partition_check_accepts_the_oracle_and_rejects_a_swap():
+    # the GPU tests' validity check (tests/parity.py) on the oracle's own
+    # order, then on that order with two rows exchanged across the root split
+    from tests.parity import check_partition
+    q, k, _ = _rand_head(1000, seed=54)
+    z = O.mahalanobis_embedding(q, k)
+    perm = O.reblock_permutation(q, k)
+    assert check_partition(z, perm, O.reblock_left_rows) == (True, "")
+    bad = perm.copy()
+    nl = O.reblock_left_rows(1000)
+    bad[0], bad[nl] = bad[nl], bad[0]
+    # keep every 128-row block ascending, as the GPU's blocks are
+    for b0 in (0, nl - nl % 128):
+        bad[b0:b0 + 128] = np.sort(bad[b0:b0 + 128])
+    bad[nl:nl + 128] = np.sort(bad[nl:nl + 128])
+    ok, msg = check_partition(z, bad, O.reblock_left_rows)
+    assert not ok and "not separated" in msg
