@@ -5,13 +5,16 @@
 //                     mode also per-block float64 partial sums of the anchor rows
 //   anchor_kernel     reweight only: per-head anchor = mean of the anchor rows
 //   pool_kv_kernel    block means of K (for scoring), summary key/value rows and
-//                     bias (mean or Spark-Reweight), V of every block transposed
-//                     into the workspace, summary values transposed likewise
-//   select_kernel     float64 block scores and a wavefront top-k with
+//                     bias (mean or Spark-Reweight)
+//   select_mfma_kernel  float64 block scores on the matrix cores (16 query
+//                     blocks a workgroup) and a wavefront top-k with
 //                     lowest-index ties, ascending output
-//   attn_fwd_kernel   fused gather attention: bf16 MFMA 32x32x16, K and V^T
-//                     tiles staged in LDS, one online softmax over the extra
-//                     tokens (if any), the selected blocks and the summary rows
+//   select_kernel     the same with float64 VALU scores, past 1,200 blocks
+//   row_order_kernel  the order in which attention visits a head's query blocks
+//   attn_fwd_kernel   fused gather attention: bf16 MFMA 32x32x16, K and V
+//                     tiles staged in LDS (V read back transposed), one online
+//                     softmax over the extra tokens (if any), the selected
+//                     blocks and the summary rows
 //   token_select_kernel  extra tokens: scores of every token of the skipped
 //                     blocks on the matrix cores, the E best per query block
 //
@@ -336,6 +339,142 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Top-k phase of the select kernels: wavefront w of an NW-wavefront workgroup
+// takes query rows rr = w, w + NW, ... of the RB rows whose float64 scores
+// against all nb key blocks sit in sc[rr * nb + c].  Scores become
+// order-preserving 64-bit keys held in registers (NCH keys per lane, key of
+// block c in lane c % 64).  An MSB-first bitwise search finds the threshold
+// T, first over the high 32 bits of the keys and, only if keys still tie
+// there at the k-th place, over the low 32 bits of those tied keys; it stops
+// as soon as exactly k keys are >= the candidate (then those k are the
+// answer).  Otherwise T is the k-th largest key and keys equal to T are taken
+// lowest index first.  The chosen indices are written in ascending order
+// with ballot prefix counts.
+template <int NCH, int NW>
+__device__ __forceinline__ void select_topk_rows(const double* sc, int RB, int r0, size_t bh,
+                                                 int32_t* __restrict__ block_idx, int nb, int ksel, int f0,
+                                                 int f1, int thr_mode, double tau, int tid) {
+  const int w = tid >> 6, lane = tid & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int rr = w; rr < RB; rr += NW) {
+    const int r = r0 + rr;
+    if (r >= nb || ksel == 0) break;
+    const double* srow = sc + rr * nb;
+    // threshold mode: only scores above mean + tau * std of the row compete
+    double thr = 0.0;
+    if (thr_mode) {
+      double sum = 0.0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int cc = i * 64 + lane;
+        if (cc < nb) sum += srow[cc];
+      }
+      const double mean = wave_sum(sum) / nb;
+      double sq = 0.0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int cc = i * 64 + lane;
+        if (cc < nb) {
+          const double dv = srow[cc] - mean;
+          sq = fma(dv, dv, sq);
+        }
+      }
+      thr = mean + tau * sqrt(wave_sum(sq) / nb);
+    }
+    uint64_t key[NCH];
+    int navail = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cc = i * 64 + lane;
+      // real keys are > 0 (their high half too) and 0 marks a block that
+      // cannot be kept; sink blocks [f0, f1] take the largest key, so they
+      // are always kept and the rest of the row is the top-k of the others
+      uint64_t kv = 0ull;
+      if (cc < nb) {
+        if (cc >= f0 && cc <= f1)
+          kv = ~0ull;
+        else if (!thr_mode || srow[cc] > thr)
+          kv = order_key(srow[cc]);
+      }
+      key[i] = kv;
+      navail += __popcll(__ballot(kv != 0ull));
+    }
+    const int kr = min(ksel, navail);  // blocks this row keeps
+    int32_t* orow = block_idx + (bh * nb + r) * (size_t)ksel;
+    if (kr > 0) {
+      // high halves: count of keys >= (c << 32) is the count of high halves >= c
+      uint32_t th = 0;
+      bool exact = false;  // exactly kr keys are >= T
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = th | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot((uint32_t)(key[i] >> 32) >= cand));
+        if (cnt >= kr) {
+          th = cand;
+          if (cnt == kr) {
+            exact = true;
+            break;
+          }
+        }
+      }
+      uint64_t T = (uint64_t)th << 32;
+      if (!exact) {
+        // th is the high half of the k-th largest key; search the low halves
+        // of the keys whose high half is th (the others read 0, below every
+        // candidate, which always has a bit set)
+        int gt_hi = 0;
+        uint32_t lo[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const uint32_t h = (uint32_t)(key[i] >> 32);
+          gt_hi += __popcll(__ballot(h > th));
+          lo[i] = h == th ? (uint32_t)key[i] : 0u;
+        }
+        uint32_t tl = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = tl | (1u << bit);
+          int cnt = gt_hi;
+#pragma unroll
+          for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot(lo[i] >= cand));
+          if (cnt >= kr) {
+            tl = cand;
+            if (cnt == kr) {
+              exact = true;
+              break;
+            }
+          }
+        }
+        T |= tl;
+      }
+      int need_eq = 0;
+      if (!exact) {
+        int gt = 0;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) gt += __popcll(__ballot(key[i] > T));
+        need_eq = kr - gt;  // keys equal to T taken lowest index first
+      }
+      int eq_before = 0, sel_before = 0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        bool sel;
+        if (exact) {
+          sel = key[i] >= T;
+        } else {
+          const bool is_eq = key[i] == T;
+          const uint64_t em = __ballot(is_eq);
+          sel = key[i] > T || (is_eq && eq_before + (int)__popcll(em & lt) < need_eq);
+          eq_before += (int)__popcll(em);
+        }
+        const uint64_t sm = __ballot(sel);
+        if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
+        sel_before += __popcll(sm);
+      }
+    }
+    for (int j = kr + lane; j < ksel; j += 64) orow[j] = -1;  // unused slots
+  }
+}
+
 template <int NKT, int RB, bool ROWSPLIT>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q_pool,
                                                      const float* __restrict__ k_pool,
@@ -455,96 +594,98 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
     }
   }
   __syncthreads();
+  select_topk_rows<NCH, 4>(sc, RB, r0, bh, block_idx, nb, ksel, f0, f1, thr_mode, tau, tid);
+}
 
-  const int w = tid >> 6, lane = tid & 63;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int rr = w; rr < RB; rr += 4) {
-    const int r = r0 + rr;
-    if (r >= nb || ksel == 0) break;
-    const double* srow = sc + rr * nb;
-    // threshold mode: only scores above mean + tau * std of the row compete
-    double thr = 0.0;
-    if (thr_mode) {
-      double sum = 0.0;
+// Select with the scores on the float64 matrix cores: one workgroup of NW
+// wavefronts per 16 query blocks of one (b, h) (same 1-D XCD-aware grid).
+// v_mfma_f64_16x16x4f64 takes 16 query rows x 16 key blocks; in step s the
+// four k-slots hold features s, 32 + s, 64 + s and 96 + s (lane group g =
+// lane / 16 supplies feature 32 g + s of its row), so each lane streams 32
+// contiguous floats of one pooled row.  Every score sums its products in the
+// same order whatever its key block, so identical key blocks tie
+// bit-exactly.  Wavefront w takes key tiles w, w + NW, ... and loads the next
+// tile's key rows before it multiplies the current one; lane (g, n) of a
+// finished tile holds the scores of query rows g + 4 i (i < 4) against key
+// block 16 T + n (the accumulator layout, checked on the chip).  Then the
+// top-k phase above, one query row per wavefront at a time.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_row32(const float* p, float (&x)[32]) {
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int cc = i * 64 + lane;
-        if (cc < nb) sum += srow[cc];
-      }
-      const double mean = wave_sum(sum) / nb;
-      double sq = 0.0;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int cc = i * 64 + lane;
-        if (cc < nb) {
-          const double dv = srow[cc] - mean;
-          sq = fma(dv, dv, sq);
-        }
-      }
-      thr = mean + tau * sqrt(wave_sum(sq) / nb);
-    }
-    uint64_t key[NCH];
-    int navail = 0;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int cc = i * 64 + lane;
-      // real keys are > 0 and 0 marks a block that cannot be kept; sink
-      // blocks [f0, f1] take the largest key, so they are always kept and the
-      // rest of the row is the top-k of the others
-      uint64_t kv = 0ull;
-      if (cc < nb) {
-        if (cc >= f0 && cc <= f1)
-          kv = ~0ull;
-        else if (!thr_mode || srow[cc] > thr)
-          kv = order_key(srow[cc]);
-      }
-      key[i] = kv;
-      navail += __popcll(__ballot(kv != 0ull));
-    }
-    const int kr = min(ksel, navail);  // blocks this row keeps
-    int32_t* orow = block_idx + (bh * nb + r) * (size_t)ksel;
-    if (kr > 0) {
-      uint64_t T = 0;
-      bool exact = false;  // exactly kr keys are >= T
-      for (int bit = 63; bit >= 0; --bit) {
-        const uint64_t cand = T | (1ull << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-        if (cnt >= kr) {
-          T = cand;
-          if (cnt == kr) {
-            exact = true;
-            break;
-          }
-        }
-      }
-      int need_eq = 0;
-      if (!exact) {
-        int gt = 0;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) gt += __popcll(__ballot(key[i] > T));
-        need_eq = kr - gt;  // keys equal to T taken lowest index first
-      }
-      int eq_before = 0, sel_before = 0;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        bool sel;
-        if (exact) {
-          sel = key[i] >= T;
-        } else {
-          const bool is_eq = key[i] == T;
-          const uint64_t em = __ballot(is_eq);
-          sel = key[i] > T || (is_eq && eq_before + (int)__popcll(em & lt) < need_eq);
-          eq_before += (int)__popcll(em);
-        }
-        const uint64_t sm = __ballot(sel);
-        if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
-        sel_before += __popcll(sm);
-      }
-    }
-    for (int j = kr + lane; j < ksel; j += 64) orow[j] = -1;  // unused slots
+  for (int j = 0; j < 8; ++j) {
+    const float4 t = *(const float4*)(p + 4 * j);
+    x[4 * j] = t.x;
+    x[4 * j + 1] = t.y;
+    x[4 * j + 2] = t.z;
+    x[4 * j + 3] = t.w;
   }
+}
+
+template <int NCH, int NW>
+__global__ __launch_bounds__(64 * NW) void select_mfma_kernel(const float* __restrict__ q_pool,
+                                                              const float* __restrict__ k_pool,
+                                                              int32_t* __restrict__ block_idx, int nb, int ksel,
+                                                              int f0, int f1, int thr_mode, double tau) {
+  constexpr int RB = 16;
+  extern __shared__ double sc[];  // [RB][nb]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_rg = (nb + RB - 1) / RB;
+  const int logical = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int r0 = (logical % n_rg) * RB;
+  const size_t bh = (size_t)(logical / n_rg);
+  const float* qpb = q_pool + bh * nb * HD;
+  const float* kpb = k_pool + bh * nb * HD;
+  const int g = lane >> 4, n = lane & 15;
+  float qa[32];  // A operand: row r0 + n (clamped), features 32 g + s
+  load_row32(qpb + (size_t)min(r0 + n, nb - 1) * HD + 32 * g, qa);
+  const int ntile = (nb + 15) / 16;
+  // two register buffers of key rows: tile T + NW loads while T multiplies
+  float kb[32], kn[32];
+  (void)kn;
+  auto tile = [&](const float(&x)[32], int T) {
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    if constexpr (NW >= 16) {
+      // steps 0..15 and 16..31 on two accumulators, added at the end (the
+      // same order for every key block)
+      f64x4 acc2 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[st], (double)x[st], acc, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[st + 16], (double)x[st + 16], acc2, 0, 0, 0);
+      }
+      acc += acc2;
+    } else {
+#pragma unroll
+      for (int st = 0; st < 32; ++st)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)qa[st], (double)x[st], acc, 0, 0, 0);
+    }
+    const int c = 16 * T + n;
+    if (c < nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[(g + 4 * i) * nb + c] = acc[i];
+    }
+  };
+  auto krow = [&](int T) { return kpb + (size_t)min(16 * T + n, nb - 1) * HD + 32 * g; };
+  if constexpr (NW >= 16) {
+    // 1,024 threads leave 128 registers a lane: one buffer, and the other
+    // wavefronts hide its loads
+    for (int T = wave; T < ntile; T += NW) {
+      load_row32(krow(T), kb);
+      tile(kb, T);
+    }
+  } else {
+    if (wave < ntile) load_row32(krow(wave), kb);
+    for (int T = wave; T < ntile; T += 2 * NW) {
+      if (T + NW < ntile) load_row32(krow(T + NW), kn);
+      tile(kb, T);
+      if (T + NW >= ntile) break;
+      if (T + 2 * NW < ntile) load_row32(krow(T + 2 * NW), kb);
+      tile(kn, T + NW);
+    }
+  }
+  __syncthreads();
+  select_topk_rows<NCH, NW>(sc, RB, r0, bh, block_idx, nb, ksel, f0, f1, thr_mode, tau, tid);
 }
 
 // ------------------------------------------------------------ row order ---
@@ -1806,6 +1947,21 @@ int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, i
   return launch_status();
 }
 
+template <int NCH, int NW>
+int launch_select_mfma(const Geometry& g, const float* q_pool, const float* k_pool, int32_t* block_idx,
+                       hipStream_t stream) {
+  const dim3 grid((unsigned)(((g.nb + 15) / 16) * g.H * g.B));
+  const size_t lds = (size_t)16 * g.nb * sizeof(double);
+  if (lds > 48 * 1024) {
+    if (hipFuncSetAttribute((const void*)select_mfma_kernel<NCH, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+      return BSA_ERR_HIP;
+  }
+  hipLaunchKernelGGL((select_mfma_kernel<NCH, NW>), grid, dim3(64 * NW), lds, stream, q_pool, k_pool, block_idx,
+                     (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1, g.threshold ? 1 : 0, g.tau);
+  return launch_status();
+}
+
 // Whether a row can skip a block, i.e. the summary rows take part: top-k
 // with k < nb, or threshold selection (rows keep at most k blocks).
 bool uses_summaries(const Geometry& g) { return g.k < g.nb || g.threshold; }
@@ -2004,13 +2160,16 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   if (!q_pool || !k_pool || !block_idx) return BSA_ERR_INVALID;
   if (!aligned16(q_pool) || !aligned16(k_pool) || ((uintptr_t)block_idx & 3u)) return BSA_ERR_INVALID;
   hipStream_t s = (hipStream_t)hip_stream;
-  // key blocks per lane (top-k phase) sized to nb.  The row-split score
-  // phase (four query rows in registers, whole-line key loads) is fastest
-  // except between 512 and 1024 blocks, where the thread-per-key phase with
-  // eight query rows per workgroup ties with it
-  if (g.nb <= 256) return launch_select<1, 4, true>(g, q_pool, k_pool, block_idx, s);
-  if (g.nb <= 512) return launch_select<2, 4, true>(g, q_pool, k_pool, block_idx, s);
-  if (g.nb <= 1024) return launch_select<4, 8, false>(g, q_pool, k_pool, block_idx, s);
+  // key blocks per lane (top-k phase) sized to nb.  Scores on the float64
+  // matrix cores while 16 score rows fit the LDS (nb <= 1200); past that the
+  // row-split VALU score phase (four query rows in registers, whole-line key
+  // loads).  Up to 512 blocks four workgroups of 4 wavefronts share a CU;
+  // past that the score rows take most of the LDS, and one workgroup of 16
+  // wavefronts keeps the CU busy (2K 5s: 0.64 ms against 0.92 with 4)
+  if (g.nb <= 256) return launch_select_mfma<4, 4>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 512) return launch_select_mfma<8, 4>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 1024) return launch_select_mfma<16, 16>(g, q_pool, k_pool, block_idx, s);
+  if (g.nb <= 1200) return launch_select_mfma<19, 16>(g, q_pool, k_pool, block_idx, s);
   return launch_select<8, 4, true>(g, q_pool, k_pool, block_idx, s);
 }
 
