@@ -1306,10 +1306,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 //  - Two phases.  First the sample blocks (one in TS_STRIDE), keeping the m
 //    best of each row in its list: the m-th key T_m is a lower bound of the
 //    row's E-th key whenever at least E candidates reach T_m.  Then the
-//    other blocks with the threshold fixed at T_m: each wavefront appends
-//    the keys reaching it to its own workspace segment per (query block,
-//    token quarter), with no lists, atomics or barriers, and a merge takes
-//    the E best of a row's phase-1 keys and segments.  A row with fewer than
+//    other blocks with the threshold fixed at T_m: wavefront w scores token
+//    eighth w of each block against all 32 query blocks (two B operands, so
+//    each token is loaded once per workgroup: the loads, 16 rows x 64 bytes
+//    per instruction, bound this phase) and appends the keys reaching T_m to
+//    its own workspace segment per (query block, token eighth), with no
+//    lists, atomics or barriers; a merge takes the E best of a row's phase-1
+//    keys and segments.  A row with fewer than
 //    E keys reaching T_m (an unrepresentative sample) or with an overflowing
 //    segment is redone from an empty list over every block by the
 //    list-and-cut sweep.  With one block in S sampled, m = E/S + 8 sqrt(E/S)
@@ -1327,7 +1330,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 constexpr int TS_ROWS = 32;    // query blocks per workgroup
 constexpr int TS_CAP = 512;    // candidate keys per query block
 constexpr int TS_STRIDE = 12;  // blocks c with c % TS_STRIDE == 3 form the sample
-constexpr int SEG_CAP = 512;   // workspace keys per (query block, token quarter) in phase 2
+constexpr int TS_SEGS = 8;     // workspace segments per query block in phase 2 (token eighths)
+constexpr int SEG_CAP = 256;   // keys per segment
 
 __device__ __forceinline__ uint32_t order_key32(float s) {
   if (s == 0.f) s = 0.f;  // -0 ties with +0
@@ -1451,7 +1455,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   __shared__ int cnt[2][TS_ROWS];
   __shared__ int cw[2][4][TS_ROWS];
   __shared__ int nge[TS_ROWS];        // rows to redo (phase 2 could not decide them)
-  __shared__ int segcnt[4][TS_ROWS];  // keys per workspace segment, -1 when it overflowed
+  __shared__ int segcnt[TS_SEGS][TS_ROWS];  // keys per workspace segment, -1 when it overflowed
   __shared__ uint32_t thr[TS_ROWS];
   __shared__ int redo;
 
@@ -1501,11 +1505,10 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     }
   }
 
-  // B operand: query block r0 + row, features 32 s + 8 q4 + [0, 8) for
+  // B operand of query block r0 + qr: features 32 s + 8 q4 + [0, 8) for
   // k-step s, as three exact bfloat16 terms
-  bf16x8 qs[3][4];
-  {
-    const float* qp = q_pool + (bh * nb + min(r0 + row, nb - 1)) * HD + 8 * q4;
+  auto split_q = [&](int qr, bf16x8(&qs)[3][4]) {
+    const float* qp = q_pool + (bh * nb + min(r0 + qr, nb - 1)) * HD + 8 * q4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u16x8 hi, mid, lo;
@@ -1524,7 +1527,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       qs[1][s] = __builtin_bit_cast(bf16x8, mid);
       qs[2][s] = __builtin_bit_cast(bf16x8, lo);
     }
-  }
+  };
   __syncthreads();
 
   // A operand of tile t: token c * 128 + 32 tq + 16 t + l16 of key block c,
@@ -1537,7 +1540,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   // the 12 MFMAs of a tile chain into its accumulator, small terms first;
   // the two tiles' chains alternate, so each MFMA's predecessor in its chain
   // has finished by the time it issues
-  auto mfma_tile = [&](const uint4* kt, f32x4* acc) {
+  auto mfma_tile = [&](const uint4* kt, f32x4* acc, const bf16x8(&qs)[3][4]) {
     acc[0] = f32x4{};
     acc[1] = f32x4{};
 #pragma unroll
@@ -1563,6 +1566,8 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   // One sweep over order[i0, i1) with lists cut to `keep`.  List sizes start
   // and end in cnt[0] (a sweep runs a multiple of 4 steps).
   auto sweep = [&](int i0, int i1, int keep) {
+    bf16x8 qs[3][4];  // this lane's query block (row)
+    split_q(row, qs);
     auto load_tile = [&](int i, uint4* kt) {
       const int tb = (int)order[min(i, i1 - 1)] * BLK + 32 * tq + l16;
 #pragma unroll
@@ -1584,7 +1589,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     // wait only for that tile's own loads, issued two steps earlier.
     auto step = [&](int i, const f32x4* acc, f32x4* accn, const uint4* kn, uint4* kl) {
       const int par = (i - i0) & 1;
-      mfma_tile(kn, accn);
+      mfma_tile(kn, accn, qs);
       __builtin_amdgcn_sched_barrier(0);
       load_tile(i + 3, kl);
       // keys of tile i: value v of tile t is token tb + 16 t + v.  A score's
@@ -1597,11 +1602,14 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
                           : (thr_reg >> 31) ? __uint_as_float(thr_reg & 0x7FFFFFFFu)
                                             : __uint_as_float(~thr_reg);
       uint32_t mask = 0u;
+      if (live) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int j = 0; j < 8; ++j) mask |= (acc[j >> 2][j & 3] >= thr_f ? 1u : 0u) << j;
+        if (tb + 19 >= N) {  // the last block: tokens past the end
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (live && tb + 16 * t + v < N && acc[t][v] >= thr_f) mask |= 1u << (4 * t + v);
+          for (int j = 0; j < 8; ++j) mask &= tb + 16 * (j >> 2) + (j & 3) < N ? ~0u : ~(1u << j);
+        }
+      }
       // the row's four lanes of this wavefront (q4 = 0..3): their total and
       // this lane's offset among them (lane swaps across 16 and 32)
       const int pc = __popc(mask);
@@ -1634,12 +1642,13 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       if (tq == 0 && q4 == 0)
         cnt[par ^ 1][row] =
             cnt[par][row] + cw[par][0][row] + cw[par][1][row] + cw[par][2][row] + cw[par][3][row];
+      for (uint32_t mm = mask; mm != 0u; mm &= mm - 1u) {  // set bits, lowest first
+        const int j = __builtin_ctz(mm);
+        float sv = acc[0][0];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if ((mask >> j) & 1u) {
-          const uint32_t t = (uint32_t)(tb + 16 * (j >> 2) + (j & 3));
-          list[row][pos++] = ((uint64_t)order_key32(acc[j >> 2][j & 3]) << 32) | (uint64_t)(0xFFFFFFFFu - t);
-        }
+        for (int u = 1; u < 8; ++u) sv = j == u ? acc[u >> 2][u & 3] : sv;
+        const uint32_t t = (uint32_t)(tb + 16 * (j >> 2) + (j & 3));
+        list[row][pos++] = ((uint64_t)order_key32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - t);
       }
     };
     f32x4 accA[2], accB[2];
@@ -1647,7 +1656,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     load_tile(i0, kA);
     load_tile(i0 + 1, kB);
     load_tile(i0 + 2, kC);
-    mfma_tile(kA, accA);
+    mfma_tile(kA, accA, qs);
     for (int i = i0; i < i1; i += 4) {
       step(i, accA, accB, kB, kD);
       step(i + 1, accB, accA, kC, kA);
@@ -1674,89 +1683,120 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     __syncthreads();
   }
   if (n1 > 0) {
-    // Phase 2 (filter): with the rows' thresholds fixed at T_m, every key
-    // reaching it goes to this wavefront's own workspace segment for its
-    // row, at positions the row's four lanes agree on; no lists, no atomics,
-    // no barriers.
+    // Phase 2 (filter): with the rows' thresholds fixed at T_m, wavefront w
+    // scores tokens 16 w + [0, 16) of each block against all 32 query blocks
+    // (each token is loaded once per workgroup), and every key reaching its
+    // row's T_m goes to the wavefront's own workspace segment for that row,
+    // at positions the row's four lanes agree on; no lists, no atomics, no
+    // barriers.  Lane l holds tokens 4 q4 + [0, 4) of the tile against query
+    // blocks l16 and 16 + l16.
     {
+      const int te = wave;  // token eighth
+      bf16x8 qh[2][3][4];
+      split_q(l16, qh[0]);
+      split_q(16 + l16, qh[1]);
       auto load_tile = [&](int i, uint4* kt) {
-        const int tb = (int)order[min(max(i, n1), nb - 1)] * BLK + 32 * tq + l16;
+        const int tok = (int)order[min(max(i, n1), nb - 1)] * BLK + 16 * te + l16;
+        const uint16_t* src = kb + (size_t)min(tok, N - 1) * HD + 8 * q4;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint16_t* src = kb + (size_t)min(tb + 16 * t, N - 1) * HD + 8 * q4;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) kt[4 * t + s] = *(const uint4*)(src + 32 * s);
-        }
+        for (int s = 0; s < 4; ++s) kt[s] = *(const uint4*)(src + 32 * s);
       };
-      const uint32_t th = (uint32_t)(tm[row] >> 32);
-      const float thr_f = th == 0u ? -INFINITY
-                          : (th >> 31) ? __uint_as_float(th & 0x7FFFFFFFu)
-                                       : __uint_as_float(~th);
-      uint64_t* seg = gseg + ((bh * nb + (size_t)min(r0 + row, nb - 1)) * 4 + tq) * SEG_CAP;
-      int scount = 0;  // the same in the row's four lanes
+      // the same chain per score as the sweep's tiles (k-steps in order,
+      // small terms first); the two row halves' chains alternate
+      auto mfma_rows = [&](const uint4* kt, f32x4* acc) {
+        acc[0] = f32x4{};
+        acc[1] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int term = 2; term >= 0; --term)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[s]), qh[h][term][s],
+                                                               acc[h], 0, 0, 0);
+      };
+      float thr_f[2];
+      uint64_t* seg[2];
+      int scount[2] = {0, 0};  // the same in the row's four lanes
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t th = (uint32_t)(tm[16 * h + l16] >> 32);
+        thr_f[h] = th == 0u ? -INFINITY : (th >> 31) ? __uint_as_float(th & 0x7FFFFFFFu) : __uint_as_float(~th);
+        seg[h] = gseg + ((bh * nb + (size_t)min(r0 + 16 * h + l16, nb - 1)) * TS_SEGS + te) * SEG_CAP;
+      }
       auto fstep = [&](int i, const f32x4* acc, f32x4* accn, const uint4* kn, uint4* kl) {
-        mfma_tile(kn, accn);
+        mfma_rows(kn, accn);
         __builtin_amdgcn_sched_barrier(0);
         load_tile(i + 3, kl);
         const int c = order[min(max(i, n1), nb - 1)];
-        const int tb = c * BLK + 32 * tq + 4 * q4;
-        const bool live = i >= n1 && i < nb && ((skip[row][c >> 5] >> (c & 31)) & 1u);
-        uint32_t mask = 0u;
+        const int tb = c * BLK + 16 * te + 4 * q4;  // value v: token tb + v
+        const bool in_range = i >= n1 && i < nb;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int h = 0; h < 2; ++h) {
+          const int xr = 16 * h + l16;
+          uint32_t mask = 0u;
+          if (in_range && ((skip[xr][c >> 5] >> (c & 31)) & 1u)) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (live && tb + 16 * t + v < N && acc[t][v] >= thr_f) mask |= 1u << (4 * t + v);
-        const int pc = __popc(mask);
-        const int p16 = lane_x16(pc), pair = pc + p16, p32 = lane_x32(pair);
-        int pos = scount + ((q4 & 1) ? p16 : 0) + ((q4 & 2) ? p32 : 0);
+            for (int v = 0; v < 4; ++v) mask |= (acc[h][v] >= thr_f[h] ? 1u : 0u) << v;
+            if (tb + 3 >= N) {  // the last block: tokens past the end
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if ((mask >> j) & 1u) {
-            const uint32_t t = (uint32_t)(tb + 16 * (j >> 2) + (j & 3));
-            if (pos < SEG_CAP)
-              seg[pos] = ((uint64_t)order_key32(acc[j >> 2][j & 3]) << 32) | (uint64_t)(0xFFFFFFFFu - t);
+              for (int v = 0; v < 4; ++v) mask &= tb + v < N ? ~0u : ~(1u << v);
+            }
+          }
+          const int pc = __popc(mask);
+          const int p16 = lane_x16(pc), pair = pc + p16, p32 = lane_x32(pair);
+          int pos = scount[h] + ((q4 & 1) ? p16 : 0) + ((q4 & 2) ? p32 : 0);
+          for (uint32_t mm = mask; mm != 0u; mm &= mm - 1u) {  // set bits, lowest first
+            const int v = __builtin_ctz(mm);
+            float sv = acc[h][0];
+#pragma unroll
+            for (int u = 1; u < 4; ++u) sv = v == u ? acc[h][u] : sv;
+            const uint32_t t = (uint32_t)(tb + v);
+            if (pos < SEG_CAP) seg[h][pos] = ((uint64_t)order_key32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - t);
             ++pos;
           }
+          scount[h] += pair + p32;
         }
-        scount += pair + p32;
       };
       // the pipeline fills inside the loop (three steps on zeroed buffers
       // before tile n1), so no load is in flight when the loop is entered
       // and every tile's MFMAs wait only for that tile's own loads
       f32x4 accA[2] = {f32x4{}, f32x4{}}, accB[2] = {f32x4{}, f32x4{}};
-      uint4 kA[8], kB[8], kC[8], kD[8];
+      uint4 kA[4], kB[4], kC[4], kD[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) kA[j] = kB[j] = kC[j] = kD[j] = make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < 4; ++j) kA[j] = kB[j] = kC[j] = kD[j] = make_uint4(0u, 0u, 0u, 0u);
       for (int i = n1 - 3; i < nb; i += 4) {
         fstep(i, accA, accB, kB, kD);
         fstep(i + 1, accB, accA, kC, kA);
         fstep(i + 2, accA, accB, kD, kB);
         fstep(i + 3, accB, accA, kA, kC);
       }
-      if (q4 == 0) segcnt[tq][row] = scount <= SEG_CAP ? scount : -1;
+      if (q4 == 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) segcnt[te][16 * h + l16] = scount[h] <= SEG_CAP ? scount[h] : -1;
+      }
     }
     __syncthreads();
-    // Merge: each row's phase-1 keys and its four segments; the E best of
+    // Merge: each row's phase-1 keys and its eight segments; the E best of
     // them are the row's answer when at least E keys reach T_m (then no key
     // below T_m can be among the E best) and no segment overflowed.
     for (int x = wave; x < TS_ROWS; x += TS_THREADS / 64) {
       const int r = r0 + x;
       bool bad = false;
       if (r < nb) {
-        int c[4], total = cnt[0][x];
+        int c[TS_SEGS], total = cnt[0][x];
         const int n0 = total;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < TS_SEGS; ++q) {
           c[q] = segcnt[q][x];
           bad |= c[q] < 0;
           total += max(c[q], 0);
         }
         if (!bad) {
-          constexpr int PER = TS_CAP / 64 + 4 * SEG_CAP / 64;
+          constexpr int PER = TS_CAP / 64 + TS_SEGS * SEG_CAP / 64;
           uint32_t hi[PER], lo[PER];
           const uint64_t tmx = tm[x];
-          const uint64_t* sb = gseg + (bh * nb + (size_t)r) * 4 * SEG_CAP;
+          const uint64_t* sb = gseg + (bh * nb + (size_t)r) * TS_SEGS * SEG_CAP;
           int nge_l = 0;
 #pragma unroll
           for (int j = 0; j < PER; ++j) {
@@ -1767,7 +1807,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
             } else if (y < total) {
               int rest = y - n0, q = 0;
 #pragma unroll
-              for (int u = 0; u < 3; ++u)
+              for (int u = 0; u < TS_SEGS - 1; ++u)
                 if (q == u && rest >= c[u]) {
                   rest -= c[u];
                   q = u + 1;
@@ -1875,14 +1915,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //   pool (reweight only): float64 anchor partial sums [B, H, nb, 128], then
 //     the anchor [B, H, 128] at pool_anchor_off();
 //   forward: the visiting order of each head's query blocks, int32 [B, H, nb];
-//   select_tokens: key segments, u64 [B, H, nb, 4, SEG_CAP].
+//   select_tokens: key segments, u64 [B, H, nb, TS_SEGS, SEG_CAP].
 size_t pool_anchor_off(const Geometry& g) { return align256((size_t)(g.B * g.H * g.nb) * HD * sizeof(double)); }
 size_t pool_ws(const Geometry& g) {
   return g.reweight ? pool_anchor_off(g) + align256((size_t)(g.B * g.H) * HD * sizeof(double)) : 0;
 }
 size_t forward_ws(const Geometry& g) { return align256((size_t)(g.B * g.H * g.nb) * sizeof(int32_t)); }
 size_t tokens_ws(const Geometry& g) {
-  return g.E > 0 ? align256((size_t)(g.B * g.H * g.nb) * 4 * SEG_CAP * sizeof(uint64_t)) : 0;
+  return g.E > 0 ? align256((size_t)(g.B * g.H * g.nb) * TS_SEGS * SEG_CAP * sizeof(uint64_t)) : 0;
 }
 size_t ws_total(const Geometry& g) { return std::max(pool_ws(g), std::max(forward_ws(g), tokens_ws(g))); }
 
