@@ -1684,19 +1684,22 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   }
   if (n1 > 0) {
     // Phase 2 (filter): with the rows' thresholds fixed at T_m, wavefront w
-    // scores tokens 16 w + [0, 16) of each block against all 32 query blocks
-    // (each token is loaded once per workgroup), and every key reaching its
-    // row's T_m goes to the wavefront's own workspace segment for that row,
-    // at positions the row's four lanes agree on; no lists, no atomics, no
-    // barriers.  Lane l holds tokens 4 q4 + [0, 4) of the tile against query
-    // blocks l16 and 16 + l16.
+    // scores tokens 8 j + w (j < 16) of each block against all 32 query
+    // blocks (each token is loaded once per workgroup), and every key
+    // reaching its row's T_m goes to the wavefront's own workspace segment
+    // for that row, at positions the row's four lanes agree on; no lists, no
+    // atomics, no barriers.  Tile row j is token 8 j + w, so lane l holds
+    // tokens 8 (4 q4 + v) + w (v < 4) against query blocks l16 and 16 + l16.
+    // Taking every eighth token (not 16 adjacent ones, which tend to score
+    // alike) spreads a row's keys evenly over its segments: fullest segment
+    // 193 of 256 keys at 768p, E = 256, against 257 (an overflow) adjacent.
     {
       const int te = wave;  // token eighth
       bf16x8 qh[2][3][4];
       split_q(l16, qh[0]);
       split_q(16 + l16, qh[1]);
       auto load_tile = [&](int i, uint4* kt) {
-        const int tok = (int)order[min(max(i, n1), nb - 1)] * BLK + 16 * te + l16;
+        const int tok = (int)order[min(max(i, n1), nb - 1)] * BLK + 8 * l16 + te;
         const uint16_t* src = kb + (size_t)min(tok, N - 1) * HD + 8 * q4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) kt[s] = *(const uint4*)(src + 32 * s);
@@ -1729,7 +1732,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
         __builtin_amdgcn_sched_barrier(0);
         load_tile(i + 3, kl);
         const int c = order[min(max(i, n1), nb - 1)];
-        const int tb = c * BLK + 16 * te + 4 * q4;  // value v: token tb + v
+        const int tb = c * BLK + 32 * q4 + te;  // value v: token tb + 8 v
         const bool in_range = i >= n1 && i < nb;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -1738,9 +1741,9 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
           if (in_range && ((skip[xr][c >> 5] >> (c & 31)) & 1u)) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) mask |= (acc[h][v] >= thr_f[h] ? 1u : 0u) << v;
-            if (tb + 3 >= N) {  // the last block: tokens past the end
+            if (tb + 24 >= N) {  // the last block: tokens past the end
 #pragma unroll
-              for (int v = 0; v < 4; ++v) mask &= tb + v < N ? ~0u : ~(1u << v);
+              for (int v = 0; v < 4; ++v) mask &= tb + 8 * v < N ? ~0u : ~(1u << v);
             }
           }
           const int pc = __popc(mask);
@@ -1751,7 +1754,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
             float sv = acc[h][0];
 #pragma unroll
             for (int u = 1; u < 4; ++u) sv = v == u ? acc[h][u] : sv;
-            const uint32_t t = (uint32_t)(tb + v);
+            const uint32_t t = (uint32_t)(tb + 8 * v);
             if (pos < SEG_CAP) seg[h][pos] = ((uint64_t)order_key32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - t);
             ++pos;
           }
