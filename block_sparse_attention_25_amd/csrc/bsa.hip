@@ -333,6 +333,12 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
+__device__ __forceinline__ uint32_t wave_max32(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off, 64));
+  return x;
+}
+
 __device__ __forceinline__ uint64_t order_key(double s) {
   if (s == 0.0) s = 0.0;  // -0 ties with +0
   const uint64_t u = (uint64_t)__double_as_longlong(s);
@@ -1346,12 +1352,26 @@ __device__ __forceinline__ uint32_t order_key32(float s) {
 // soon as exactly `keep` keys reach the candidate; only when several keys
 // share the upper half at the boundary does a second search order those by
 // their lower halves (larger = lower token).
+//
+// lb, when nonzero, is a lower bound of the keep-th largest upper half: the
+// bits above the highest one on which it and the largest upper half differ
+// are then taken at once.
 template <int PER>
 __device__ void top_keys(const uint32_t (&hi)[PER], const uint32_t (&lo)[PER], int keep, uint32_t& T,
-                         uint32_t& L, bool& exact) {
+                         uint32_t& L, bool& exact, uint32_t lb = 0u) {
   T = 0u;
   exact = false;
-  for (int bit = 31; bit >= 0; --bit) {
+  int top = 31;
+  if (lb != 0u) {
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) mx = max(mx, hi[j]);
+    mx = wave_max32(mx);
+    const uint32_t x = lb ^ mx;
+    top = x == 0u ? -1 : 31 - __clz(x);
+    T = top < 0 ? mx : mx & ~((2u << top) - 1u);
+  }
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
 #pragma unroll
@@ -1796,26 +1816,22 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
           total += max(c[q], 0);
         }
         if (!bad) {
-          constexpr int PER = TS_CAP / 64 + TS_SEGS * SEG_CAP / 64;
+          // fixed register slots: the phase-1 keys, then SPER per segment
+          constexpr int LPER = TS_CAP / 64, SPER = SEG_CAP / 64;
+          constexpr int PER = LPER + TS_SEGS * SPER;
           uint32_t hi[PER], lo[PER];
           const uint64_t tmx = tm[x];
           const uint64_t* sb = gseg + (bh * nb + (size_t)r) * TS_SEGS * SEG_CAP;
           int nge_l = 0;
 #pragma unroll
           for (int j = 0; j < PER; ++j) {
-            const int y = lane + 64 * j;
             uint64_t kv = 0ull;
-            if (y < n0) {
-              kv = list[x][y];
-            } else if (y < total) {
-              int rest = y - n0, q = 0;
-#pragma unroll
-              for (int u = 0; u < TS_SEGS - 1; ++u)
-                if (q == u && rest >= c[u]) {
-                  rest -= c[u];
-                  q = u + 1;
-                }
-              kv = sb[q * SEG_CAP + rest];
+            if (j < LPER) {
+              const int y = lane + 64 * j;
+              if (y < n0) kv = list[x][y];
+            } else {
+              const int q = (j - LPER) / SPER, y = lane + 64 * ((j - LPER) % SPER);
+              if (y < c[q]) kv = sb[q * SEG_CAP + y];
             }
             hi[j] = (uint32_t)(kv >> 32);
             lo[j] = (uint32_t)kv;
@@ -1829,9 +1845,10 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
           } else {
             const int keep = min(E, total);
             if (keep > 0) {
+              // at least E keys reach T_m, so the E-th largest does too
               uint32_t T, L;
               bool exact;
-              top_keys<PER>(hi, lo, keep, T, L, exact);
+              top_keys<PER>(hi, lo, keep, T, L, exact, (uint32_t)(tmx >> 32));
               write_kept<PER>(list[x], hi, lo, T, L, exact, lane);
             }
             if (lane == 0) cnt[0][x] = keep;
