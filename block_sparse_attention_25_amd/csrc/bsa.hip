@@ -1473,7 +1473,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   // double-buffered by step parity: a step reads one copy and writes the
   // other, so no wavefront overwrites a value another still reads
   __shared__ int cnt[2][TS_ROWS];
-  __shared__ int cw[2][4][TS_ROWS];
+  __shared__ int cw[2][TS_SEGS][TS_ROWS];
   __shared__ int nge[TS_ROWS];        // rows to redo (phase 2 could not decide them)
   __shared__ int segcnt[TS_SEGS][TS_ROWS];  // keys per workspace segment, -1 when it overflowed
   __shared__ uint32_t thr[TS_ROWS];
@@ -1485,9 +1485,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   const size_t bh = (size_t)(logical / ngrp);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tq = wave & 3, rh = wave >> 2;   // token quarter, row half
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int row = 16 * rh + l16;             // this lane's query block in the group
   const int nwords = (nb + 31) >> 5;
   const int n1 = m > 0 ? (nb + TS_STRIDE - 4) / TS_STRIDE : 0;  // sample blocks
 
@@ -1550,28 +1548,13 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   };
   __syncthreads();
 
-  // A operand of tile t: token c * 128 + 32 tq + 16 t + l16 of key block c,
-  // features 32 s + 8 q4 + [0, 8) for k-step s (so each load instruction
-  // reads 64 contiguous bytes of every row it touches).  Past the end of the
-  // sequence the last row is read again: such a token's scores fill only its
-  // own accumulator row and it is never inserted, so the loaded data needs no
-  // zeroing (and a load needs no wait until the MFMAs that read it).
+  // A operand (K) of a tile: tile row j of key block c, features 32 s +
+  // 8 q4 + [0, 8) for k-step s (so each load instruction reads 64 contiguous
+  // bytes of every row it touches).  Past the end of the sequence the last
+  // row is read again: such a token's scores fill only its own accumulator
+  // row and it is never inserted, so the loaded data needs no zeroing (and a
+  // load needs no wait until the MFMAs that read it).
   const uint16_t* kb = k + bh * (size_t)N * HD;
-  // the 12 MFMAs of a tile chain into its accumulator, small terms first;
-  // the two tiles' chains alternate, so each MFMA's predecessor in its chain
-  // has finished by the time it issues
-  auto mfma_tile = [&](const uint4* kt, f32x4* acc, const bf16x8(&qs)[3][4]) {
-    acc[0] = f32x4{};
-    acc[1] = f32x4{};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int term = 2; term >= 0; --term)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[4 * t + s]),
-                                                           qs[term][s], acc[t], 0, 0, 0);
-  };
 
   // value of lane l ^ 16 and of lane l ^ 32 (VALU lane swaps)
   auto lane_x16 = [&](int x) {
@@ -1583,66 +1566,93 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     return (int)((lane & 32) ? r[0] : r[1]);
   };
 
+  // Token eighths (every phase): wavefront w scores tokens 8 j + w (j < 16)
+  // of a key block against all 32 query blocks of the group, with two B
+  // operands, so each token is loaded once per workgroup.  Tile row j is
+  // token 8 j + w, so lane l holds tokens 8 (4 q4 + v) + w (v < 4) against
+  // query blocks l16 and 16 + l16 (row halves h = 0, 1).  Taking every
+  // eighth token (not 16 adjacent ones, which tend to score alike) spreads a
+  // row's keys evenly over its workspace segments in phase 2.
+  const int te = wave;
+  auto load8 = [&](int c, uint4* kt) {  // key block c
+    const uint16_t* src = kb + (size_t)min(c * BLK + 8 * l16 + te, N - 1) * HD + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kt[s] = *(const uint4*)(src + 32 * s);
+  };
+  // each score's chain: k-steps in order, small terms first; the two row
+  // halves' chains alternate
+  auto mfma_rows = [&](const uint4* kt, f32x4* acc, const bf16x8(&qh)[2][3][4]) {
+    acc[0] = f32x4{};
+    acc[1] = f32x4{};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int term = 2; term >= 0; --term)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[s]), qh[h][term][s],
+                                                           acc[h], 0, 0, 0);
+  };
+
   // One sweep over order[i0, i1) with lists cut to `keep`.  List sizes start
   // and end in cnt[0] (a sweep runs a multiple of 4 steps).
   auto sweep = [&](int i0, int i1, int keep) {
-    bf16x8 qs[3][4];  // this lane's query block (row)
-    split_q(row, qs);
-    auto load_tile = [&](int i, uint4* kt) {
-      const int tb = (int)order[min(i, i1 - 1)] * BLK + 32 * tq + l16;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const uint16_t* src = kb + (size_t)min(tb + 16 * t, N - 1) * HD + 8 * q4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kt[4 * t + s] = *(const uint4*)(src + 32 * s);
-      }
-    };
-    uint32_t thr_reg = thr[row];
+    bf16x8 qh[2][3][4];
+    split_q(l16, qh[0]);
+    split_q(16 + l16, qh[1]);
+    uint32_t thr_reg[2] = {thr[l16], thr[16 + l16]};
     // Step i (software pipeline): the MFMAs of tile i+1 and the loads of tile
     // i+3 go out first; the keys of tile i (scored by the previous step) are
-    // filtered by the row threshold and each token quarter publishes how many
+    // filtered by the row threshold and each token eighth publishes how many
     // it inserts per row; between the two barriers the lists that would
     // overflow are cut; then every lane writes its keys at positions given by
-    // the list size and the counts of the quarters before it (no atomics, and
-    // each row's list stays in token order within a step).  Every step issues
-    // the same loads and waits (no branch around them), so each tile's MFMAs
-    // wait only for that tile's own loads, issued two steps earlier.
+    // the list size and the counts of the eighths before it (no atomics).
+    // Every step issues the same loads and waits (no branch around them), so
+    // each tile's MFMAs wait only for that tile's own loads, issued two steps
+    // earlier.
     auto step = [&](int i, const f32x4* acc, f32x4* accn, const uint4* kn, uint4* kl) {
       const int par = (i - i0) & 1;
-      mfma_tile(kn, accn, qs);
+      mfma_rows(kn, accn, qh);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(i + 3, kl);
-      // keys of tile i: value v of tile t is token tb + 16 t + v.  A score's
+      load8((int)order[min(i + 3, i1 - 1)], kl);
+      // keys of tile i: value v of row half h is token tb + 8 v.  A score's
       // key reaches the threshold key exactly when the score reaches the
       // float with that key (the key map is monotone; -0 counts as +0)
       const int c = order[min(i, i1 - 1)];
-      const int tb = c * BLK + 32 * tq + 4 * q4;
-      const bool live = i < i1 && ((skip[row][c >> 5] >> (c & 31)) & 1u);
-      const float thr_f = thr_reg == 0u ? -INFINITY
-                          : (thr_reg >> 31) ? __uint_as_float(thr_reg & 0x7FFFFFFFu)
-                                            : __uint_as_float(~thr_reg);
-      uint32_t mask = 0u;
-      if (live) {
+      const int tb = c * BLK + 32 * q4 + te;
+      uint32_t mask[2];
+      int before[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mask |= (acc[j >> 2][j & 3] >= thr_f ? 1u : 0u) << j;
-        if (tb + 19 >= N) {  // the last block: tokens past the end
+      for (int h = 0; h < 2; ++h) {
+        const int xr = 16 * h + l16;
+        const float thr_f = thr_reg[h] == 0u ? -INFINITY
+                            : (thr_reg[h] >> 31) ? __uint_as_float(thr_reg[h] & 0x7FFFFFFFu)
+                                                 : __uint_as_float(~thr_reg[h]);
+        uint32_t mk = 0u;
+        if (i < i1 && ((skip[xr][c >> 5] >> (c & 31)) & 1u)) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) mask &= tb + 16 * (j >> 2) + (j & 3) < N ? ~0u : ~(1u << j);
+          for (int v = 0; v < 4; ++v) mk |= (acc[h][v] >= thr_f ? 1u : 0u) << v;
+          if (tb + 24 >= N) {  // the last block: tokens past the end
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mk &= tb + 8 * v < N ? ~0u : ~(1u << v);
+          }
         }
+        mask[h] = mk;
+        // the row's four lanes of this wavefront (q4 = 0..3): their total and
+        // this lane's offset among them (lane swaps across 16 and 32)
+        const int pc = __popc(mk);
+        const int p16 = lane_x16(pc), pair = pc + p16, p32 = lane_x32(pair);
+        before[h] = ((q4 & 1) ? p16 : 0) + ((q4 & 2) ? p32 : 0);
+        if (q4 == 0) cw[par][te][xr] = pair + p32;
       }
-      // the row's four lanes of this wavefront (q4 = 0..3): their total and
-      // this lane's offset among them (lane swaps across 16 and 32)
-      const int pc = __popc(mask);
-      const int p16 = lane_x16(pc), pair = pc + p16, p32 = lane_x32(pair);
-      const int before = ((q4 & 1) ? p16 : 0) + ((q4 & 2) ? p32 : 0);
-      if (q4 == 0) cw[par][tq][row] = pair + p32;
       __syncthreads();
       // a list whose keys this step could overflow is cut first; a wavefront
       // cuts only its own rows (x = wave mod 8)
       const int lr = lane & (TS_ROWS - 1);
-      const uint64_t full =
-          __ballot(lane < TS_ROWS && cnt[par][lr] + cw[par][0][lr] + cw[par][1][lr] + cw[par][2][lr] +
-                                         cw[par][3][lr] > TS_CAP);
+      int grow = 0;
+#pragma unroll
+      for (int q = 0; q < TS_SEGS; ++q) grow += cw[par][q][lr];
+      const uint64_t full = __ballot(lane < TS_ROWS && cnt[par][lr] + grow > TS_CAP);
       if (full) {
         for (int x = wave; x < TS_ROWS; x += TS_THREADS / 64) {
           if ((full >> x) & 1ull) {
@@ -1655,28 +1665,34 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
         }
       }
       __syncthreads();
-      thr_reg = thr[row];
-      int pos = cnt[par][row] + before;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pos += q < tq ? cw[par][q][row] : 0;
-      if (tq == 0 && q4 == 0)
-        cnt[par ^ 1][row] =
-            cnt[par][row] + cw[par][0][row] + cw[par][1][row] + cw[par][2][row] + cw[par][3][row];
-      for (uint32_t mm = mask; mm != 0u; mm &= mm - 1u) {  // set bits, lowest first
-        const int j = __builtin_ctz(mm);
-        float sv = acc[0][0];
+      for (int h = 0; h < 2; ++h) {
+        const int xr = 16 * h + l16;
+        thr_reg[h] = thr[xr];
+        int pos = cnt[par][xr] + before[h], tot = 0;
 #pragma unroll
-        for (int u = 1; u < 8; ++u) sv = j == u ? acc[u >> 2][u & 3] : sv;
-        const uint32_t t = (uint32_t)(tb + 16 * (j >> 2) + (j & 3));
-        list[row][pos++] = ((uint64_t)order_key32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - t);
+        for (int q = 0; q < TS_SEGS; ++q) {
+          const int cq = cw[par][q][xr];
+          pos += q < te ? cq : 0;
+          tot += cq;
+        }
+        if (te == 0 && q4 == 0) cnt[par ^ 1][xr] = cnt[par][xr] + tot;
+        for (uint32_t mm = mask[h]; mm != 0u; mm &= mm - 1u) {  // set bits, lowest first
+          const int v = __builtin_ctz(mm);
+          float sv = acc[h][0];
+#pragma unroll
+          for (int u = 1; u < 4; ++u) sv = v == u ? acc[h][u] : sv;
+          const uint32_t t = (uint32_t)(tb + 8 * v);
+          list[xr][pos++] = ((uint64_t)order_key32(sv) << 32) | (uint64_t)(0xFFFFFFFFu - t);
+        }
       }
     };
     f32x4 accA[2], accB[2];
-    uint4 kA[8], kB[8], kC[8], kD[8];
-    load_tile(i0, kA);
-    load_tile(i0 + 1, kB);
-    load_tile(i0 + 2, kC);
-    mfma_tile(kA, accA, qs);
+    uint4 kA[4], kB[4], kC[4], kD[4];
+    load8((int)order[min(i0, i1 - 1)], kA);
+    load8((int)order[min(i0 + 1, i1 - 1)], kB);
+    load8((int)order[min(i0 + 2, i1 - 1)], kC);
+    mfma_rows(kA, accA, qh);
     for (int i = i0; i < i1; i += 4) {
       step(i, accA, accB, kB, kD);
       step(i + 1, accB, accA, kC, kA);
@@ -1703,41 +1719,16 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     __syncthreads();
   }
   if (n1 > 0) {
-    // Phase 2 (filter): with the rows' thresholds fixed at T_m, wavefront w
-    // scores tokens 8 j + w (j < 16) of each block against all 32 query
-    // blocks (each token is loaded once per workgroup), and every key
+    // Phase 2 (filter): with the rows' thresholds fixed at T_m, every key
     // reaching its row's T_m goes to the wavefront's own workspace segment
-    // for that row, at positions the row's four lanes agree on; no lists, no
-    // atomics, no barriers.  Tile row j is token 8 j + w, so lane l holds
-    // tokens 8 (4 q4 + v) + w (v < 4) against query blocks l16 and 16 + l16.
-    // Taking every eighth token (not 16 adjacent ones, which tend to score
-    // alike) spreads a row's keys evenly over its segments: fullest segment
-    // 193 of 256 keys at 768p, E = 256, against 257 (an overflow) adjacent.
+    // for that row (token eighth), at positions the row's four lanes agree
+    // on; no lists, no atomics, no barriers.  Strided eighths: fullest
+    // segment 193 of 256 keys at 768p, E = 256, against 257 (an overflow)
+    // with 16 adjacent tokens per eighth.
     {
-      const int te = wave;  // token eighth
       bf16x8 qh[2][3][4];
       split_q(l16, qh[0]);
       split_q(16 + l16, qh[1]);
-      auto load_tile = [&](int i, uint4* kt) {
-        const int tok = (int)order[min(max(i, n1), nb - 1)] * BLK + 8 * l16 + te;
-        const uint16_t* src = kb + (size_t)min(tok, N - 1) * HD + 8 * q4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kt[s] = *(const uint4*)(src + 32 * s);
-      };
-      // the same chain per score as the sweep's tiles (k-steps in order,
-      // small terms first); the two row halves' chains alternate
-      auto mfma_rows = [&](const uint4* kt, f32x4* acc) {
-        acc[0] = f32x4{};
-        acc[1] = f32x4{};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int term = 2; term >= 0; --term)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kt[s]), qh[h][term][s],
-                                                               acc[h], 0, 0, 0);
-      };
       float thr_f[2];
       uint64_t* seg[2];
       int scount[2] = {0, 0};  // the same in the row's four lanes
@@ -1748,9 +1739,9 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
         seg[h] = gseg + ((bh * nb + (size_t)min(r0 + 16 * h + l16, nb - 1)) * TS_SEGS + te) * SEG_CAP;
       }
       auto fstep = [&](int i, const f32x4* acc, f32x4* accn, const uint4* kn, uint4* kl) {
-        mfma_rows(kn, accn);
+        mfma_rows(kn, accn, qh);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(i + 3, kl);
+        load8((int)order[min(max(i + 3, n1), nb - 1)], kl);
         const int c = order[min(max(i, n1), nb - 1)];
         const int tb = c * BLK + 32 * q4 + te;  // value v: token tb + 8 v
         const bool in_range = i >= n1 && i < nb;
