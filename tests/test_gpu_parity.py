@@ -224,12 +224,16 @@ def test_threshold_selection(torch_cuda, N, top_k, tau, sink, summary):
                     sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau)
 
 
+@pytest.mark.parametrize("N", [140000, 166000])
 @pytest.mark.parametrize("variant", ["plain", "ties", "sinks", "threshold"])
-def test_many_blocks_selection(torch_cuda, variant):
-    """Past 1024 blocks the selection runs its row-split score phase: every
-    index of the head against the oracle, and sampled query blocks."""
-    N = 140000                                  # 1094 blocks, short last block
-    _log("case many blocks %s" % variant)
+def test_many_blocks_selection(torch_cuda, variant, N):
+    """The selection's large-row forms: up to 1,200 blocks the float64 matrix
+    scores with one 16-wavefront workgroup per 16 query blocks (1,094 blocks,
+    short last block), past that the row-split float64 VALU scores (1,297
+    blocks).  Every index of the head against the oracle, and sampled query
+    blocks."""
+    _log("case many blocks %s N=%d" % (variant, N))
+    nb = O.n_blocks(N)
     w = custom(N, heads=1, seed=17)
     qb, kb, vb = generate(w, threads=16)
     kw = dict(top_k=16)
@@ -245,8 +249,8 @@ def test_many_blocks_selection(torch_cuda, variant):
         kw.update(tau=1.5, top_k=40)
         check.update(tau=1.5)
     host = _run_gpu(torch_cuda, qb, kb, vb, **kw)
-    _check_head(host, qb, kb, vb, 0, 0, kw["top_k"], query_blocks=[0, 250, 1092, 1093],
-                label="nb1094-" + variant, **check)
+    _check_head(host, qb, kb, vb, 0, 0, kw["top_k"], query_blocks=[0, 250, nb - 2, nb - 1],
+                label="nb%d-%s" % (nb, variant), **check)
     if variant == "ties":
         s = O.block_scores(O.pool_mean(widen(qb[0, 0])), O.pool_mean(widen(kb[0, 0])))
         assert np.array_equal(host["block_idx"][0, 0].numpy(), O.select_topk(s, 16))
