@@ -9,7 +9,11 @@
 //   select_mfma_kernel  float64 block scores on the matrix cores (16 query
 //                     blocks a workgroup) and a wavefront top-k with
 //                     lowest-index ties, ascending output
+//   select_mfma_hi_kernel  the same for top-k past 512 blocks with only the
+//                     high 32 bits of each key in LDS (two workgroups a CU);
+//                     blocks that tie there are ranked by recomputed scores
 //   select_kernel     the same with float64 VALU scores, past 1,200 blocks
+//                     (1,280 for top-k)
 //   row_order_kernel  the order in which attention visits a head's query blocks
 //   attn_fwd_kernel   fused gather attention: bf16 MFMA 32x32x16, K and V
 //                     tiles staged in LDS (V read back transposed), one online
@@ -628,20 +632,15 @@ __device__ __forceinline__ void load_row32(const float* p, float (&x)[32]) {
   }
 }
 
-template <int NCH, int NW>
-__global__ __launch_bounds__(64 * NW) void select_mfma_kernel(const float* __restrict__ q_pool,
-                                                              const float* __restrict__ k_pool,
-                                                              int32_t* __restrict__ block_idx, int nb, int ksel,
-                                                              int f0, int f1, int thr_mode, double tau) {
-  constexpr int RB = 16;
-  extern __shared__ double sc[];  // [RB][nb]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_rg = (nb + RB - 1) / RB;
-  const int logical = xcd_remap(blockIdx.x, (int)gridDim.x);
-  const int r0 = (logical % n_rg) * RB;
-  const size_t bh = (size_t)(logical / n_rg);
-  const float* qpb = q_pool + bh * nb * HD;
-  const float* kpb = k_pool + bh * nb * HD;
+// Score phase of the matrix-core select kernels: the 16 query rows r0 ..
+// r0 + 15 of one (b, h) against all nb key blocks; store(row, c, s) takes the
+// float64 score of query row r0 + row against key block c < nb.  ONEBUF: one
+// register buffer of key rows and two accumulator chains (for 128 registers
+// a lane, where the other wavefronts hide the loads), else two buffers and
+// one chain.
+template <int NW, bool ONEBUF, typename Store>
+__device__ __forceinline__ void mfma_scores(const float* qpb, const float* kpb, int nb, int r0, int lane, int wave,
+                                            Store&& store) {
   const int g = lane >> 4, n = lane & 15;
   float qa[32];  // A operand: row r0 + n (clamped), features 32 g + s
   load_row32(qpb + (size_t)min(r0 + n, nb - 1) * HD + 32 * g, qa);
@@ -651,7 +650,7 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(const float* __res
   (void)kn;
   auto tile = [&](const float(&x)[32], int T) {
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-    if constexpr (NW >= 16) {
+    if constexpr (ONEBUF) {
       // steps 0..15 and 16..31 on two accumulators, added at the end (the
       // same order for every key block)
       f64x4 acc2 = {0.0, 0.0, 0.0, 0.0};
@@ -669,13 +668,11 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(const float* __res
     const int c = 16 * T + n;
     if (c < nb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[(g + 4 * i) * nb + c] = acc[i];
+      for (int i = 0; i < 4; ++i) store(g + 4 * i, c, acc[i]);
     }
   };
   auto krow = [&](int T) { return kpb + (size_t)min(16 * T + n, nb - 1) * HD + 32 * g; };
-  if constexpr (NW >= 16) {
-    // 1,024 threads leave 128 registers a lane: one buffer, and the other
-    // wavefronts hide its loads
+  if constexpr (ONEBUF) {
     for (int T = wave; T < ntile; T += NW) {
       load_row32(krow(T), kb);
       tile(kb, T);
@@ -690,8 +687,191 @@ __global__ __launch_bounds__(64 * NW) void select_mfma_kernel(const float* __res
       tile(kn, T + NW);
     }
   }
+}
+
+template <int NCH, int NW>
+__global__ __launch_bounds__(64 * NW) void select_mfma_kernel(const float* __restrict__ q_pool,
+                                                              const float* __restrict__ k_pool,
+                                                              int32_t* __restrict__ block_idx, int nb, int ksel,
+                                                              int f0, int f1, int thr_mode, double tau) {
+  constexpr int RB = 16;
+  extern __shared__ double sc[];  // [RB][nb]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_rg = (nb + RB - 1) / RB;
+  const int logical = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int r0 = (logical % n_rg) * RB;
+  const size_t bh = (size_t)(logical / n_rg);
+  mfma_scores<NW, (NW >= 16)>(q_pool + bh * nb * HD, k_pool + bh * nb * HD, nb, r0, lane, wave,
+                  [&](int row, int c, double s) { sc[row * nb + c] = s; });
   __syncthreads();
   select_topk_rows<NCH, NW>(sc, RB, r0, bh, block_idx, nb, ksel, f0, f1, thr_mode, tau, tid);
+}
+
+// Top-k phase on the high halves of the keys: sch[rr * nb + c] holds the top
+// 32 bits of order_key of the float64 score, which is all the LDS has to
+// keep, so two workgroups share a CU.  The bitwise search of
+// select_topk_rows runs over those halves.  Where keys still tie there at the
+// k-th place (scores within 2^-20 of each other, or equal), the float64
+// scores of just the tied blocks are computed again, one lane each, with the
+// features in ascending order (identical key blocks tie exactly again), and
+// the same search over their 64-bit keys takes the rest; exact ties go lowest
+// index first, and so do tied sink blocks.  Top-k mode only.
+__device__ __forceinline__ double dot_f64(const float* a, const float* b) {
+  double s = 0.0;
+#pragma unroll 2
+  for (int f = 0; f < HD; f += 4) {
+    const float4 x = *(const float4*)(a + f), y = *(const float4*)(b + f);
+    s = fma((double)x.x, (double)y.x, s);
+    s = fma((double)x.y, (double)y.y, s);
+    s = fma((double)x.z, (double)y.z, s);
+    s = fma((double)x.w, (double)y.w, s);
+  }
+  return s;
+}
+
+// The m-th largest of the 64-bit keys (1 <= m <= number of nonzero keys; key
+// of block c in lane c % 64 of slot c / 64); exact is set when exactly m keys
+// are >= the result, else the result is that key itself.
+template <int NCH>
+__device__ __forceinline__ uint64_t kth_key64(const uint64_t (&key)[NCH], int m, bool& exact) {
+  uint32_t th = 0;
+  exact = false;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot((uint32_t)(key[i] >> 32) >= cand));
+    if (cnt >= m) {
+      th = cand;
+      if (cnt == m) {
+        exact = true;
+        return (uint64_t)th << 32;
+      }
+    }
+  }
+  int gt_hi = 0;
+  uint32_t lo[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const uint32_t h = (uint32_t)(key[i] >> 32);
+    gt_hi += __popcll(__ballot(h > th));
+    lo[i] = h == th ? (uint32_t)key[i] : 0u;
+  }
+  uint32_t tl = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tl | (1u << bit);
+    int cnt = gt_hi;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot(lo[i] >= cand));
+    if (cnt >= m) {
+      tl = cand;
+      if (cnt == m) {
+        exact = true;
+        break;
+      }
+    }
+  }
+  return ((uint64_t)th << 32) | tl;
+}
+
+template <int NCH, int NW>
+__device__ __forceinline__ void select_topk_rows_hi(const uint32_t* sch, int r0, size_t bh, const float* qpb,
+                                                    const float* kpb, int32_t* __restrict__ block_idx, int nb,
+                                                    int ksel, int f0, int f1, int tid) {
+  const int w = tid >> 6, lane = tid & 63;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int rr = w; rr < 16; rr += NW) {
+    const int r = r0 + rr;
+    if (r >= nb || ksel == 0) break;
+    const uint32_t* srow = sch + rr * nb;
+    // every high half of a real key is > 0; sink blocks take the largest
+    uint32_t key[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int cc = i * 64 + lane;
+      key[i] = cc >= nb ? 0u : (cc >= f0 && cc <= f1) ? ~0u : srow[cc];
+    }
+    const int kr = min(ksel, nb);
+    int32_t* orow = block_idx + (bh * nb + r) * (size_t)ksel;
+    uint32_t th = 0;
+    bool exact = false;  // exactly kr high halves are >= th
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = th | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+      if (cnt >= kr) {
+        th = cand;
+        if (cnt == kr) {
+          exact = true;
+          break;
+        }
+      }
+    }
+    // th is the k-th largest high half; unless exact, the keys whose high
+    // half is th are ranked by their full keys (sink blocks all alike)
+    uint64_t full[NCH];
+    uint64_t T2 = 0;
+    bool exact2 = true;
+    int need_eq = 0;
+    if (!exact) {
+      int gt = 0;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        gt += __popcll(__ballot(key[i] > th));
+        full[i] = 0;
+        if (key[i] == th) full[i] = th == ~0u ? 1ull : order_key(dot_f64(qpb + (size_t)r * HD, kpb + (size_t)(i * 64 + lane) * HD));
+      }
+      const int need = kr - gt;
+      T2 = kth_key64<NCH>(full, need, exact2);
+      if (!exact2) {
+        int gt2 = 0;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) gt2 += __popcll(__ballot(full[i] > T2));
+        need_eq = need - gt2;  // full keys equal to T2 taken lowest index first
+      }
+    }
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      bool sel;
+      if (exact) {
+        sel = key[i] >= th;
+      } else {
+        const bool is_eq = full[i] == T2;  // T2 > 0, so only tied blocks
+        const uint64_t em = __ballot(is_eq && !exact2);
+        sel = key[i] > th || full[i] > T2 || (is_eq && (exact2 || eq_before + (int)__popcll(em & lt) < need_eq));
+        eq_before += (int)__popcll(em);
+      }
+      const uint64_t sm = __ballot(sel);
+      if (sel) orow[sel_before + __popcll(sm & lt)] = i * 64 + lane;
+      sel_before += __popcll(sm);
+    }
+    for (int j = kr + lane; j < ksel; j += 64) orow[j] = -1;  // unused slots
+  }
+}
+
+// Select on the matrix cores keeping only the high halves of the keys in LDS
+// (16 x nb x 4 bytes): top-k mode from 513 to 1,280 blocks, two workgroups
+// of 8 wavefronts per CU, so one scores while the other ranks.
+template <int NCH>
+__global__ __launch_bounds__(512, 4) void select_mfma_hi_kernel(const float* __restrict__ q_pool,
+                                                               const float* __restrict__ k_pool,
+                                                               int32_t* __restrict__ block_idx, int nb, int ksel,
+                                                               int f0, int f1) {
+  constexpr int RB = 16, NW = 8;
+  extern __shared__ uint32_t sch[];  // [RB][nb]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_rg = (nb + RB - 1) / RB;
+  const int logical = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int r0 = (logical % n_rg) * RB;
+  const size_t bh = (size_t)(logical / n_rg);
+  const float* qpb = q_pool + bh * nb * HD;
+  const float* kpb = k_pool + bh * nb * HD;
+  mfma_scores<NW, true>(qpb, kpb, nb, r0, lane, wave,
+                  [&](int row, int c, double s) { sch[row * nb + c] = (uint32_t)(order_key(s) >> 32); });
+  __syncthreads();
+  select_topk_rows_hi<NCH, NW>(sch, r0, bh, qpb, kpb, block_idx, nb, ksel, f0, f1, tid);
 }
 
 // ------------------------------------------------------------ row order ---
@@ -2023,6 +2203,21 @@ int launch_select_mfma(const Geometry& g, const float* q_pool, const float* k_po
   return launch_status();
 }
 
+template <int NCH>
+int launch_select_mfma_hi(const Geometry& g, const float* q_pool, const float* k_pool, int32_t* block_idx,
+                          hipStream_t stream) {
+  const dim3 grid((unsigned)(((g.nb + 15) / 16) * g.H * g.B));
+  const size_t lds = (size_t)16 * g.nb * sizeof(uint32_t);
+  if (lds > 48 * 1024) {
+    if (hipFuncSetAttribute((const void*)select_mfma_hi_kernel<NCH>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+      return BSA_ERR_HIP;
+  }
+  hipLaunchKernelGGL((select_mfma_hi_kernel<NCH>), grid, dim3(512), lds, stream, q_pool, k_pool, block_idx,
+                     (int)g.nb, (int)g.k, (int)g.f0, (int)g.f1);
+  return launch_status();
+}
+
 // Whether a row can skip a block, i.e. the summary rows take part: top-k
 // with k < nb, or threshold selection (rows keep at most k blocks).
 bool uses_summaries(const Geometry& g) { return g.k < g.nb || g.threshold; }
@@ -2224,11 +2419,16 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   // key blocks per lane (top-k phase) sized to nb.  Scores on the float64
   // matrix cores while 16 score rows fit the LDS (nb <= 1200); past that the
   // row-split VALU score phase (four query rows in registers, whole-line key
-  // loads).  Up to 512 blocks four workgroups of 4 wavefronts share a CU;
-  // past that the score rows take most of the LDS, and one workgroup of 16
-  // wavefronts keeps the CU busy (2K 5s: 0.64 ms against 0.92 with 4)
+  // loads).  Up to 512 blocks four workgroups of 4 wavefronts share a CU.
+  // Past that, top-k keeps only the high halves of the keys in LDS (two
+  // workgroups of 8 wavefronts a CU, one scoring while the other ranks); the
+  // threshold mode needs the float64 rows for its mean and deviation, so one
+  // workgroup of 16 wavefronts keeps the CU busy (2K 5s: 0.64 ms against
+  // 0.92 with 4)
   if (g.nb <= 256) return launch_select_mfma<4, 4>(g, q_pool, k_pool, block_idx, s);
   if (g.nb <= 512) return launch_select_mfma<8, 4>(g, q_pool, k_pool, block_idx, s);
+  if (!g.threshold && g.nb <= 1024) return launch_select_mfma_hi<16>(g, q_pool, k_pool, block_idx, s);
+  if (!g.threshold && g.nb <= 1280) return launch_select_mfma_hi<20>(g, q_pool, k_pool, block_idx, s);
   if (g.nb <= 1024) return launch_select_mfma<16, 16>(g, q_pool, k_pool, block_idx, s);
   if (g.nb <= 1200) return launch_select_mfma<19, 16>(g, q_pool, k_pool, block_idx, s);
   return launch_select<8, 4, true>(g, q_pool, k_pool, block_idx, s);

@@ -227,11 +227,11 @@ def test_threshold_selection(torch_cuda, N, top_k, tau, sink, summary):
 @pytest.mark.parametrize("N", [140000, 166000])
 @pytest.mark.parametrize("variant", ["plain", "ties", "sinks", "threshold"])
 def test_many_blocks_selection(torch_cuda, variant, N):
-    """The selection's large-row forms: up to 1,200 blocks the float64 matrix
-    scores with one 16-wavefront workgroup per 16 query blocks (1,094 blocks,
-    short last block), past that the row-split float64 VALU scores (1,297
-    blocks).  Every index of the head against the oracle, and sampled query
-    blocks."""
+    """The selection's large-row forms at 1,094 blocks (short last block): the
+    float64 matrix scores, with the high key halves in LDS for top-k and the
+    float64 rows of one 16-wavefront workgroup for the threshold; at 1,297
+    blocks the row-split float64 VALU scores.  Every index of the head
+    against the oracle, and sampled query blocks."""
     _log("case many blocks %s N=%d" % (variant, N))
     nb = O.n_blocks(N)
     w = custom(N, heads=1, seed=17)
@@ -254,6 +254,38 @@ def test_many_blocks_selection(torch_cuda, variant, N):
     if variant == "ties":
         s = O.block_scores(O.pool_mean(widen(qb[0, 0])), O.pool_mean(widen(kb[0, 0])))
         assert np.array_equal(host["block_idx"][0, 0].numpy(), O.select_topk(s, 16))
+
+
+@pytest.mark.parametrize("nb", [600, 1094, 1250])
+def test_select_near_ties_past_512_blocks(torch_cuda, nb):
+    """Top-k past 512 blocks keeps only the high 32 bits of each score's key in
+    LDS and ranks the blocks that tie there by their float64 scores computed
+    again.  Pooled vectors made here, through bsa_select: every key block is
+    one vector plus 0..3 float32 ulps on six features, so a row's scores lie
+    within about 1e-6 of each other (most share their high bits, some exactly
+    equal).  The indices must equal the float64 oracle's, ties to the lower
+    index."""
+    torch = torch_cuda
+    _log("case select near ties nb=%d" % nb)
+    rng = np.random.default_rng(nb)
+    qp = rng.standard_normal((nb, 128)).astype(np.float32)
+    base = rng.standard_normal(128).astype(np.float32) + np.float32(4.0)
+    kp = np.repeat(base[None, :], nb, axis=0)
+    feats = rng.choice(128, size=6, replace=False)
+    steps = rng.integers(0, 4, size=(nb, 6))
+    for j, f in enumerate(feats):
+        kp[:, f] = base[f] + steps[:, j].astype(np.float32) * np.spacing(base[f])
+    top_k = 16
+    p = bsa.make_problem(1, 1, nb * 128, top_k=top_k)
+    dq = torch.from_numpy(qp).reshape(1, 1, nb, 128).cuda()
+    dk = torch.from_numpy(kp).reshape(1, 1, nb, 128).cuda()
+    idx = torch.full((1, 1, nb, top_k), -7, dtype=torch.int32, device="cuda")
+    bsa.bsa_select(p, dq, dk, idx)
+    torch.cuda.synchronize()
+    want = O.select_topk(O.block_scores(qp.astype(np.float64), kp.astype(np.float64)), top_k)
+    got = idx[0, 0].cpu().numpy()
+    bad = np.nonzero(np.any(got != want, axis=1))[0]
+    assert bad.size == 0, "rows %s: gpu %s want %s" % (bad[:4], list(got[bad[0]]), list(want[bad[0]]))
 
 
 def test_forward_with_given_indices(torch_cuda):
