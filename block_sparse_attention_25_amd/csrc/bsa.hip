@@ -9,9 +9,9 @@
 //   select_mfma_kernel  float64 block scores on the matrix cores (16 query
 //                     blocks a workgroup) and a wavefront top-k with
 //                     lowest-index ties, ascending output
-//   select_mfma_hi_kernel  the same for top-k past 512 blocks with only the
-//                     high 32 bits of each key in LDS (two workgroups a CU);
-//                     blocks that tie there are ranked by recomputed scores
+//   select_mfma_hi_kernel  the same for top-k with only the high 32 bits of
+//                     each key in LDS (two workgroups a CU); blocks that
+//                     tie there are ranked by recomputed scores
 //   select_kernel     the same with float64 VALU scores, past 1,200 blocks
 //                     (1,280 for top-k)
 //   row_order_kernel  the order in which attention visits a head's query blocks
@@ -852,8 +852,8 @@ __device__ __forceinline__ void select_topk_rows_hi(const uint32_t* sch, int r0,
 }
 
 // Select on the matrix cores keeping only the high halves of the keys in LDS
-// (16 x nb x 4 bytes): top-k mode from 513 to 1,280 blocks, two workgroups
-// of 8 wavefronts per CU, so one scores while the other ranks.
+// (16 x nb x 4 bytes): top-k mode up to 1,280 blocks, two workgroups of 8
+// wavefronts per CU, so one scores while the other ranks.
 template <int NCH>
 __global__ __launch_bounds__(512, 4) void select_mfma_hi_kernel(const float* __restrict__ q_pool,
                                                                const float* __restrict__ k_pool,
@@ -2419,16 +2419,20 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   // key blocks per lane (top-k phase) sized to nb.  Scores on the float64
   // matrix cores while 16 score rows fit the LDS (nb <= 1200); past that the
   // row-split VALU score phase (four query rows in registers, whole-line key
-  // loads).  Up to 512 blocks four workgroups of 4 wavefronts share a CU.
-  // Past that, top-k keeps only the high halves of the keys in LDS (two
-  // workgroups of 8 wavefronts a CU, one scoring while the other ranks); the
-  // threshold mode needs the float64 rows for its mean and deviation, so one
+  // loads).  Top-k keeps only the high halves of the keys in LDS (two
+  // workgroups of 8 wavefronts a CU, one scoring while the other ranks).  The
+  // threshold mode needs the float64 rows for its mean and deviation: up to
+  // 512 blocks four workgroups of 4 wavefronts share a CU, past that one
   // workgroup of 16 wavefronts keeps the CU busy (2K 5s: 0.64 ms against
   // 0.92 with 4)
+  if (!g.threshold) {
+    if (g.nb <= 256) return launch_select_mfma_hi<4>(g, q_pool, k_pool, block_idx, s);
+    if (g.nb <= 512) return launch_select_mfma_hi<8>(g, q_pool, k_pool, block_idx, s);
+    if (g.nb <= 1024) return launch_select_mfma_hi<16>(g, q_pool, k_pool, block_idx, s);
+    if (g.nb <= 1280) return launch_select_mfma_hi<20>(g, q_pool, k_pool, block_idx, s);
+  }
   if (g.nb <= 256) return launch_select_mfma<4, 4>(g, q_pool, k_pool, block_idx, s);
   if (g.nb <= 512) return launch_select_mfma<8, 4>(g, q_pool, k_pool, block_idx, s);
-  if (!g.threshold && g.nb <= 1024) return launch_select_mfma_hi<16>(g, q_pool, k_pool, block_idx, s);
-  if (!g.threshold && g.nb <= 1280) return launch_select_mfma_hi<20>(g, q_pool, k_pool, block_idx, s);
   if (g.nb <= 1024) return launch_select_mfma<16, 16>(g, q_pool, k_pool, block_idx, s);
   if (g.nb <= 1200) return launch_select_mfma<19, 16>(g, q_pool, k_pool, block_idx, s);
   return launch_select<8, 4, true>(g, q_pool, k_pool, block_idx, s);

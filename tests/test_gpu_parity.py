@@ -256,11 +256,11 @@ def test_many_blocks_selection(torch_cuda, variant, N):
         assert np.array_equal(host["block_idx"][0, 0].numpy(), O.select_topk(s, 16))
 
 
-@pytest.mark.parametrize("nb", [600, 1094, 1250])
-def test_select_near_ties_past_512_blocks(torch_cuda, nb):
-    """Top-k past 512 blocks keeps only the high 32 bits of each score's key in
-    LDS and ranks the blocks that tie there by their float64 scores computed
-    again.  Pooled vectors made here, through bsa_select: every key block is
+@pytest.mark.parametrize("nb", [200, 300, 600, 1094, 1250])
+def test_select_near_ties_high_half_keys(torch_cuda, nb):
+    """Top-k keeps only the high 32 bits of each score's key in LDS and ranks
+    the blocks that tie there by their float64 scores computed again (every
+    kernel size up to 1,280 blocks).  Pooled vectors made here, through bsa_select: every key block is
     one vector plus 0..3 float32 ulps on six features, so a row's scores lie
     within about 1e-6 of each other (most share their high bits, some exactly
     equal).  The indices must equal the float64 oracle's, ties to the lower
