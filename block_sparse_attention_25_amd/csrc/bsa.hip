@@ -1522,12 +1522,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 //    its per-row counts, and after a barrier every lane derives positions.
 //  - At the end each list is cut to E and written in ascending token order
 //    (a token's slot is the number of kept tokens below it), -1 after.
+//  - One workgroup per CU (its LDS), so the groups run in rounds of 256.
+//    The groups past the last whole round split their key blocks into up to
+//    8 ranges (parts), so that round fills the chip.  A part runs all of the
+//    above over its own range, samples one block in 6 (so that few blocks
+//    still give a safe threshold) and leaves its E best keys per row in the
+//    workspace.  token_merge_kernel then takes each row's E best over its
+//    parts.  Every score is computed as in a whole group, so the tokens are
+//    the same.
 
 constexpr int TS_ROWS = 32;    // query blocks per workgroup
 constexpr int TS_CAP = 512;    // candidate keys per query block
 constexpr int TS_STRIDE = 12;  // blocks c with c % TS_STRIDE == 3 form the sample
+constexpr int TS_STRIDE_PART = 6;  // the same for a part of a group
 constexpr int TS_SEGS = 8;     // workspace segments per query block in phase 2 (token eighths)
 constexpr int SEG_CAP = 256;   // keys per segment
+constexpr int TS_MAX_PARTS = 8;  // parts a group of the last dispatch round may split into
+constexpr int TS_CUS = 256;      // compute units of the chip: one token-select workgroup each
 
 __device__ __forceinline__ uint32_t order_key32(float s) {
   if (s == 0.f) s = 0.f;  // -0 ties with +0
@@ -1639,6 +1650,31 @@ __device__ uint64_t cut_list(uint64_t* list, int n, int keep, int lane) {
   return write_kept<PER>(list, hi, lo, T, L, exact, lane);
 }
 
+// The tokens of n <= E kept keys in ascending order, -1 after, into orow[0, E).
+// A token's slot is the number of kept tokens below it, i.e. of kept keys
+// with a larger lower half.  One wavefront.
+__device__ void write_tokens(const uint64_t* keys, int n, int E, int32_t* orow, int lane) {
+  uint32_t lo[BSA_MAX_EXTRA / 64];
+  int rank[BSA_MAX_EXTRA / 64];
+#pragma unroll
+  for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) {
+    const int y = lane + 64 * j;
+    lo[j] = y < n ? (uint32_t)keys[y] : 0u;
+    rank[j] = 0;
+  }
+  for (int y = 0; y < n; ++y) {
+    const uint32_t o = (uint32_t)keys[y];
+#pragma unroll
+    for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) rank[j] += o > lo[j];
+  }
+#pragma unroll
+  for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) {
+    const int y = lane + 64 * j;
+    if (y < n) orow[rank[j]] = (int32_t)(0xFFFFFFFFu - lo[j]);
+  }
+  for (int y = n + lane; y < E; y += 64) orow[y] = -1;
+}
+
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1652,7 +1688,9 @@ constexpr int TS_THREADS = 512;
 __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     const float* __restrict__ q_pool, const uint16_t* __restrict__ k,
     const int32_t* __restrict__ block_idx, int32_t* __restrict__ token_idx,
-    uint64_t* __restrict__ gseg, int N, int nb, int krow, int E, int m, int f0, int f1, int total_wg) {
+    uint64_t* __restrict__ gseg, uint64_t* __restrict__ pseg, uint64_t* __restrict__ plist,
+    int32_t* __restrict__ pcount, int N, int nb, int krow, int E, int m_whole, int m_part, int f0, int f1,
+    int n_whole, int parts) {
   // row strides padded by one element, so that lanes of different rows at
   // equal positions fall into different LDS banks
   __shared__ uint64_t list[TS_ROWS][TS_CAP + 1];
@@ -1669,15 +1707,34 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
   __shared__ uint32_t thr[TS_ROWS];
   __shared__ int redo;
 
+  // workgroups [0, n_whole) take whole groups; the rest take one part (a
+  // range of key blocks) each of the last groups, `parts` per group
   const int ngrp = (nb + TS_ROWS - 1) / TS_ROWS;
-  const int logical = xcd_remap(blockIdx.x, total_wg);
+  const int wg = (int)blockIdx.x;
+  const int pidx = wg - n_whole;  // part workgroup index, < 0 for a whole group
+  const int logical = pidx < 0 ? xcd_remap(wg, n_whole) : n_whole + pidx / parts;
+  const int c_lo = pidx < 0 ? 0 : (pidx % parts) * nb / parts;
+  const int c_hi = pidx < 0 ? nb : (pidx % parts + 1) * nb / parts;
+  const int nbr = c_hi - c_lo;  // key blocks this workgroup visits
   const int r0 = (logical % ngrp) * TS_ROWS;
   const size_t bh = (size_t)(logical / ngrp);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, q4 = lane >> 4;
   const int nwords = (nb + 31) >> 5;
-  const int n1 = m > 0 ? (nb + TS_STRIDE - 4) / TS_STRIDE : 0;  // sample blocks
+  // sample blocks c % S == 3 below c: S = TS_STRIDE for a whole group, the
+  // denser TS_STRIDE_PART for a part (its range holds few blocks, and a
+  // sample of a few blocks misjudges a row's threshold more often), each with
+  // its own m
+  const int S = pidx < 0 ? TS_STRIDE : TS_STRIDE_PART;
+  const int m = pidx < 0 ? m_whole : m_part;
+  auto n_sample_below = [&](int c) { return (c + S - 4) / S; };
+  const int n1 = m > 0 ? n_sample_below(c_hi) - n_sample_below(c_lo) : 0;  // sample blocks
+  // workspace segments of row xr of the group (TS_SEGS x SEG_CAP keys)
+  auto seg_row = [&](int xr) {
+    return pidx < 0 ? gseg + (bh * nb + (size_t)min(r0 + xr, nb - 1)) * TS_SEGS * SEG_CAP
+                    : pseg + ((size_t)pidx * TS_ROWS + xr) * TS_SEGS * SEG_CAP;
+  };
 
   // candidates of row r0 + i: the blocks it did not keep; none for a sink
   // query block (it attends to every block exactly) or past the last row
@@ -1685,8 +1742,9 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     const int i = x / nwords, wd = x % nwords, r = r0 + i;
     uint32_t mk = 0u;
     if (r < nb && !(r >= f0 && r <= f1)) {
-      const int left = nb - 32 * wd;
-      mk = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+      // the bits of blocks [c_lo, c_hi) in word wd
+      const int lo = max(c_lo - 32 * wd, 0), hi = min(c_hi - 32 * wd, 32);
+      if (hi > lo) mk = (hi == 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
     }
     skip[i][wd] = mk;
   }
@@ -1697,12 +1755,12 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
     tm[tid] = 0ull;
   }
   if (tid == 0) redo = 0;
-  // visiting order: the sample blocks (c % TS_STRIDE == 3) first, then the
-  // others, each in block order
-  for (int c = tid; c < nb; c += TS_THREADS) {
-    const bool smp = n1 > 0 && c % TS_STRIDE == 3;
-    const int below = n1 > 0 ? (c + TS_STRIDE - 4) / TS_STRIDE : 0;  // sample blocks < c
-    order[smp ? c / TS_STRIDE : n1 + c - below] = (uint16_t)c;
+  // visiting order of the blocks [c_lo, c_hi): the sample blocks (c % S ==
+  // 3) first, then the others, each in block order
+  for (int c = c_lo + tid; c < c_hi; c += TS_THREADS) {
+    const bool smp = n1 > 0 && c % S == 3;
+    const int below = n1 > 0 ? n_sample_below(c) - n_sample_below(c_lo) : 0;  // sample blocks in [c_lo, c)
+    order[smp ? below : n1 + (c - c_lo) - below] = (uint16_t)c;
   }
   __syncthreads();
   for (int x = tid; x < TS_ROWS * krow; x += TS_THREADS) {
@@ -1926,15 +1984,15 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       for (int h = 0; h < 2; ++h) {
         const uint32_t th = (uint32_t)(tm[16 * h + l16] >> 32);
         thr_f[h] = th == 0u ? -INFINITY : (th >> 31) ? __uint_as_float(th & 0x7FFFFFFFu) : __uint_as_float(~th);
-        seg[h] = gseg + ((bh * nb + (size_t)min(r0 + 16 * h + l16, nb - 1)) * TS_SEGS + te) * SEG_CAP;
+        seg[h] = seg_row(16 * h + l16) + te * SEG_CAP;
       }
       auto fstep = [&](int i, const f32x4* acc, f32x4* accn, const uint4* kn, uint4* kl) {
         mfma_rows(kn, accn, qh);
         __builtin_amdgcn_sched_barrier(0);
-        load8((int)order[min(max(i + 3, n1), nb - 1)], kl);
-        const int c = order[min(max(i, n1), nb - 1)];
+        load8((int)order[min(max(i + 3, n1), nbr - 1)], kl);
+        const int c = order[min(max(i, n1), nbr - 1)];
         const int tb = c * BLK + 32 * q4 + te;  // value v: token tb + 8 v
-        const bool in_range = i >= n1 && i < nb;
+        const bool in_range = i >= n1 && i < nbr;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int xr = 16 * h + l16;
@@ -1969,7 +2027,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
       uint4 kA[4], kB[4], kC[4], kD[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) kA[j] = kB[j] = kC[j] = kD[j] = make_uint4(0u, 0u, 0u, 0u);
-      for (int i = n1 - 3; i < nb; i += 4) {
+      for (int i = n1 - 3; i < nbr; i += 4) {
         fstep(i, accA, accB, kB, kD);
         fstep(i + 1, accB, accA, kC, kA);
         fstep(i + 2, accA, accB, kD, kB);
@@ -2002,7 +2060,7 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
           constexpr int PER = LPER + TS_SEGS * SPER;
           uint32_t hi[PER], lo[PER];
           const uint64_t tmx = tm[x];
-          const uint64_t* sb = gseg + (bh * nb + (size_t)r) * TS_SEGS * SEG_CAP;
+          const uint64_t* sb = seg_row(x);
           int nge_l = 0;
 #pragma unroll
           for (int j = 0; j < PER; ++j) {
@@ -2057,44 +2115,74 @@ __global__ __launch_bounds__(TS_THREADS, 1) void token_select_kernel(
         tm[tid] = 0ull;
       }
       __syncthreads();
-      sweep(0, nb, E);
+      sweep(0, nbr, E);
     }
   } else {
-    // small E: no sample, one list-and-cut sweep over every block
-    sweep(0, nb, E);
+    // small E (or a part without sample blocks): one list-and-cut sweep over
+    // every block
+    sweep(0, nbr, E);
   }
 
   for (int x = wave; x < TS_ROWS; x += TS_THREADS / 64) {
     const int r = r0 + x;
     if (r >= nb) break;
-    int32_t* orow = token_idx + (bh * nb + r) * (size_t)E;
     int n = cnt[0][x];
     if (n > E) {
       cut_list(list[x], n, E, lane);
       n = E;
     }
-    // output slot of a kept token = number of kept tokens below it, i.e. of
-    // kept keys with a larger lower half
-    uint32_t lo[BSA_MAX_EXTRA / 64];
-    int rank[BSA_MAX_EXTRA / 64];
-#pragma unroll
-    for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) {
-      const int y = lane + 64 * j;
-      lo[j] = y < n ? (uint32_t)list[x][y] : 0u;
-      rank[j] = 0;
+    if (pidx < 0) {
+      write_tokens(list[x], n, E, token_idx + (bh * nb + r) * (size_t)E, lane);
+    } else {
+      // a part: its E best keys, for token_merge_kernel
+      uint64_t* prow = plist + ((size_t)pidx * TS_ROWS + x) * E;
+      for (int y = lane; y < n; y += 64) prow[y] = list[x][y];
+      if (lane == 0) pcount[pidx * TS_ROWS + x] = n;
     }
-    for (int y = 0; y < n; ++y) {
-      const uint32_t o = (uint32_t)list[x][y];
-#pragma unroll
-      for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) rank[j] += o > lo[j];
-    }
-#pragma unroll
-    for (int j = 0; j < BSA_MAX_EXTRA / 64; ++j) {
-      const int y = lane + 64 * j;
-      if (y < n) orow[rank[j]] = (int32_t)(0xFFFFFFFFu - lo[j]);
-    }
-    for (int y = n + lane; y < E; y += 64) orow[y] = -1;
   }
+}
+
+// One query block of the last groups: the E best keys of its parts' lists
+// (disjoint key ranges, so every key is distinct), written as tokens in
+// ascending order.  One wavefront a row, 8 rows a workgroup.
+__global__ __launch_bounds__(512) void token_merge_kernel(const uint64_t* __restrict__ plist,
+                                                          const int32_t* __restrict__ pcount,
+                                                          int32_t* __restrict__ token_idx, int nb, int E,
+                                                          int n_whole, int parts, int n_rows) {
+  constexpr int EPL = BSA_MAX_EXTRA / 64, PER = TS_MAX_PARTS * EPL;
+  __shared__ uint64_t kept[8][BSA_MAX_EXTRA];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int xa = blockIdx.x * 8 + wave;  // row slot over the last groups
+  if (xa >= n_rows) return;
+  const int ngrp = (nb + TS_ROWS - 1) / TS_ROWS;
+  const int logical = n_whole + xa / TS_ROWS, x = xa % TS_ROWS;
+  const int r = (logical % ngrp) * TS_ROWS + x;
+  if (r >= nb) return;
+  const size_t bh = (size_t)(logical / ngrp);
+  uint32_t hi[PER], lo[PER];
+  int total = 0;
+#pragma unroll
+  for (int q = 0; q < TS_MAX_PARTS; ++q) {
+    const int pidx = (xa / TS_ROWS) * parts + q;
+    const int n = q < parts ? pcount[pidx * TS_ROWS + x] : 0;
+    const uint64_t* prow = plist + ((size_t)pidx * TS_ROWS + x) * E;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int y = lane + 64 * j;
+      const uint64_t kv = y < n ? prow[y] : 0ull;
+      hi[q * EPL + j] = (uint32_t)(kv >> 32);
+      lo[q * EPL + j] = (uint32_t)kv;
+    }
+    total += n;
+  }
+  const int keep = min(E, total);
+  if (keep > 0) {
+    uint32_t T, L;
+    bool exact;
+    top_keys<PER>(hi, lo, keep, T, L, exact);
+    write_kept<PER>(kept[wave], hi, lo, T, L, exact, lane);
+  }
+  write_tokens(kept[wave], keep, E, token_idx + (bh * nb + r) * (size_t)E, lane);
 }
 
 // ------------------------------------------------------------------ host ---
@@ -2116,14 +2204,39 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 //   pool (reweight only): float64 anchor partial sums [B, H, nb, 128], then
 //     the anchor [B, H, 128] at pool_anchor_off();
 //   forward: the visiting order of each head's query blocks, int32 [B, H, nb];
-//   select_tokens: key segments, u64 [B, H, nb, TS_SEGS, SEG_CAP].
+//   select_tokens: key segments, u64 [B, H, nb, TS_SEGS, SEG_CAP]; then, when
+//     the last groups split into parts (token_split), each part's segments
+//     u64 [parts total, TS_ROWS, TS_SEGS, SEG_CAP], its E best keys per row
+//     u64 [parts total, TS_ROWS, E] and their counts int32 [parts total,
+//     TS_ROWS].
 size_t pool_anchor_off(const Geometry& g) { return align256((size_t)(g.B * g.H * g.nb) * HD * sizeof(double)); }
 size_t pool_ws(const Geometry& g) {
   return g.reweight ? pool_anchor_off(g) + align256((size_t)(g.B * g.H) * HD * sizeof(double)) : 0;
 }
 size_t forward_ws(const Geometry& g) { return align256((size_t)(g.B * g.H * g.nb) * sizeof(int32_t)); }
+// Token selection runs one workgroup per CU; groups of TS_ROWS query blocks
+// past the last whole dispatch round split their key blocks into `parts`
+// ranges (a workgroup each, merged by token_merge_kernel), so that the last
+// round fills the chip.  The first n_whole groups run whole.
+void token_split(const Geometry& g, int* n_whole, int* parts) {
+  const int G = (int)(((g.nb + TS_ROWS - 1) / TS_ROWS) * g.H * g.B);
+  const int tail = G > TS_CUS ? G % TS_CUS : 0;
+  int P = tail > 0 ? std::min(TS_MAX_PARTS, std::min(TS_CUS / tail, (int)g.nb)) : 1;
+  if (P < 2) P = 1;
+  *parts = P;
+  *n_whole = P > 1 ? G - tail : G;
+}
+size_t tokens_seg_bytes(const Geometry& g) {
+  return align256((size_t)(g.B * g.H * g.nb) * TS_SEGS * SEG_CAP * sizeof(uint64_t));
+}
 size_t tokens_ws(const Geometry& g) {
-  return g.E > 0 ? align256((size_t)(g.B * g.H * g.nb) * TS_SEGS * SEG_CAP * sizeof(uint64_t)) : 0;
+  if (g.E == 0) return 0;
+  int n_whole, parts;
+  token_split(g, &n_whole, &parts);
+  const size_t G = (size_t)((g.nb + TS_ROWS - 1) / TS_ROWS) * g.H * g.B;
+  const size_t prow = parts > 1 ? (G - n_whole) * parts * TS_ROWS : 0;  // part rows
+  return tokens_seg_bytes(g) + align256(prow * TS_SEGS * SEG_CAP * sizeof(uint64_t)) +
+         align256(prow * g.E * sizeof(uint64_t)) + align256(prow * sizeof(int32_t));
 }
 size_t ws_total(const Geometry& g) { return std::max(pool_ws(g), std::max(forward_ws(g), tokens_ws(g))); }
 
@@ -2480,12 +2593,25 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
   if (!workspace || workspace_bytes < tokens_ws(g) || ((uintptr_t)workspace & 255u)) return BSA_ERR_WORKSPACE;
   // sample size of the first phase: T_m lands near the 2E- to 3E-th score,
   // with a margin for samples that are not random (small E: no sample)
-  const double S = TS_STRIDE;
-  const int m = g.E >= 64 ? std::min(g.E, (int)ceil(g.E / S + 8.0 * sqrt(g.E / S))) : 0;
-  const int total = (int)(((g.nb + TS_ROWS - 1) / TS_ROWS) * g.H * g.B);
-  hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)total), dim3(TS_THREADS), 0, (hipStream_t)hip_stream,
-                     q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx, (uint64_t*)workspace,
-                     (int)g.N, (int)g.nb, (int)g.k, g.E, m, (int)g.f0, (int)g.f1, total);
+  auto sample_m = [&](double S) { return g.E >= 64 ? std::min(g.E, (int)ceil(g.E / S + 8.0 * sqrt(g.E / S))) : 0; };
+  const int G = (int)(((g.nb + TS_ROWS - 1) / TS_ROWS) * g.H * g.B);
+  int n_whole, parts;
+  token_split(g, &n_whole, &parts);
+  const int tail = G - n_whole;
+  const size_t prow = (size_t)tail * parts * TS_ROWS;
+  char* ws = (char*)workspace;
+  uint64_t* pseg = (uint64_t*)(ws + tokens_seg_bytes(g));
+  uint64_t* plist = (uint64_t*)((char*)pseg + align256(prow * TS_SEGS * SEG_CAP * sizeof(uint64_t)));
+  int32_t* pcount = (int32_t*)((char*)plist + align256(prow * g.E * sizeof(uint64_t)));
+  hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)(n_whole + tail * parts)), dim3(TS_THREADS), 0,
+                     (hipStream_t)hip_stream, q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx,
+                     (uint64_t*)workspace, pseg, plist, pcount, (int)g.N, (int)g.nb, (int)g.k, g.E,
+                     sample_m(TS_STRIDE), sample_m(TS_STRIDE_PART), (int)g.f0, (int)g.f1, n_whole, parts);
+  if (parts > 1) {
+    const int rows = tail * TS_ROWS;
+    hipLaunchKernelGGL(token_merge_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(512), 0, (hipStream_t)hip_stream,
+                       plist, pcount, token_idx, (int)g.nb, g.E, n_whole, parts, rows);
+  }
   return launch_status();
 }
 

@@ -542,6 +542,23 @@ def test_extra_tokens(torch_cuda, N, top_k, E, sink, summary, tau):
                     sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau, extra=E)
 
 
+@pytest.mark.parametrize("N,heads,check", [
+    (4200, 129, (0, 127, 128)),   # 258 groups: the last 2 split into 8 parts of 4-5 blocks
+    (9000, 90, (0, 85, 89)),      # 270 groups: the last 14 (from head 85 on) in 8 parts of ~9 blocks
+])
+def test_extra_tokens_split_groups(torch_cuda, N, heads, check):
+    """Token selection runs one workgroup per CU; the groups of 32 query
+    blocks past the last whole round split their key blocks into parts whose
+    best keys a merge kernel combines.  Every row of heads on both sides of
+    that line against the oracle."""
+    _log("case extra tokens, split groups N=%d heads=%d" % (N, heads))
+    w = custom(N, heads=heads, seed=N + heads)
+    qb, kb, vb = generate(w, threads=16)
+    host = _run_gpu(torch_cuda, qb, kb, vb, top_k=16, extra_tokens=256)
+    for h in check:
+        _check_head(host, qb, kb, vb, 0, h, 16, label="split%d-h%d" % (N, h), extra=256)
+
+
 def test_extra_token_ties_take_lower_index(torch_cuda):
     """300 copies of one strong key row in blocks 20..31 tie bit-exactly: where
     the E-th place falls among the copies, the lowest copies must win."""
