@@ -496,10 +496,23 @@ __device__ __forceinline__ bool rb_better(double t, int r, double bt, int br) {
   return t > bt || (t == bt && r < br);
 }
 
-__device__ __forceinline__ double rb_wave_sum(double x) {
+// Sums over the wavefront of eight per-lane values x[u] at once: lane l ends
+// with the sum of x[u], u = (l >> 3) & 7 (its bits 5, 4, 3).  Each sum pairs
+// lanes as a plain butterfly does (lane ^ 32 first, then ^ 16, ..., ^ 1),
+// so it has the same bits, with 10 exchanges instead of 48: at the first
+// three steps a lane keeps the half of its values its bit selects and adds
+// the partner's copy of that half.
+__device__ __forceinline__ double rb_wave_sum8(const double (&x)[8], int lane) {
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+  double a[4], b[2];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  for (int k = 0; k < 4; ++k) a[k] = (b5 ? x[4 + k] : x[k]) + __shfl_xor(b5 ? x[k] : x[4 + k], 32, 64);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) b[k] = (b4 ? a[2 + k] : a[k]) + __shfl_xor(b4 ? a[k] : a[2 + k], 16, 64);
+  double c = (b3 ? b[1] : b[0]) + __shfl_xor(b3 ? b[0] : b[1], 8, 64);
+#pragma unroll
+  for (int off = 4; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  return c;
 }
 
 // One workgroup of 4 wavefronts per (slice, batch x head): the squared
@@ -535,6 +548,7 @@ __global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ z
   }
   const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
   const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
+  const int mu = (lane >> 3) & 7;  // the row of each group of 8 rows whose sum this lane ends with
   double bt = -1.0;
   int br = 0x7fffffff;
 #pragma unroll
@@ -546,14 +560,29 @@ __global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ z
       r[u] = __builtin_amdgcn_readlane(myrow, i0 + u);
       v[u] = *(const float2*)(zb + (size_t)r[u] * RB_HD + 2 * lane);
     }
+    double d[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const double dx = (double)v[u].x - v0, dy = (double)v[u].y - v1;
-      const double t = rb_wave_sum(dx * dx + dy * dy);
-      if (wave + 4 * (i0 + u) < cnt && rb_better(t, r[u], bt, br)) {
-        bt = t;
-        br = r[u];
-      }
+      d[u] = dx * dx + dy * dy;
+    }
+    const double t = rb_wave_sum8(d, lane);
+    int rm = r[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) rm = mu == u ? r[u] : rm;
+    if (wave + 4 * (i0 + mu) < cnt && rb_better(t, rm, bt, br)) {
+      bt = t;
+      br = rm;
+    }
+  }
+  // the wavefront's farthest row: a total order, so any pairing gives it
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ot = __shfl_xor(bt, off, 64);
+    const int orr = __shfl_xor(br, off, 64);
+    if (rb_better(ot, orr, bt, br)) {
+      bt = ot;
+      br = orr;
     }
   }
   if (lane == 0) {
@@ -630,6 +659,7 @@ __global__ __launch_bounds__(256) void rb_keys_kernel(const float* __restrict__ 
   const double w0 = (double)zbb.x - (double)za.x, w1 = (double)zbb.y - (double)za.y;
   const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
   const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
+  const int mu = (lane >> 3) & 7;  // the row of each group of 8 rows whose sum this lane ends with
 #pragma unroll
   for (int i0 = 0; i0 < 32; i0 += 8) {
     float2 v[8];
@@ -638,12 +668,12 @@ __global__ __launch_bounds__(256) void rb_keys_kernel(const float* __restrict__ 
       const int r = __builtin_amdgcn_readlane(myrow, i0 + u);
       v[u] = *(const float2*)(zb + (size_t)r * RB_HD + 2 * lane);
     }
+    double x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const double key = rb_wave_sum((double)v[u].x * w0 + (double)v[u].y * w1);
-      const int pos = wave + 4 * (i0 + u);
-      if (lane == 0 && pos < cnt) keys[bh * N + p0 + pos] = rb_key((float)key);
-    }
+    for (int u = 0; u < 8; ++u) x[u] = (double)v[u].x * w0 + (double)v[u].y * w1;
+    const double key = rb_wave_sum8(x, lane);
+    const int pos = wave + 4 * (i0 + mu);
+    if ((lane & 7) == 0 && pos < cnt) keys[bh * N + p0 + pos] = rb_key((float)key);
   }
 }
 
