@@ -323,14 +323,15 @@ __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t*
 }
 
 // ------------------------------------------------------------- level ---
-// One level of the bisection in two kernels.  rb_stats_kernel sums z and z^2
-// per coordinate over each 128-position slice of the current order (groups
-// start on multiples of 128, so a slice lies in one group), for the root and
-// the left children only; rb_split_kernel takes one group per workgroup, adds
-// its slices' sums in slice order (a right child: its left sibling's, taken
-// from the parent's totals), keeps the group's totals for its own children,
-// picks the split coordinate, selects the split value and partitions the rows.
-// Reading only the left children's rows halves the level's traffic.
+// One level of the bisection.  rb_stats_kernel sums z per coordinate over
+// each 128-position slice of the current order (groups start on multiples of
+// 128, so a slice lies in one group), for the root and the left children
+// only; rb_center_kernel adds a group's slices in slice order (a right child:
+// its parent's totals, kept from the level before, less its left sibling's
+// slices) into its totals and centroid.  Reading only the left children's
+// rows halves the sums' traffic.  Then the two pivots (rb_far_kernel and
+// rb_pivot_kernel, twice), the keys (rb_keys_kernel) and the split
+// (rb_split_*_kernel).
 
 // the group [s, s + n) that holds position pos after `level` splits (the
 // tree's shape depends on N only); a finished leaf keeps its range.  right:
