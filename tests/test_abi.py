@@ -74,6 +74,36 @@ def test_blocks_and_workspace():
     assert bsa.lib().bsa_workspace_bytes(ctypes.byref(bad)) == 0
 
 
+@pytest.mark.parametrize("heads,seq_len,tail_parts", [
+    (56, 37740, (48, 5)),   # 560 groups of 32 query blocks: the last 48 in 5 parts each
+    (2, 4096, (0, 1)),      # fewer groups than CUs: all whole
+    (512, 4096, (0, 1)),    # 512 groups: two full rounds, nothing to split
+    (456, 4096, (0, 1)),    # 200 in the last round: 256 // 200 = 1 part, nothing to split
+    (257, 300, (1, 3)),     # one group left over, its 3 blocks cap the parts
+    (129, 4200, (2, 8)),    # two groups left over, at most 8 parts
+])
+def test_token_selection_workspace_with_split_groups(heads, seq_len, tail_parts):
+    """Token selection runs one workgroup per CU (256 of them); the groups of
+    the last round (G mod 256, when there are more than 256 groups) split
+    their key blocks into min(8, 256 // tail, nb) parts if that is at least
+    2, and each part keeps segments, a list of E keys and a count per row in
+    the workspace after the whole groups' segments."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    E = 256
+    p = _prob(heads=heads, seq_len=seq_len, top_k=8, extra_tokens=E)
+    nb = -(-seq_len // 128)
+    groups = -(-nb // 32) * heads
+    tail = groups % 256 if groups > 256 else 0
+    parts = min(8, 256 // tail, nb) if tail else 1
+    if parts < 2:
+        tail, parts = 0, 1
+    assert (tail, parts) == tail_parts
+    rows = tail * parts * 32
+    want = a256(heads * nb * 8 * 256 * 8) + a256(rows * 8 * 256 * 8) + a256(rows * E * 8) + a256(rows * 4)
+    assert bsa.bsa_workspace_bytes(p) == want
+
+
 def test_struct_layout_matches_header():
     """The ctypes mirror has the header's fields, in order, with the
     header's size (14 four-byte fields)."""
