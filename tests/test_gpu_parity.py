@@ -542,21 +542,22 @@ def test_extra_tokens(torch_cuda, N, top_k, E, sink, summary, tau):
                     sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau, extra=E)
 
 
-@pytest.mark.parametrize("N,heads,check", [
-    (4200, 129, (0, 127, 128)),   # 258 groups: the last 2 split into 8 parts of 4-5 blocks
-    (9000, 90, (0, 85, 89)),      # 270 groups: the last 14 (from head 85 on) in 8 parts of ~9 blocks
+@pytest.mark.parametrize("N,batch,heads,check", [
+    (4200, 1, 129, ((0, 0), (0, 127), (0, 128))),  # 258 groups: the last 2 split into 8 parts of 4-5 blocks
+    (9000, 1, 90, ((0, 0), (0, 85), (0, 89))),     # 270 groups: the last 14 (from head 85 on) in 8 parts of ~9 blocks
+    (4200, 2, 65, ((0, 0), (1, 63), (1, 64))),     # 260 groups over two batch entries: the last 4 (b 1, h 63 and 64) split
 ])
-def test_extra_tokens_split_groups(torch_cuda, N, heads, check):
+def test_extra_tokens_split_groups(torch_cuda, N, batch, heads, check):
     """Token selection runs one workgroup per CU; the groups of 32 query
     blocks past the last whole round split their key blocks into parts whose
     best keys a merge kernel combines.  Every row of heads on both sides of
     that line against the oracle."""
-    _log("case extra tokens, split groups N=%d heads=%d" % (N, heads))
-    w = custom(N, heads=heads, seed=N + heads)
+    _log("case extra tokens, split groups N=%d batch=%d heads=%d" % (N, batch, heads))
+    w = custom(N, heads=heads, batch=batch, seed=N + heads + batch)
     qb, kb, vb = generate(w, threads=16)
     host = _run_gpu(torch_cuda, qb, kb, vb, top_k=16, extra_tokens=256)
-    for h in check:
-        _check_head(host, qb, kb, vb, 0, h, 16, label="split%d-h%d" % (N, h), extra=256)
+    for b, h in check:
+        _check_head(host, qb, kb, vb, b, h, 16, label="split%d-b%dh%d" % (N, b, h), extra=256)
 
 
 def test_extra_token_ties_take_lower_index(torch_cuda):
