@@ -29,15 +29,19 @@
 //                       three bf16 terms whose sum is the float32 value of
 //                       each entry
 //   rb_embed_kernel     z = Q L on the matrix cores (three terms), each row
-//                       normalised (float32); the identity order
+//                       normalised (float32, and a float16 copy); the
+//                       identity order
 //   per level of the bisection:
 //   rb_stats_kernel     float64 sums of z per coordinate over 128-position
 //                       slices of the root and of left children (a right
 //                       child's sums are its parent's less its left sibling's)
 //   rb_center_kernel    per group: its totals and centroid
-//   rb_far_kernel       per slice: the row farthest from the group's centroid
-//                       (then from its first pivot), float64 distances
-//   rb_pivot_kernel     per group: the farthest of its slices' rows
+//   rb_far16_kernel     per slice: each row's distance from the group's
+//                       centroid (then from its first pivot) from the float16
+//                       copy of z, and the slice's largest
+//   rb_pivot_kernel     per group: the rows within the float16 error bound of
+//                       the largest, their float64 distances from the float32
+//                       z, the farthest (lowest row on ties)
 //   rb_keys_kernel      per slice: each row's split key z_i . (z_b - z_a)
 //   rb_split_*_kernel   per group: the split value of the keys (a radix
 //                       select, or a bitwise search for small groups), a
@@ -69,6 +73,12 @@ __device__ __forceinline__ uint16_t rb_f2bf(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// two floats -> float16 bits (round to nearest even), the first in the low half
+__device__ __forceinline__ uint32_t rb_half2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
 // order-preserving key of a float (-0 and +0 equal)
@@ -251,6 +261,7 @@ constexpr int EM_WAVES = 8;
 __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ ltw,
                                                                  float* __restrict__ zh,
+                                                                 uint16_t* __restrict__ zl,
                                                                  int32_t* __restrict__ order0, int N,
                                                                  int ntile) {
   __shared__ __attribute__((aligned(16))) uint16_t lb[3 * RB_HD * RB_HD];
@@ -279,6 +290,7 @@ __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t*
     for (int s = 0; s < 8; ++s) dst[s] = *(const uint4*)(qr + 16 * s + 8 * g);
   };
   float* zb = zh + bh * (size_t)N * RB_HD;
+  uint16_t* zlb = zl + bh * (size_t)N * RB_HD;
   uint4 bq[8], bn[8];
   int t = wave;
   if (t < ntl) load_b(t, bq);
@@ -310,12 +322,16 @@ __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t*
     const int row = row0 + 32 * t + ln;
     if (row < N) {
       float* zr = zb + (size_t)row * RB_HD + 4 * g;
+      uint16_t* zlr = zlb + (size_t)row * RB_HD + 4 * g;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *(float4*)(zr + 32 * mt + 8 * j) = make_float4(acc[mt][4 * j] * inv, acc[mt][4 * j + 1] * inv,
-                                                         acc[mt][4 * j + 2] * inv, acc[mt][4 * j + 3] * inv);
+        for (int j = 0; j < 4; ++j) {
+          const float4 f = make_float4(acc[mt][4 * j] * inv, acc[mt][4 * j + 1] * inv, acc[mt][4 * j + 2] * inv,
+                                       acc[mt][4 * j + 3] * inv);
+          *(float4*)(zr + 32 * mt + 8 * j) = f;
+          *(uint2*)(zlr + 32 * mt + 8 * j) = make_uint2(rb_half2(f.x, f.y), rb_half2(f.z, f.w));
+        }
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) bq[s] = bn[s];
@@ -329,7 +345,7 @@ __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t*
 // only; rb_center_kernel adds a group's slices in slice order (a right child:
 // its parent's totals, kept from the level before, less its left sibling's
 // slices) into its totals and centroid.  Reading only the left children's
-// rows halves the sums' traffic.  Then the two pivots (rb_far_kernel and
+// rows halves the sums' traffic.  Then the two pivots (rb_far16_kernel and
 // rb_pivot_kernel, twice), the keys (rb_keys_kernel) and the split
 // (rb_split_*_kernel).
 
@@ -503,32 +519,47 @@ __device__ __forceinline__ bool rb_better(double t, int r, double bt, int br) {
 // so it has the same bits, with 10 exchanges instead of 48: at the first
 // three steps a lane keeps the half of its values its bit selects and adds
 // the partner's copy of that half.
-__device__ __forceinline__ double rb_wave_sum8(const double (&x)[8], int lane) {
+template <typename T>
+__device__ __forceinline__ T rb_wave_sum8(const T (&x)[8], int lane) {
   const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
-  double a[4], b[2];
+  T a[4], b[2];
 #pragma unroll
   for (int k = 0; k < 4; ++k) a[k] = (b5 ? x[4 + k] : x[k]) + __shfl_xor(b5 ? x[k] : x[4 + k], 32, 64);
 #pragma unroll
   for (int k = 0; k < 2; ++k) b[k] = (b4 ? a[2 + k] : a[k]) + __shfl_xor(b4 ? a[k] : a[2 + k], 16, 64);
-  double c = (b3 ? b[1] : b[0]) + __shfl_xor(b3 ? b[0] : b[1], 8, 64);
+  T c = (b3 ? b[1] : b[0]) + __shfl_xor(b3 ? b[0] : b[1], 8, 64);
 #pragma unroll
   for (int off = 4; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
   return c;
 }
 
-// One workgroup of 4 wavefronts per (slice, batch x head): the squared
-// distance, in float64, of each row of the slice from the group's centroid
-// (FROM_PIVOT false) or from its first pivot's z row (FROM_PIVOT true), and
-// the farthest row of the slice (lowest row on ties).  Wavefront w takes
-// positions w + 4 i, lane l coordinates 2 l and 2 l + 1.
+// Pivot search, two stages.  The farthest row is first looked for in the
+// float16 copy of z: with RNE rounding each coordinate moves by at most 2^-11
+// of itself (2^-25 below the normal range), so a unit row moves by at most
+// 4.9e-4, and as every row and the reference (the centroid, or the first
+// pivot's row) lie within distance 2 of each other, a squared distance moves
+// by at most 2 * 2 * 4.9e-4 + 3e-7 plus the float32 sum's rounding (below
+// 1e-5): under 2.1e-3.  RB_FAR_EPS takes twice that.  The farthest row by the
+// float64 distance from the float32 z, which defines the pivot, is then among
+// the rows within 2 RB_FAR_EPS of the largest float16 distance; only those
+// rows are measured again exactly (on the 768p inputs one to nine per group).
+constexpr float RB_FAR_EPS = 4.2e-3f;
+constexpr int RB_CAND = 2048;  // more rows in the band: every row of the group is measured exactly
+
+// Stage one, one workgroup of 4 wavefronts per (slice, batch x head): the
+// squared distance, in float32 from the float16 copy of z, of each row of the
+// slice from the group's centroid (FROM_PIVOT false) or from its first pivot's
+// z row (FROM_PIVOT true), at the row's position in dt, and the slice's
+// largest in best_t.  Wavefront w takes positions w + 4 i, lane l coordinates
+// 2 l and 2 l + 1, eight rows per exchange sequence.
 template <bool FROM_PIVOT>
-__global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ zh, const int32_t* __restrict__ pin,
-                                                     const double* __restrict__ cen,
-                                                     const int32_t* __restrict__ piv,
-                                                     double* __restrict__ best_t, int32_t* __restrict__ best_r,
-                                                     int N, int nb, int level) {
-  __shared__ double wt[4];
-  __shared__ int wr[4];
+__global__ __launch_bounds__(256) void rb_far16_kernel(const uint16_t* __restrict__ zl,
+                                                       const float* __restrict__ zh,
+                                                       const int32_t* __restrict__ pin,
+                                                       const double* __restrict__ cen,
+                                                       const int32_t* __restrict__ piv, float* __restrict__ dt,
+                                                       double* __restrict__ best_t, int N, int nb, int level) {
+  __shared__ float wm[4];
   const int c = blockIdx.x % nb;
   const size_t bh = blockIdx.x / nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -537,9 +568,97 @@ __global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ z
   rb_group_of(N, level, c * RB_BLK, s, n, right);
   if (n <= RB_BLK) return;  // a leaf
   const size_t g0 = bh * nb + s / RB_BLK;
+  const uint16_t* zlb = zl + bh * (size_t)N * RB_HD;
+  float v0, v1;
+  if (FROM_PIVOT) {
+    const float2 pz = *(const float2*)(zh + (bh * (size_t)N + piv[2 * g0]) * RB_HD + 2 * lane);
+    v0 = pz.x;
+    v1 = pz.y;
+  } else {
+    v0 = (float)cen[g0 * RB_HD + 2 * lane];
+    v1 = (float)cen[g0 * RB_HD + 2 * lane + 1];
+  }
+  const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
+  const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
+  const int mu = (lane >> 3) & 7;  // the row of each group of 8 rows whose sum this lane ends with
+  float mx = -1.f;
+#pragma unroll
+  for (int i0 = 0; i0 < 32; i0 += 8) {
+    uint32_t hv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = __builtin_amdgcn_readlane(myrow, i0 + u);
+      hv[u] = *(const uint32_t*)(zlb + (size_t)r * RB_HD + 2 * lane);
+    }
+    float d[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[u] & 0xFFFFu));
+      const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(hv[u] >> 16));
+      const float dx = x0 - v0, dy = x1 - v1;
+      d[u] = dx * dx + dy * dy;
+    }
+    const float t = rb_wave_sum8(d, lane);
+    const int pos = wave + 4 * (i0 + mu);
+    if (pos < cnt) {
+      if ((lane & 7) == 0) dt[bh * N + p0 + pos] = t;
+      mx = fmaxf(mx, t);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) wm[wave] = mx;
+  __syncthreads();
+  if (tid == 0) best_t[bh * nb + c] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+}
+
+// Stage two, one workgroup of 4 wavefronts per group slot: the group's
+// largest float16 distance over its slices, the positions whose float16
+// distance is within 2 RB_FAR_EPS of it, and for those rows the float64
+// squared distance from the float32 z (lane l coordinates 2 l and 2 l + 1,
+// summed over the wavefront lane ^ 32 first, then ^ 16, ..., ^ 1, eight rows
+// per exchange sequence with their loads in flight together); the farthest,
+// lowest row on ties, is pivot WHICH (0: a, from the centroid; 1: b, from a)
+// of the group.  At 2K 5s the band holds about 250 rows at the root (its
+// 1,024 random conditioning rows lie at nearly one distance), a few below.
+template <int WHICH>
+__global__ __launch_bounds__(256) void rb_pivot_kernel(const float* __restrict__ zh, const int32_t* __restrict__ pin,
+                                                       const double* __restrict__ cen, const float* __restrict__ dt,
+                                                       const double* __restrict__ best_t, int32_t* __restrict__ piv,
+                                                       int N, int nb, int level) {
+  __shared__ int cand[RB_CAND];
+  __shared__ int ncand;
+  __shared__ float wm[4];
+  __shared__ double wt[4];
+  __shared__ int wr[4];
+  const int ng = 1 << level;
+  const int gi = blockIdx.x % ng;
+  const size_t bh = blockIdx.x / ng;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int s, n, sp;
+  if (!rb_locate(N, level, gi, s, n, sp)) return;
+  if (n <= RB_BLK) return;
+  const int c0 = s / RB_BLK, m = (n + RB_BLK - 1) / RB_BLK;
+  const size_t g0 = bh * nb + c0;
+  if (tid == 0) ncand = 0;
+  float mx = -1.f;
+  for (int j = tid; j < m; j += 256) mx = fmaxf(mx, (float)best_t[g0 + j]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) wm[wave] = mx;
+  __syncthreads();
+  const float thr = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])) - 2.f * RB_FAR_EPS;
+  const float* dg = dt + bh * N + s;
+  for (int j = tid; j < n; j += 256)
+    if (dg[j] >= thr) {
+      const int x = atomicAdd(&ncand, 1);
+      if (x < RB_CAND) cand[x] = j;
+    }
+  __syncthreads();
+  const int nc = ncand;
   const float* zb = zh + bh * (size_t)N * RB_HD;
   double v0, v1;
-  if (FROM_PIVOT) {
+  if (WHICH == 1) {
     const float2 pz = *(const float2*)(zb + (size_t)piv[2 * g0] * RB_HD + 2 * lane);
     v0 = pz.x;
     v1 = pz.y;
@@ -547,18 +666,21 @@ __global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ z
     v0 = cen[g0 * RB_HD + 2 * lane];
     v1 = cen[g0 * RB_HD + 2 * lane + 1];
   }
-  const int p0 = c * RB_BLK, cnt = min(RB_BLK, N - p0);
-  const int myrow = pin[bh * N + p0 + min(wave + 4 * (lane & 31), cnt - 1)];
-  const int mu = (lane >> 3) & 7;  // the row of each group of 8 rows whose sum this lane ends with
   double bt = -1.0;
   int br = 0x7fffffff;
-#pragma unroll
-  for (int i0 = 0; i0 < 32; i0 += 8) {
-    float2 v[8];
+  const int mu = (lane >> 3) & 7;  // the row of each batch of 8 whose sum this lane ends with
+  // rows x0 .. x0 + 7 of the list (the candidates, or every position of the
+  // group when there are too many): lane u < 8 fetches the row of item x0 + u
+  const bool all = nc > RB_CAND;
+  const int items = all ? n : nc;
+  for (int x0 = 8 * wave; x0 < items; x0 += 32) {
+    const int xi = min(x0 + (lane & 7), items - 1);
+    const int myrow = pin[bh * N + s + (all ? xi : cand[xi])];
     int r[8];
+    float2 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      r[u] = __builtin_amdgcn_readlane(myrow, i0 + u);
+      r[u] = __builtin_amdgcn_readlane(myrow, u);
       v[u] = *(const float2*)(zb + (size_t)r[u] * RB_HD + 2 * lane);
     }
     double d[8];
@@ -571,12 +693,12 @@ __global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ z
     int rm = r[0];
 #pragma unroll
     for (int u = 1; u < 8; ++u) rm = mu == u ? r[u] : rm;
-    if (wave + 4 * (i0 + mu) < cnt && rb_better(t, rm, bt, br)) {
+    if (x0 + mu < items && rb_better(t, rm, bt, br)) {
       bt = t;
       br = rm;
     }
   }
-  // the wavefront's farthest row: a total order, so any pairing gives it
+  // the wavefront's farthest: a total order, so any pairing gives it
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const double ot = __shfl_xor(bt, off, 64);
@@ -597,47 +719,10 @@ __global__ __launch_bounds__(256) void rb_far_kernel(const float* __restrict__ z
         bt = wt[w];
         br = wr[w];
       }
-    best_t[bh * nb + c] = bt;
-    best_r[bh * nb + c] = br;
+    // a row of the head even if no distance compared as a number (non-finite
+    // inputs), so that later reads stay inside z
+    piv[2 * g0 + WHICH] = min(max(br, 0), N - 1);
   }
-}
-
-// One wavefront per group slot: the farthest row over the group's slices
-// (lowest row on ties), written as pivot WHICH (0: a, 1: b) of the group.
-template <int WHICH>
-__global__ __launch_bounds__(64) void rb_pivot_kernel(const double* __restrict__ best_t,
-                                                      const int32_t* __restrict__ best_r,
-                                                      int32_t* __restrict__ piv, int N, int nb, int level) {
-  const int ng = 1 << level;
-  const int gi = blockIdx.x % ng;
-  const size_t bh = blockIdx.x / ng;
-  const int lane = threadIdx.x;
-  int s, n, sp;
-  if (!rb_locate(N, level, gi, s, n, sp)) return;
-  if (n <= RB_BLK) return;
-  const int c0 = s / RB_BLK, m = (n + RB_BLK - 1) / RB_BLK;
-  double bt = -1.0;
-  int br = 0x7fffffff;
-  for (int j = lane; j < m; j += 64) {
-    const double t = best_t[bh * nb + c0 + j];
-    const int r = best_r[bh * nb + c0 + j];
-    if (rb_better(t, r, bt, br)) {
-      bt = t;
-      br = r;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const double ot = __shfl_xor(bt, off, 64);
-    const int orr = __shfl_xor(br, off, 64);
-    if (rb_better(ot, orr, bt, br)) {
-      bt = ot;
-      br = orr;
-    }
-  }
-  // a row of the head even if no distance compared as a number (non-finite
-  // inputs), so that later reads stay inside z
-  if (lane == 0) piv[2 * (bh * nb + c0) + WHICH] = min(max(br, 0), N - 1);
 }
 
 // One workgroup of 4 wavefronts per (slice, batch x head): the split key of
@@ -1006,7 +1091,7 @@ struct RbGeom {
 };
 
 struct RbLayout {
-  size_t part, msum, ltw, zh, keys, perm, stats, tot, cen, best_t, best_r, piv, total;
+  size_t part, msum, ltw, zh, zl, dt, keys, perm, stats, tot, cen, best_t, piv, total;
 };
 
 size_t rb_align(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1046,6 +1131,10 @@ RbLayout rb_layout(const RbGeom& g) {
   off = rb_align(off + (size_t)g.BH * 3 * RB_HD * RB_HD * sizeof(uint16_t));
   w.zh = off;
   off = rb_align(off + (size_t)g.BH * g.N * RB_HD * sizeof(float));
+  w.zl = off;  // z as float16
+  off = rb_align(off + (size_t)g.BH * g.N * RB_HD * sizeof(uint16_t));
+  w.dt = off;  // each position's float16 distance from the current reference
+  off = rb_align(off + (size_t)g.BH * g.N * sizeof(float));
   w.keys = off;
   off = rb_align(off + (size_t)g.BH * g.N * sizeof(uint32_t));
   w.perm = off;
@@ -1056,10 +1145,8 @@ RbLayout rb_layout(const RbGeom& g) {
   off = rb_align(off + 2 * (size_t)g.BH * g.nb * RB_HD * sizeof(double));
   w.cen = off;  // group centroids
   off = rb_align(off + (size_t)g.BH * g.nb * RB_HD * sizeof(double));
-  w.best_t = off;  // each slice's farthest row: distance and row
+  w.best_t = off;  // each slice's largest float16 distance
   off = rb_align(off + (size_t)g.BH * g.nb * sizeof(double));
-  w.best_r = off;
-  off = rb_align(off + (size_t)g.BH * g.nb * sizeof(int32_t));
   w.piv = off;  // each group's two pivot rows
   off = rb_align(off + (size_t)g.BH * g.nb * 2 * sizeof(int32_t));
   w.total = off;
@@ -1097,6 +1184,8 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
   float* part = (float*)(ws + w.part);
   uint16_t* ltw = (uint16_t*)(ws + w.ltw);
   float* zh = (float*)(ws + w.zh);
+  uint16_t* zl = (uint16_t*)(ws + w.zl);
+  float* dt = (float*)(ws + w.dt);
   uint32_t* keys = (uint32_t*)(ws + w.keys);
   int32_t* tmp = (int32_t*)(ws + w.perm);
   // level l reads buf[l % 2] and writes buf[(l + 1) % 2]; the last level
@@ -1111,14 +1200,13 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
   hipLaunchKernelGGL(rb_factor_kernel, dim3((unsigned)g.BH), dim3(1024), 0, s, (const double*)msum, ltw);
   const int ntile = (N + EM_ROWS - 1) / EM_ROWS;
   hipLaunchKernelGGL(rb_embed_kernel, dim3((unsigned)(g.BH * ntile)), dim3(64 * EM_WAVES), 0, s, (const uint16_t*)q,
-                     (const uint16_t*)ltw, zh, buf[0], N, ntile);
+                     (const uint16_t*)ltw, zh, zl, buf[0], N, ntile);
   double* stats = (double*)(ws + w.stats);
   // level l writes its groups' totals to tot[l % 2] and reads its parents'
   // from tot[(l + 1) % 2]
   double* tot[2] = {(double*)(ws + w.tot), (double*)(ws + w.tot) + (size_t)g.BH * g.nb * RB_HD};
   double* cen = (double*)(ws + w.cen);
   double* best_t = (double*)(ws + w.best_t);
-  int32_t* best_r = (int32_t*)(ws + w.best_r);
   int32_t* piv = (int32_t*)(ws + w.piv);
   const int nb = (int)g.nb;
   const dim3 slices((unsigned)(g.BH * nb));
@@ -1129,14 +1217,14 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
     hipLaunchKernelGGL(rb_stats_kernel, slices, dim3(256), 0, s, (const float*)zh, pin, stats, N, nb, l);
     hipLaunchKernelGGL(rb_center_kernel, groups, dim3(RB_HD), 0, s, (const double*)stats,
                        (const double*)tot[(l + 1) & 1], tot[l & 1], cen, N, nb, l);
-    hipLaunchKernelGGL(rb_far_kernel<false>, slices, dim3(256), 0, s, (const float*)zh, pin, (const double*)cen,
-                       (const int32_t*)piv, best_t, best_r, N, nb, l);
-    hipLaunchKernelGGL(rb_pivot_kernel<0>, groups, dim3(64), 0, s, (const double*)best_t, (const int32_t*)best_r,
-                       piv, N, nb, l);
-    hipLaunchKernelGGL(rb_far_kernel<true>, slices, dim3(256), 0, s, (const float*)zh, pin, (const double*)cen,
-                       (const int32_t*)piv, best_t, best_r, N, nb, l);
-    hipLaunchKernelGGL(rb_pivot_kernel<1>, groups, dim3(64), 0, s, (const double*)best_t, (const int32_t*)best_r,
-                       piv, N, nb, l);
+    hipLaunchKernelGGL(rb_far16_kernel<false>, slices, dim3(256), 0, s, (const uint16_t*)zl, (const float*)zh, pin,
+                       (const double*)cen, (const int32_t*)piv, dt, best_t, N, nb, l);
+    hipLaunchKernelGGL(rb_pivot_kernel<0>, groups, dim3(256), 0, s, (const float*)zh, pin, (const double*)cen,
+                       (const float*)dt, (const double*)best_t, piv, N, nb, l);
+    hipLaunchKernelGGL(rb_far16_kernel<true>, slices, dim3(256), 0, s, (const uint16_t*)zl, (const float*)zh, pin,
+                       (const double*)cen, (const int32_t*)piv, dt, best_t, N, nb, l);
+    hipLaunchKernelGGL(rb_pivot_kernel<1>, groups, dim3(256), 0, s, (const float*)zh, pin, (const double*)cen,
+                       (const float*)dt, (const double*)best_t, piv, N, nb, l);
     hipLaunchKernelGGL(rb_keys_kernel, slices, dim3(256), 0, s, (const float*)zh, pin, (const int32_t*)piv, keys, N,
                        nb, l);
     // largest group at this level: 128 ceil(nb / 2^l) rows

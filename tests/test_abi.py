@@ -244,13 +244,14 @@ def test_reblock_entry_points_validate():
     big = 1 << 40
     p = bsa.make_problem(1, 2, 4096, top_k=8)
     # workspace: float32 chunk moments, M (float64), the three terms of L,
-    # z (float32), keys, an order buffer, float64 slice sums, float64 group
-    # totals of two levels and group centroids, each slice's farthest row
-    # (distance, row) and each group's two pivots
+    # z (float32 and float16), each position's float16 distance, keys, an
+    # order buffer, float64 slice sums, float64 group totals of two levels and
+    # group centroids, each slice's largest float16 distance and each group's
+    # two pivots
     n = bsa.bsa_reblock_workspace_bytes(p)
-    expect = (2 * 2 * 128 * 128 * 4 + 2 * 128 * 128 * 8 + 2 * 3 * 128 * 128 * 2 + 2 * 4096 * 128 * 4
-              + 2 * 2 * 4096 * 4 + 4 * 2 * 32 * 128 * 8 + 2 * 32 * (8 + 4 + 2 * 4))
-    assert expect <= n <= expect + 12 * 256
+    expect = (2 * 2 * 128 * 128 * 4 + 2 * 128 * 128 * 8 + 2 * 3 * 128 * 128 * 2 + 2 * 4096 * 128 * (4 + 2)
+              + 2 * 4096 * 4 + 2 * 2 * 4096 * 4 + 4 * 2 * 32 * 128 * 8 + 2 * 32 * (8 + 2 * 4))
+    assert expect <= n <= expect + 13 * 256
     assert L.bsa_reblock(ctypes.byref(p), None, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_reblock(ctypes.byref(p), fake, fake, None, fake, big, None) == bsa.BSA_ERR_INVALID
     assert L.bsa_reblock(ctypes.byref(p), odd, fake, fake, fake, big, None) == bsa.BSA_ERR_INVALID
