@@ -214,23 +214,51 @@ __global__ __launch_bounds__(1024) void rb_factor_kernel(const double* __restric
   // a step: step j subtracts A[i][j] A[c][j] / d_j from every entry (i, c),
   // j < c <= i, with d_j = A[j][j] (held at the ridge when float32 rounding
   // of M pushed it below); L[j][j] = sqrt(d_j), L[i][j] = A[i][j] / sqrt(d_j).
-  // Entry x of the rows below j, counted row by row, is (i, c) with
-  // x = i (i + 1) / 2 + c, c <= i.
-  for (int j = 0; j < RB_HD; ++j) {
-    const double dj = fmax(A[j][j], ridge);
-    if (tid == 0) piv[j] = dj;
-    const double inv = 1.0 / dj;
-    const int nr = RB_HD - 1 - j;
-    const int tot = nr * (nr + 1) / 2;
-    for (int x = tid; x < tot; x += 1024) {
-      int i = (int)((sqrtf(8.0f * (float)x + 1.0f) - 1.0f) * 0.5f);
+  // Thread t keeps the entries x = t + 1024 u of the lower triangle (x = i
+  // (i + 1) / 2 + c, c <= i) in registers; column j + 1, once step j has
+  // updated it, goes through LDS (two buffers by step parity), which is all
+  // that step j + 1 reads.
+  constexpr int NTRI = RB_HD * (RB_HD + 1) / 2, PER = (NTRI + 1023) / 1024;
+  __shared__ double col[2][RB_HD];
+  double a[PER];
+  int ei[PER], ec[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int x = tid + 1024 * u;
+    int i = 0, c = 0;
+    if (x < NTRI) {
+      i = (int)((sqrtf(8.0f * (float)x + 1.0f) - 1.0f) * 0.5f);
       if ((i + 1) * (i + 2) / 2 <= x) ++i;
       if (i * (i + 1) / 2 > x) --i;
-      const int c = x - i * (i + 1) / 2;
-      A[j + 1 + i][j + 1 + c] -= A[j + 1 + i][j] * A[j + 1 + c][j] * inv;
+      c = x - i * (i + 1) / 2;
+    }
+    ei[u] = x < NTRI ? i : -1;  // -1: no entry
+    ec[u] = c;
+    a[u] = x < NTRI ? A[i][c] : 0.0;
+    if (x < NTRI && c == 0) col[0][i] = a[u];
+  }
+  __syncthreads();
+  for (int j = 0; j < RB_HD; ++j) {
+    const double* cj = col[j & 1];
+    double* cn = col[(j + 1) & 1];
+    const double dj = fmax(cj[j], ridge);
+    if (tid == 0) piv[j] = dj;
+    const double inv = 1.0 / dj;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = ei[u], c = ec[u];
+      if (c > j) {  // and so i >= c > j (entries without one have i = -1, c = 0)
+        a[u] -= cj[i] * cj[c] * inv;
+        if (c == j + 1) cn[i] = a[u];
+      }
     }
     __syncthreads();
   }
+  // the final values back to LDS for the output
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (ei[u] >= 0) A[ei[u]][ec[u]] = a[u];
+  __syncthreads();
   if (tid < RB_HD) piv[tid] = sqrt(piv[tid]);
   __syncthreads();
   uint16_t* lb = ltw + bh * 3 * (size_t)RB_HD * RB_HD;
