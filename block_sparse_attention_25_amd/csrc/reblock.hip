@@ -676,12 +676,19 @@ __global__ __launch_bounds__(256) void rb_pivot_kernel(const float* __restrict__
   if (lane == 0) wm[wave] = mx;
   __syncthreads();
   const float thr = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])) - 2.f * RB_FAR_EPS;
+  // eight loads in flight per thread; a position is listed once
   const float* dg = dt + bh * N + s;
-  for (int j = tid; j < n; j += 256)
-    if (dg[j] >= thr) {
-      const int x = atomicAdd(&ncand, 1);
-      if (x < RB_CAND) cand[x] = j;
-    }
+  for (int j0 = tid; j0 < n; j0 += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = dg[min(j0 + 256 * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + 256 * u < n && v[u] >= thr) {
+        const int x = atomicAdd(&ncand, 1);
+        if (x < RB_CAND) cand[x] = j0 + 256 * u;
+      }
+  }
   __syncthreads();
   const int nc = ncand;
   const float* zb = zh + bh * (size_t)N * RB_HD;
