@@ -200,12 +200,14 @@ def test_reblock_rejects_position_options(torch_cuda):
     bsa.attention(q, k, v, top_k=2, summary="reweight", anchor_rows=1000, reblock=True)
 
 
-def test_reblock_all_zero_inputs(torch_cuda):
+@pytest.mark.parametrize("N", [1500, 5000])
+def test_reblock_all_zero_inputs(torch_cuda, N):
     # zero keys leave only the ridge and zero queries embed to zero: every
     # split value ties, so the order is the identity; every logit is 0 (the
-    # selection ties too: the three lowest blocks)
+    # selection ties too: the three lowest blocks).  Every distance ties as
+    # well, so every row of a group lies in the pivot search's band: at 5,000
+    # rows more than its list holds, and the whole group is measured exactly
     torch = torch_cuda
-    N = 1500
     qb = np.zeros((1, 1, N, 128), dtype=np.uint16)
     _, _, vb = generate(custom(N, heads=1, seed=68), threads=1)
     host, perm = _run_reblocked(torch, qb, qb, vb, top_k=3)
