@@ -293,6 +293,10 @@ __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t*
                                                                  int32_t* __restrict__ order0, int N,
                                                                  int ntile) {
   __shared__ __attribute__((aligned(16))) uint16_t lb[3 * RB_HD * RB_HD];
+  // each wavefront's output, 32 rows x 32 coordinates at a time, so that the
+  // stores write whole 128-byte pieces of rows (16-byte chunk c of row r at
+  // chunk c ^ (r & 7))
+  __shared__ __attribute__((aligned(16))) float4 stage[EM_WAVES][32 * 8];
   const int tile = blockIdx.x % ntile;
   const size_t bh = blockIdx.x / ntile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -347,19 +351,28 @@ __global__ __launch_bounds__(64 * EM_WAVES) void rb_embed_kernel(const uint16_t*
       for (int e = 0; e < 16; ++e) ss += acc[mt][e] * acc[mt][e];
     ss += __shfl_xor(ss, 32, 64);
     const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
-    const int row = row0 + 32 * t + ln;
-    if (row < N) {
-      float* zr = zb + (size_t)row * RB_HD + 4 * g;
-      uint16_t* zlr = zlb + (size_t)row * RB_HD + 4 * g;
+    // coordinates 32 mt + [0, 32) of the tile's rows through the wavefront's
+    // stage: lane (ln, g) puts its chunks 2 j + g of row ln, then lane l
+    // takes chunk l % 8 of rows 8 k + l / 8 and stores it (float32 and float16)
+    float4* st = stage[wave];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 f = make_float4(acc[mt][4 * j] * inv, acc[mt][4 * j + 1] * inv, acc[mt][4 * j + 2] * inv,
-                                       acc[mt][4 * j + 3] * inv);
-          *(float4*)(zr + 32 * mt + 8 * j) = f;
-          *(uint2*)(zlr + 32 * mt + 8 * j) = make_uint2(rb_half2(f.x, f.y), rb_half2(f.z, f.w));
+      for (int j = 0; j < 4; ++j)
+        st[ln * 8 + ((2 * j + g) ^ (ln & 7))] = make_float4(acc[mt][4 * j] * inv, acc[mt][4 * j + 1] * inv,
+                                                          acc[mt][4 * j + 2] * inv, acc[mt][4 * j + 3] * inv);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3), c = lane & 7;
+        const float4 f = st[r * 8 + (c ^ (r & 7))];
+        const int row = row0 + 32 * t + r;
+        if (row < N) {
+          *(float4*)(zb + (size_t)row * RB_HD + 32 * mt + 4 * c) = f;
+          *(uint2*)(zlb + (size_t)row * RB_HD + 32 * mt + 4 * c) = make_uint2(rb_half2(f.x, f.y), rb_half2(f.z, f.w));
         }
+      }
+      __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) bq[s] = bn[s];
