@@ -224,14 +224,15 @@ def test_threshold_selection(torch_cuda, N, top_k, tau, sink, summary):
                     sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau)
 
 
-@pytest.mark.parametrize("N", [140000, 166000])
+@pytest.mark.parametrize("N", [140000, 159900, 166000])
 @pytest.mark.parametrize("variant", ["plain", "ties", "sinks", "threshold"])
 def test_many_blocks_selection(torch_cuda, variant, N):
     """The selection's large-row forms at 1,094 blocks (short last block): the
     float64 matrix scores, with the high key halves in LDS for top-k and the
-    float64 rows of one 16-wavefront workgroup for the threshold; at 1,297
-    blocks the row-split float64 VALU scores.  Every index of the head
-    against the oracle, and sampled query blocks."""
+    float64 rows of one 16-wavefront workgroup for the threshold; at 1,250
+    blocks the high-half kernel for top-k and the row-split float64 VALU
+    scores for the threshold; at 1,297 blocks the VALU scores for all.  Every
+    index of the head against the oracle, and sampled query blocks."""
     _log("case many blocks %s N=%d" % (variant, N))
     nb = O.n_blocks(N)
     w = custom(N, heads=1, seed=17)
