@@ -635,8 +635,10 @@ def test_full_size_workloads(torch_cuda, name, heads):
     the oracle's float64 ranking (tie zone aside), one query block compared
     element-wise (a different one per head, so the launch's whole grid map is
     sampled; with extra tokens its token row too), and no NaN left anywhere.
-    The heads listed also get the first, second, middle, last-but-one and
-    short last query blocks.  Prints the worst output error of the workload."""
+    The first head listed is compared in every query block (its whole output
+    and, with extra tokens, every token row); the others listed also get the
+    first, second, middle, last-but-one and short last query blocks.  Prints
+    the worst output error of the workload."""
     torch = torch_cuda
     w = WORKLOADS[name]
     _log("case full %s (H=%d N=%d)" % (name, w.heads, w.seq_len))
@@ -662,7 +664,7 @@ def test_full_size_workloads(torch_cuda, name, heads):
         sampled = sorted(set(sampled + [sinks[0] - 1, sinks[0]]))  # last video block, first sink block
     worst_max, worst_mean, ties = 0.0, 0.0, 0
     for h in range(w.heads):
-        qbs = sorted(set([(7 * h + 3) % nb] + (sampled if h in heads else [])))
+        qbs = None if h == heads[0] else sorted(set([(7 * h + 3) % nb] + (sampled if h in heads else [])))
         t, mx, mean = _check_head(host, qb, kb, vb, 0, h, top_k, w.summary,
                                   w.anchor_rows if w.summary == "reweight" else 0, query_blocks=qbs,
                                   label=name, sink_start=w.sink_start, sink_rows=w.sink_rows, tau=w.tau,
