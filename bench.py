@@ -42,7 +42,30 @@ def parse():
                     help="approximate budget of the oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-gemm-ref", action="store_true",
+                    help="skip the dense bf16 GEMM reference timed after the steps")
     return ap.parse_args()
+
+
+def gemm_reference(torch, dev, n=8192, iters=10):
+    """TFLOP/s of the vendor library's dense bf16 GEMM (torch.matmul, i.e.
+    hipBLASLt) at n^3 on random operands, timed after the steps on the same
+    device: context for the attention kernel's rate, since the clock a chip
+    holds under MFMA load differs from box to box.  Not part of the path."""
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    del c
+    return 2.0 * n ** 3 / (e0.elapsed_time(e1) / iters * 1e-3) / 1e12
 
 
 def measured_traffic(workload):
@@ -280,6 +303,8 @@ def main():
     sel_bytes = 2 * B * H * nb * 128 * 4 + B * H * nb * kk * 4
     tie_rows = tie_zone_rows(torch, q_pool, k_pool, kk, w.tau is None and w.sink_rows == 0)
 
+    gemm_tflops = None if args.no_gemm_ref else gemm_reference(torch, dev)
+
     if args.calib_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         bcopy = torch.empty_like(a)
@@ -330,6 +355,10 @@ def main():
                      "traffic": measured_traffic(w.name),
                      "traffic_unit": "bytes per launch (HBM, from rocprofv3 FETCH_SIZE + WRITE_SIZE)"},
         "peak_from_reported_clock": reported_clock_peak(),
+        **({"context_gemm": {"what": "torch.matmul bf16 8192^3 (hipBLASLt), same device, after the steps",
+                             "tflops": round(gemm_tflops, 1),
+                             "attention_over_gemm": round(attn_tflops / gemm_tflops, 4)}}
+           if gemm_tflops else {}),
         "input_gen_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:
