@@ -7,7 +7,8 @@ prefilled with NaN, and checks every head (every query block of short
 sequences, four of long ones) against the oracle as test_gpu_parity does.
 About one case in eight uses 129 to 140 heads, enough groups of 32 query
 blocks for the token selection to split its last dispatch round into parts.
-The draws are fixed by the seed, so every run checks the same cases.
+The draws are fixed by the seed, so every run checks the same cases.  A
+second test draws cases for the Spark-Reblock order.
 """
 import sys
 
@@ -63,3 +64,44 @@ def test_random_combinations(torch_cuda):
             for h in (range(heads) if heads <= 3 else [0, heads - 2, heads - 1]):
                 _check_head(host, qb, kb, vb, b, h, top_k, summary, anchor, query_blocks=qbs, label=label,
                             sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau, extra=extra)
+
+
+def _reblock_cases(seed=3, n=20):
+    rng = np.random.default_rng(seed)
+    for case in range(n):
+        N = int(rng.choice([1, 100, 128, 129, 255, 257, 1000, 2049, 3000, 4096, 5000, 9000, 20000, 33000]))
+        heads, batch = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        nb = O.n_blocks(N)
+        top_k = int(rng.integers(0, nb + 2))
+        summary = str(rng.choice(["mean", "reweight"]))
+        tau = None if rng.random() < 0.7 else float(rng.choice([0.5, 1.0]))
+        extra = 0 if rng.random() < 0.6 or top_k == 0 else int(rng.choice([1, 64, 256]))
+        yield case, N, batch, heads, top_k, summary, tau, extra
+
+
+def test_random_reblock_combinations(torch_cuda):
+    """The same on the Spark-Reblock order (no sinks or partial anchors, which
+    the reordered path rejects): every head's order against the oracle's
+    (exactly, away from near-ties), then the path's outputs on that order."""
+    from tests.parity import widen
+    from tests.test_gpu_reblock import _check_perm, _permuted, _run_reblocked
+    torch = torch_cuda
+    for case, N, batch, heads, top_k, summary, tau, extra in _reblock_cases():
+        label = "reblock case %d: N=%d B=%d H=%d top_k=%d %s tau=%s E=%d" % (
+            case, N, batch, heads, top_k, summary, tau, extra)
+        sys.stdout.write(label + "\n")
+        sys.stdout.flush()
+        w = custom(N, heads=heads, batch=batch, seed=2000 + case)
+        qb, kb, vb = generate(w, threads=16)
+        host, perm = _run_reblocked(torch, qb, kb, vb, top_k=top_k, summary=summary, tau=tau, extra_tokens=extra)
+        for b in range(batch):
+            for h in range(heads):
+                assert np.array_equal(np.sort(perm[b, h]), np.arange(N)), label
+                _check_perm(perm[b, h], widen(qb[b, h]), widen(kb[b, h]), "%s b%d h%d" % (label, b, h))
+        host_p, qp, kp, vp = _permuted(torch, host, perm, qb, kb, vb)
+        nb = O.n_blocks(N)
+        qbs = None if nb <= 40 else [0, nb // 2, nb - 1]
+        for b in range(batch):
+            for h in range(heads):
+                _check_head(host_p, qp, kp, vp, b, h, top_k, summary, 0, query_blocks=qbs, label=label,
+                            tau=tau, extra=extra)
