@@ -296,9 +296,23 @@ def attention(q, k, v, top_k=None, top_k_ratio=None, summary="mean", anchor_rows
     and an anchor over part of the rows.  Returns out
     [B, H, N, 128] bf16 (written into `out` when given: a contiguous bf16
     tensor of q's shape on its device, not overlapping q, k or v), plus a
-    dict of intermediate tensors when return_aux is set."""
+    dict of intermediate tensors when return_aux is set.  The calls run with
+    q's device current, on `stream` when given (a torch.cuda.Stream of that
+    device), else on the device's current stream; the outputs and scratch
+    tensors are allocated on that same stream, so torch's caching allocator
+    does not hand them to other work while its kernels still run."""
     import torch
     _check_qkv(q, k, v)
+    if stream is not None and stream.device != q.device:
+        raise ValueError("stream must belong to q's device")
+    with torch.cuda.device(q.device), torch.cuda.stream(stream):
+        return _attention(q, k, v, top_k, top_k_ratio, summary, anchor_rows, scale, sink_rows,
+                          sink_start, tau, extra_tokens, reblock, return_aux, stream, out)
+
+
+def _attention(q, k, v, top_k, top_k_ratio, summary, anchor_rows, scale, sink_rows, sink_start, tau,
+               extra_tokens, reblock, return_aux, stream, out):
+    import torch
     B, H, N, _ = q.shape
     p = make_problem(B, H, N, top_k, top_k_ratio, summary, anchor_rows, scale, sink_rows, sink_start,
                      tau, extra_tokens)
