@@ -1013,6 +1013,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   __shared__ float addv0[HT], addv1[HT];
   __shared__ uint32_t selmask[BSA_MAX_BLOCKS / 32];
   __shared__ int32_t sidx[BSA_MAX_BLOCKS];  // this query block's selected blocks
+  __shared__ int32_t tokl[BSA_MAX_EXTRA];    // this query block's extra tokens
 
   // Workgroup -> (b, h, position in the head's visiting order).  Workgroups
   // are dealt to the 8 XCDs round-robin.  With chunk = 0 each XCD takes a
@@ -1200,30 +1201,48 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 sA[2], sB[2];
   if (E > 0 && !dense_row) {
-    // Extra tokens first, 64 at a time: their K and V rows gathered into ks0
-    // and vs0 (the tile layout), then S^T = K Q^T, a softmax update with the
-    // exact max and O^T += V^T P^T.  The state (o, m_run, l_run) carries into
-    // the online softmax of the main loop.  ks1 holds the row's token list
-    // until the main loop's first loads.
-    int* tok = (int*)ks1;
+    // Extra tokens first, 64 at a time: their K and V rows gathered straight
+    // into LDS in the tile layout by the direct-to-LDS loads (each lane reads
+    // the row of its slot's token; the loads of group g + 1 fly while group g
+    // is computed, in the other buffer pair), then S^T = K Q^T, a softmax
+    // update with the exact max and O^T += V^T P^T.  The state (o, m_run,
+    // l_run) carries into the online softmax of the main loop.
     const int t_in = tid < E ? tok_idx[(bh * nb + r) * (size_t)E + tid] : -1;
-    tok[tid] = t_in;
+    tokl[tid] = t_in;
     const int nval = __syncthreads_count(t_in >= 0);  // valid tokens come first
-    const uint16_t* kb = k + bh * (size_t)N * HD;
-    const uint16_t* vb = v + bh * (size_t)N * HD;
-    for (int base = 0; base < nval; base += HT) {
-      // 16-byte chunk x = tid + 256 j is chunk x % 16 of gathered row x / 16
+    // byte offset of row i of the token list; past the valid tokens, the end
+    // of the buffer (those rows read as zeros)
+    const uint32_t past_end = (uint32_t)N * (HD * 2);
+    auto tok_off = [&](int i) { return i < nval ? (uint32_t)tokl[i] * (HD * 2) : past_end; };
+    // the slot -> (row, chunk) maps of the tile loads (see load_k1, load_v1)
+    const int krow0 = 16 * wave + (lane >> 4);
+    const uint32_t kxg = (uint32_t)(((lane & 15) ^ (lane >> 4)) * 16);
+    const int vrow0 = 16 * wave + 4 * ((lane >> 4) & 1) + ((lane >> 1) & 3);
+    const uint32_t vch = (uint32_t)((4 * (lane >> 5) + 2 * ((lane >> 3) & 1) + (lane & 1)) * 16);
+    auto gather = [&](int base, uint16_t* kd, uint16_t* vd) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int x = tid + 256 * j, row = x >> 4, ch = x & 15;
-        const int t = base + row < nval ? tok[base + row] : -1;
-        uint4 kd = make_uint4(0u, 0u, 0u, 0u), vd = kd;
-        if (t >= 0) {
-          kd = *(const uint4*)(kb + (size_t)t * HD + 8 * ch);
-          vd = *(const uint4*)(vb + (size_t)t * HD + 8 * ch);
-        }
-        *(uint4*)(ks0 + swz_k(row, ch)) = kd;
-        *(uint4*)(vs0 + 8 * vslot(row, ch)) = vd;
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(kd + (4 * wave + j) * 512), 16,
+                                                 (int)(tok_off(base + krow0 + 4 * j) + (kxg ^ (64u * j))), 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(vd + (4 * wave + j) * 512), 16,
+                                                 (int)(tok_off(base + vrow0 + 8 * (j >> 1)) + vch + 128u * (j & 1)),
+                                                 0, 0, 0);
+    };
+    const int ngroups = (nval + HT - 1) / HT;
+    if (ngroups > 0) gather(0, ks0, vs0);
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const int base = gi * HT;
+      const uint16_t* kc = (gi & 1) ? ks1 : ks0;
+      const uint16_t* vc = (gi & 1) ? vs1 : vs0;
+      if (gi + 1 < ngroups) {
+        // the next group into the pair the previous group read (free since
+        // the barrier that ended it); then wait for this group's 8 loads only
+        gather(base + HT, (gi & 1) ? ks0 : ks1, (gi & 1) ? vs0 : vs1);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       __syncthreads();
       // S^T: sA[mb] element ii is key base + 32 mb + 8 (ii / 4) + 4 g + ii % 4
@@ -1232,7 +1251,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         sA[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ld_bf16x8(ks0 + swz_k(32 * (i & 1) + ln, 2 * (i >> 1) + g)), qf[i >> 1], sA[i & 1], 0, 0, 0);
+            ld_bf16x8(kc + swz_k(32 * (i & 1) + ln, 2 * (i >> 1) + g)), qf[i >> 1], sA[i & 1], 0, 0, 0);
       float mx = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -1267,7 +1286,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_db(vs0, i & 3, i >> 2), pb[i >> 2], o[i & 3],
+        o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_db(vc, i & 3, i >> 2), pb[i >> 2], o[i & 3],
                                                            0, 0, 0);
       __syncthreads();
     }
