@@ -21,7 +21,7 @@ from tests.test_gpu_parity import _check_head, _run_gpu, torch_cuda  # noqa: F40
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 80
 LENGTHS = [1, 100, 128, 129, 257, 1000, 2049, 3000, 4096, 5000, 9000, 20000, 40000, 70000]
 
 
@@ -66,7 +66,7 @@ def test_random_combinations(torch_cuda):
                             sink_start=N - sink if sink else 0, sink_rows=sink, tau=tau, extra=extra)
 
 
-def _reblock_cases(seed=3, n=20):
+def _reblock_cases(seed=3, n=40):
     rng = np.random.default_rng(seed)
     for case in range(n):
         N = int(rng.choice([1, 100, 128, 129, 255, 257, 1000, 2049, 3000, 4096, 5000, 9000, 20000, 33000]))
