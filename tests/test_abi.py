@@ -115,6 +115,55 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(bsa.Problem) == 4 * len(fields) == 56
 
 
+def _declarations():
+    """name -> (return type, [parameter declarations]) for every function
+    include/bsa.h declares."""
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    out = {}
+    for m in re.finditer(r"([A-Za-z_][\w \t*]*?)\b(bsa_[a-z_]+)\s*\(([^)]*)\)\s*;", text):
+        params = " ".join(m.group(3).split())
+        out[m.group(2)] = (m.group(1).strip(), [] if params in ("", "void") else
+                           [x.strip() for x in params.split(",")])
+    return out
+
+
+def _c_kind(decl):
+    c = " ".join(decl.replace("const", " ").split())
+    if "*" in c:
+        return "ptr"
+    head = c.split()[0]
+    return {"size_t": "size", "int": "int", "int32_t": "int", "float": "float"}[head]
+
+
+def _ctypes_kind(t):
+    if t in (ctypes.c_void_p, ctypes.c_char_p) or (isinstance(t, type) and issubclass(t, ctypes._Pointer)):
+        return "ptr"
+    if t is ctypes.c_size_t:
+        return "size"
+    if t in (ctypes.c_int, ctypes.c_int32):
+        return "int"
+    if t is ctypes.c_float:
+        return "float"
+    raise AssertionError(t)
+
+
+def test_binding_signatures_match_header():
+    """Every declared function has ctypes argtypes and restype in the binding,
+    with the header's parameter count and, per position, the same kind
+    (pointer, size_t, int, float), so a changed declaration cannot drift
+    from the binding unnoticed."""
+    L = bsa.lib()
+    decls = _declarations()
+    assert len(decls) == len(_declared_functions())
+    for name, (ret, params) in decls.items():
+        fn = getattr(L, name)
+        assert fn.argtypes is not None, name
+        assert [_ctypes_kind(t) for t in fn.argtypes] == [_c_kind(x) for x in params], name
+        assert _ctypes_kind(fn.restype) == _c_kind(ret + (" x" if "*" not in ret else "")), name
+
+
 def test_sink_blocks_and_k():
     # 768p 5s: conditioning rows 36,288 .. 37,739 sit in blocks 283 .. 294
     p = _prob(seq_len=37740, heads=56, top_k=64, sink_rows=1452)
