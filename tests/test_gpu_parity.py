@@ -406,19 +406,25 @@ def test_all_zero_inputs(torch_cuda):
     assert not bool(host["out"].float().abs().gt(0).any())
 
 
-def test_large_logits(torch_cuda):
+@pytest.mark.parametrize("summary,extra,tau", [
+    ("mean", 0, None),
+    ("reweight", 0, None),   # the summary bias on top of large logits
+    ("mean", 64, None),      # exact-max extra-token groups, then the lazy running max
+    ("mean", 0, 1.0),        # threshold selection: rows of different lengths
+])
+def test_large_logits(torch_cuda, summary, extra, tau):
     """Q and K scaled up so logits span thousands: the softmax is close to
     one-hot; the online rescaling must match the oracle's max subtraction."""
-    _log("case large logits")
+    _log("case large logits %s E=%d tau=%s" % (summary, extra, tau))
     N = 1500
     w = custom(N, heads=2, seed=13)
     qb, kb, vb = generate(w)
     from block_sparse_attention_25_amd.synth import bf16_bits
     qb = bf16_bits((widen(qb) * 24.0).astype(np.float32))
     kb = bf16_bits((widen(kb) * 24.0).astype(np.float32))
-    host = _run_gpu(torch_cuda, qb, kb, vb, top_k=4)
+    host = _run_gpu(torch_cuda, qb, kb, vb, top_k=4, summary=summary, tau=tau, extra_tokens=extra)
     for h in range(2):
-        _check_head(host, qb, kb, vb, 0, h, 4, label="large")
+        _check_head(host, qb, kb, vb, 0, h, 4, summary, 0, label="large", tau=tau, extra=extra)
 
 
 def test_batch_and_heads(torch_cuda):
