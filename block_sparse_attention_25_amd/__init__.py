@@ -55,7 +55,10 @@ class Problem(ctypes.Structure):
 class BsaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__("%s: %s (status %d)" % (where, bsa_status_str(status), status))
+        msg = "%s: %s (status %d)" % (where, bsa_status_str(status), status)
+        if status == 4:
+            msg += ": " + lib().bsa_hip_error_str().decode()
+        super().__init__(msg)
 
 
 _lib = None
@@ -70,9 +73,15 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(library_path):
             raise ImportError("libbsa.so is not built (%s); build it with "
                               "python -m block_sparse_attention_25_amd.build" % library_path)
+        # torch ships its own HIP runtime under the same soname as the one
+        # the library links; loading torch first makes the process use that
+        # one runtime whichever module asks for the library first
+        import torch  # noqa: F401
         L = ctypes.CDLL(library_path)
         L.bsa_status_str.argtypes = [ctypes.c_int]
         L.bsa_status_str.restype = ctypes.c_char_p
+        L.bsa_hip_error_str.argtypes = []
+        L.bsa_hip_error_str.restype = ctypes.c_char_p
         L.bsa_problem_blocks.argtypes = [_P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         L.bsa_problem_blocks.restype = ctypes.c_int
         L.bsa_workspace_bytes.argtypes = [_P]

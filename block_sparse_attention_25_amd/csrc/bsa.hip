@@ -37,6 +37,11 @@
 
 #include "bsa.h"
 
+// the runtime error behind the last BSA_ERR_HIP on this thread (also set by
+// the reblock calls)
+static thread_local hipError_t last_hip_error = hipSuccess;
+void bsa_note_hip_error(hipError_t e) { last_hip_error = e; }
+
 namespace {
 
 constexpr int BLK = 128;  // tokens per block
@@ -2302,7 +2307,19 @@ int make_geometry(const bsa_problem* p, Geometry* g) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int launch_status() { return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
+// hipGetLastError reports the last failure of any runtime call on this thread,
+// also one made by other code in the process before this library was called.
+// Each entry point drops such an error before its launches, so the status it
+// returns is that of its own launches; the name of the last failure it saw is
+// kept per thread for bsa_hip_error_str.
+void drop_stale_error() { (void)hipGetLastError(); }
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return BSA_OK;
+  bsa_note_hip_error(e);
+  return BSA_ERR_HIP;
+}
 
 template <int NKT, int RB, bool ROWSPLIT>
 int launch_select(const Geometry& g, const float* q_pool, const float* k_pool, int32_t* block_idx,
@@ -2488,11 +2505,15 @@ const char* bsa_status_str(int status) {
     case BSA_ERR_INVALID: return "invalid argument";
     case BSA_ERR_UNSUPPORTED: return "unsupported problem (head_dim/block must be 128, nb <= 2048)";
     case BSA_ERR_WORKSPACE: return "workspace missing or too small";
-    case BSA_ERR_HIP: return "HIP launch failed";
+    case BSA_ERR_HIP: return "HIP launch failed (bsa_hip_error_str names the runtime's error)";
     case BSA_ERR_SCRATCH:
       return "problem too large for the static scratch of bsa_forward_noalloc (B*H*nb > 1048576)";
     default: return "unknown status";
   }
+}
+
+const char* bsa_hip_error_str(void) {
+  return last_hip_error == hipSuccess ? "none" : hipGetErrorName(last_hip_error);
 }
 
 int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff) {
@@ -2518,6 +2539,7 @@ int bsa_pool(const bsa_problem* p, const void* q, const void* k, const void* v, 
   if (st != BSA_OK) return st;
   if ((st = check_pool(g, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, workspace_bytes)) != BSA_OK)
     return st;
+  drop_stale_error();
   return launch_pool(g, nullptr, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, nullptr, nullptr,
                      (char*)workspace, (hipStream_t)hip_stream);
 }
@@ -2535,6 +2557,7 @@ int bsa_pool_reordered(const bsa_problem* p, const int32_t* perm, const void* q,
     return BSA_ERR_INVALID;
   if ((st = check_pool(g, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, workspace, workspace_bytes)) != BSA_OK)
     return st;
+  drop_stale_error();
   return launch_pool(g, perm, q, k, v, q_pool, k_pool, sum_k, sum_v, sum_bias, k_out, v_out, (char*)workspace,
                      (hipStream_t)hip_stream);
 }
@@ -2547,6 +2570,7 @@ int bsa_select(const bsa_problem* p, const float* q_pool, const float* k_pool, i
   if (g.k == 0) return BSA_OK;
   if (!q_pool || !k_pool || !block_idx) return BSA_ERR_INVALID;
   if (!aligned16(q_pool) || !aligned16(k_pool) || ((uintptr_t)block_idx & 3u)) return BSA_ERR_INVALID;
+  drop_stale_error();
   hipStream_t s = (hipStream_t)hip_stream;
   // key blocks per lane (top-k phase) sized to nb.  Scores on the float64
   // matrix cores while 16 score rows fit the LDS (nb <= 1200); past that the
@@ -2580,6 +2604,7 @@ int bsa_forward(const bsa_problem* p, const void* q, const void* k, const void* 
   if ((st = check_forward(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, workspace, workspace_bytes)) !=
       BSA_OK)
     return st;
+  drop_stale_error();
   return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, nullptr, nullptr, out,
                           (int32_t*)workspace, (hipStream_t)hip_stream);
 }
@@ -2593,8 +2618,10 @@ int bsa_forward_noalloc(const bsa_problem* p, const void* q, const void* k, cons
   if (g.E > 0) return BSA_ERR_INVALID;
   if ((st = check_forward(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, out, nullptr, 0)) != BSA_OK) return st;
   if ((size_t)(g.B * g.H * g.nb) > NOALLOC_ORDER_MAX) return BSA_ERR_SCRATCH;
+  drop_stale_error();
   int32_t* order = device_scratch();
   if (!order) return BSA_ERR_HIP;
+  drop_stale_error();
   return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, nullptr, nullptr, out, order,
                           (hipStream_t)hip_stream);
 }
@@ -2622,6 +2649,7 @@ int bsa_select_tokens(const bsa_problem* p, const float* q_pool, const void* k,
   uint64_t* pseg = (uint64_t*)(ws + tokens_seg_bytes(g));
   uint64_t* plist = (uint64_t*)((char*)pseg + align256(prow * TS_SEGS * SEG_CAP * sizeof(uint64_t)));
   int32_t* pcount = (int32_t*)((char*)plist + align256(prow * g.E * sizeof(uint64_t)));
+  drop_stale_error();
   hipLaunchKernelGGL(token_select_kernel, dim3((unsigned)(n_whole + tail * parts)), dim3(TS_THREADS), 0,
                      (hipStream_t)hip_stream, q_pool, (const uint16_t*)k, g.k > 0 ? block_idx : nullptr, token_idx,
                      (uint64_t*)workspace, pseg, plist, pcount, (int)g.N, (int)g.nb, (int)g.k, g.E,
@@ -2645,6 +2673,7 @@ int bsa_forward_tokens(const bsa_problem* p, const void* q, const void* k, const
       BSA_OK)
     return st;
   if (g.E > 0 && (!token_idx || ((uintptr_t)token_idx & 3u))) return BSA_ERR_INVALID;
+  drop_stale_error();
   return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, g.E > 0 ? token_idx : nullptr, nullptr,
                           out, (int32_t*)workspace, (hipStream_t)hip_stream);
 }
@@ -2663,6 +2692,7 @@ int bsa_forward_reordered(const bsa_problem* p, const int32_t* perm, const void*
     return st;
   if (out == q || out == k_r || out == v_r) return BSA_ERR_INVALID;
   if (g.E > 0 && (!token_idx || ((uintptr_t)token_idx & 3u))) return BSA_ERR_INVALID;
+  drop_stale_error();
   return launch_attention(g, q, k_r, v_r, sum_k, sum_v, sum_bias, block_idx, g.E > 0 ? token_idx : nullptr, perm,
                           out, nullptr, (hipStream_t)hip_stream);
 }

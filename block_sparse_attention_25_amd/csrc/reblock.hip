@@ -55,6 +55,9 @@
 
 #include "bsa.h"
 
+// keeps the runtime error behind a failed launch for bsa_hip_error_str (bsa.hip)
+void bsa_note_hip_error(hipError_t e);
+
 namespace {
 
 constexpr int RB_BLK = 128;    // rows per leaf
@@ -1203,7 +1206,12 @@ RbLayout rb_layout(const RbGeom& g) {
 
 bool rb_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int rb_status() { return hipGetLastError() == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
+int rb_status() {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return BSA_OK;
+  bsa_note_hip_error(e);
+  return BSA_ERR_HIP;
+}
 
 }  // namespace
 
@@ -1227,6 +1235,7 @@ int bsa_reblock(const bsa_problem* p, const void* q, const void* k, int32_t* per
   if (!rb_aligned16(q) || !rb_aligned16(k) || ((uintptr_t)perm & 3u)) return BSA_ERR_INVALID;
   const RbLayout w = rb_layout(g);
   if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return BSA_ERR_WORKSPACE;
+  (void)hipGetLastError();  // an error earlier code left pending is not this call's
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   float* part = (float*)(ws + w.part);
@@ -1306,6 +1315,7 @@ int bsa_permute_rows(const bsa_problem* p, const int32_t* perm, const void* q, c
       !rb_aligned16(k_out) || !rb_aligned16(v_out))
     return BSA_ERR_INVALID;
   const int ntile = (int)((g.N + 15) / 16);
+  (void)hipGetLastError();  // an error earlier code left pending is not this call's
   hipLaunchKernelGGL(rb_permute_kernel, dim3((unsigned)(g.BH * ntile)), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, perm, (uint16_t*)q_out,
                      (uint16_t*)k_out, (uint16_t*)v_out, (int)g.N, ntile);
@@ -1319,6 +1329,7 @@ int bsa_unpermute_rows(const bsa_problem* p, const int32_t* perm, const void* x,
   if (!perm || !x || !out) return BSA_ERR_INVALID;
   if (!rb_aligned16(x) || !rb_aligned16(out)) return BSA_ERR_INVALID;
   const int ntile = (int)((g.N + 15) / 16);
+  (void)hipGetLastError();  // an error earlier code left pending is not this call's
   hipLaunchKernelGGL(rb_unpermute_kernel, dim3((unsigned)(g.BH * ntile)), dim3(256), 0, (hipStream_t)stream,
                      (const uint16_t*)x, perm, (uint16_t*)out, (int)g.N, ntile);
   return rb_status();

@@ -112,6 +112,12 @@ enum { BSA_SELECT_TOPK = 0, BSA_SELECT_THRESHOLD = 1 };
 /* Text of a status code (static storage, never NULL). */
 const char* bsa_status_str(int status);
 
+/* Name of the HIP runtime error behind the last BSA_ERR_HIP that a call on
+ * this thread returned ("none" if there was none).  Static storage, never
+ * NULL.  Each launching call first drops a runtime error that earlier code
+ * on the thread left pending, so BSA_ERR_HIP always names its own launches. */
+const char* bsa_hip_error_str(void);
+
 /* Number of blocks per sequence and the effective k for a problem. */
 int bsa_problem_blocks(const bsa_problem* p, int32_t* n_blocks, int32_t* k_eff);
 

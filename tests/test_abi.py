@@ -42,6 +42,8 @@ def test_status_strings():
     for st in range(6):
         assert bsa.bsa_status_str(st) != "unknown status"
     assert bsa.bsa_status_str(99) == "unknown status"
+    # no launch has failed in this process
+    assert bsa.lib().bsa_hip_error_str().decode() == "none"
 
 
 def _prob(**kw):
