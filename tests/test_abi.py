@@ -38,6 +38,26 @@ def test_loaded_library_is_the_one_named():
     assert want in maps
 
 
+def test_one_hip_runtime_whichever_loads_first():
+    """torch ships its own HIP runtime (its libraries name it libamdhip64.so)
+    and the library links libamdhip64.so.7.  Loaded through the binding
+    before torch, the process must still map one runtime only: with two,
+    torch's streams and memory belong to a runtime the library's launches
+    do not use (a launch then fails on the GPU)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import block_sparse_attention_25_amd as b; b.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n" % ROOT)
+    env = dict(os.environ)
+    env.pop("BSA_LIBRARY", None)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip().splitlines()[-1] == "1"
+
+
 def test_status_strings():
     for st in range(6):
         assert bsa.bsa_status_str(st) != "unknown status"
