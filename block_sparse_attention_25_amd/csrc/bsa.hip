@@ -2485,11 +2485,23 @@ int32_t* scratch_ptr[NOALLOC_MAX_DEVICES] = {};
 // that device current), or nullptr on failure.
 int32_t* device_scratch() {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    bsa_note_hip_error(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) {
+    bsa_note_hip_error(hipErrorInvalidDevice);
+    return nullptr;
+  }
   std::lock_guard<std::mutex> lock(scratch_mutex);
   if (!scratch_ptr[dev]) {
     void* ptr = nullptr;
-    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      bsa_note_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
     scratch_ptr[dev] = (int32_t*)ptr;
   }
   return scratch_ptr[dev];
@@ -2621,7 +2633,6 @@ int bsa_forward_noalloc(const bsa_problem* p, const void* q, const void* k, cons
   drop_stale_error();
   int32_t* order = device_scratch();
   if (!order) return BSA_ERR_HIP;
-  drop_stale_error();
   return launch_attention(g, q, k, v, sum_k, sum_v, sum_bias, block_idx, nullptr, nullptr, out, order,
                           (hipStream_t)hip_stream);
 }
