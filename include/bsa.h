@@ -17,7 +17,9 @@
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     never allocates, frees or synchronises, and keeps no state between calls.
+ *     never allocates, frees or synchronises, and keeps no state between calls
+ *     (apart from the name of the last HIP error, per thread, for
+ *     bsa_hip_error_str).
  *   - Tensors are contiguous.  Q, K, V and out are [B, H, N, 128] bfloat16
  *     (raw 16-bit storage), row-major with the feature dimension fastest.
  *   - nb = ceil(N / 128); k = min(top_k, nb) without conditioning sinks, else
@@ -25,7 +27,10 @@
  *   - Arguments are validated on the host before anything is launched; on any
  *     error nothing is launched and no output is touched.
  *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
- *     the null stream).  A failed launch returns BSA_ERR_HIP.
+ *     the null stream).  A failed launch returns BSA_ERR_HIP.  Streams and
+ *     device memory must come from the HIP runtime the library is bound to:
+ *     a process that also loads torch's bundled runtime maps it before
+ *     this library, so that the library binds to that one runtime.
  *   - Results are bit-deterministic: no floating-point atomics.
  *   - Calls on one stream are ordered; the caller orders calls on different
  *     streams that share buffers.
